@@ -1,0 +1,158 @@
+"""CPU oracle for 3D Deformable Slide Attention (fp64).  TEST INFRASTRUCTURE ONLY.
+
+ctypes wrapper over oracle.c (see its header for the definition and the readings of
+the paper it follows).  Only the tests, the smoke check and the benchmark's CPU
+baseline import this package; the HIP library never does.
+
+Inputs are host numpy arrays: q/k/v/dout as float32, float64 or raw bf16 bits (uint16),
+[N][H][D] row-major; offsets int32 [N][3] (dt, dy, dx).  Outputs are float64.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIBPATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("F", ctypes.c_int), ("Hp", ctypes.c_int), ("Wp", ctypes.c_int),
+                ("H", ctypes.c_int), ("D", ctypes.c_int),
+                ("kt", ctypes.c_int), ("ky", ctypes.c_int), ("kx", ctypes.c_int),
+                ("scale", ctypes.c_double), ("dtype", ctypes.c_int)]
+
+
+def build():
+    tmp = _LIBPATH + ".tmp"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, _LIBPATH)
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIBPATH):
+            raise RuntimeError(f"{_LIBPATH} is missing: run __graft_entry__.build() first")
+        lib = ctypes.CDLL(_LIBPATH)
+        P, vp, i64, i32 = ctypes.POINTER(_Cfg), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_window_starts.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.oracle_forward.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        lib.oracle_forward_rows.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp]
+        lib.oracle_weights.argtypes = [P, vp, vp, vp, vp, i64, i32, vp, vp]
+        lib.oracle_weights.restype = ctypes.c_double
+        lib.oracle_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_backward_q_rows.argtypes = [P, vp, vp, vp, vp, vp, i64, vp, vp]
+        lib.oracle_backward_kv_rows.argtypes = [P, vp, vp, vp, vp, vp, i64, vp, vp, vp]
+        for f in ("oracle_window_starts", "oracle_forward", "oracle_forward_rows", "oracle_backward",
+                  "oracle_backward_q_rows", "oracle_backward_kv_rows"):
+            getattr(lib, f).restype = None
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(a):
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    if a.dtype == np.float64:
+        return 2
+    raise TypeError(f"oracle inputs are float32, float64 or bf16 bits (uint16), got {a.dtype}")
+
+
+def _cfg(q, grid, window, scale):
+    F, Hp, Wp = grid
+    kt, ky, kx = window
+    N, H, D = q.shape
+    assert N == F * Hp * Wp and D <= 256
+    return _Cfg(F, Hp, Wp, H, D, kt, ky, kx, float(scale), _dtype_code(q))
+
+
+def _c(a, dtype=None):
+    a = np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
+    return a
+
+
+def window_starts(offsets, grid, window):
+    off = _c(offsets, np.int32)
+    N = grid[0] * grid[1] * grid[2]
+    assert off.shape == (N, 3)
+    out = np.empty((N, 3), dtype=np.int32)
+    _load().oracle_window_starts(off.ctypes.data, *grid, *window, out.ctypes.data)
+    return out
+
+
+def forward(q, k, v, offsets, grid, window, scale):
+    """O [N][H][D] float64 and LSE [H][N] float64."""
+    q, k, v, off = _c(q), _c(k), _c(v), _c(offsets, np.int32)
+    cfg = _cfg(q, grid, window, scale)
+    N, H, D = q.shape
+    out = np.empty((N, H, D), dtype=np.float64)
+    lse = np.empty((H, N), dtype=np.float64)
+    _load().oracle_forward(ctypes.byref(cfg), q.ctypes.data, k.ctypes.data, v.ctypes.data, off.ctypes.data,
+                           out.ctypes.data, lse.ctypes.data)
+    return out, lse
+
+
+def forward_rows(q, k, v, offsets, grid, window, scale, rows):
+    """O and LSE for the rows r = n*H + h only: out [R][D], lse [R]."""
+    q, k, v, off = _c(q), _c(k), _c(v), _c(offsets, np.int32)
+    rows = _c(rows, np.int64)
+    cfg = _cfg(q, grid, window, scale)
+    out = np.empty((len(rows), q.shape[2]), dtype=np.float64)
+    lse = np.empty(len(rows), dtype=np.float64)
+    _load().oracle_forward_rows(ctypes.byref(cfg), q.ctypes.data, k.ctypes.data, v.ctypes.data, off.ctypes.data,
+                                len(rows), rows.ctypes.data, out.ctypes.data, lse.ctypes.data)
+    return out, lse
+
+
+def weights(q, k, v, offsets, grid, window, scale, n, h):
+    """(keys [K] int64, P [K] float64, lse) of one (query, head)."""
+    q, k, v, off = _c(q), _c(k), _c(v), _c(offsets, np.int32)
+    cfg = _cfg(q, grid, window, scale)
+    K = window[0] * window[1] * window[2]
+    keys = np.empty(K, dtype=np.int64)
+    p = np.empty(K, dtype=np.float64)
+    lse = _load().oracle_weights(ctypes.byref(cfg), q.ctypes.data, k.ctypes.data, v.ctypes.data, off.ctypes.data,
+                                 int(n), int(h), keys.ctypes.data, p.ctypes.data)
+    return keys, p, lse
+
+
+def backward(q, k, v, dout, offsets, grid, window, scale):
+    """dq, dk, dv [N][H][D] float64 (per-head scatter form)."""
+    q, k, v, do, off = _c(q), _c(k), _c(v), _c(dout), _c(offsets, np.int32)
+    assert do.dtype == q.dtype
+    cfg = _cfg(q, grid, window, scale)
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(q.shape, dtype=np.float64)
+    dv = np.empty(q.shape, dtype=np.float64)
+    _load().oracle_backward(ctypes.byref(cfg), q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+                            off.ctypes.data, dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    return dq, dk, dv
+
+
+def backward_q_rows(q, k, v, dout, offsets, grid, window, scale, rows):
+    q, k, v, do, off = _c(q), _c(k), _c(v), _c(dout), _c(offsets, np.int32)
+    rows = _c(rows, np.int64)
+    cfg = _cfg(q, grid, window, scale)
+    dq = np.empty((len(rows), q.shape[2]), dtype=np.float64)
+    _load().oracle_backward_q_rows(ctypes.byref(cfg), q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+                                   off.ctypes.data, len(rows), rows.ctypes.data, dq.ctypes.data)
+    return dq
+
+
+def backward_kv_rows(q, k, v, dout, offsets, grid, window, scale, rows):
+    """dk, dv for key rows r = j*H + h (key-centric gather form): [R][D] each."""
+    q, k, v, do, off = _c(q), _c(k), _c(v), _c(dout), _c(offsets, np.int32)
+    rows = _c(rows, np.int64)
+    cfg = _cfg(q, grid, window, scale)
+    dk = np.empty((len(rows), q.shape[2]), dtype=np.float64)
+    dv = np.empty((len(rows), q.shape[2]), dtype=np.float64)
+    _load().oracle_backward_kv_rows(ctypes.byref(cfg), q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                    do.ctypes.data, off.ctypes.data, len(rows), rows.ctypes.data, dk.ctypes.data,
+                                    dv.ctypes.data)
+    return dk, dv
