@@ -1,0 +1,253 @@
+// Window starts and the query bucketing shared by the forward and backward passes.
+//
+// Every query's window start (the clamped, offset-shifted window of the 3D
+// Deformable Slide Attention section) is turned into a start cell of the lattice
+// (F-kt+1) x (Hp-ky+1) x (Wp-kx+1).  Queries are then stably sorted by cell (LSD
+// radix sort, ascending query id inside a cell), which gives
+//   - cell_ptr: the CSR of queries per start cell, walked in a fixed order by the
+//     key-centric dK/dV pass (deterministic, no atomics on values);
+//   - groups: up to 16 queries of one 1 x 4 x 4 start blob; the queries of a
+//     group have windows inside a kt x (ky+3) x (kx+3) box, so they share most of
+//     their keys.
+#include "internal.hpp"
+
+namespace dsa3d {
+
+Geom make_geom(int F, int Hp, int Wp, int H, int kt, int ky, int kx) {
+  Geom g;
+  g.F = F; g.Hp = Hp; g.Wp = Wp;
+  g.kt = kt; g.ky = ky; g.kx = kx;
+  g.Lt = F - kt + 1; g.Ly = Hp - ky + 1; g.Lx = Wp - kx + 1;
+  g.nby = (g.Ly + BLOB_Y - 1) / BLOB_Y;
+  g.nbx = (g.Lx + BLOB_X - 1) / BLOB_X;
+  g.H = H;
+  g.N = F * Hp * Wp;
+  g.nblobs = g.Lt * g.nby * g.nbx;
+  g.keyspace = g.nblobs * BLOB_CELLS;
+  return g;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Carves the workspace (base may be null to only size it).  Returns its size.
+size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
+  const size_t N = (size_t)g.N;
+  const int rb = (int)((N + RADIX_TILE - 1) / RADIX_TILE);
+  int bits = 1;
+  while ((1u << bits) < (uint32_t)g.keyspace) ++bits;
+  const int passes = (bits + 7) / 8;
+  const int max_groups = g.N / GROUP_Q + g.nblobs + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* ptr = base ? base + off : nullptr;
+    off += align256(bytes);
+    return ptr;
+  };
+  Prep q;
+  q.starts = (int4*)take(N * sizeof(int4));
+  q.keys[0] = (uint32_t*)take(N * 4);
+  q.keys[1] = (uint32_t*)take(N * 4);
+  q.vals[0] = (int*)take(N * 4);
+  q.vals[1] = (int*)take(N * 4);
+  q.ghist = (uint32_t*)take((size_t)256 * rb * 4);
+  q.cell_ptr = (int*)take(((size_t)g.keyspace + 1) * 4);
+  q.goff = (int*)take(((size_t)g.nblobs + 1) * 4);
+  q.groups = (int2*)take((size_t)max_groups * sizeof(int2));
+  q.ngroups = (int*)take(4);
+  q.delta = backward ? (float*)take(N * g.H * 4) : nullptr;
+  q.perm = q.vals[passes & 1];
+  q.radix_blocks = rb;
+  q.radix_passes = passes;
+  q.max_groups = max_groups;
+  if (p) *p = q;
+  return off;
+}
+
+// ---- window starts ----------------------------------------------------------
+
+__device__ __forceinline__ int clamp_start(int p, int o, int k, int G) {
+  // |o| > G moves the centre off the grid either way; clamping o first keeps the
+  // sum inside int32 and gives the same start.
+  o = min(max(o, -G), G);
+  const int s = p + o - (k - 1) / 2;
+  return min(max(s, 0), G - k);
+}
+
+__device__ __forceinline__ int4 query_start(const int32_t* off, const Geom& g, int n) {
+  const int plane = g.Hp * g.Wp;
+  const int t = n / plane, rem = n - t * plane, y = rem / g.Wp, x = rem - y * g.Wp;
+  int4 s;
+  s.x = clamp_start(t, off[3 * n + 0], g.kt, g.F);
+  s.y = clamp_start(y, off[3 * n + 1], g.ky, g.Hp);
+  s.z = clamp_start(x, off[3 * n + 2], g.kx, g.Wp);
+  s.w = 0;
+  return s;
+}
+
+__global__ __launch_bounds__(256) void k_window_starts(const int32_t* off, Geom g, int32_t* starts3) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= g.N) return;
+  const int4 s = query_start(off, g, n);
+  starts3[3 * n + 0] = s.x;
+  starts3[3 * n + 1] = s.y;
+  starts3[3 * n + 2] = s.z;
+}
+
+__global__ __launch_bounds__(256) void k_starts_keys(const int32_t* off, Geom g, int4* starts, uint32_t* keys) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= g.N) return;
+  const int4 s = query_start(off, g, n);
+  starts[n] = s;
+  keys[n] = (uint32_t)cell_key(g, s.x, s.y, s.z);
+}
+
+// ---- stable LSD radix sort (8-bit digits) ---------------------------------------
+// Each block owns RADIX_TILE consecutive items.  hist: per-block digit counts,
+// stored digit-major so one exclusive scan gives every (digit, block) its output
+// base.  scatter: items are ranked in their original order (16 rounds of 256),
+// which keeps the sort stable.
+
+__global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* keys, int n, int shift, uint32_t* ghist, int nblk) {
+  __shared__ uint32_t h[256];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * RADIX_TILE;
+  for (int i = tid; i < RADIX_TILE; i += 256) {
+    const int idx = base + i;
+    if (idx < n) atomicAdd(&h[(keys[idx] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  ghist[(size_t)tid * nblk + blockIdx.x] = h[tid];
+}
+
+// In-place exclusive scan of n values by one block of 1024 threads.
+__global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n) {
+  __shared__ uint32_t part[1024];
+  const int tid = threadIdx.x;
+  const int seg = (n + 1023) / 1024;
+  const int beg = min(tid * seg, n), end = min(beg + seg, n);
+  uint32_t s = 0;
+  for (int i = beg; i < end; ++i) s += data[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const uint32_t u = tid >= d ? part[tid - d] : 0u;
+    __syncthreads();
+    part[tid] += u;
+    __syncthreads();
+  }
+  uint32_t run = part[tid] - s;
+  for (int i = beg; i < end; ++i) {
+    const uint32_t x = data[i];
+    data[i] = run;
+    run += x;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* kin, const int* vin, int n, int shift,
+                                                       const uint32_t* gbase, int nblk, uint32_t* kout, int* vout) {
+  __shared__ uint32_t base[256], run[256];
+  __shared__ uint32_t wcnt[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  base[tid] = gbase[(size_t)tid * nblk + blockIdx.x];
+  run[tid] = 0;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = 0; r < RADIX_TILE / 256; ++r) {
+    const int idx = blockIdx.x * RADIX_TILE + r * 256 + tid;
+    const bool valid = idx < n;
+    const uint32_t key = valid ? kin[idx] : 0u;
+    const uint32_t d = (key >> shift) & 255u;
+    const int val = valid ? (vin ? vin[idx] : idx) : 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+    __syncthreads();
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const uint32_t rank = (uint32_t)__popcll(m & lt);
+    if (valid && rank == 0) wcnt[wave][d] = (uint32_t)__popcll(m);
+    __syncthreads();
+    {
+      uint32_t acc = run[tid];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t c = wcnt[w][tid];
+        wcnt[w][tid] = acc;
+        acc += c;
+      }
+      run[tid] = acc;
+    }
+    __syncthreads();
+    if (valid) {
+      const uint32_t pos = base[d] + wcnt[wave][d] + rank;
+      kout[pos] = key;
+      vout[pos] = val;
+    }
+    __syncthreads();
+  }
+}
+
+// cell_ptr[c] = number of sorted keys below c, for c = 0 .. keyspace.
+__global__ __launch_bounds__(256) void k_cell_ptr(const uint32_t* skeys, int n, int keyspace, int* cell_ptr) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c > keyspace) return;
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (skeys[mid] < (uint32_t)c) lo = mid + 1; else hi = mid;
+  }
+  cell_ptr[c] = lo;
+}
+
+__global__ __launch_bounds__(256) void k_blob_ngroups(const int* cell_ptr, int nblobs, int* goff) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b > nblobs) return;
+  if (b == nblobs) { goff[b] = 0; return; }
+  const int cnt = cell_ptr[(b + 1) * BLOB_CELLS] - cell_ptr[b * BLOB_CELLS];
+  goff[b] = (cnt + GROUP_Q - 1) / GROUP_Q;
+}
+
+__global__ __launch_bounds__(256) void k_groups(const int* cell_ptr, const int* goff, int nblobs, int2* groups,
+                                                int* ngroups) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b == 0) *ngroups = goff[nblobs];
+  if (b >= nblobs) return;
+  const int beg = cell_ptr[b * BLOB_CELLS];
+  const int cnt = cell_ptr[(b + 1) * BLOB_CELLS] - beg;
+  const int g0 = goff[b], ng = goff[b + 1] - g0;
+  for (int i = 0; i < ng; ++i) groups[g0 + i] = make_int2(beg + i * GROUP_Q, min(GROUP_Q, cnt - i * GROUP_Q));
+}
+
+static unsigned blocks(long long n, int per) { return (unsigned)((n + per - 1) / per); }
+
+hipError_t launch_window_starts(const int32_t* off, const Geom& g, int32_t* starts3, hipStream_t s) {
+  k_window_starts<<<blocks(g.N, 256), 256, 0, s>>>(off, g, starts3);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, hipStream_t s) {
+  const int n = g.N, nb = p.radix_blocks;
+  k_starts_keys<<<blocks(n, 256), 256, 0, s>>>(off, g, p.starts, p.keys[0]);
+  int cur = 0;
+  for (int pass = 0; pass < p.radix_passes; ++pass) {
+    k_radix_hist<<<nb, 256, 0, s>>>(p.keys[cur], n, 8 * pass, p.ghist, nb);
+    k_scan_excl<<<1, 1024, 0, s>>>(p.ghist, 256 * nb);
+    k_radix_scatter<<<nb, 256, 0, s>>>(p.keys[cur], pass == 0 ? nullptr : p.vals[cur], n, 8 * pass, p.ghist, nb,
+                                       p.keys[cur ^ 1], p.vals[cur ^ 1]);
+    cur ^= 1;
+  }
+  // p.perm was set to vals[passes & 1] == vals[cur]
+  k_cell_ptr<<<blocks((long long)g.keyspace + 1, 256), 256, 0, s>>>(p.keys[cur], n, g.keyspace, p.cell_ptr);
+  k_blob_ngroups<<<blocks((long long)g.nblobs + 1, 256), 256, 0, s>>>(p.cell_ptr, g.nblobs, p.goff);
+  k_scan_excl<<<1, 1024, 0, s>>>(reinterpret_cast<uint32_t*>(p.goff), g.nblobs + 1);
+  k_groups<<<blocks(g.nblobs > 0 ? g.nblobs : 1, 256), 256, 0, s>>>(p.cell_ptr, p.goff, g.nblobs, p.groups,
+                                                                     p.ngroups);
+  return hipGetLastError();
+}
+
+}  // namespace dsa3d
