@@ -51,9 +51,10 @@ int dsa3d_window_starts(const int32_t* offsets, int F, int Hp, int Wp, int kt, i
   return launch_window_starts(offsets, g, starts, stream) == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
 
-int dsa3d_forward(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
-                  int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out, float* lse,
-                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int dsa3d_forward_timed(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
+                        int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out,
+                        float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        const hipEvent_t* events) {
   if (!q || !k || !v || !offsets || !out || !lse || !workspace) return DSA3D_ERR_NULL;
   const int st = check_common(F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype);
   if (st != DSA3D_OK) return st;
@@ -64,18 +65,29 @@ int dsa3d_forward(const void* q, const void* k, const void* v, const int32_t* of
   if (workspace_bytes < workspace_layout(g, false, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
   Prep p;
   workspace_layout(g, false, static_cast<char*>(workspace), &p);
+  if (events) hipEventRecord(events[0], stream);
   if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (events) hipEventRecord(events[1], stream);
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v;
   a.out = out; a.lse_out = lse;
   a.scale = scale;
-  return launch_forward(dtype, head_dim, a, g, p, stream) == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
+  const hipError_t e = launch_forward(dtype, head_dim, a, g, p, stream);
+  if (events) hipEventRecord(events[2], stream);
+  return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
 
-int dsa3d_backward(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
-                   const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
-                   int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+int dsa3d_forward(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
+                  int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out, float* lse,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return dsa3d_forward_timed(q, k, v, offsets, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype, out, lse,
+                             workspace, workspace_bytes, stream, nullptr);
+}
+
+int dsa3d_backward_timed(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
+                         const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim,
+                         int kt, int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream, const hipEvent_t* events) {
   if (!q || !k || !v || !offsets || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return DSA3D_ERR_NULL;
   const int st = check_common(F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype);
   if (st != DSA3D_OK) return st;
@@ -87,13 +99,25 @@ int dsa3d_backward(const void* q, const void* k, const void* v, const int32_t* o
   if (workspace_bytes < workspace_layout(g, true, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
   Prep p;
   workspace_layout(g, true, static_cast<char*>(workspace), &p);
+  if (events) hipEventRecord(events[0], stream);
   if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (events) hipEventRecord(events[1], stream);
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v;
   a.o = out; a.dout = dout; a.lse = lse;
   a.out = dq; a.dk = dk; a.dv = dv;
   a.scale = scale;
-  return launch_backward(dtype, head_dim, a, g, p, stream) == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
+  return launch_backward(dtype, head_dim, a, g, p, stream, events ? events + 2 : nullptr) == hipSuccess
+             ? DSA3D_OK
+             : DSA3D_ERR_LAUNCH;
+}
+
+int dsa3d_backward(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
+                   const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
+                   int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  return dsa3d_backward_timed(q, k, v, offsets, out, lse, dout, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype,
+                              dq, dk, dv, workspace, workspace_bytes, stream, nullptr);
 }
 
 const char* dsa3d_status_string(int status) {

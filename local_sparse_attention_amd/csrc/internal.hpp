@@ -49,6 +49,8 @@ struct AttnArgs {
 };
 
 hipError_t launch_forward(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
-hipError_t launch_backward(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
+// ev (nullable): events recorded between the dQ and dK/dV kernels ([0]) and after them ([1]).
+hipError_t launch_backward(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s,
+                           const hipEvent_t* ev);
 
 }  // namespace dsa3d
