@@ -1,6 +1,7 @@
 // C ABI entry points (include/dsa3d.h): argument checks, workspace carving and the
 // launch sequence on the caller's stream.  Everything here runs on the host.
 #include <math.h>
+#include <stdlib.h>
 
 #include "dsa3d.h"
 #include "internal.hpp"
@@ -8,6 +9,13 @@
 using namespace dsa3d;
 
 namespace {
+
+// Set DSA3D_GENERIC_KERNELS=1 to run the per-group kernels for every geometry
+// (used by the tests to cover both kernel families on the same inputs).
+bool generic_only() {
+  const char* e = getenv("DSA3D_GENERIC_KERNELS");
+  return e && e[0] == '1';
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -72,7 +80,8 @@ int dsa3d_forward_timed(const void* q, const void* k, const void* v, const int32
   a.q = q; a.k = k; a.v = v;
   a.out = out; a.lse_out = lse;
   a.scale = scale;
-  const hipError_t e = launch_forward(dtype, head_dim, a, g, p, stream);
+  const hipError_t e = (!generic_only() && tube_eligible(g, dtype, head_dim)) ? launch_forward_tube(dtype, head_dim, a, g, p, stream)
+                                                              : launch_forward_v1(dtype, head_dim, a, g, p, stream);
   if (events) hipEventRecord(events[2], stream);
   return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
@@ -107,7 +116,7 @@ int dsa3d_backward_timed(const void* q, const void* k, const void* v, const int3
   a.o = out; a.dout = dout; a.lse = lse;
   a.out = dq; a.dk = dk; a.dv = dv;
   a.scale = scale;
-  return launch_backward(dtype, head_dim, a, g, p, stream, events ? events + 2 : nullptr) == hipSuccess
+  return launch_backward_v1(dtype, head_dim, a, g, p, stream, events ? events + 2 : nullptr) == hipSuccess
              ? DSA3D_OK
              : DSA3D_ERR_LAUNCH;
 }

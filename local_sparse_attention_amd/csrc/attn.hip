@@ -468,12 +468,12 @@ static hipError_t bwd_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipS
   return e;
 }
 
-hipError_t launch_forward(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+hipError_t launch_forward_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
   if (dtype == 1) return D == 64 ? fwd_impl<u16, 64>(a, g, p, s) : fwd_impl<u16, 128>(a, g, p, s);
   return D == 64 ? fwd_impl<float, 64>(a, g, p, s) : fwd_impl<float, 128>(a, g, p, s);
 }
 
-hipError_t launch_backward(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s,
+hipError_t launch_backward_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s,
                            const hipEvent_t* ev) {
   if (dtype == 1) return D == 64 ? bwd_impl<u16, 64>(a, g, p, s, ev) : bwd_impl<u16, 128>(a, g, p, s, ev);
   return D == 64 ? bwd_impl<float, 64>(a, g, p, s, ev) : bwd_impl<float, 128>(a, g, p, s, ev);

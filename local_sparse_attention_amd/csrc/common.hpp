@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dsa3d {
 
 typedef uint16_t u16;  // bf16 bits
@@ -121,6 +123,17 @@ __device__ __forceinline__ void store4(u16* p, float a, float b, float c, float 
 }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = B .. E-1: loop bodies whose index
+// must be a compile-time constant (register-array subscripts) whatever the unroller
+// decides.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // ---- wave helpers ---------------------------------------------------------

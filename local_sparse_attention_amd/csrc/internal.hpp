@@ -48,9 +48,14 @@ struct AttnArgs {
   float scale;
 };
 
-hipError_t launch_forward(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
+// Per-group kernels: any geometry.
+hipError_t launch_forward_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
 // ev (nullable): events recorded between the dQ and dK/dV kernels ([0]) and after them ([1]).
-hipError_t launch_backward(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s,
-                           const hipEvent_t* ev);
+hipError_t launch_backward_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s,
+                              const hipEvent_t* ev);
+// Frame-sweeping kernels that share each staged key tile between the queries of
+// kt slices: windows up to 8 x 9 x 9.
+bool tube_eligible(const Geom& g, int dtype, int D);
+hipError_t launch_forward_tube(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
 
 }  // namespace dsa3d

@@ -39,6 +39,18 @@ def assert_close(gpu, ref, dtype, what):
     return float(err.max())
 
 
+# The log-sum-exp is an fp32 output computed from fp32 logits even for bf16 inputs, so
+# it is checked tightly for every dtype: a dropped or stale product shows up there.
+LSE_ATOL = 1e-4
+
+
+def assert_lse_close(gpu, ref, what="lse"):
+    err = np.abs(np.asarray(gpu, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
+    i = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= LSE_ATOL, f"{what}: max abs err {err.max():.3e} at {i}"
+    return float(err.max())
+
+
 def border_and_random_rows(grid, heads, count, seed):
     """Query (or key) rows r = n*H + h: every corner and edge-centre token of the grid
     with random heads, plus random rows."""
