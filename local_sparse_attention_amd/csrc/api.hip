@@ -110,15 +110,20 @@ int dsa3d_backward_timed(const void* q, const void* k, const void* v, const int3
   workspace_layout(g, true, static_cast<char*>(workspace), &p);
   if (events) hipEventRecord(events[0], stream);
   if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  const bool kv_tube = !generic_only() && dkdv_tube_eligible(g, dtype, head_dim);
+  if (kv_tube && launch_kv_items(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   if (events) hipEventRecord(events[1], stream);
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v;
   a.o = out; a.dout = dout; a.lse = lse;
   a.out = dq; a.dk = dk; a.dv = dv;
   a.scale = scale;
-  return launch_backward_v1(dtype, head_dim, a, g, p, stream, events ? events + 2 : nullptr) == hipSuccess
-             ? DSA3D_OK
-             : DSA3D_ERR_LAUNCH;
+  if (launch_backward_dq_v1(dtype, head_dim, a, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (events) hipEventRecord(events[2], stream);
+  const hipError_t e = kv_tube ? launch_dkdv_tube(head_dim, a, g, p, stream)
+                               : launch_backward_dkdv_v1(dtype, head_dim, a, g, p, stream);
+  if (events) hipEventRecord(events[3], stream);
+  return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
 
 int dsa3d_backward(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,

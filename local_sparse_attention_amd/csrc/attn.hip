@@ -451,21 +451,21 @@ static hipError_t fwd_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipS
 }
 
 template <typename T, int D>
-static hipError_t bwd_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s, const hipEvent_t* ev) {
+static hipError_t dq_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
   dim3 grid_q(p.max_groups, g.H);
   k_backward_dq<T, D><<<grid_q, 64, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.o,
                                             (const T*)a.dout, a.lse, (T*)a.out, p.delta, g, p, a.scale * LOG2E,
                                             a.scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev) hipEventRecord(ev[0], s);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t dkdv_impl_v1(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
   const int nkb = g.F * ((g.Hp + 3) / 4) * ((g.Wp + 3) / 4);
   dim3 grid_k(nkb, g.H);
   k_backward_dkdv<T, D><<<grid_k, 64, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
                                               a.lse, p.delta, (T*)a.dk, (T*)a.dv, g, p, a.scale * LOG2E, a.scale);
-  e = hipGetLastError();
-  if (ev) hipEventRecord(ev[1], s);
-  return e;
+  return hipGetLastError();
 }
 
 hipError_t launch_forward_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
@@ -473,10 +473,14 @@ hipError_t launch_forward_v1(int dtype, int D, const AttnArgs& a, const Geom& g,
   return D == 64 ? fwd_impl<float, 64>(a, g, p, s) : fwd_impl<float, 128>(a, g, p, s);
 }
 
-hipError_t launch_backward_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s,
-                           const hipEvent_t* ev) {
-  if (dtype == 1) return D == 64 ? bwd_impl<u16, 64>(a, g, p, s, ev) : bwd_impl<u16, 128>(a, g, p, s, ev);
-  return D == 64 ? bwd_impl<float, 64>(a, g, p, s, ev) : bwd_impl<float, 128>(a, g, p, s, ev);
+hipError_t launch_backward_dq_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  if (dtype == 1) return D == 64 ? dq_impl<u16, 64>(a, g, p, s) : dq_impl<u16, 128>(a, g, p, s);
+  return D == 64 ? dq_impl<float, 64>(a, g, p, s) : dq_impl<float, 128>(a, g, p, s);
+}
+
+hipError_t launch_backward_dkdv_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  if (dtype == 1) return D == 64 ? dkdv_impl_v1<u16, 64>(a, g, p, s) : dkdv_impl_v1<u16, 128>(a, g, p, s);
+  return D == 64 ? dkdv_impl_v1<float, 64>(a, g, p, s) : dkdv_impl_v1<float, 128>(a, g, p, s);
 }
 
 }  // namespace dsa3d

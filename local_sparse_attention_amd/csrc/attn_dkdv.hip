@@ -1,0 +1,348 @@
+// Key-centric dK / dV for 3D Deformable Slide Attention (MegaSlide-DiT, section
+// "3D Deformable Slide Attention": the gradient of the windowed softmax attention,
+// dV = P^T dO and dK = scale * dS^T Q with dS = P * (dP - rowsum(dO * O))).
+//
+// A workgroup owns one 4 x 4 key block column (kby, kbx) of one head and a chunk
+// of frames, and holds the dK / dV of its keys in registers: wave w owns the frames
+// t = w (mod kt), so while the queries of start slice tau stream past, the kt
+// waves hold exactly the kt frames tau .. tau+kt-1 those queries read.  A frame's
+// sums are complete once slice t has gone by; its owner writes them and moves on
+// to frame t + kt.  Every key gets its sums from one workgroup, in a fixed order:
+// no atomics, and the result does not depend on timing.
+//
+// The queries of a slice that can reach the key block (start cells in the blob box
+// of the column) are packed into items of 16 by a prep pass.  Items and, once per
+// slice, the K / V rows of the frame that enters, stream through an LDS ring with
+// direct global->LDS loads, PD entries ahead of the MFMAs.
+//
+// Per item and wave (16 queries x the 16 keys of its frame), bf16 MFMA:
+//   S = Q K^T, dP = dO V^T          (16x16x32, K / V fragments held in registers)
+//   P = exp(S scale - lse) on the query's window, dS = P (dP - Delta)
+//   dV^T += dO^T P, dK^T += Q^T dS  (16x16x16, dO^T / Q^T by transposed LDS reads)
+#include "internal.hpp"
+#include "tube.hpp"
+
+namespace dsa3d {
+
+typedef short shortx4v __attribute__((ext_vector_type(4)));
+
+// Blob rows (or columns) of start cells whose windows reach key block kb along an
+// axis with window k, lattice length L: cells [4 kb - k + 1, 4 kb + 3] clipped.
+__device__ __forceinline__ void blob_span(int kb, int k, int L, int& b0, int& b1) {
+  const int lo = max(4 * kb - k + 1, 0), hi = min(4 * kb + 3, L - 1);
+  b0 = lo >> 2;
+  b1 = hi >> 2;
+}
+
+// ---- item lists -------------------------------------------------------------
+
+// Items (16 queries) per (key block column, slice): into off[kb * Lt + tau].
+__global__ __launch_bounds__(256) void k_kvitem_count(Geom g, const int* __restrict__ cell_ptr, int* __restrict__ off) {
+  const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)nkb * g.Lt) return;
+  const int kb = (int)(i / g.Lt), tau = (int)(i - (long long)kb * g.Lt);
+  const int kby = kb / nkbx, kbx = kb - kby * nkbx;
+  int by0, by1, bx0, bx1;
+  blob_span(kby, g.ky, g.Ly, by0, by1);
+  blob_span(kbx, g.kx, g.Lx, bx0, bx1);
+  int cnt = 0;
+  for (int by = by0; by <= by1; ++by) {
+    const int b0 = (tau * g.nby + by) * g.nbx + bx0, b1 = (tau * g.nby + by) * g.nbx + bx1;
+    cnt += cell_ptr[(b1 + 1) * BLOB_CELLS] - cell_ptr[b0 * BLOB_CELLS];
+  }
+  off[i] = (cnt + 15) >> 4;
+}
+
+// One wave per (key block column, slice): the queries of the blob box in sort
+// order, then padding (query 0 with a start no key matches) to whole items.
+__global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restrict__ cell_ptr,
+                                                     const int* __restrict__ perm, const int4* __restrict__ starts,
+                                                     const int* __restrict__ off, int* __restrict__ ids,
+                                                     int2* __restrict__ kst) {
+  const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
+  const long long i = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= (long long)nkb * g.Lt) return;
+  const int kb = (int)(i / g.Lt), tau = (int)(i - (long long)kb * g.Lt);
+  const int kby = kb / nkbx, kbx = kb - kby * nkbx;
+  int by0, by1, bx0, bx1;
+  blob_span(kby, g.ky, g.Ly, by0, by1);
+  blob_span(kbx, g.kx, g.Lx, bx0, bx1);
+  const size_t base = (size_t)off[i] * 16;
+  const int total = (off[i + 1] - off[i]) * 16;
+  int pos = 0;
+  for (int by = by0; by <= by1; ++by) {
+    const int b0 = (tau * g.nby + by) * g.nbx + bx0, b1 = (tau * g.nby + by) * g.nbx + bx1;
+    const int s0 = cell_ptr[b0 * BLOB_CELLS], n = cell_ptr[(b1 + 1) * BLOB_CELLS] - s0;
+    for (int j = lane; j < n; j += 64) {
+      const int qid = perm[s0 + j];
+      const int4 st = starts[qid];
+      ids[base + pos + j] = qid;
+      kst[base + pos + j] = make_int2(st.y, st.z);
+    }
+    pos += n;
+  }
+  for (int j = pos + lane; j < total; j += 64) {
+    ids[base + j] = 0;
+    kst[base + j] = make_int2(-(1 << 29), -(1 << 29));
+  }
+}
+
+// ---- the dK / dV kernel -----------------------------------------------------
+
+template <int D>
+struct DkdvCfg {
+  static constexpr int NPH = D / 64;                 // 128-byte column phases of a bf16 row
+  static constexpr int TILE = 16 * 128;              // one phase of 16 rows
+  static constexpr int META = 2 * NPH * TILE;        // item: starts (128 B), lse (64 B), delta (64 B)
+  static constexpr int ENTRY = META + 256;
+  static constexpr int NL = 4 * NPH + 3;             // direct loads per entry
+  static constexpr int NBUF = D == 128 ? 8 : 12;     // ring entries
+  static constexpr int PD = NBUF - 1;                // entries in flight ahead of the one in use
+  static constexpr int NC = D / 32, NT = D / 16;
+};
+
+struct KvItems {
+  const int* off;   // [nkb * Lt + 1]: items of (kb, tau) are off[kb Lt + tau] .. off[kb Lt + tau + 1]
+  const int* ids;   // [items * 16] query tokens
+  const int2* st;   // [items * 16] (sy, sx) window starts
+};
+
+// Position in the entry stream of a workgroup: slice tau, entry j of the slice
+// (j < 0: the K / V rows of frame tau + kt + j; j >= 0: item j of the slice).
+struct Cursor {
+  int tau, j, n, base;  // n items in the slice, the first is item `base`
+};
+
+constexpr int DKDV_TS = 32;  // frames per workgroup
+
+template <int D>
+__global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, const u16* __restrict__ k,
+                                                   const u16* __restrict__ v, const u16* __restrict__ dout,
+                                                   const float* __restrict__ lse, const float* __restrict__ delta,
+                                                   u16* __restrict__ dk, u16* __restrict__ dv, Geom g, KvItems it,
+                                                   float sl2, float scale) {
+  using C = DkdvCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::ENTRY];
+
+  const int kt = g.kt, NW = kt;
+  const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
+  const int nchunk = (g.F + DKDV_TS - 1) / DKDV_TS;
+  int L = xcd_remap(blockIdx.x, nkb * nchunk * g.H);
+  const int h = L / (nkb * nchunk);
+  L -= h * nkb * nchunk;
+  const int chunk = L / nkb, kb = L - chunk * nkb;
+  const int kby = kb / nkbx, kbx = kb - kby * nkbx;
+  const int t0 = chunk * DKDV_TS, t1 = min(t0 + DKDV_TS, g.F);  // frames written here
+  const int tau_lo = max(t0 - kt + 1, 0), tau_hi = min(t1 - 1, g.Lt - 1);
+
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int my_loads = (C::NL - wave + NW - 1) / NW;
+  cint_ptr offp = (cint_ptr)it.off + (size_t)kb * g.Lt;
+
+  // this lane's key (key r16 of the block) for the window test
+  const int key_y = 4 * kby + (r16 >> 2), key_x = 4 * kbx + (r16 & 3);
+
+  auto start_cursor = [&]() {
+    Cursor c;
+    c.tau = tau_lo;
+    c.j = -kt;
+    c.base = offp[tau_lo];
+    c.n = offp[tau_lo + 1] - c.base;
+    return c;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.j == c.n) {
+      ++c.tau;
+      if (c.tau <= tau_hi) {
+        c.base += c.n;
+        c.n = offp[c.tau + 1] - c.base;
+      }
+      c.j = -1;
+    }
+  };
+
+  // ---- direct loads of one entry into ring slot e
+  auto issue = [&](const Cursor& c, char* e) {
+    if (c.j < 0) {
+      const int f = c.tau + kt + c.j;
+      for (int j = wave; j < C::NL; j += NW) {
+        if (j < 4 * C::NPH) {
+          const int ti = j >> 1, hh = j & 1, tensor = ti / C::NPH, ph = ti - tensor * C::NPH;
+          const int row = 8 * hh + (lane >> 3), ch = (lane & 7) ^ (row & 7);
+          const int y = 4 * kby + (row >> 2), x = 4 * kbx + (row & 3);
+          const int tok = (y < g.Hp && x < g.Wp) ? (f * g.Hp + y) * g.Wp + x : 0;
+          const u16* src = (tensor ? v : k) + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8;
+          dma16(src, e + ti * C::TILE + hh * 1024);
+        } else {
+          // keeps the per-entry load count uniform; lands in the unused meta area
+          if (lane < 16) dma4(lse, e + C::META + 128);
+        }
+      }
+    } else {
+      const int item = c.base + c.j;
+      cint_ptr idp = (cint_ptr)it.ids + (size_t)item * 16;
+      int idv = 0;  // lane r < 16: token of query r
+#define DSA3D_WRITELANE(r) __asm__("v_writelane_b32 %0, %1, " #r : "+v"(idv) : "s"(idp[r]));
+      DSA3D_WRITELANE(0) DSA3D_WRITELANE(1) DSA3D_WRITELANE(2) DSA3D_WRITELANE(3)
+      DSA3D_WRITELANE(4) DSA3D_WRITELANE(5) DSA3D_WRITELANE(6) DSA3D_WRITELANE(7)
+      DSA3D_WRITELANE(8) DSA3D_WRITELANE(9) DSA3D_WRITELANE(10) DSA3D_WRITELANE(11)
+      DSA3D_WRITELANE(12) DSA3D_WRITELANE(13) DSA3D_WRITELANE(14) DSA3D_WRITELANE(15)
+#undef DSA3D_WRITELANE
+      for (int j = wave; j < C::NL; j += NW) {
+        if (j < 4 * C::NPH) {
+          const int ti = j >> 1, hh = j & 1, tensor = ti / C::NPH, ph = ti - tensor * C::NPH;
+          const int row = 8 * hh + (lane >> 3), ch = (lane & 7) ^ (row & 7);
+          const int tok = __shfl(idv, row, 64);
+          const u16* src = (tensor ? dout : q) + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8;
+          dma16(src, e + ti * C::TILE + hh * 1024);
+        } else if (j == 4 * C::NPH) {
+          if (lane < 8) dma16(it.st + (size_t)item * 16 + 2 * lane, e + C::META);
+        } else {
+          const float* src = (j == 4 * C::NPH + 1 ? lse : delta) + (size_t)h * g.N + idv;
+          if (lane < 16) dma4(src, e + C::META + (j == 4 * C::NPH + 1 ? 128 : 192));
+        }
+      }
+    }
+  };
+
+  // tile offsets: Q / dO (item) or K / V (frame) of phase ph
+  auto tile = [&](char* e, int tensor, int ph) { return e + (tensor * C::NPH + ph) * C::TILE; };
+
+  Frag<u16> kf[C::NC], vf[C::NC];
+  f32x4_t dka[C::NT], dva[C::NT];
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t) {
+    dka[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    dva[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  int cur_f = -1;
+
+  auto finalize = [&](int f) {
+    if (f >= t0 && f < t1 && key_y < g.Hp && key_x < g.Wp) {
+      const size_t row = ((size_t)((f * g.Hp + key_y) * g.Wp + key_x) * g.H + h) * D;
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t) {
+        store4(dk + row + 16 * t + 4 * quad, dka[t][0] * scale, dka[t][1] * scale, dka[t][2] * scale,
+               dka[t][3] * scale);
+        store4(dv + row + 16 * t + 4 * quad, dva[t][0], dva[t][1], dva[t][2], dva[t][3]);
+      }
+    }
+  };
+
+  Cursor ic = start_cursor(), cc = start_cursor();
+  int issued = 0;
+  for (; issued < C::PD && ic.tau <= tau_hi; ++issued, advance(ic)) issue(ic, ring[issued % C::NBUF]);
+  wait_vmcnt(my_loads * max(issued - 1, 0));
+  lds_barrier();
+
+  for (int st = 0; cc.tau <= tau_hi; ++st, advance(cc)) {
+    if (ic.tau <= tau_hi) {
+      issue(ic, ring[(st + C::PD) % C::NBUF]);
+      ++issued;
+      advance(ic);
+    }
+    char* e = ring[st % C::NBUF];
+    if (cc.j < 0) {
+      // ---- a frame enters: its owner writes the frame it leaves and takes K / V
+      const int f = cc.tau + kt + cc.j;
+      if (wave == f % kt) {
+        if (cur_f >= 0) {
+          finalize(cur_f);
+#pragma unroll
+          for (int t = 0; t < C::NT; ++t) {
+            dka[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dva[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) {
+          const int off = sw(r16, (c & 1) * 64 + quad * 16);
+          load_frag(kf[c], (const u16*)(tile(e, 0, c >> 1) + off));
+          load_frag(vf[c], (const u16*)(tile(e, 1, c >> 1) + off));
+        }
+        cur_f = f;
+      }
+    } else {
+      // ---- an item: 16 queries against this wave's frame of the key block
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        const int off = sw(r16, (c & 1) * 64 + quad * 16);
+        Frag<u16> a;
+        load_frag(a, (const u16*)(tile(e, 0, c >> 1) + off));
+        s = mma(a, kf[c], s);
+        load_frag(a, (const u16*)(tile(e, 1, c >> 1) + off));
+        dp = mma(a, vf[c], dp);
+      }
+      // queries 4 quad + i of the item: window start, lse, delta
+      const int4 sa = *reinterpret_cast<const int4*>(e + C::META + quad * 32);
+      const int4 sb = *reinterpret_cast<const int4*>(e + C::META + quad * 32 + 16);
+      const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 128 + quad * 16);
+      const float4 de = *reinterpret_cast<const float4*>(e + C::META + 192 + quad * 16);
+      const int sy[4] = {sa.x, sa.z, sb.x, sb.z}, sx[4] = {sa.y, sa.w, sb.y, sb.w};
+      const float lq[4] = {ls.x, ls.y, ls.z, ls.w}, dq[4] = {de.x, de.y, de.z, de.w};
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (unsigned)(key_y - sy[i]) < (unsigned)g.ky && (unsigned)(key_x - sx[i]) < (unsigned)g.kx;
+        const float p = __builtin_amdgcn_exp2f(s[i] * sl2 - lq[i] * LOG2E);
+        pv[i] = ok ? p : 0.f;
+        dsv[i] = pv[i] * (dp[i] - dq[i]);
+      }
+      shortx4v pb, db;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = __builtin_bit_cast(short, static_cast<__bf16>(pv[i]));
+        db[i] = __builtin_bit_cast(short, static_cast<__bf16>(dsv[i]));
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: A = 4 query rows x 16 d columns, transposed
+      const int trow = 4 * quad + (r16 >> 2);
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t) {
+        const int off = sw(trow, ((t & 3) * 16 + 4 * (r16 & 3)) * 2);
+        const shortx4v ao = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(tile(e, 1, t >> 2) + off));
+        const shortx4v aq = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(tile(e, 0, t >> 2) + off));
+        dva[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pb, dva[t], 0, 0, 0);
+        dka[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aq, db, dka[t], 0, 0, 0);
+      }
+    }
+    // entry st + 1 must have landed; entries st + 2 .. issued - 1 may stay in flight
+    wait_vmcnt(my_loads * max(issued - st - 2, 0));
+    lds_barrier();
+  }
+  finalize(cur_f);
+}
+
+bool dkdv_tube_eligible(const Geom& g, int dtype, int D) {
+  (void)D;
+  return dtype == 1 && kv_items_geometry(g);
+}
+
+hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s) {
+  const long long n = (long long)kv_item_columns(g) * g.Lt;
+  k_kvitem_count<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(g, p.cell_ptr, p.kv_off);
+  if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.kv_off), (int)(n + 1), s) != hipSuccess) return hipGetLastError();
+  k_kvitem_fill<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(g, p.cell_ptr, p.perm, p.starts, p.kv_off, p.kv_ids, p.kv_st);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dkdv_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  const int nkb = kv_item_columns(g);
+  const int nchunk = (g.F + DKDV_TS - 1) / DKDV_TS;
+  const long long total = (long long)nkb * nchunk * g.H;
+  KvItems it{p.kv_off, p.kv_ids, p.kv_st};
+  k_dkdv_tube<D><<<(unsigned)total, 64 * g.kt, 0, s>>>((const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
+                                                       (const u16*)a.dout, a.lse, p.delta, (u16*)a.dk, (u16*)a.dv, g,
+                                                       it, a.scale * LOG2E, a.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkdv_tube(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  return D == 64 ? dkdv_impl<64>(a, g, p, s) : dkdv_impl<128>(a, g, p, s);
+}
+
+}  // namespace dsa3d

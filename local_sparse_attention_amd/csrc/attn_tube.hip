@@ -22,15 +22,10 @@
 // rows; the 16-byte chunk c of row r sits at chunk position c ^ (r & 7), which
 // spreads the row-wise and the transposed fragment reads over the banks.
 #include "internal.hpp"
+#include "tube.hpp"
 
 namespace dsa3d {
 
-typedef short shortx4_t __attribute__((ext_vector_type(4)));
-// Read-only tables (query order, start-cell boundaries) read at wave-uniform
-// addresses: through the constant address space they become scalar loads, which
-// keeps the vector memory counter free for the direct tile loads.
-typedef const __attribute__((address_space(4))) int* cint_ptr;
-typedef __attribute__((address_space(3))) shortx4_t lds_shortx4_t;
 
 template <typename T, int D>
 struct TubeCfg {
@@ -55,10 +50,6 @@ struct TubeCfg {
 constexpr int TUBE_TS = 32;      // start slices per workgroup
 constexpr int TUBE_MAX_TS = 64;
 
-// byte offset of (row, byte-in-row) in a swizzled 128-byte-row tile
-__device__ __forceinline__ int sw(int row, int byte) {
-  return row * 128 + ((((byte >> 4) ^ row) & 7) << 4) + (byte & 15);
-}
 
 // Row-wise fragment: 8 elements of row `row` starting at element `e0` (16 or 32 bytes).
 __device__ __forceinline__ void lds_frag_row(Frag<u16>& f, const char* tile, int row, int e0) {
@@ -137,21 +128,6 @@ struct TubeGeo {
   int nb;       // key blocks in the tile
 };
 
-// One 16-byte direct global->LDS load per lane (global_load_lds_dwordx4): lane l's
-// 16 bytes land at lds_base + 16 l, lds_base wave-uniform (it goes to M0).  Issued
-// from inline asm so the compiler does not track it: left to itself it waits for
-// every such load to finish before any LDS read that might alias, which would drain
-// the prefetch ring.  Completion is awaited with explicit vmcnt waits (wait_vmcnt)
-// before the barrier that publishes the data.
-__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
-  const unsigned m0 = (unsigned)(size_t)(const __attribute__((address_space(3))) char*)lds_base;
-  __asm__ __volatile__("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
-}
-
-// Workgroup barrier for the pipelined loop: the LDS reads and writes of this wave
-// are complete, the direct loads are covered by the preceding vmcnt wait.
-// (__syncthreads() would also wait for every outstanding global access.)
-__device__ __forceinline__ void lds_barrier() { __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Token of tile row `row` at frame f, or -1 outside the grid / past the tile.
 __device__ __forceinline__ int tile_token(const Geom& g, const TubeGeo& tg, int f, int row) {
@@ -182,35 +158,7 @@ __device__ __forceinline__ void issue_tile(char* dst, const T* __restrict__ src,
   }
 }
 
-// s_waitcnt vmcnt(n) for a run-time n (the immediate must be a constant).
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-#define DSA3D_VMCNT_CASE(k) \
-  case k:                   \
-    __asm__ __volatile__("s_waitcnt vmcnt(" #k ")" ::: "memory"); \
-    break;
-    DSA3D_VMCNT_CASE(0) DSA3D_VMCNT_CASE(1) DSA3D_VMCNT_CASE(2) DSA3D_VMCNT_CASE(3) DSA3D_VMCNT_CASE(4)
-    DSA3D_VMCNT_CASE(5) DSA3D_VMCNT_CASE(6) DSA3D_VMCNT_CASE(7) DSA3D_VMCNT_CASE(8) DSA3D_VMCNT_CASE(9)
-    DSA3D_VMCNT_CASE(10) DSA3D_VMCNT_CASE(11) DSA3D_VMCNT_CASE(12) DSA3D_VMCNT_CASE(13) DSA3D_VMCNT_CASE(14)
-    DSA3D_VMCNT_CASE(15) DSA3D_VMCNT_CASE(16) DSA3D_VMCNT_CASE(17) DSA3D_VMCNT_CASE(18) DSA3D_VMCNT_CASE(19)
-    DSA3D_VMCNT_CASE(20) DSA3D_VMCNT_CASE(21) DSA3D_VMCNT_CASE(22) DSA3D_VMCNT_CASE(23) DSA3D_VMCNT_CASE(24)
-    DSA3D_VMCNT_CASE(25) DSA3D_VMCNT_CASE(26) DSA3D_VMCNT_CASE(27) DSA3D_VMCNT_CASE(28) DSA3D_VMCNT_CASE(29)
-    DSA3D_VMCNT_CASE(30) DSA3D_VMCNT_CASE(31) DSA3D_VMCNT_CASE(32) DSA3D_VMCNT_CASE(33) DSA3D_VMCNT_CASE(34)
-    DSA3D_VMCNT_CASE(35) DSA3D_VMCNT_CASE(36) DSA3D_VMCNT_CASE(37) DSA3D_VMCNT_CASE(38) DSA3D_VMCNT_CASE(39)
-    DSA3D_VMCNT_CASE(40) DSA3D_VMCNT_CASE(41) DSA3D_VMCNT_CASE(42)
-#undef DSA3D_VMCNT_CASE
-    default:
-      __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-}
 
-// Logical workgroup index from the hardware one: consecutive workgroups go round
-// robin to the 8 XCDs, so hand each XCD a contiguous range of logical indices
-// (neighbouring tubes then share that XCD's L2).
-__device__ __forceinline__ int xcd_remap(int L, int total) {
-  const int per = total >> 3, rem = total & 7, xcd = L & 7, slot = L >> 3;
-  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-}
 
 __device__ __forceinline__ void wait_direct_loads() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); }
 

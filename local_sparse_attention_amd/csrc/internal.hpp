@@ -20,6 +20,10 @@ struct Prep {
   int2* groups;        // [max_groups]: (first index into perm, query count <= 16)
   int* ngroups;        // [1]
   float* delta;        // [H][N] (backward only)
+  // key-centric dK/dV item lists (backward, kv_items_geometry() only)
+  int* kv_off;         // [nkb * Lt + 1]: items of key block column kb, slice tau
+  int* kv_ids;         // [max_kv_items * 16] query tokens, 16 per item
+  int2* kv_st;         // [max_kv_items * 16] (sy, sx) window starts
   int* perm;           // = the vals buffer the sort ends in
   int radix_blocks;
   int radix_passes;
@@ -33,6 +37,18 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p);
 
 hipError_t launch_window_starts(const int32_t* off, const Geom& g, int32_t* starts3, hipStream_t s);
 hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, hipStream_t s);
+// In-place exclusive scan of n uint32 values (one workgroup).
+hipError_t launch_scan_excl(uint32_t* data, int n, hipStream_t s);
+
+// Key-centric dK/dV: windows whose key blocks reach at most 3 x 3 start blobs
+// (ky, kx <= 9) and kt <= 8 (one wave per frame in flight).
+inline bool kv_items_geometry(const Geom& g) { return g.kt <= 8 && g.ky <= 9 && g.kx <= 9; }
+inline int kv_item_columns(const Geom& g) { return ((g.Hp + 3) / 4) * ((g.Wp + 3) / 4); }
+// Items are 16 queries of one slice whose start blob can reach the column: every
+// query counts for at most 3 x 3 columns.
+inline size_t max_kv_items(const Geom& g) {
+  return ((size_t)9 * g.N + 15) / 16 + (size_t)kv_item_columns(g) * g.Lt + 1;
+}
 
 struct AttnArgs {
   const void* q;
@@ -50,12 +66,17 @@ struct AttnArgs {
 
 // Per-group kernels: any geometry.
 hipError_t launch_forward_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
-// ev (nullable): events recorded between the dQ and dK/dV kernels ([0]) and after them ([1]).
-hipError_t launch_backward_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s,
-                              const hipEvent_t* ev);
 // Frame-sweeping kernels that share each staged key tile between the queries of
 // kt slices: windows up to 8 x 9 x 9.
 bool tube_eligible(const Geom& g, int dtype, int D);
 hipError_t launch_forward_tube(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
+
+// v1 backward pieces: dQ (also writes p.delta) and dK/dV.
+hipError_t launch_backward_dq_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
+hipError_t launch_backward_dkdv_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
+// Key-centric pipelined dK/dV (bf16): item lists, then the kernel (needs p.delta).
+bool dkdv_tube_eligible(const Geom& g, int dtype, int D);
+hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s);
+hipError_t launch_dkdv_tube(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
 
 }  // namespace dsa3d

@@ -55,6 +55,10 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   q.groups = (int2*)take((size_t)max_groups * sizeof(int2));
   q.ngroups = (int*)take(4);
   q.delta = backward ? (float*)take(N * g.H * 4) : nullptr;
+  const bool kv = backward && kv_items_geometry(g);
+  q.kv_off = kv ? (int*)take(((size_t)kv_item_columns(g) * g.Lt + 1) * 4) : nullptr;
+  q.kv_ids = kv ? (int*)take(max_kv_items(g) * 16 * 4) : nullptr;
+  q.kv_st = kv ? (int2*)take(max_kv_items(g) * 16 * sizeof(int2)) : nullptr;
   q.perm = q.vals[passes & 1];
   q.radix_blocks = rb;
   q.radix_passes = passes;
@@ -224,6 +228,11 @@ __global__ __launch_bounds__(256) void k_groups(const int* cell_ptr, const int* 
 }
 
 static unsigned blocks(long long n, int per) { return (unsigned)((n + per - 1) / per); }
+
+hipError_t launch_scan_excl(uint32_t* data, int n, hipStream_t s) {
+  k_scan_excl<<<1, 1024, 0, s>>>(data, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_window_starts(const int32_t* off, const Geom& g, int32_t* starts3, hipStream_t s) {
   k_window_starts<<<blocks(g.N, 256), 256, 0, s>>>(off, g, starts3);
