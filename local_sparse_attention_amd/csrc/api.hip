@@ -75,13 +75,15 @@ int dsa3d_forward_timed(const void* q, const void* k, const void* v, const int32
   workspace_layout(g, false, static_cast<char*>(workspace), &p);
   if (events) hipEventRecord(events[0], stream);
   if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  const bool qs = !generic_only() && fwd_qs_eligible(g, dtype, head_dim);
+  if (qs && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   if (events) hipEventRecord(events[1], stream);
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v;
   a.out = out; a.lse_out = lse;
   a.scale = scale;
-  const hipError_t e = (!generic_only() && tube_eligible(g, dtype, head_dim)) ? launch_forward_tube(dtype, head_dim, a, g, p, stream)
-                                                              : launch_forward_v1(dtype, head_dim, a, g, p, stream);
+  const hipError_t e = qs ? launch_forward_qs(head_dim, a, g, p, stream)
+                          : launch_forward_v1(dtype, head_dim, a, g, p, stream);
   if (events) hipEventRecord(events[2], stream);
   return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }

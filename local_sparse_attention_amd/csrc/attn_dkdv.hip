@@ -100,6 +100,7 @@ struct DkdvCfg {
   static constexpr int NL = 4 * NPH + 3;             // direct loads per entry
   static constexpr int NBUF = D == 128 ? 8 : 12;     // ring entries
   static constexpr int PD = NBUF - 1;                // entries in flight ahead of the one in use
+  static constexpr int NIDS = PD + 2;                // token ring (loaded 2 PD + 1 entries ahead)
   static constexpr int NC = D / 32, NT = D / 16;
 };
 
@@ -140,17 +141,26 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int my_loads = (C::NL - wave + NW - 1) / NW;
-  cint_ptr offp = (cint_ptr)it.off + (size_t)kb * g.Lt;
+  // Nothing in the loop below reads memory through the scalar unit: a scalar load
+  // in flight makes every LDS wait a full lgkmcnt(0) wait, which would put its
+  // latency in front of the MFMAs.  The slice boundaries of this workgroup go to
+  // LDS once; item tokens arrive by direct loads into a small ring, 2 PD + 1
+  // entries ahead of use.
+  __shared__ int s_off[DKDV_TS + 8 + 1];
+  __shared__ int s_ids[C::NIDS][16];
+  for (int i = tid; i <= tau_hi - tau_lo + 1; i += 64 * NW) s_off[i] = it.off[(size_t)kb * g.Lt + tau_lo + i];
+  __syncthreads();
 
   // this lane's key (key r16 of the block) for the window test
   const int key_y = 4 * kby + (r16 >> 2), key_x = 4 * kbx + (r16 & 3);
 
+  auto slice_off = [&](int tau) { return __builtin_amdgcn_readfirstlane(s_off[tau - tau_lo]); };
   auto start_cursor = [&]() {
     Cursor c;
     c.tau = tau_lo;
     c.j = -kt;
-    c.base = offp[tau_lo];
-    c.n = offp[tau_lo + 1] - c.base;
+    c.base = slice_off(tau_lo);
+    c.n = slice_off(tau_lo + 1) - c.base;
     return c;
   };
   auto advance = [&](Cursor& c) {
@@ -158,14 +168,15 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
       ++c.tau;
       if (c.tau <= tau_hi) {
         c.base += c.n;
-        c.n = offp[c.tau + 1] - c.base;
+        c.n = slice_off(c.tau + 1) - c.base;
       }
       c.j = -1;
     }
   };
 
-  // ---- direct loads of one entry into ring slot e
-  auto issue = [&](const Cursor& c, char* e) {
+  // ---- direct loads of entry x (at cursor c) into ring slot e; an item's tokens
+  // are in s_ids[x % NIDS]
+  auto issue = [&](const Cursor& c, int x, char* e) {
     if (c.j < 0) {
       const int f = c.tau + kt + c.j;
       for (int j = wave; j < C::NL; j += NW) {
@@ -183,29 +194,26 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
       }
     } else {
       const int item = c.base + c.j;
-      cint_ptr idp = (cint_ptr)it.ids + (size_t)item * 16;
-      int idv = 0;  // lane r < 16: token of query r
-#define DSA3D_WRITELANE(r) __asm__("v_writelane_b32 %0, %1, " #r : "+v"(idv) : "s"(idp[r]));
-      DSA3D_WRITELANE(0) DSA3D_WRITELANE(1) DSA3D_WRITELANE(2) DSA3D_WRITELANE(3)
-      DSA3D_WRITELANE(4) DSA3D_WRITELANE(5) DSA3D_WRITELANE(6) DSA3D_WRITELANE(7)
-      DSA3D_WRITELANE(8) DSA3D_WRITELANE(9) DSA3D_WRITELANE(10) DSA3D_WRITELANE(11)
-      DSA3D_WRITELANE(12) DSA3D_WRITELANE(13) DSA3D_WRITELANE(14) DSA3D_WRITELANE(15)
-#undef DSA3D_WRITELANE
+      const int* ids = s_ids[x % C::NIDS];
       for (int j = wave; j < C::NL; j += NW) {
         if (j < 4 * C::NPH) {
           const int ti = j >> 1, hh = j & 1, tensor = ti / C::NPH, ph = ti - tensor * C::NPH;
           const int row = 8 * hh + (lane >> 3), ch = (lane & 7) ^ (row & 7);
-          const int tok = __shfl(idv, row, 64);
+          const int tok = ids[row];
           const u16* src = (tensor ? dout : q) + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8;
           dma16(src, e + ti * C::TILE + hh * 1024);
         } else if (j == 4 * C::NPH) {
           if (lane < 8) dma16(it.st + (size_t)item * 16 + 2 * lane, e + C::META);
-        } else {
-          const float* src = (j == 4 * C::NPH + 1 ? lse : delta) + (size_t)h * g.N + idv;
-          if (lane < 16) dma4(src, e + C::META + (j == 4 * C::NPH + 1 ? 128 : 192));
+        } else if (lane < 16) {
+          const float* src = (j == 4 * C::NPH + 1 ? lse : delta) + (size_t)h * g.N + ids[lane];
+          dma4(src, e + C::META + (j == 4 * C::NPH + 1 ? 128 : 192));
         }
       }
     }
+  };
+  // tokens of entry x (items only), by the last wave
+  auto issue_ids = [&](const Cursor& c, int x) {
+    if (c.j >= 0 && wave == NW - 1 && lane < 16) dma4(it.ids + (size_t)(c.base + c.j) * 16 + lane, s_ids[x % C::NIDS]);
   };
 
   // tile offsets: Q / dO (item) or K / V (frame) of phase ph
@@ -232,17 +240,33 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
     }
   };
 
-  Cursor ic = start_cursor(), cc = start_cursor();
-  int issued = 0;
-  for (; issued < C::PD && ic.tau <= tau_hi; ++issued, advance(ic)) issue(ic, ring[issued % C::NBUF]);
-  wait_vmcnt(my_loads * max(issued - 1, 0));
-  lds_barrier();
+  // Three cursors over the same entry stream: token loads (pc, 2 PD + 1 ahead),
+  // row loads (ic, PD ahead) and the MFMAs (cc).  Steps st < 0 only fill the
+  // pipeline.
+  Cursor pc = start_cursor(), ic = start_cursor(), cc = start_cursor();
+  int npc = 0;
+  for (; npc <= C::PD && pc.tau <= tau_hi; ++npc, advance(pc)) issue_ids(pc, npc);
+  wait_vmcnt(0);
+  __syncthreads();
 
-  for (int st = 0; cc.tau <= tau_hi; ++st, advance(cc)) {
+  int issued = 0;
+  for (int st = -C::PD; cc.tau <= tau_hi; ++st) {
     if (ic.tau <= tau_hi) {
-      issue(ic, ring[(st + C::PD) % C::NBUF]);
+      issue(ic, issued, ring[issued % C::NBUF]);
       ++issued;
       advance(ic);
+    }
+    if (pc.tau <= tau_hi) {
+      issue_ids(pc, npc);
+      ++npc;
+      advance(pc);
+    }
+    if (st < 0) {
+      // (token loads only add to the count of loads issued later: the wait is exact
+      // or stricter)
+      wait_vmcnt(my_loads * max(issued - st - 2, 0));
+      lds_barrier();
+      continue;
     }
     char* e = ring[st % C::NBUF];
     if (cc.j < 0) {
@@ -312,6 +336,7 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
     // entry st + 1 must have landed; entries st + 2 .. issued - 1 may stay in flight
     wait_vmcnt(my_loads * max(issued - st - 2, 0));
     lds_barrier();
+    advance(cc);
   }
   finalize(cur_f);
 }

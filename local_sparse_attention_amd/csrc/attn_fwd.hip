@@ -1,0 +1,337 @@
+// Frame-sweeping forward of 3D Deformable Slide Attention (MegaSlide-DiT, section
+// "3D Deformable Slide Attention", the attention of Eq. (1)) on gfx950, bf16.
+//
+// A workgroup owns one start blob column (by, bx) of one head and QS_TS slices of
+// it, and sweeps the frames its row tiles read (the pass schedule built by
+// qsched.hip).  Every frame's key tile -- the (4 + ky - 1) x (4 + kx - 1) keys
+// anchored at (4 by, 4 bx), in NBY x NBX blocks of 4 x 4 -- is staged once into an
+// LDS ring with direct global->LDS loads and read by all QS_SLOTS row tiles in
+// flight (2 per wave), which belong to the kt slices that read that frame.
+//
+// Per frame and wave, for both of its slots (always, busy or idle: no branch on
+// the MFMA path):
+//   S^T = K Q^T        16x16x32 bf16 MFMA, K rows from LDS, Q^T held in registers
+//   mask to the query's own window (additive 0 / -inf biases set at activation),
+//   online softmax in the log2 domain, P kept as bf16 fragments
+//   O^T += V^T P^T     V^T by transposed LDS reads (ds_read_b64_tr_b16)
+// A slot's row tile is activated at its first frame (Q rows staged by direct
+// loads issued with the frame's first tile loads) and written out after its kt-th.
+#include "internal.hpp"
+#include "tube.hpp"
+
+namespace dsa3d {
+
+template <int D, int NBY, int NBX>
+struct FwdCfg {
+  static constexpr int NB = NBY * NBX;              // key blocks of a frame tile
+  static constexpr int NBPAD = (NB + 1) & ~1;       // whole 32-key pairs for the V pass
+  static constexpr int NPAIR = NBPAD / 2;
+  static constexpr int NPH = D / 64;                // 128-byte column phases per K (or V) row
+  static constexpr int NPH2 = 2 * NPH;              // ring steps per frame
+  static constexpr int TILE = NBPAD * 16 * 128;     // one phase tile
+  static constexpr int NLOADS = NB * 2;             // 1 KB direct loads per phase tile
+  static constexpr int NBUF = 5, PD = NBUF - 1;     // ring depth, steps loaded ahead
+  static constexpr int NC = D / 32, NT = D / 16;
+  static constexpr int QTILE = 16 * 128;            // one phase of a staged row tile
+};
+
+constexpr int FWD_NW = QS_SLOTS / 2;  // waves; 2 slots each
+
+template <int D, int NBY, int NBX>
+__global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restrict__ q, const u16* __restrict__ k,
+                                                           const u16* __restrict__ v, u16* __restrict__ out,
+                                                           float* __restrict__ lse, Geom g, Prep p, float sl2) {
+  using C = FwdCfg<D, NBY, NBX>;
+  constexpr int NS = 2;
+  __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::TILE];
+  __shared__ __attribute__((aligned(1024))) char stage[QS_SLOTS][C::NPH * C::QTILE];
+  __shared__ int s_ids[QS_MAXT][16];
+  __shared__ int2 s_st[QS_MAXT][16];
+  __shared__ int s_tau[QS_MAXT];
+  __shared__ short s_act[QS_TS + 16][QS_SLOTS];  // tile activated on (frame index, slot), or -1
+  __shared__ int s_frames[QS_TS + 16];
+  __shared__ int s_hdr[2];
+
+  const int nbc = g.nby * g.nbx, nw = qs_items(g);
+  int L = xcd_remap(blockIdx.x, nw * g.H);
+  const int h = L / nw, w = L - h * nw;
+  const int chunk = w / nbc, bc = w - chunk * nbc;
+  const int by = bc / g.nbx, bx = bc - by * g.nbx;
+  (void)chunk;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int my_loads = (C::NLOADS - wave + FWD_NW - 1) / FWD_NW;
+
+  // zero the ring once: pad rows (the odd block of the last pair) stay zero
+  for (int i = tid; i < C::NBUF * C::TILE / 16; i += 64 * FWD_NW)
+    reinterpret_cast<uint4*>(&ring[0][0])[i] = uint4{0u, 0u, 0u, 0u};
+
+  // per-lane LDS offsets of the fragments inside a phase tile (block 0)
+  int roff[C::NC / C::NPH], toff[C::NT / C::NPH];
+#pragma unroll
+  for (int c = 0; c < C::NC / C::NPH; ++c) roff[c] = sw(r16, c * 64 + quad * 16);
+#pragma unroll
+  for (int t = 0; t < C::NT / C::NPH; ++t) toff[t] = sw(4 * quad + (r16 >> 2), (t * 16 + 4 * (r16 & 3)) * 2);
+
+  // slot state (slots 2 wave, 2 wave + 1)
+  Frag<u16> qf[NS][C::NC];
+  f32x4_t oacc[NS][C::NT];
+  f32x4_t sacc[NS][C::NB];
+  Frag<u16> pf[NS][C::NPAIR];
+  float ybias[NS][NBY], xbias[NS][NBX][4];
+  float m_run[NS], l_run[NS];
+  int qn[NS], fend[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) zero_frag(qf[s][c]);
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) oacc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NBY; ++i) ybias[s][i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NBX; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xbias[s][j][i] = 0.f;
+    m_run[s] = 0.f;
+    l_run[s] = 0.f;
+    qn[s] = -1;
+    fend[s] = -1;
+  }
+
+  // direct loads of phase ph of frame f into ring slot dst: rows of the key tile,
+  // (row & 15) = key (row-in-block, col-in-block) of block row >> 4
+  auto issue_tile = [&](char* dst, const u16* src, int f, int ph) {
+    for (int j = wave; j < C::NLOADS; j += FWD_NW) {
+      const int row = 8 * j + (lane >> 3), b = row >> 4, kk = row & 15;
+      const int bi = b / NBX, bj = b - bi * NBX;
+      const int y = 4 * by + 4 * bi + (kk >> 2), x = 4 * bx + 4 * bj + (kk & 3);
+      // rows outside the grid read token 0: finite values that the mask weighs 0
+      const int tok = (y < g.Hp && x < g.Wp) ? (f * g.Hp + y) * g.Wp + x : 0;
+      const int ch = (lane & 7) ^ (row & 7);
+      dma16(src + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8, dst + j * 1024);
+    }
+  };
+  // Q rows of pass tile t into slot sl's staging area (this wave's slots only)
+  auto issue_q = [&](int sl, int t) {
+#pragma unroll
+    for (int j = 0; j < 2 * C::NPH; ++j) {
+      const int ph = j >> 1, hh = j & 1;
+      const int row = 8 * hh + (lane >> 3), ch = (lane & 7) ^ (row & 7);
+      const int tok = s_ids[t][row];
+      dma16(q + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8, stage[sl] + ph * C::QTILE + hh * 1024);
+    }
+  };
+
+  const int* sp = p.qs + p.qs_off[w];
+  const int npass = sp[0];
+  sp += 1;
+  for (int pass = 0; pass < npass; ++pass) {
+    // ---- the pass schedule into LDS
+    if (tid == 0) {
+      s_hdr[0] = sp[0];
+      s_hdr[1] = sp[1];
+    }
+    for (int i = tid; i < (QS_TS + 16) * QS_SLOTS; i += 64 * FWD_NW) (&s_act[0][0])[i] = -1;
+    __syncthreads();
+    const int nf = __builtin_amdgcn_readfirstlane(s_hdr[0]), nt = __builtin_amdgcn_readfirstlane(s_hdr[1]);
+    for (int i = tid; i < nf; i += 64 * FWD_NW) s_frames[i] = sp[2 + i];
+    const int* tl = sp + 2 + nf;
+    for (int i = tid; i < nt * 16; i += 64 * FWD_NW) {
+      const int t = i >> 4, j = i & 15;
+      const int gi = tl[4 * t];
+      s_ids[t][j] = p.tq_ids[(size_t)gi * 16 + j];
+      s_st[t][j] = p.tq_st[(size_t)gi * 16 + j];
+      if (j == 0) {
+        s_tau[t] = tl[4 * t + 1];
+        s_act[tl[4 * t + 3]][tl[4 * t + 2]] = (short)t;
+      }
+    }
+    sp += 2 + nf + 4 * nt;
+    __syncthreads();
+
+    const int nsteps = nf * C::NPH2;
+    // step x: phase x % NPH2 of frame index x / NPH2; K phases first, then V.  Q rows
+    // of the tiles that start at a frame go out just before its first tile loads,
+    // so the wait that covers those covers them too.
+    auto issue_step = [&](int x) {
+      const int fi = x / C::NPH2, ph = x - fi * C::NPH2;
+      const int f = __builtin_amdgcn_readfirstlane(s_frames[fi]);
+      if (ph == 0) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int t = __builtin_amdgcn_readfirstlane((int)s_act[fi][2 * wave + s]);
+          if (t >= 0) issue_q(2 * wave + s, t);
+        }
+      }
+      issue_tile(ring[x % C::NBUF], ph < C::NPH ? k : v, f, ph % C::NPH);
+    };
+    int issued = 0;
+    for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
+    wait_vmcnt(0);
+    __syncthreads();
+
+    for (int fi = 0; fi < nf; ++fi) {
+      const int f = __builtin_amdgcn_readfirstlane(s_frames[fi]);
+      // ---- activations: Q fragments, window biases, fresh softmax state
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int sl = 2 * wave + s;
+        const int t = __builtin_amdgcn_readfirstlane((int)s_act[fi][sl]);
+        if (t >= 0) {
+#pragma unroll
+          for (int c = 0; c < C::NC; ++c)
+            load_frag(qf[s][c], (const u16*)(stage[sl] + (c >> 1) * C::QTILE + sw(r16, (c & 1) * 64 + quad * 16)));
+          const int2 st = s_st[t][r16];
+#pragma unroll
+          for (int i = 0; i < NBY; ++i)
+            ybias[s][i] = (unsigned)(4 * by + 4 * i + quad - st.x) < (unsigned)g.ky ? 0.f : -INFINITY;
+#pragma unroll
+          for (int j = 0; j < NBX; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              xbias[s][j][i] = (unsigned)(4 * bx + 4 * j + i - st.y) < (unsigned)g.kx ? 0.f : -INFINITY;
+          qn[s] = st.x >= 0 ? s_ids[t][r16] : -1;
+          fend[s] = __builtin_amdgcn_readfirstlane(s_tau[t]) + g.kt - 1;
+          m_run[s] = -INFINITY;  // the first rescale (alpha = 0) clears O and l
+        }
+      }
+
+      static_for<0, C::NPH2>([&](auto PHC) {
+        constexpr int ph = decltype(PHC)::value;
+        const int st = fi * C::NPH2 + ph;
+        if (issued < nsteps) {
+          issue_step(issued);
+          ++issued;
+        }
+        const char* tb = ring[st % C::NBUF];
+        if constexpr (ph < C::NPH) {
+          // ---- S^T += K Q^T over this column phase
+          if constexpr (ph == 0) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+              for (int b = 0; b < C::NB; ++b) sacc[s][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int c = 0; c < C::NC / C::NPH; ++c) {
+#pragma unroll
+            for (int b = 0; b < C::NB; ++b) {
+              Frag<u16> a;
+              load_frag(a, (const u16*)(tb + b * 2048 + roff[c]));
+#pragma unroll
+              for (int s = 0; s < NS; ++s) sacc[s][b] = mma(a, qf[s][ph * (C::NC / C::NPH) + c], sacc[s][b]);
+            }
+          }
+          if constexpr (ph == C::NPH - 1) {
+            // ---- window mask, online softmax (log2 domain), P as bf16 pairs
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              float cm = -INFINITY;
+#pragma unroll
+              for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const float x = sacc[s][b][i] * sl2 + (ybias[s][b / NBX] + xbias[s][b % NBX][i]);
+                  sacc[s][b][i] = x;
+                  cm = fmaxf(cm, x);
+                }
+              cm = quad_max(cm);
+              const float mn = fmaxf(m_run[s], cm);
+              const float mref = (mn == -INFINITY) ? 0.f : mn;
+              const float alpha = __builtin_amdgcn_exp2f(m_run[s] - mref);
+              float ps = 0.f;
+              static_for<0, C::NPAIR>([&](auto CC) {
+                constexpr int c = decltype(CC)::value;
+                constexpr bool odd = 2 * c + 1 < C::NB;  // else the pad block: P = 0
+                float pr[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  pr[i] = __builtin_amdgcn_exp2f(sacc[s][2 * c][i] - mref);
+                  pr[i + 4] = odd ? __builtin_amdgcn_exp2f(sacc[s][odd ? 2 * c + 1 : 0][i] - mref) : 0.f;
+                  ps += pr[i] + pr[i + 4];
+                }
+                set_frag(pf[s][c], pr);
+              });
+              ps = quad_sum(ps);
+              l_run[s] = l_run[s] * alpha + ps;
+              m_run[s] = mn;
+#pragma unroll
+              for (int t = 0; t < C::NT; ++t) oacc[s][t] *= alpha;
+            }
+          }
+        } else {
+          // ---- O^T += V^T P^T over this column phase
+          constexpr int vph = ph - C::NPH;
+#pragma unroll
+          for (int c = 0; c < C::NPAIR; ++c) {
+#pragma unroll
+            for (int dt = 0; dt < C::NT / C::NPH; ++dt) {
+              const char* pa = tb + (2 * c) * 2048 + toff[dt];
+              const shortx4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
+              const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
+              Frag<u16> a;
+              const shortx4_t both[2] = {lo, hi};
+              __builtin_memcpy(&a.v, both, 16);
+#pragma unroll
+              for (int s = 0; s < NS; ++s) {
+                constexpr int ot = vph * (C::NT / C::NPH);
+                oacc[s][ot + dt] = mma(a, pf[s][c], oacc[s][ot + dt]);
+              }
+            }
+          }
+          if constexpr (ph == C::NPH2 - 1) {
+            // ---- tiles whose last frame this was: normalise and write
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              if (f == fend[s]) {
+                if (qn[s] >= 0) {
+                  const float inv = 1.f / l_run[s];
+                  u16* orow = out + ((size_t)qn[s] * g.H + h) * D;
+#pragma unroll
+                  for (int t = 0; t < C::NT; ++t)
+                    store4(orow + t * 16 + quad * 4, oacc[s][t][0] * inv, oacc[s][t][1] * inv, oacc[s][t][2] * inv,
+                           oacc[s][t][3] * inv);
+                  if (quad == 0) lse[(size_t)h * g.N + qn[s]] = (m_run[s] + log2f(l_run[s])) * LN2;
+                }
+                fend[s] = -1;
+              }
+            }
+          }
+        }
+        // step st + 1 (and the Q rows issued before it) must have landed; later
+        // steps may stay in flight (Q rows only make the count stricter)
+        wait_vmcnt(my_loads * max(issued - st - 2, 0));
+        lds_barrier();
+      });
+    }
+  }
+}
+
+// bf16 rows of 64 or 128, windows whose key tile spans at most 3 x 3 blocks, and
+// 3 <= kt <= 16 (a slot's next Q rows load while its current tile reads its last
+// frames; a pass lists at most QS_TS + kt - 1 frames).
+bool fwd_qs_eligible(const Geom& g, int dtype, int D) {
+  return dtype == 1 && (D == 64 || D == 128) && qs_geometry(g);
+}
+
+template <int D, int NBY, int NBX>
+static hipError_t fwd_qs_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  const long long total = (long long)qs_items(g) * g.H;
+  k_forward_qs<D, NBY, NBX><<<(unsigned)total, 64 * FWD_NW, 0, s>>>(
+      (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.out, a.lse_out, g, p, a.scale * LOG2E);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t fwd_qs_dispatch(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  const int nby = (4 + g.ky - 1 + 3) / 4 <= 2 ? 2 : 3, nbx = (4 + g.kx - 1 + 3) / 4 <= 2 ? 2 : 3;
+  if (nby == 2) return nbx == 2 ? fwd_qs_impl<D, 2, 2>(a, g, p, s) : fwd_qs_impl<D, 2, 3>(a, g, p, s);
+  return nbx == 2 ? fwd_qs_impl<D, 3, 2>(a, g, p, s) : fwd_qs_impl<D, 3, 3>(a, g, p, s);
+}
+
+hipError_t launch_forward_qs(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  return D == 64 ? fwd_qs_dispatch<64>(a, g, p, s) : fwd_qs_dispatch<128>(a, g, p, s);
+}
+
+}  // namespace dsa3d

@@ -24,6 +24,11 @@ struct Prep {
   int* kv_off;         // [nkb * Lt + 1]: items of key block column kb, slice tau
   int* kv_ids;         // [max_kv_items * 16] query tokens, 16 per item
   int2* kv_st;         // [max_kv_items * 16] (sy, sx) window starts
+  // query-side frame-sweeping kernels (qs_geometry() only)
+  int* tq_ids;         // [max_groups * 16] row tile query tokens
+  int2* tq_st;         // [max_groups * 16] row tile (sy, sx) window starts
+  int* qs_off;         // [qs_items + 1] schedule of work item w at qs + qs_off[w]
+  int* qs;             // schedules (see qsched.hip)
   int* perm;           // = the vals buffer the sort ends in
   int radix_blocks;
   int radix_passes;
@@ -50,6 +55,18 @@ inline size_t max_kv_items(const Geom& g) {
   return ((size_t)9 * g.N + 15) / 16 + (size_t)kv_item_columns(g) * g.Lt + 1;
 }
 
+// Query-side schedules: a work item is one start blob column and QS_TS slices;
+// QS_SLOTS row tiles in flight, at most QS_MAXT per pass.
+constexpr int QS_TS = 32, QS_SLOTS = 8, QS_MAXT = 64;
+__host__ __device__ inline bool qs_geometry(const Geom& g) { return g.kt >= 3 && g.kt <= 16 && g.ky <= 9 && g.kx <= 9; }
+__host__ __device__ inline int qs_items(const Geom& g) { return g.nby * g.nbx * ((g.Lt + QS_TS - 1) / QS_TS); }
+// A pass holds 2 + (frames <= QS_TS + kt - 1) + 4 ints per tile and schedules at
+// least one tile; every item has a pass count.
+inline size_t qs_ints(const Geom& g, int max_groups) {
+  return (size_t)qs_items(g) + (size_t)max_groups * (QS_TS + g.kt + 5);
+}
+hipError_t launch_qsched(const Geom& g, const Prep& p, hipStream_t s);
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -66,10 +83,9 @@ struct AttnArgs {
 
 // Per-group kernels: any geometry.
 hipError_t launch_forward_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
-// Frame-sweeping kernels that share each staged key tile between the queries of
-// kt slices: windows up to 8 x 9 x 9.
-bool tube_eligible(const Geom& g, int dtype, int D);
-hipError_t launch_forward_tube(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
+// Query-side frame-sweeping forward (bf16, qs_geometry()): needs launch_qsched().
+bool fwd_qs_eligible(const Geom& g, int dtype, int D);
+hipError_t launch_forward_qs(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
 
 // v1 backward pieces: dQ (also writes p.delta) and dK/dV.
 hipError_t launch_backward_dq_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
