@@ -1,0 +1,322 @@
+// Frame-sweeping dQ of 3D Deformable Slide Attention (MegaSlide-DiT, section
+// "3D Deformable Slide Attention": the gradient of the windowed softmax attention
+// with respect to the queries, dQ = scale * dS K with dS = P (dP - Delta),
+// P = exp(scale Q K^T - lse), dP = dO V^T, Delta = rowsum(dO * O)), bf16.
+//
+// Same work decomposition as the forward (attn_fwd.hip): a workgroup sweeps the
+// frames of one start blob column, every frame's key tile goes through an LDS ring
+// once and serves the QS_SLOTS row tiles in flight, 2 per wave, always computed.
+// A frame takes four ring steps (D = 128): V columns 0-63 and 64-127 (dP^T =
+// V dO^T), then K columns 0-63 and 64-127 (S^T = K Q^T); at the last one P^T and
+// dS^T follow and dQ^T += K^T dS^T reads both K steps transposed, so the ring keeps
+// the previous step's tile (prefetch distance NBUF - 2).
+//
+// Delta comes from k_delta, one pass over O and dO.
+#include "qs_common.hpp"
+
+namespace dsa3d {
+
+// Delta[h][n] = sum_d dO[n][h][d] O[n][h][d] (fp32), D / 8 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void k_delta(const u16* __restrict__ o, const u16* __restrict__ dout,
+                                               float* __restrict__ delta, int N, int H) {
+  constexpr int LPR = D / 8, RPW = 64 / LPR;  // lanes per row, rows per wave
+  const int lane = threadIdx.x & 63, sub = lane % LPR;
+  const long long rows = (long long)N * H;
+  for (long long r0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW; r0 < rows;
+       r0 += (long long)gridDim.x * 4 * RPW) {
+    const long long r = r0 + lane / LPR;
+    float s = 0.f;
+    if (r < rows) {
+      const uint4 a = *reinterpret_cast<const uint4*>(o + r * D + sub * 8);
+      const uint4 b = *reinterpret_cast<const uint4*>(dout + r * D + sub * 8);
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s += __uint_as_float(av[i] << 16) * __uint_as_float(bv[i] << 16);
+        s += __uint_as_float(av[i] & 0xffff0000u) * __uint_as_float(bv[i] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m, 64);
+    if (r < rows && sub == 0) {
+      const long long n = r / H, h = r - n * H;
+      delta[h * N + n] = s;
+    }
+  }
+}
+
+template <int D, int NBY, int NBX>
+struct DqCfg {
+  static constexpr int NB = NBY * NBX;
+  static constexpr int NBPAD = (NB + 1) & ~1;
+  static constexpr int NPAIR = NBPAD / 2;
+  static constexpr int NPH = D / 64, NPH2 = 2 * NPH;
+  static constexpr int TILE = NBPAD * 16 * 128;
+  static constexpr int NLOADS = NB * 2;
+  static constexpr int NBUF = 4, PD = NBUF - 2;  // the previous K step stays readable
+  static constexpr int NC = D / 32, NT = D / 16;
+  static constexpr int RTILE = NPH * 2048;       // one staged row tile (Q or dO)
+  static constexpr int SLOT = 2 * RTILE + 128;   // Q, dO, lse (64 B), Delta (64 B)
+};
+
+constexpr int DQ_NW = QS_SLOTS / 2;
+
+template <int D, int NBY, int NBX>
+__global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q, const u16* __restrict__ k,
+                                                     const u16* __restrict__ v, const u16* __restrict__ dout,
+                                                     const float* __restrict__ lse, const float* __restrict__ delta,
+                                                     u16* __restrict__ dq, Geom g, Prep p, float sl2, float scale) {
+  using C = DqCfg<D, NBY, NBX>;
+  constexpr int NS = 2;
+  __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::TILE];
+  __shared__ __attribute__((aligned(1024))) char stage[QS_SLOTS][C::SLOT];
+  __shared__ QsPass T;
+
+  const int nbc = g.nby * g.nbx, nw = qs_items(g);
+  int L = xcd_remap(blockIdx.x, nw * g.H);
+  const int h = L / nw, w = L - h * nw;
+  const int bc = w % nbc;
+  const int by = bc / g.nbx, bx = bc - by * g.nbx;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int my_loads = (C::NLOADS - wave + DQ_NW - 1) / DQ_NW;
+
+  for (int i = tid; i < C::NBUF * C::TILE / 16; i += 64 * DQ_NW)
+    reinterpret_cast<uint4*>(&ring[0][0])[i] = uint4{0u, 0u, 0u, 0u};
+
+  int roff[C::NC / C::NPH], toff[C::NT / C::NPH];
+#pragma unroll
+  for (int c = 0; c < C::NC / C::NPH; ++c) roff[c] = sw(r16, c * 64 + quad * 16);
+#pragma unroll
+  for (int t = 0; t < C::NT / C::NPH; ++t) toff[t] = sw(4 * quad + (r16 >> 2), (t * 16 + 4 * (r16 & 3)) * 2);
+
+  Frag<u16> qf[NS][C::NC], dof[NS][C::NC];
+  f32x4_t dqa[NS][C::NT];
+  f32x4_t sacc[NS][C::NB], dpa[NS][C::NB];
+  Frag<u16> dsf[NS][C::NPAIR];
+  float ybias[NS][NBY], xbias[NS][NBX][4];
+  float lse2[NS], dlt[NS];
+  int qn[NS], fend[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      zero_frag(qf[s][c]);
+      zero_frag(dof[s][c]);
+    }
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) dqa[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NBY; ++i) ybias[s][i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NBX; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xbias[s][j][i] = 0.f;
+    lse2[s] = 0.f;
+    dlt[s] = 0.f;
+    qn[s] = -1;
+    fend[s] = -1;
+  }
+
+  const int* sp = p.qs + p.qs_off[w];
+  const int npass = sp[0];
+  sp += 1;
+  for (int pass = 0; pass < npass; ++pass) {
+    load_pass(T, sp, p, tid, 64 * DQ_NW);
+    const int nf = __builtin_amdgcn_readfirstlane(T.hdr[0]);
+    const int nsteps = nf * C::NPH2;
+    // step x: V phases first, then K phases.  The rows, lse and Delta of tiles that
+    // start at a frame go out just before its first tile loads.
+    auto issue_step = [&](int x) {
+      const int fi = x / C::NPH2, ph = x - fi * C::NPH2;
+      const int f = __builtin_amdgcn_readfirstlane(T.frames[fi]);
+      if (ph == 0) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int sl = 2 * wave + s;
+          const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
+          if (t >= 0) {
+            issue_rows<D>(stage[sl], q, T.ids[t], g, h, lane);
+            issue_rows<D>(stage[sl] + C::RTILE, dout, T.ids[t], g, h, lane);
+            if (lane < 16) {
+              const size_t n = T.ids[t][lane];
+              dma4(lse + (size_t)h * g.N + n, stage[sl] + 2 * C::RTILE);
+              dma4(delta + (size_t)h * g.N + n, stage[sl] + 2 * C::RTILE + 64);
+            }
+          }
+        }
+      }
+      issue_key_tile<D, NBX, C::NB, DQ_NW>(ring[x % C::NBUF], ph < C::NPH ? v : k, g, by, bx, h, f, ph % C::NPH, wave,
+                                            lane);
+    };
+    int issued = 0;
+    for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
+    wait_vmcnt(0);
+    __syncthreads();
+
+    for (int fi = 0; fi < nf; ++fi) {
+      const int f = __builtin_amdgcn_readfirstlane(T.frames[fi]);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int sl = 2 * wave + s;
+        const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
+        if (t >= 0) {
+#pragma unroll
+          for (int c = 0; c < C::NC; ++c) {
+            const int off = (c >> 1) * 2048 + sw(r16, (c & 1) * 64 + quad * 16);
+            load_frag(qf[s][c], (const u16*)(stage[sl] + off));
+            load_frag(dof[s][c], (const u16*)(stage[sl] + C::RTILE + off));
+          }
+          lse2[s] = reinterpret_cast<const float*>(stage[sl] + 2 * C::RTILE)[r16] * LOG2E;
+          dlt[s] = reinterpret_cast<const float*>(stage[sl] + 2 * C::RTILE + 64)[r16];
+          const int2 st = T.st[t][r16];
+#pragma unroll
+          for (int i = 0; i < NBY; ++i)
+            ybias[s][i] = (unsigned)(4 * by + 4 * i + quad - st.x) < (unsigned)g.ky ? 0.f : -INFINITY;
+#pragma unroll
+          for (int j = 0; j < NBX; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              xbias[s][j][i] = (unsigned)(4 * bx + 4 * j + i - st.y) < (unsigned)g.kx ? 0.f : -INFINITY;
+          qn[s] = st.x >= 0 ? T.ids[t][r16] : -1;
+          fend[s] = __builtin_amdgcn_readfirstlane(T.tau[t]) + g.kt - 1;
+#pragma unroll
+          for (int tt = 0; tt < C::NT; ++tt) dqa[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+
+      static_for<0, C::NPH2>([&](auto PHC) {
+        constexpr int ph = decltype(PHC)::value;
+        constexpr int kph = ph - C::NPH;  // K column phase (ph >= NPH)
+        const int st = fi * C::NPH2 + ph;
+        if (issued < nsteps) {
+          issue_step(issued);
+          ++issued;
+        }
+        const char* tb = ring[st % C::NBUF];
+        // ---- dP^T += V dO^T (ph < NPH) or S^T += K Q^T (ph >= NPH) over this column phase
+        if constexpr (ph == 0 || ph == C::NPH) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int b = 0; b < C::NB; ++b) {
+              if constexpr (ph == 0)
+                dpa[s][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              else
+                sacc[s][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < C::NC / C::NPH; ++c) {
+#pragma unroll
+          for (int b = 0; b < C::NB; ++b) {
+            Frag<u16> a;
+            load_frag(a, (const u16*)(tb + b * 2048 + roff[c]));
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              if constexpr (ph < C::NPH)
+                dpa[s][b] = mma(a, dof[s][ph * (C::NC / C::NPH) + c], dpa[s][b]);
+              else
+                sacc[s][b] = mma(a, qf[s][kph * (C::NC / C::NPH) + c], sacc[s][b]);
+            }
+          }
+        }
+        if constexpr (ph == C::NPH2 - 1) {
+          // ---- P^T and dS^T on the window, as bf16 pairs of key blocks
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            auto ds_of = [&](int b, int i) {
+              const float x = sacc[s][b][i] * sl2 + (ybias[s][b / NBX] + xbias[s][b % NBX][i]) - lse2[s];
+              return __builtin_amdgcn_exp2f(x) * (dpa[s][b][i] - dlt[s]);
+            };
+            static_for<0, C::NPAIR>([&](auto CC) {
+              constexpr int c = decltype(CC)::value;
+              constexpr bool odd = 2 * c + 1 < C::NB;  // else the pad block: dS = 0
+              float d8[8];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                d8[i] = ds_of(2 * c, i);
+                d8[i + 4] = odd ? ds_of(odd ? 2 * c + 1 : 0, i) : 0.f;
+              }
+              set_frag(dsf[s][c], d8);
+            });
+          }
+          // ---- dQ^T += K^T dS^T: this step's K columns and the previous step's
+#pragma unroll
+          for (int kp = 0; kp < C::NPH; ++kp) {
+            const char* kt_ = (kp == C::NPH - 1) ? tb : ring[(st - (C::NPH - 1 - kp)) % C::NBUF];
+#pragma unroll
+            for (int c = 0; c < C::NPAIR; ++c) {
+#pragma unroll
+              for (int dt = 0; dt < C::NT / C::NPH; ++dt) {
+                const char* pa = kt_ + (2 * c) * 2048 + toff[dt];
+                const shortx4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
+                const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
+                Frag<u16> a;
+                const shortx4_t both[2] = {lo, hi};
+                __builtin_memcpy(&a.v, both, 16);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                  const int ot = kp * (C::NT / C::NPH) + dt;
+                  dqa[s][ot] = mma(a, dsf[s][c], dqa[s][ot]);
+                }
+              }
+            }
+          }
+          // ---- tiles whose last frame this was: write dQ = scale dQ^T^T
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            if (f == fend[s]) {
+              if (qn[s] >= 0) {
+                u16* row = dq + ((size_t)qn[s] * g.H + h) * D;
+#pragma unroll
+                for (int t = 0; t < C::NT; ++t)
+                  store4(row + t * 16 + quad * 4, dqa[s][t][0] * scale, dqa[s][t][1] * scale, dqa[s][t][2] * scale,
+                         dqa[s][t][3] * scale);
+              }
+              fend[s] = -1;
+            }
+          }
+        }
+        wait_vmcnt(my_loads * max(issued - st - 2, 0));
+        lds_barrier();
+      });
+    }
+  }
+}
+
+bool dq_qs_eligible(const Geom& g, int dtype, int D) { return fwd_qs_eligible(g, dtype, D); }
+
+template <int D, int NBY, int NBX>
+static hipError_t dq_qs_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  const long long total = (long long)qs_items(g) * g.H;
+  k_dq_qs<D, NBY, NBX><<<(unsigned)total, 64 * DQ_NW, 0, s>>>((const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
+                                                              (const u16*)a.dout, a.lse, p.delta, (u16*)a.out, g, p,
+                                                              a.scale * LOG2E, a.scale);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dq_qs_dispatch(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  const int nby = (4 + g.ky - 1 + 3) / 4 <= 2 ? 2 : 3, nbx = (4 + g.kx - 1 + 3) / 4 <= 2 ? 2 : 3;
+  if (nby == 2) return nbx == 2 ? dq_qs_impl<D, 2, 2>(a, g, p, s) : dq_qs_impl<D, 2, 3>(a, g, p, s);
+  return nbx == 2 ? dq_qs_impl<D, 3, 2>(a, g, p, s) : dq_qs_impl<D, 3, 3>(a, g, p, s);
+}
+
+hipError_t launch_delta(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  const long long rows = (long long)g.N * g.H;
+  const int rpb = 4 * (64 / (D / 8));
+  const unsigned blocks = (unsigned)min((rows + rpb - 1) / rpb, 8192LL);
+  if (D == 64)
+    k_delta<64><<<blocks, 256, 0, s>>>((const u16*)a.o, (const u16*)a.dout, p.delta, g.N, g.H);
+  else
+    k_delta<128><<<blocks, 256, 0, s>>>((const u16*)a.o, (const u16*)a.dout, p.delta, g.N, g.H);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_qs(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  return D == 64 ? dq_qs_dispatch<64>(a, g, p, s) : dq_qs_dispatch<128>(a, g, p, s);
+}
+
+}  // namespace dsa3d

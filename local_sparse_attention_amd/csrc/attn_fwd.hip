@@ -16,8 +16,7 @@
 //   O^T += V^T P^T     V^T by transposed LDS reads (ds_read_b64_tr_b16)
 // A slot's row tile is activated at its first frame (Q rows staged by direct
 // loads issued with the frame's first tile loads) and written out after its kt-th.
-#include "internal.hpp"
-#include "tube.hpp"
+#include "qs_common.hpp"
 
 namespace dsa3d {
 
@@ -45,12 +44,7 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
   constexpr int NS = 2;
   __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::TILE];
   __shared__ __attribute__((aligned(1024))) char stage[QS_SLOTS][C::NPH * C::QTILE];
-  __shared__ int s_ids[QS_MAXT][16];
-  __shared__ int2 s_st[QS_MAXT][16];
-  __shared__ int s_tau[QS_MAXT];
-  __shared__ short s_act[QS_TS + 16][QS_SLOTS];  // tile activated on (frame index, slot), or -1
-  __shared__ int s_frames[QS_TS + 16];
-  __shared__ int s_hdr[2];
+  __shared__ QsPass T;
 
   const int nbc = g.nby * g.nbx, nw = qs_items(g);
   int L = xcd_remap(blockIdx.x, nw * g.H);
@@ -99,56 +93,12 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
     fend[s] = -1;
   }
 
-  // direct loads of phase ph of frame f into ring slot dst: rows of the key tile,
-  // (row & 15) = key (row-in-block, col-in-block) of block row >> 4
-  auto issue_tile = [&](char* dst, const u16* src, int f, int ph) {
-    for (int j = wave; j < C::NLOADS; j += FWD_NW) {
-      const int row = 8 * j + (lane >> 3), b = row >> 4, kk = row & 15;
-      const int bi = b / NBX, bj = b - bi * NBX;
-      const int y = 4 * by + 4 * bi + (kk >> 2), x = 4 * bx + 4 * bj + (kk & 3);
-      // rows outside the grid read token 0: finite values that the mask weighs 0
-      const int tok = (y < g.Hp && x < g.Wp) ? (f * g.Hp + y) * g.Wp + x : 0;
-      const int ch = (lane & 7) ^ (row & 7);
-      dma16(src + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8, dst + j * 1024);
-    }
-  };
-  // Q rows of pass tile t into slot sl's staging area (this wave's slots only)
-  auto issue_q = [&](int sl, int t) {
-#pragma unroll
-    for (int j = 0; j < 2 * C::NPH; ++j) {
-      const int ph = j >> 1, hh = j & 1;
-      const int row = 8 * hh + (lane >> 3), ch = (lane & 7) ^ (row & 7);
-      const int tok = s_ids[t][row];
-      dma16(q + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8, stage[sl] + ph * C::QTILE + hh * 1024);
-    }
-  };
-
   const int* sp = p.qs + p.qs_off[w];
   const int npass = sp[0];
   sp += 1;
   for (int pass = 0; pass < npass; ++pass) {
-    // ---- the pass schedule into LDS
-    if (tid == 0) {
-      s_hdr[0] = sp[0];
-      s_hdr[1] = sp[1];
-    }
-    for (int i = tid; i < (QS_TS + 16) * QS_SLOTS; i += 64 * FWD_NW) (&s_act[0][0])[i] = -1;
-    __syncthreads();
-    const int nf = __builtin_amdgcn_readfirstlane(s_hdr[0]), nt = __builtin_amdgcn_readfirstlane(s_hdr[1]);
-    for (int i = tid; i < nf; i += 64 * FWD_NW) s_frames[i] = sp[2 + i];
-    const int* tl = sp + 2 + nf;
-    for (int i = tid; i < nt * 16; i += 64 * FWD_NW) {
-      const int t = i >> 4, j = i & 15;
-      const int gi = tl[4 * t];
-      s_ids[t][j] = p.tq_ids[(size_t)gi * 16 + j];
-      s_st[t][j] = p.tq_st[(size_t)gi * 16 + j];
-      if (j == 0) {
-        s_tau[t] = tl[4 * t + 1];
-        s_act[tl[4 * t + 3]][tl[4 * t + 2]] = (short)t;
-      }
-    }
-    sp += 2 + nf + 4 * nt;
-    __syncthreads();
+    load_pass(T, sp, p, tid, 64 * FWD_NW);
+    const int nf = __builtin_amdgcn_readfirstlane(T.hdr[0]);
 
     const int nsteps = nf * C::NPH2;
     // step x: phase x % NPH2 of frame index x / NPH2; K phases first, then V.  Q rows
@@ -156,15 +106,16 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
     // so the wait that covers those covers them too.
     auto issue_step = [&](int x) {
       const int fi = x / C::NPH2, ph = x - fi * C::NPH2;
-      const int f = __builtin_amdgcn_readfirstlane(s_frames[fi]);
+      const int f = __builtin_amdgcn_readfirstlane(T.frames[fi]);
       if (ph == 0) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const int t = __builtin_amdgcn_readfirstlane((int)s_act[fi][2 * wave + s]);
-          if (t >= 0) issue_q(2 * wave + s, t);
+          const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][2 * wave + s]);
+          if (t >= 0) issue_rows<D>(stage[2 * wave + s], q, T.ids[t], g, h, lane);
         }
       }
-      issue_tile(ring[x % C::NBUF], ph < C::NPH ? k : v, f, ph % C::NPH);
+      issue_key_tile<D, NBX, C::NB, FWD_NW>(ring[x % C::NBUF], ph < C::NPH ? k : v, g, by, bx, h, f, ph % C::NPH, wave,
+                                             lane);
     };
     int issued = 0;
     for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
@@ -172,17 +123,17 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
     __syncthreads();
 
     for (int fi = 0; fi < nf; ++fi) {
-      const int f = __builtin_amdgcn_readfirstlane(s_frames[fi]);
+      const int f = __builtin_amdgcn_readfirstlane(T.frames[fi]);
       // ---- activations: Q fragments, window biases, fresh softmax state
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int sl = 2 * wave + s;
-        const int t = __builtin_amdgcn_readfirstlane((int)s_act[fi][sl]);
+        const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
         if (t >= 0) {
 #pragma unroll
           for (int c = 0; c < C::NC; ++c)
             load_frag(qf[s][c], (const u16*)(stage[sl] + (c >> 1) * C::QTILE + sw(r16, (c & 1) * 64 + quad * 16)));
-          const int2 st = s_st[t][r16];
+          const int2 st = T.st[t][r16];
 #pragma unroll
           for (int i = 0; i < NBY; ++i)
             ybias[s][i] = (unsigned)(4 * by + 4 * i + quad - st.x) < (unsigned)g.ky ? 0.f : -INFINITY;
@@ -191,8 +142,8 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               xbias[s][j][i] = (unsigned)(4 * bx + 4 * j + i - st.y) < (unsigned)g.kx ? 0.f : -INFINITY;
-          qn[s] = st.x >= 0 ? s_ids[t][r16] : -1;
-          fend[s] = __builtin_amdgcn_readfirstlane(s_tau[t]) + g.kt - 1;
+          qn[s] = st.x >= 0 ? T.ids[t][r16] : -1;
+          fend[s] = __builtin_amdgcn_readfirstlane(T.tau[t]) + g.kt - 1;
           m_run[s] = -INFINITY;  // the first rescale (alpha = 0) clears O and l
         }
       }

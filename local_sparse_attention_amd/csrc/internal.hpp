@@ -86,6 +86,10 @@ hipError_t launch_forward_v1(int dtype, int D, const AttnArgs& a, const Geom& g,
 // Query-side frame-sweeping forward (bf16, qs_geometry()): needs launch_qsched().
 bool fwd_qs_eligible(const Geom& g, int dtype, int D);
 hipError_t launch_forward_qs(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
+// Query-side dQ (same eligibility and schedule) and the Delta pass it needs.
+bool dq_qs_eligible(const Geom& g, int dtype, int D);
+hipError_t launch_delta(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
+hipError_t launch_dq_qs(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
 
 // v1 backward pieces: dQ (also writes p.delta) and dK/dV.
 hipError_t launch_backward_dq_v1(int dtype, int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);

@@ -1,0 +1,76 @@
+// Pieces shared by the query-side frame-sweeping kernels (forward, dQ): the pass
+// tables a workgroup keeps in LDS and the direct loads of key tiles.
+#pragma once
+
+#include "internal.hpp"
+#include "tube.hpp"
+
+namespace dsa3d {
+
+// One pass of a work item's schedule (see qsched.hip), in LDS.
+struct QsPass {
+  int ids[QS_MAXT][16];             // query tokens of each tile of the pass
+  int2 st[QS_MAXT][16];             // their window starts (sy, sx)
+  int tau[QS_MAXT];                 // slice of each tile
+  short act[QS_TS + 16][QS_SLOTS];  // tile activated at (frame index, slot), or -1
+  int frames[QS_TS + 16];           // frames swept by the pass
+  int hdr[2];                       // frame count, tile count
+};
+
+// Reads the pass at sp into T (all threads of the workgroup; ends with a barrier)
+// and advances sp past it.
+__device__ __forceinline__ void load_pass(QsPass& T, const int*& sp, const Prep& p, int tid, int nthreads) {
+  if (tid == 0) {
+    T.hdr[0] = sp[0];
+    T.hdr[1] = sp[1];
+  }
+  for (int i = tid; i < (QS_TS + 16) * QS_SLOTS; i += nthreads) (&T.act[0][0])[i] = -1;
+  __syncthreads();
+  const int nf = T.hdr[0], nt = T.hdr[1];
+  for (int i = tid; i < nf; i += nthreads) T.frames[i] = sp[2 + i];
+  const int* tl = sp + 2 + nf;
+  for (int i = tid; i < nt * 16; i += nthreads) {
+    const int t = i >> 4, j = i & 15;
+    const int gi = tl[4 * t];
+    T.ids[t][j] = p.tq_ids[(size_t)gi * 16 + j];
+    T.st[t][j] = p.tq_st[(size_t)gi * 16 + j];
+    if (j == 0) {
+      T.tau[t] = tl[4 * t + 1];
+      T.act[tl[4 * t + 3]][tl[4 * t + 2]] = (short)t;
+    }
+  }
+  sp += 2 + nf + 4 * nt;
+  __syncthreads();
+}
+
+// Direct loads of column phase ph (64 bf16 columns) of the key tile of frame f
+// anchored at start blob (by, bx): NBLK blocks of 4 x 4 keys, NBX per tile row, 16
+// rows of 128 bytes each in the swizzled layout; this wave's share of the 2 NBLK
+// 1 KB loads.  Rows outside the grid read token 0 (finite values that the window
+// mask weighs 0).
+template <int D, int NBX, int NBLK, int NW>
+__device__ __forceinline__ void issue_key_tile(char* dst, const u16* src, const Geom& g, int by, int bx, int h, int f,
+                                               int ph, int wave, int lane) {
+  for (int j = wave; j < 2 * NBLK; j += NW) {
+    const int row = 8 * j + (lane >> 3), b = row >> 4, kk = row & 15;
+    const int bi = b / NBX, bj = b - bi * NBX;
+    const int y = 4 * by + 4 * bi + (kk >> 2), x = 4 * bx + 4 * bj + (kk & 3);
+    const int tok = (y < g.Hp && x < g.Wp) ? (f * g.Hp + y) * g.Wp + x : 0;
+    const int ch = (lane & 7) ^ (row & 7);
+    dma16(src + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8, dst + j * 1024);
+  }
+}
+
+// Direct loads of the 16 rows (tokens ids[0..15]) of a [N][H][D] bf16 tensor into a
+// staged row tile: NPH phases of 16 x 128 bytes, swizzled like the key tiles.
+template <int D>
+__device__ __forceinline__ void issue_rows(char* dst, const u16* src, const int* ids, const Geom& g, int h, int lane) {
+#pragma unroll
+  for (int j = 0; j < 2 * (D / 64); ++j) {
+    const int ph = j >> 1, hh = j & 1;
+    const int row = 8 * hh + (lane >> 3), ch = (lane & 7) ^ (row & 7);
+    dma16(src + ((size_t)ids[row] * g.H + h) * D + ph * 64 + ch * 8, dst + ph * 2048 + hh * 1024);
+  }
+}
+
+}  // namespace dsa3d
