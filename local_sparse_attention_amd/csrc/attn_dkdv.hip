@@ -11,14 +11,16 @@
 // no atomics, and the result does not depend on timing.
 //
 // The queries of a slice that can reach the key block (start cells in the blob box
-// of the column) are packed into items of 16 by a prep pass.  Items and, once per
-// slice, the K / V rows of the frame that enters, stream through an LDS ring with
-// direct global->LDS loads, PD entries ahead of the MFMAs.
+// of the column) are packed into items of KV_Q = 32 by a prep pass.  Items and,
+// once per slice, the K / V rows of the frame that enters, stream through an LDS
+// ring with direct global->LDS loads, PD entries ahead of the MFMAs.
 //
-// Per item and wave (16 queries x the 16 keys of its frame), bf16 MFMA:
-//   S = Q K^T, dP = dO V^T          (16x16x32, K / V fragments held in registers)
+// Per item and wave (2 row tiles of 16 queries x the 16 keys of its frame), bf16
+// MFMA 16x16x32:
+//   S = Q K^T, dP = dO V^T          (per row tile, K / V fragments held in registers)
 //   P = exp(S scale - lse) on the query's window, dS = P (dP - Delta)
-//   dV^T += dO^T P, dK^T += Q^T dS  (16x16x16, dO^T / Q^T by transposed LDS reads)
+//   dV^T += dO^T P, dK^T += Q^T dS  (32-query contraction, dO^T / Q^T by transposed
+//                                    LDS reads, P / dS straight from the S layout)
 #include "internal.hpp"
 #include "tube.hpp"
 
@@ -36,7 +38,7 @@ __device__ __forceinline__ void blob_span(int kb, int k, int L, int& b0, int& b1
 
 // ---- item lists -------------------------------------------------------------
 
-// Items (16 queries) per (key block column, slice): into off[kb * Lt + tau].
+// Items (KV_Q queries) per (key block column, slice): into off[kb * Lt + tau].
 __global__ __launch_bounds__(256) void k_kvitem_count(Geom g, const int* __restrict__ cell_ptr, int* __restrict__ off) {
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256) void k_kvitem_count(Geom g, const int* __restr
     const int b0 = (tau * g.nby + by) * g.nbx + bx0, b1 = (tau * g.nby + by) * g.nbx + bx1;
     cnt += cell_ptr[(b1 + 1) * BLOB_CELLS] - cell_ptr[b0 * BLOB_CELLS];
   }
-  off[i] = (cnt + 15) >> 4;
+  off[i] = (cnt + KV_Q - 1) / KV_Q;
 }
 
 // One wave per (key block column, slice): the queries of the blob box in sort
@@ -69,8 +71,8 @@ __global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restri
   int by0, by1, bx0, bx1;
   blob_span(kby, g.ky, g.Ly, by0, by1);
   blob_span(kbx, g.kx, g.Lx, bx0, bx1);
-  const size_t base = (size_t)off[i] * 16;
-  const int total = (off[i + 1] - off[i]) * 16;
+  const size_t base = (size_t)off[i] * KV_Q;
+  const int total = (off[i + 1] - off[i]) * KV_Q;
   int pos = 0;
   for (int by = by0; by <= by1; ++by) {
     const int b0 = (tau * g.nby + by) * g.nbx + bx0, b1 = (tau * g.nby + by) * g.nbx + bx1;
@@ -94,11 +96,11 @@ __global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restri
 template <int D>
 struct DkdvCfg {
   static constexpr int NPH = D / 64;                 // 128-byte column phases of a bf16 row
-  static constexpr int TILE = 16 * 128;              // one phase of 16 rows
-  static constexpr int META = 2 * NPH * TILE;        // item: starts (128 B), lse (64 B), delta (64 B)
-  static constexpr int ENTRY = META + 256;
-  static constexpr int NL = 4 * NPH + 3;             // direct loads per entry
-  static constexpr int NBUF = D == 128 ? 8 : 12;     // ring entries
+  static constexpr int TILE = KV_Q * 128;            // one phase of an item's KV_Q rows
+  static constexpr int META = 2 * NPH * TILE;        // item: starts (8 B), lse, delta (4 B each) per query
+  static constexpr int ENTRY = META + 16 * KV_Q;
+  static constexpr int NL = 2 * NPH * (TILE / 1024) + 3;  // direct loads per entry
+  static constexpr int NBUF = D == 128 ? 6 : 10;     // ring entries
   static constexpr int PD = NBUF - 1;                // entries in flight ahead of the one in use
   static constexpr int NIDS = PD + 2;                // token ring (loaded 2 PD + 1 entries ahead)
   static constexpr int NC = D / 32, NT = D / 16;
@@ -106,8 +108,8 @@ struct DkdvCfg {
 
 struct KvItems {
   const int* off;   // [nkb * Lt + 1]: items of (kb, tau) are off[kb Lt + tau] .. off[kb Lt + tau + 1]
-  const int* ids;   // [items * 16] query tokens
-  const int2* st;   // [items * 16] (sy, sx) window starts
+  const int* ids;   // [items * KV_Q] query tokens
+  const int2* st;   // [items * KV_Q] (sy, sx) window starts
 };
 
 // Position in the entry stream of a workgroup: slice tau, entry j of the slice
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
   // LDS once; item tokens arrive by direct loads into a small ring, 2 PD + 1
   // entries ahead of use.
   __shared__ int s_off[DKDV_TS + 8 + 1];
-  __shared__ int s_ids[C::NIDS][16];
+  __shared__ int s_ids[C::NIDS][KV_Q];
   for (int i = tid; i <= tau_hi - tau_lo + 1; i += 64 * NW) s_off[i] = it.off[(size_t)kb * g.Lt + tau_lo + i];
   __syncthreads();
 
@@ -181,6 +183,7 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
       const int f = c.tau + kt + c.j;
       for (int j = wave; j < C::NL; j += NW) {
         if (j < 4 * C::NPH) {
+          // the 16 key rows fill the first 2 KB of each phase tile
           const int ti = j >> 1, hh = j & 1, tensor = ti / C::NPH, ph = ti - tensor * C::NPH;
           const int row = 8 * hh + (lane >> 3), ch = (lane & 7) ^ (row & 7);
           const int y = 4 * kby + (row >> 2), x = 4 * kbx + (row & 3);
@@ -188,32 +191,34 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
           const u16* src = (tensor ? v : k) + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8;
           dma16(src, e + ti * C::TILE + hh * 1024);
         } else {
-          // keeps the per-entry load count uniform; lands in the unused meta area
-          if (lane < 16) dma4(lse, e + C::META + 128);
+          // keeps the per-entry load count uniform (one lane); lands in the unused meta area
+          if (lane == 0) dma4(lse, e + C::META);
         }
       }
     } else {
       const int item = c.base + c.j;
       const int* ids = s_ids[x % C::NIDS];
+      constexpr int NR = 2 * C::NPH * (C::TILE / 1024);  // row loads: 8 rows of 128 B each
       for (int j = wave; j < C::NL; j += NW) {
-        if (j < 4 * C::NPH) {
-          const int ti = j >> 1, hh = j & 1, tensor = ti / C::NPH, ph = ti - tensor * C::NPH;
-          const int row = 8 * hh + (lane >> 3), ch = (lane & 7) ^ (row & 7);
+        if (j < NR) {
+          const int ti = j / (C::TILE / 1024), part = j % (C::TILE / 1024);
+          const int tensor = ti / C::NPH, ph = ti - tensor * C::NPH;
+          const int row = 8 * part + (lane >> 3), ch = (lane & 7) ^ (row & 7);
           const int tok = ids[row];
           const u16* src = (tensor ? dout : q) + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8;
-          dma16(src, e + ti * C::TILE + hh * 1024);
-        } else if (j == 4 * C::NPH) {
-          if (lane < 8) dma16(it.st + (size_t)item * 16 + 2 * lane, e + C::META);
-        } else if (lane < 16) {
-          const float* src = (j == 4 * C::NPH + 1 ? lse : delta) + (size_t)h * g.N + ids[lane];
-          dma4(src, e + C::META + (j == 4 * C::NPH + 1 ? 128 : 192));
+          dma16(src, e + ti * C::TILE + part * 1024);
+        } else if (j == NR) {
+          if (lane < KV_Q / 2) dma16(it.st + (size_t)item * KV_Q + 2 * lane, e + C::META);
+        } else if (lane < KV_Q) {
+          const float* src = (j == NR + 1 ? lse : delta) + (size_t)h * g.N + ids[lane];
+          dma4(src, e + C::META + 8 * KV_Q + (j == NR + 1 ? 0 : 4 * KV_Q));
         }
       }
     }
   };
   // tokens of entry x (items only), by the last wave
   auto issue_ids = [&](const Cursor& c, int x) {
-    if (c.j >= 0 && wave == NW - 1 && lane < 16) dma4(it.ids + (size_t)(c.base + c.j) * 16 + lane, s_ids[x % C::NIDS]);
+    if (c.j >= 0 && wave == NW - 1 && lane < KV_Q) dma4(it.ids + (size_t)(c.base + c.j) * KV_Q + lane, s_ids[x % C::NIDS]);
   };
 
   // tile offsets: Q / dO (item) or K / V (frame) of phase ph
@@ -290,47 +295,70 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
         cur_f = f;
       }
     } else {
-      // ---- an item: 16 queries against this wave's frame of the key block
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      // ---- an item: 2 row tiles of 16 queries against this wave's frame of the key block
+      f32x4_t sc[2], dp[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        sc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        dp[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
-        const int off = sw(r16, (c & 1) * 64 + quad * 16);
-        Frag<u16> a;
-        load_frag(a, (const u16*)(tile(e, 0, c >> 1) + off));
-        s = mma(a, kf[c], s);
-        load_frag(a, (const u16*)(tile(e, 1, c >> 1) + off));
-        dp = mma(a, vf[c], dp);
-      }
-      // queries 4 quad + i of the item: window start, lse, delta
-      const int4 sa = *reinterpret_cast<const int4*>(e + C::META + quad * 32);
-      const int4 sb = *reinterpret_cast<const int4*>(e + C::META + quad * 32 + 16);
-      const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 128 + quad * 16);
-      const float4 de = *reinterpret_cast<const float4*>(e + C::META + 192 + quad * 16);
-      const int sy[4] = {sa.x, sa.z, sb.x, sb.z}, sx[4] = {sa.y, sa.w, sb.y, sb.w};
-      const float lq[4] = {ls.x, ls.y, ls.z, ls.w}, dq[4] = {de.x, de.y, de.z, de.w};
-      float pv[4], dsv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = (unsigned)(key_y - sy[i]) < (unsigned)g.ky && (unsigned)(key_x - sx[i]) < (unsigned)g.kx;
-        const float p = __builtin_amdgcn_exp2f(s[i] * sl2 - lq[i] * LOG2E);
-        pv[i] = ok ? p : 0.f;
-        dsv[i] = pv[i] * (dp[i] - dq[i]);
+        for (int r = 0; r < 2; ++r) {
+          const int off = sw(16 * r + r16, (c & 1) * 64 + quad * 16);
+          Frag<u16> a;
+          load_frag(a, (const u16*)(tile(e, 0, c >> 1) + off));
+          sc[r] = mma(a, kf[c], sc[r]);
+          load_frag(a, (const u16*)(tile(e, 1, c >> 1) + off));
+          dp[r] = mma(a, vf[c], dp[r]);
+        }
       }
-      shortx4v pb, db;
+      // P and dS of queries 16 r + 4 quad + i (slots 4 r + i of the B fragments)
+      float pv[8], dsv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = __builtin_bit_cast(short, static_cast<__bf16>(pv[i]));
-        db[i] = __builtin_bit_cast(short, static_cast<__bf16>(dsv[i]));
+      for (int r = 0; r < 2; ++r) {
+        const int q0 = 16 * r + 4 * quad;
+        const int4 sa = *reinterpret_cast<const int4*>(e + C::META + q0 * 8);
+        const int4 sb = *reinterpret_cast<const int4*>(e + C::META + q0 * 8 + 16);
+        const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 8 * KV_Q + q0 * 4);
+        const float4 de = *reinterpret_cast<const float4*>(e + C::META + 12 * KV_Q + q0 * 4);
+        const int sy[4] = {sa.x, sa.z, sb.x, sb.z}, sx[4] = {sa.y, sa.w, sb.y, sb.w};
+        const float lq[4] = {ls.x, ls.y, ls.z, ls.w}, dq[4] = {de.x, de.y, de.z, de.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (unsigned)(key_y - sy[i]) < (unsigned)g.ky && (unsigned)(key_x - sx[i]) < (unsigned)g.kx;
+          const float pe = __builtin_amdgcn_exp2f(sc[r][i] * sl2 - lq[i] * LOG2E);
+          pv[4 * r + i] = ok ? pe : 0.f;
+          dsv[4 * r + i] = pv[4 * r + i] * (dp[r][i] - dq[i]);
+        }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS: A = 4 query rows x 16 d columns, transposed
+      Frag<u16> pb, db;
+      set_frag(pb, pv);
+      set_frag(db, dsv);
+      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries: A slots j < 4 are rows
+      // 4 quad + j of row tile 0, slots j >= 4 the same rows of row tile 1 (transposed)
       const int trow = 4 * quad + (r16 >> 2);
 #pragma unroll
       for (int t = 0; t < C::NT; ++t) {
         const int off = sw(trow, ((t & 3) * 16 + 4 * (r16 & 3)) * 2);
-        const shortx4v ao = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(tile(e, 1, t >> 2) + off));
-        const shortx4v aq = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(tile(e, 0, t >> 2) + off));
-        dva[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pb, dva[t], 0, 0, 0);
-        dka[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aq, db, dka[t], 0, 0, 0);
+        Frag<u16> ao, aq;
+        {
+          const char* base = tile(e, 1, t >> 2) + off;
+          const shortx4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)base);
+          const shortx4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(base + 16 * 128));
+          const shortx4v both[2] = {lo, hi};
+          __builtin_memcpy(&ao.v, both, 16);
+        }
+        {
+          const char* base = tile(e, 0, t >> 2) + off;
+          const shortx4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)base);
+          const shortx4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(base + 16 * 128));
+          const shortx4v both[2] = {lo, hi};
+          __builtin_memcpy(&aq.v, both, 16);
+        }
+        dva[t] = mma(ao, pb, dva[t]);
+        dka[t] = mma(aq, db, dka[t]);
       }
     }
     // entry st + 1 must have landed; entries st + 2 .. issued - 1 may stay in flight

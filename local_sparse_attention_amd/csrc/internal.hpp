@@ -22,8 +22,8 @@ struct Prep {
   float* delta;        // [H][N] (backward only)
   // key-centric dK/dV item lists (backward, kv_items_geometry() only)
   int* kv_off;         // [nkb * Lt + 1]: items of key block column kb, slice tau
-  int* kv_ids;         // [max_kv_items * 16] query tokens, 16 per item
-  int2* kv_st;         // [max_kv_items * 16] (sy, sx) window starts
+  int* kv_ids;         // [max_kv_items * KV_Q] query tokens, KV_Q per item
+  int2* kv_st;         // [max_kv_items * KV_Q] (sy, sx) window starts
   // query-side frame-sweeping kernels (qs_geometry() only)
   int* tq_ids;         // [max_groups * 16] row tile query tokens
   int2* tq_st;         // [max_groups * 16] row tile (sy, sx) window starts
@@ -49,10 +49,11 @@ hipError_t launch_scan_excl(uint32_t* data, int n, hipStream_t s);
 // (ky, kx <= 9) and kt <= 8 (one wave per frame in flight).
 inline bool kv_items_geometry(const Geom& g) { return g.kt <= 8 && g.ky <= 9 && g.kx <= 9; }
 inline int kv_item_columns(const Geom& g) { return ((g.Hp + 3) / 4) * ((g.Wp + 3) / 4); }
-// Items are 16 queries of one slice whose start blob can reach the column: every
+// Items are KV_Q queries of one slice whose start blob can reach the column: every
 // query counts for at most 3 x 3 columns.
+constexpr int KV_Q = 32;
 inline size_t max_kv_items(const Geom& g) {
-  return ((size_t)9 * g.N + 15) / 16 + (size_t)kv_item_columns(g) * g.Lt + 1;
+  return ((size_t)9 * g.N + KV_Q - 1) / KV_Q + (size_t)kv_item_columns(g) * g.Lt + 1;
 }
 
 // Query-side schedules: a work item is one start blob column and QS_TS slices;

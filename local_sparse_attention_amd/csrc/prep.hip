@@ -57,8 +57,8 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   q.delta = backward ? (float*)take(N * g.H * 4) : nullptr;
   const bool kv = backward && kv_items_geometry(g);
   q.kv_off = kv ? (int*)take(((size_t)kv_item_columns(g) * g.Lt + 1) * 4) : nullptr;
-  q.kv_ids = kv ? (int*)take(max_kv_items(g) * 16 * 4) : nullptr;
-  q.kv_st = kv ? (int2*)take(max_kv_items(g) * 16 * sizeof(int2)) : nullptr;
+  q.kv_ids = kv ? (int*)take(max_kv_items(g) * KV_Q * 4) : nullptr;
+  q.kv_st = kv ? (int2*)take(max_kv_items(g) * KV_Q * sizeof(int2)) : nullptr;
   const bool qsg = qs_geometry(g);
   q.tq_ids = qsg ? (int*)take((size_t)max_groups * 16 * 4) : nullptr;
   q.tq_st = qsg ? (int2*)take((size_t)max_groups * 16 * sizeof(int2)) : nullptr;
