@@ -4,6 +4,8 @@ N = 2,088,960 tokens, a 16-head slice of head_dim 128, window 5 x 9 x 9, bf16, s
 drifting motion field), inputs resident in HBM.
 
 One step = dsa3d_forward + dsa3d_backward over the whole grid.  Prints one JSON line.
+  phases_ms  per step, from HIP events the library records on its stream: bucketing
+             and work lists (+ Delta in the backward), then each attention kernel
   value      query-token-heads per second (N * heads / step time)
   roofline   the dominant kernel's algorithmic bytes per launch / its mean duration,
              timed with HIP events on the library's stream, against 8 TB/s HBM
@@ -52,17 +54,22 @@ class Hip:
         return float(ms.value)
 
 
+# timed phase -> the attention kernel it holds on the bf16 path (rocprofv3 names)
+KERNEL_OF = {"k_forward": "k_forward_qs", "k_backward_dq": "k_dq_qs", "k_backward_dkdv": "k_dkdv_tube"}
+
+
 def kernel_work(wl):
     """Algorithmic flops and HBM bytes per launch of each attention kernel (per
     (query token, head) unit times N*H units):
       forward  4KD flops (QK^T, PV);            reads Q, K, V, writes O, LSE: 4Ds + 4 B
-      dQ       6KD flops (S, dP, dQ);           reads Q, K, V, O, dO, LSE, writes dQ, Delta: 6Ds + 8 B
+      dQ       6KD flops (S, dP, dQ);           reads Q, K, V, dO, LSE, Delta, writes dQ: 5Ds + 8 B
       dK/dV    8KD flops (S, dP, dV, dK);       reads Q, K, V, dO, LSE, Delta, writes dK, dV: 6Ds + 8 B
+    (Delta = rowsum(dO * O) is its own pass, 2Ds + 4 B, timed with the backward prep.)
     """
     K, D, s, NH = wl.K, wl.head_dim, wl.elem_bytes, wl.N * wl.heads
     return {
         "k_forward": (4 * K * D * NH, (4 * D * s + 4) * NH),
-        "k_backward_dq": (6 * K * D * NH, (6 * D * s + 8) * NH),
+        "k_backward_dq": (6 * K * D * NH, (5 * D * s + 8) * NH),
         "k_backward_dkdv": (8 * K * D * NH, (6 * D * s + 8) * NH),
     }
 
@@ -217,8 +224,8 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": kf / t_dom / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom, wl.name)
-    roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(KERNEL_OF[dom], wl.name)
+    roof["kernel"] = KERNEL_OF[dom] if wl.dtype == "bf16" else dom
     roof["kernel_ms"] = phases[dom]
 
     res = {

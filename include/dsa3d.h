@@ -104,10 +104,11 @@ int dsa3d_backward(const void* q, const void* k, const void* v, const int32_t* o
 /* Profiling variants: the same work as dsa3d_forward / dsa3d_backward, plus
    hipEventRecord(events[i], stream) at the phase boundaries, so the caller can
    time each kernel on the stream it runs on.  `events` holds caller-created
-   events: forward 3 ([0] before the bucketing of queries by window start, [1]
-   before the attention kernel, [2] after it); backward 4 ([0] before the
-   bucketing, [1] before the dQ kernel, [2] before the dK/dV kernel, [3] after
-   it).  A null `events` gives the untimed call. */
+   events: forward 3 ([0] before the bucketing of queries by window start and the
+   work lists, [1] before the attention kernel, [2] after it); backward 4 ([0]
+   before the bucketing, the work lists and the Delta = rowsum(dO * O) pass, [1]
+   before the dQ kernel, [2] before the dK/dV kernel, [3] after it).  A null
+   `events` gives the untimed call. */
 int dsa3d_forward_timed(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
                         int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out,
                         float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,

@@ -116,19 +116,17 @@ int dsa3d_backward_timed(const void* q, const void* k, const void* v, const int3
   const bool qs = !generic_only() && dq_qs_eligible(g, dtype, head_dim);
   if (kv_tube && launch_kv_items(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   if (qs && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  if (events) hipEventRecord(events[1], stream);
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v;
   a.o = out; a.dout = dout; a.lse = lse;
   a.out = dq; a.dk = dk; a.dv = dv;
   a.scale = scale;
-  // dQ; both dQ paths leave Delta = rowsum(dO * O) in the workspace for dK/dV
-  if (qs) {
-    if (launch_delta(head_dim, a, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-    if (launch_dq_qs(head_dim, a, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  } else if (launch_backward_dq_v1(dtype, head_dim, a, g, p, stream) != hipSuccess) {
+  // Delta = rowsum(dO * O) for both kernels (the per-group dQ kernel makes its own)
+  if (qs && launch_delta(head_dim, a, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (events) hipEventRecord(events[1], stream);
+  if (qs ? launch_dq_qs(head_dim, a, g, p, stream) != hipSuccess
+         : launch_backward_dq_v1(dtype, head_dim, a, g, p, stream) != hipSuccess)
     return DSA3D_ERR_LAUNCH;
-  }
   if (events) hipEventRecord(events[2], stream);
   const hipError_t e = kv_tube ? launch_dkdv_tube(head_dim, a, g, p, stream)
                                : launch_backward_dkdv_v1(dtype, head_dim, a, g, p, stream);
