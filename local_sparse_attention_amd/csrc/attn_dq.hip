@@ -147,8 +147,8 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           }
         }
       }
-      issue_key_tile<D, NBX, C::NB, DQ_NW>(ring[x % C::NBUF], ph < C::NPH ? v : k, g, by, bx, h, f, ph % C::NPH, wave,
-                                            lane);
+      issue_key_tile<D, NBX, C::NB, C::NB, DQ_NW>(ring[x % C::NBUF], ph < C::NPH ? v : k, g, by, bx, h, f,
+                                                   ph % C::NPH, wave, lane);
     };
     int issued = 0;
     for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);

@@ -28,7 +28,7 @@ struct FwdCfg {
   static constexpr int NPH = D / 64;                // 128-byte column phases per K (or V) row
   static constexpr int NPH2 = 2 * NPH;              // ring steps per frame
   static constexpr int TILE = NBPAD * 16 * 128;     // one phase tile
-  static constexpr int NLOADS = NB * 2;             // 1 KB direct loads per phase tile
+  static constexpr int NLOADS = NBPAD * 2;          // 1 KB direct loads per phase tile (pad block too)
   static constexpr int NBUF = 5, PD = NBUF - 1;     // ring depth, steps loaded ahead
   static constexpr int NC = D / 32, NT = D / 16;
   static constexpr int QTILE = 16 * 128;            // one phase of a staged row tile
@@ -54,11 +54,7 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
   (void)chunk;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int my_loads = (C::NLOADS - wave + FWD_NW - 1) / FWD_NW;
-
-  // zero the ring once: pad rows (the odd block of the last pair) stay zero
-  for (int i = tid; i < C::NBUF * C::TILE / 16; i += 64 * FWD_NW)
-    reinterpret_cast<uint4*>(&ring[0][0])[i] = uint4{0u, 0u, 0u, 0u};
+  constexpr int MY_LOADS = C::NLOADS / FWD_NW;  // per wave and step
 
   // per-lane LDS offsets of the fragments inside a phase tile (block 0)
   int roff[C::NC / C::NPH], toff[C::NT / C::NPH];
@@ -114,8 +110,8 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
           if (t >= 0) issue_rows<D>(stage[2 * wave + s], q, T.ids[t], g, h, lane);
         }
       }
-      issue_key_tile<D, NBX, C::NB, FWD_NW>(ring[x % C::NBUF], ph < C::NPH ? k : v, g, by, bx, h, f, ph % C::NPH, wave,
-                                             lane);
+      issue_key_tile<D, NBX, C::NB, C::NBPAD, FWD_NW>(ring[x % C::NBUF], ph < C::NPH ? k : v, g, by, bx, h, f,
+                                                      ph % C::NPH, wave, lane);
     };
     int issued = 0;
     for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
@@ -188,9 +184,19 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
                   cm = fmaxf(cm, x);
                 }
               cm = quad_max(cm);
-              const float mn = fmaxf(m_run[s], cm);
-              const float mref = (mn == -INFINITY) ? 0.f : mn;
-              const float alpha = __builtin_amdgcn_exp2f(m_run[s] - mref);
+              // The reference max moves only when a score exceeds it by more than
+              // 2^8 (or on a tile's first frame, m = -inf): P <= 256 otherwise, and
+              // O and l need no rescale.
+              if (__ballot(cm > m_run[s] + 8.f)) {
+                const float mn = fmaxf(m_run[s], cm);
+                const float mref = (mn == -INFINITY) ? 0.f : mn;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[s] - mref);
+                l_run[s] *= alpha;
+#pragma unroll
+                for (int t = 0; t < C::NT; ++t) oacc[s][t] *= alpha;
+                m_run[s] = mref;
+              }
+              const float mref = m_run[s] == -INFINITY ? 0.f : m_run[s];
               float ps = 0.f;
               static_for<0, C::NPAIR>([&](auto CC) {
                 constexpr int c = decltype(CC)::value;
@@ -205,10 +211,7 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
                 set_frag(pf[s][c], pr);
               });
               ps = quad_sum(ps);
-              l_run[s] = l_run[s] * alpha + ps;
-              m_run[s] = mn;
-#pragma unroll
-              for (int t = 0; t < C::NT; ++t) oacc[s][t] *= alpha;
+              l_run[s] += ps;
             }
           }
         } else {
@@ -252,7 +255,10 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
         }
         // step st + 1 (and the Q rows issued before it) must have landed; later
         // steps may stay in flight (Q rows only make the count stricter)
-        wait_vmcnt(my_loads * max(issued - st - 2, 0));
+        if (issued - st - 2 == C::PD - 1)
+          wait_vmcnt_c<MY_LOADS * (C::PD - 1)>();
+        else
+          wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
         lds_barrier();
       });
     }

@@ -45,17 +45,17 @@ __device__ __forceinline__ void load_pass(QsPass& T, const int*& sp, const Prep&
 
 // Direct loads of column phase ph (64 bf16 columns) of the key tile of frame f
 // anchored at start blob (by, bx): NBLK blocks of 4 x 4 keys, NBX per tile row, 16
-// rows of 128 bytes each in the swizzled layout; this wave's share of the 2 NBLK
-// 1 KB loads.  Rows outside the grid read token 0 (finite values that the window
-// mask weighs 0).
-template <int D, int NBX, int NBLK, int NW>
+// rows of 128 bytes each in the swizzled layout; this wave's share of the 2 NLB
+// 1 KB loads (NLB >= NBLK: the extra blocks, like rows outside the grid, read the
+// frame's token (0, 0), finite values that the window mask or a zero weight ignores).
+template <int D, int NBX, int NBLK, int NLB, int NW>
 __device__ __forceinline__ void issue_key_tile(char* dst, const u16* src, const Geom& g, int by, int bx, int h, int f,
                                                int ph, int wave, int lane) {
-  for (int j = wave; j < 2 * NBLK; j += NW) {
+  for (int j = wave; j < 2 * NLB; j += NW) {
     const int row = 8 * j + (lane >> 3), b = row >> 4, kk = row & 15;
     const int bi = b / NBX, bj = b - bi * NBX;
     const int y = 4 * by + 4 * bi + (kk >> 2), x = 4 * bx + 4 * bj + (kk & 3);
-    const int tok = (y < g.Hp && x < g.Wp) ? (f * g.Hp + y) * g.Wp + x : 0;
+    const int tok = (b < NBLK && y < g.Hp && x < g.Wp) ? (f * g.Hp + y) * g.Wp + x : f * g.Hp * g.Wp;
     const int ch = (lane & 7) ^ (row & 7);
     dma16(src + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8, dst + j * 1024);
   }

@@ -58,6 +58,13 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
+// s_waitcnt vmcnt(N) for a compile-time N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
+  __asm__ __volatile__("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Logical workgroup index from the hardware one: consecutive workgroups go round
 // robin to the 8 XCDs, so hand each XCD a contiguous range of logical indices
 // (neighbouring tubes then share that XCD's L2).
