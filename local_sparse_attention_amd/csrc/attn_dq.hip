@@ -53,7 +53,7 @@ struct DqCfg {
   static constexpr int NPAIR = NBPAD / 2;
   static constexpr int NPH = D / 64, NPH2 = 2 * NPH;
   static constexpr int TILE = NBPAD * 16 * 128;
-  static constexpr int NLOADS = NB * 2;
+  static constexpr int NLOADS = NBPAD * 2;      // 1 KB loads per phase tile (pad block too)
   static constexpr int NBUF = 4, PD = NBUF - 2;  // the previous K step stays readable
   static constexpr int NC = D / 32, NT = D / 16;
   static constexpr int RTILE = NPH * 2048;       // one staged row tile (Q or dO)
@@ -80,10 +80,8 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
   const int by = bc / g.nbx, bx = bc - by * g.nbx;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int my_loads = (C::NLOADS - wave + DQ_NW - 1) / DQ_NW;
-
-  for (int i = tid; i < C::NBUF * C::TILE / 16; i += 64 * DQ_NW)
-    reinterpret_cast<uint4*>(&ring[0][0])[i] = uint4{0u, 0u, 0u, 0u};
+  constexpr int MY_LOADS = C::NLOADS / DQ_NW;  // per wave and step
+  const KeyLane klane = key_lane<D>(g, h, lane);
 
   int roff[C::NC / C::NPH], toff[C::NT / C::NPH];
 #pragma unroll
@@ -147,8 +145,8 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           }
         }
       }
-      issue_key_tile<D, NBX, C::NB, C::NB, DQ_NW>(ring[x % C::NBUF], ph < C::NPH ? v : k, g, by, bx, h, f,
-                                                   ph % C::NPH, wave, lane);
+      issue_key_tile<D, NBX, C::NB, C::NBPAD, DQ_NW>(ring[x % C::NBUF], ph < C::NPH ? v : k, g, klane, by, bx, f,
+                                                     ph % C::NPH, wave);
     };
     int issued = 0;
     for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
@@ -279,7 +277,10 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
             }
           }
         }
-        wait_vmcnt(my_loads * max(issued - st - 2, 0));
+        if (issued - st - 2 == C::PD - 1)
+          wait_vmcnt_c<MY_LOADS * (C::PD - 1)>();
+        else
+          wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
         lds_barrier();
       });
     }

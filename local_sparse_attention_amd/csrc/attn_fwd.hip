@@ -110,8 +110,8 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
           if (t >= 0) issue_rows<D>(stage[2 * wave + s], q, T.ids[t], g, h, lane);
         }
       }
-      issue_key_tile<D, NBX, C::NB, C::NBPAD, FWD_NW>(ring[x % C::NBUF], ph < C::NPH ? k : v, g, by, bx, h, f,
-                                                      ph % C::NPH, wave, lane);
+      issue_key_tile_loop<D, NBX, C::NB, C::NBPAD, FWD_NW>(ring[x % C::NBUF], ph < C::NPH ? k : v, g, by, bx, h, f,
+                                                           ph % C::NPH, wave, lane);
     };
     int issued = 0;
     for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);

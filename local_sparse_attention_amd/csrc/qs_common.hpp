@@ -43,14 +43,56 @@ __device__ __forceinline__ void load_pass(QsPass& T, const int*& sp, const Prep&
   __syncthreads();
 }
 
+// Lane constants of the key tile loads below.  Load j, lane l covers row
+// 8 j + (l >> 3) of the tile: key (2 (j & 1) + (l >> 5), (l >> 3) & 3) of block
+// j >> 1, 16-byte chunk (l & 7) ^ ((l >> 3) & 7) of the swizzled row.
+struct KeyLane {
+  int ly, lx;           // key offset inside the block's half (rows), column
+  uint32_t off, off0;   // element offset of the lane's key inside a frame; of token (0, 0)
+};
+template <int D>
+__device__ __forceinline__ KeyLane key_lane(const Geom& g, int h, int lane) {
+  KeyLane kl;
+  kl.ly = lane >> 5;
+  kl.lx = (lane >> 3) & 3;
+  kl.off0 = (uint32_t)(h * D + ((lane & 7) ^ ((lane >> 3) & 7)) * 8);
+  kl.off = (uint32_t)((kl.ly * g.Wp + kl.lx) * g.H * D) + kl.off0;
+  return kl;
+}
+
 // Direct loads of column phase ph (64 bf16 columns) of the key tile of frame f
 // anchored at start blob (by, bx): NBLK blocks of 4 x 4 keys, NBX per tile row, 16
-// rows of 128 bytes each in the swizzled layout; this wave's share of the 2 NLB
-// 1 KB loads (NLB >= NBLK: the extra blocks, like rows outside the grid, read the
-// frame's token (0, 0), finite values that the window mask or a zero weight ignores).
+// rows of 128 bytes each in the swizzled layout; this wave's share (PER loads) of
+// the 2 NLB 1 KB loads.  NLB >= NBLK: the extra blocks, like rows outside the grid,
+// read the frame's token (0, 0), finite values that the window mask or a zero
+// weight ignores.  Only the in-grid test and one add depend on the lane.
 template <int D, int NBX, int NBLK, int NLB, int NW>
-__device__ __forceinline__ void issue_key_tile(char* dst, const u16* src, const Geom& g, int by, int bx, int h, int f,
-                                               int ph, int wave, int lane) {
+__device__ __forceinline__ void issue_key_tile(char* dst, const u16* src, const Geom& g, const KeyLane& kl, int by,
+                                               int bx, int f, int ph, int wave) {
+  static_assert((2 * NLB) % NW == 0, "loads must split evenly over the waves");
+  const u16* base = src + (size_t)f * g.Hp * g.Wp * g.H * D + ph * 64;
+#pragma unroll
+  for (int jj = 0; jj < 2 * NLB / NW; ++jj) {
+    int j = wave + NW * jj;
+    // opaque to the optimiser: the per-load values below do not depend on the frame,
+    // and hoisting all of them out of the frame loop costs more registers than the
+    // few instructions it saves
+    __asm__ __volatile__("" : "+s"(j));
+    const int b = j >> 1;
+    const int bi = b / NBX, bj = b - bi * NBX;
+    const int y0 = 4 * by + 4 * bi + 2 * (j & 1), x0 = 4 * bx + 4 * bj;
+    const bool in = b < NBLK && kl.ly < g.Hp - y0 && kl.lx < g.Wp - x0;
+    const uint32_t off = in ? (uint32_t)((y0 * g.Wp + x0) * g.H * D) + kl.off : kl.off0;
+    dma16(base + off, dst + j * 1024);
+  }
+}
+
+// The same loads as issue_key_tile, as a loop over this wave's loads with the
+// address computed per lane (kernels whose registers are too tight to keep the
+// unrolled version's values live).
+template <int D, int NBX, int NBLK, int NLB, int NW>
+__device__ __forceinline__ void issue_key_tile_loop(char* dst, const u16* src, const Geom& g, int by, int bx, int h,
+                                                    int f, int ph, int wave, int lane) {
   for (int j = wave; j < 2 * NLB; j += NW) {
     const int row = 8 * j + (lane >> 3), b = row >> 4, kk = row & 15;
     const int bi = b / NBX, bj = b - bi * NBX;
