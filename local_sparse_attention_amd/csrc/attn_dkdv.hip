@@ -98,7 +98,8 @@ struct DkdvCfg {
   static constexpr int NPH = D / 64;                 // 128-byte column phases of a bf16 row
   static constexpr int TILE = KV_Q * 128;            // one phase of an item's KV_Q rows
   static constexpr int META = 2 * NPH * TILE;        // item: starts (8 B), lse, delta (4 B each) per query
-  static constexpr int ENTRY = META + 16 * KV_Q;
+  static constexpr int SINK = META + 16 * KV_Q;      // 16 bytes nobody reads: target of the padding loads
+  static constexpr int ENTRY = SINK + 16;
   static constexpr int NL = 2 * NPH * (TILE / 1024) + 3;  // direct loads per entry
   static constexpr int NBUF = D == 128 ? 6 : 10;     // ring entries
   static constexpr int PD = NBUF - 1;                // entries in flight ahead of the one in use
@@ -120,8 +121,8 @@ struct Cursor {
 
 constexpr int DKDV_TS = 32;  // frames per workgroup
 
-template <int D>
-__global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, const u16* __restrict__ k,
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_dkdv_tube(const u16* __restrict__ q, const u16* __restrict__ k,
                                                    const u16* __restrict__ v, const u16* __restrict__ dout,
                                                    const float* __restrict__ lse, const float* __restrict__ delta,
                                                    u16* __restrict__ dk, u16* __restrict__ dv, Geom g, KvItems it,
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
   using C = DkdvCfg<D>;
   __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::ENTRY];
 
-  const int kt = g.kt, NW = kt;
+  constexpr int kt = NW;  // one wave per frame in flight
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
   const int nchunk = (g.F + DKDV_TS - 1) / DKDV_TS;
   int L = xcd_remap(blockIdx.x, nkb * nchunk * g.H);
@@ -142,7 +143,9 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int my_loads = (C::NL - wave + NW - 1) / NW;
+  // every wave issues MY_LOADS loads per entry (the count is padded with one-lane
+  // loads), so the steady-state wait is a single immediate
+  constexpr int MY_LOADS = (C::NL + NW - 1) / NW, NLP = MY_LOADS * NW;
   // Nothing in the loop below reads memory through the scalar unit: a scalar load
   // in flight makes every LDS wait a full lgkmcnt(0) wait, which would put its
   // latency in front of the MFMAs.  The slice boundaries of this workgroup go to
@@ -181,7 +184,9 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
   auto issue = [&](const Cursor& c, int x, char* e) {
     if (c.j < 0) {
       const int f = c.tau + kt + c.j;
-      for (int j = wave; j < C::NL; j += NW) {
+#pragma unroll
+      for (int jj = 0; jj < MY_LOADS; ++jj) {
+        const int j = wave + NW * jj;
         if (j < 4 * C::NPH) {
           // the 16 key rows fill the first 2 KB of each phase tile
           const int ti = j >> 1, hh = j & 1, tensor = ti / C::NPH, ph = ti - tensor * C::NPH;
@@ -191,15 +196,17 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
           const u16* src = (tensor ? v : k) + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8;
           dma16(src, e + ti * C::TILE + hh * 1024);
         } else {
-          // keeps the per-entry load count uniform (one lane); lands in the unused meta area
-          if (lane == 0) dma4(lse, e + C::META);
+          // keeps the per-entry load count uniform (one lane)
+          if (lane == 0) dma4(lse, e + C::SINK);
         }
       }
     } else {
       const int item = c.base + c.j;
       const int* ids = s_ids[x % C::NIDS];
       constexpr int NR = 2 * C::NPH * (C::TILE / 1024);  // row loads: 8 rows of 128 B each
-      for (int j = wave; j < C::NL; j += NW) {
+#pragma unroll
+      for (int jj = 0; jj < MY_LOADS; ++jj) {
+        const int j = wave + NW * jj;
         if (j < NR) {
           const int ti = j / (C::TILE / 1024), part = j % (C::TILE / 1024);
           const int tensor = ti / C::NPH, ph = ti - tensor * C::NPH;
@@ -209,9 +216,13 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
           dma16(src, e + ti * C::TILE + part * 1024);
         } else if (j == NR) {
           if (lane < KV_Q / 2) dma16(it.st + (size_t)item * KV_Q + 2 * lane, e + C::META);
-        } else if (lane < KV_Q) {
-          const float* src = (j == NR + 1 ? lse : delta) + (size_t)h * g.N + ids[lane];
-          dma4(src, e + C::META + 8 * KV_Q + (j == NR + 1 ? 0 : 4 * KV_Q));
+        } else if (j < C::NL) {
+          if (lane < KV_Q) {
+            const float* src = (j == NR + 1 ? lse : delta) + (size_t)h * g.N + ids[lane];
+            dma4(src, e + C::META + 8 * KV_Q + (j == NR + 1 ? 0 : 4 * KV_Q));
+          }
+        } else if (lane == 0) {
+          dma4(lse, e + C::SINK);  // padding of the load count
         }
       }
     }
@@ -269,7 +280,7 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
     if (st < 0) {
       // (token loads only add to the count of loads issued later: the wait is exact
       // or stricter)
-      wait_vmcnt(my_loads * max(issued - st - 2, 0));
+      wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
       lds_barrier();
       continue;
     }
@@ -362,7 +373,10 @@ __global__ __launch_bounds__(512) void k_dkdv_tube(const u16* __restrict__ q, co
       }
     }
     // entry st + 1 must have landed; entries st + 2 .. issued - 1 may stay in flight
-    wait_vmcnt(my_loads * max(issued - st - 2, 0));
+    if (issued - st - 2 == C::PD - 1)
+      wait_vmcnt_c<MY_LOADS * (C::PD - 1)>();
+    else
+      wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
     lds_barrier();
     advance(cc);
   }
@@ -382,20 +396,28 @@ hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int NW>
 static hipError_t dkdv_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
   const int nkb = kv_item_columns(g);
   const int nchunk = (g.F + DKDV_TS - 1) / DKDV_TS;
   const long long total = (long long)nkb * nchunk * g.H;
   KvItems it{p.kv_off, p.kv_ids, p.kv_st};
-  k_dkdv_tube<D><<<(unsigned)total, 64 * g.kt, 0, s>>>((const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
+  k_dkdv_tube<D, NW><<<(unsigned)total, 64 * NW, 0, s>>>((const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
                                                        (const u16*)a.dout, a.lse, p.delta, (u16*)a.dk, (u16*)a.dv, g,
                                                        it, a.scale * LOG2E, a.scale);
   return hipGetLastError();
 }
 
 hipError_t launch_dkdv_tube(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
-  return D == 64 ? dkdv_impl<64>(a, g, p, s) : dkdv_impl<128>(a, g, p, s);
+  switch (g.kt) {
+#define DSA3D_DKDV_KT(n) \
+  case n:                \
+    return D == 64 ? dkdv_impl<64, n>(a, g, p, s) : dkdv_impl<128, n>(a, g, p, s);
+    DSA3D_DKDV_KT(1) DSA3D_DKDV_KT(3) DSA3D_DKDV_KT(5) DSA3D_DKDV_KT(7)
+#undef DSA3D_DKDV_KT
+    default:
+      return hipErrorInvalidValue;  // kv_items_geometry() admits odd kt <= 8 only
+  }
 }
 
 }  // namespace dsa3d

@@ -58,11 +58,12 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
-// s_waitcnt vmcnt(N) for a compile-time N.
+// s_waitcnt vmcnt(N) for a compile-time N >= 0.  The field holds 6 bits; a larger
+// N is clamped to 63, which only makes the wait stricter.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_c() {
-  static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
-  __asm__ __volatile__("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0, "vmcnt counts are non-negative");
+  __asm__ __volatile__("s_waitcnt vmcnt(%0)" ::"n"(N > 63 ? 63 : N) : "memory");
 }
 
 // Logical workgroup index from the hardware one: consecutive workgroups go round
