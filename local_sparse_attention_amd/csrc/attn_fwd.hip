@@ -34,14 +34,21 @@ struct FwdCfg {
   static constexpr int QTILE = 16 * 128;            // one phase of a staged row tile
 };
 
-constexpr int FWD_NW = QS_SLOTS / 2;  // waves; 2 slots each
+// Row-tile slots per wave: with one, the QS_SLOTS slots take 8 waves (2 per SIMD),
+// so one wave's LDS and scalar work issues beside the other's VALU and MFMA work;
+// with two, a K / V fragment read from LDS feeds the MFMAs of both slots.
+#ifndef DSA3D_FWD_NS
+#define DSA3D_FWD_NS 1
+#endif
+constexpr int FWD_NS = DSA3D_FWD_NS;
+constexpr int FWD_NW = QS_SLOTS / FWD_NS;
 
 template <int D, int NBY, int NBX>
 __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restrict__ q, const u16* __restrict__ k,
                                                            const u16* __restrict__ v, u16* __restrict__ out,
                                                            float* __restrict__ lse, Geom g, Prep p, float sl2) {
   using C = FwdCfg<D, NBY, NBX>;
-  constexpr int NS = 2;
+  constexpr int NS = FWD_NS;
   __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::TILE];
   __shared__ __attribute__((aligned(1024))) char stage[QS_SLOTS][C::NPH * C::QTILE];
   __shared__ QsPass T;
@@ -54,7 +61,11 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
   (void)chunk;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int MY_LOADS = C::NLOADS / FWD_NW;  // per wave and step
+  // tile loads per wave and step: the same for every wave (waves past the remainder
+  // add one padding load), so the steady-state wait is one immediate
+  constexpr int MY_LOADS = (C::NLOADS + FWD_NW - 1) / FWD_NW;
+  constexpr int NREM = C::NLOADS % FWD_NW;
+  __shared__ int s_sink[4];
 
   // per-lane LDS offsets of the fragments inside a phase tile (block 0)
   int roff[C::NC / C::NPH], toff[C::NT / C::NPH];
@@ -106,12 +117,13 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
       if (ph == 0) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][2 * wave + s]);
-          if (t >= 0) issue_rows<D>(stage[2 * wave + s], q, T.ids[t], g, h, lane);
+          const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][NS * wave + s]);
+          if (t >= 0) issue_rows<D>(stage[NS * wave + s], q, T.ids[t], g, h, lane);
         }
       }
       issue_key_tile_loop<D, NBX, C::NB, C::NBPAD, FWD_NW>(ring[x % C::NBUF], ph < C::NPH ? k : v, g, by, bx, h, f,
                                                            ph % C::NPH, wave, lane);
+      if (NREM != 0 && wave >= NREM && lane == 0) dma4(k, s_sink);
     };
     int issued = 0;
     for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
@@ -123,7 +135,7 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
       // ---- activations: Q fragments, window biases, fresh softmax state
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int sl = 2 * wave + s;
+        const int sl = NS * wave + s;
         const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
         if (t >= 0) {
 #pragma unroll
