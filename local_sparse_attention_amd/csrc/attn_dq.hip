@@ -60,7 +60,12 @@ struct DqCfg {
   static constexpr int SLOT = 2 * RTILE + 128;   // Q, dO, lse (64 B), Delta (64 B)
 };
 
-constexpr int DQ_NW = QS_SLOTS / 2;
+// Row-tile slots per wave (see attn_fwd.hip): one, so 8 waves run 2 per SIMD.
+#ifndef DSA3D_DQ_NS
+#define DSA3D_DQ_NS 1
+#endif
+constexpr int DQ_NS = DSA3D_DQ_NS;
+constexpr int DQ_NW = QS_SLOTS / DQ_NS;
 
 template <int D, int NBY, int NBX>
 __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q, const u16* __restrict__ k,
@@ -68,7 +73,7 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
                                                      const float* __restrict__ lse, const float* __restrict__ delta,
                                                      u16* __restrict__ dq, Geom g, Prep p, float sl2, float scale) {
   using C = DqCfg<D, NBY, NBX>;
-  constexpr int NS = 2;
+  constexpr int NS = DQ_NS;
   __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::TILE];
   __shared__ __attribute__((aligned(1024))) char stage[QS_SLOTS][C::SLOT];
   __shared__ QsPass T;
@@ -80,8 +85,10 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
   const int by = bc / g.nbx, bx = bc - by * g.nbx;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int MY_LOADS = C::NLOADS / DQ_NW;  // per wave and step
-  const KeyLane klane = key_lane<D>(g, h, lane);
+  // tile loads per wave and step, the same for every wave (padding loads)
+  constexpr int MY_LOADS = (C::NLOADS + DQ_NW - 1) / DQ_NW;
+  constexpr int NREM = C::NLOADS % DQ_NW;
+  __shared__ int s_sink[4];
 
   int roff[C::NC / C::NPH], toff[C::NT / C::NPH];
 #pragma unroll
@@ -132,7 +139,7 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
       if (ph == 0) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const int sl = 2 * wave + s;
+          const int sl = NS * wave + s;
           const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
           if (t >= 0) {
             issue_rows<D>(stage[sl], q, T.ids[t], g, h, lane);
@@ -145,8 +152,9 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           }
         }
       }
-      issue_key_tile<D, NBX, C::NB, C::NBPAD, DQ_NW>(ring[x % C::NBUF], ph < C::NPH ? v : k, g, klane, by, bx, f,
-                                                     ph % C::NPH, wave);
+      issue_key_tile_loop<D, NBX, C::NB, C::NBPAD, DQ_NW>(ring[x % C::NBUF], ph < C::NPH ? v : k, g, by, bx, h, f,
+                                                          ph % C::NPH, wave, lane);
+      if (NREM != 0 && wave >= NREM && lane == 0) dma4(k, s_sink);
     };
     int issued = 0;
     for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
       const int f = __builtin_amdgcn_readfirstlane(T.frames[fi]);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int sl = 2 * wave + s;
+        const int sl = NS * wave + s;
         const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
         if (t >= 0) {
 #pragma unroll
