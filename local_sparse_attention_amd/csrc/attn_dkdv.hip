@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restri
 
 // ---- the dK / dV kernel -----------------------------------------------------
 
-template <int D>
+template <int D, int KT>
 struct DkdvCfg {
   static constexpr int NPH = D / 64;                 // 128-byte column phases of a bf16 row
   static constexpr int TILE = KV_Q * 128;            // one phase of an item's KV_Q rows
@@ -101,8 +101,9 @@ struct DkdvCfg {
   static constexpr int SINK = META + 16 * KV_Q;      // 16 bytes nobody reads: target of the padding loads
   static constexpr int ENTRY = SINK + 16;
   static constexpr int NL = 2 * NPH * (TILE / 1024) + 3;  // direct loads per entry
-  static constexpr int NBUF = D == 128 ? 6 : 10;     // ring entries
-  static constexpr int PD = NBUF - 1;                // entries in flight ahead of the one in use
+  static constexpr int NBUF = D == 128 ? (KT >= 7 ? 4 : 5) : 8;  // ring entries (LDS: ring, P / dS, K / V copies)
+  static constexpr int KV = 2 * NPH * 2048;          // K and V rows of one frame's key block
+  static constexpr int PD = NBUF - 2;                // entries in flight (the previous one stays readable)
   static constexpr int NIDS = PD + 2;                // token ring (loaded 2 PD + 1 entries ahead)
   static constexpr int NC = D / 32, NT = D / 16;
 };
@@ -121,16 +122,27 @@ struct Cursor {
 
 constexpr int DKDV_TS = 32;  // frames per workgroup
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void k_dkdv_tube(const u16* __restrict__ q, const u16* __restrict__ k,
-                                                   const u16* __restrict__ v, const u16* __restrict__ dout,
-                                                   const float* __restrict__ lse, const float* __restrict__ delta,
-                                                   u16* __restrict__ dk, u16* __restrict__ dv, Geom g, KvItems it,
-                                                   float sl2, float scale) {
-  using C = DkdvCfg<D>;
+template <int D, int KT>
+__global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ q, const u16* __restrict__ k,
+                                                       const u16* __restrict__ v, const u16* __restrict__ dout,
+                                                       const float* __restrict__ lse,
+                                                       const float* __restrict__ delta, u16* __restrict__ dk,
+                                                       u16* __restrict__ dv, Geom g, KvItems it, float sl2,
+                                                       float scale) {
+  using C = DkdvCfg<D, KT>;
+  constexpr int kt = KT;
+  // Two waves per frame in flight: wave 2 s + hf holds K / V of the frames
+  // t = s (mod kt) and the dK / dV columns [hf D / 2, (hf + 1) D / 2) of their keys.
+  // For each item, wave hf of a pair forms S, dP, P and dS of row tile hf and leaves
+  // P and dS in LDS; in the next step both apply dV^T += dO^T P and dK^T += Q^T dS
+  // over all 32 queries to their half.  The ring therefore keeps the previous entry
+  // (prefetch distance NBUF - 2).
+  constexpr int NW = 2 * KT;
+  constexpr int NTH = C::NT / 2;  // d tiles per half
   __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::ENTRY];
+  __shared__ __attribute__((aligned(16))) char xch[2][KT][2][64 * 16];  // [step parity][frame slot][P, dS]
+  __shared__ __attribute__((aligned(1024))) char kvs[KT][C::KV];          // K, V rows of each pair's frame
 
-  constexpr int kt = NW;  // one wave per frame in flight
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
   const int nchunk = (g.F + DKDV_TS - 1) / DKDV_TS;
   int L = xcd_remap(blockIdx.x, nkb * nchunk * g.H);
@@ -143,9 +155,10 @@ __global__ __launch_bounds__(64 * NW) void k_dkdv_tube(const u16* __restrict__ q
 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fslot = wave >> 1, hf = wave & 1;
   // every wave issues MY_LOADS loads per entry (the count is padded with one-lane
   // loads), so the steady-state wait is a single immediate
-  constexpr int MY_LOADS = (C::NL + NW - 1) / NW, NLP = MY_LOADS * NW;
+  constexpr int MY_LOADS = (C::NL + NW - 1) / NW;
   // Nothing in the loop below reads memory through the scalar unit: a scalar load
   // in flight makes every LDS wait a full lgkmcnt(0) wait, which would put its
   // latency in front of the MFMAs.  The slice boundaries of this workgroup go to
@@ -195,9 +208,8 @@ __global__ __launch_bounds__(64 * NW) void k_dkdv_tube(const u16* __restrict__ q
           const int tok = (y < g.Hp && x < g.Wp) ? (f * g.Hp + y) * g.Wp + x : 0;
           const u16* src = (tensor ? v : k) + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8;
           dma16(src, e + ti * C::TILE + hh * 1024);
-        } else {
-          // keeps the per-entry load count uniform (one lane)
-          if (lane == 0) dma4(lse, e + C::SINK);
+        } else if (lane == 0) {
+          dma4(lse, e + C::SINK);  // keeps the per-entry load count uniform
         }
       }
     } else {
@@ -235,10 +247,9 @@ __global__ __launch_bounds__(64 * NW) void k_dkdv_tube(const u16* __restrict__ q
   // tile offsets: Q / dO (item) or K / V (frame) of phase ph
   auto tile = [&](char* e, int tensor, int ph) { return e + (tensor * C::NPH + ph) * C::TILE; };
 
-  Frag<u16> kf[C::NC], vf[C::NC];
-  f32x4_t dka[C::NT], dva[C::NT];
+  f32x4_t dka[NTH], dva[NTH];
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
+  for (int t = 0; t < NTH; ++t) {
     dka[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     dva[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -246,14 +257,84 @@ __global__ __launch_bounds__(64 * NW) void k_dkdv_tube(const u16* __restrict__ q
 
   auto finalize = [&](int f) {
     if (f >= t0 && f < t1 && key_y < g.Hp && key_x < g.Wp) {
-      const size_t row = ((size_t)((f * g.Hp + key_y) * g.Wp + key_x) * g.H + h) * D;
+      const size_t row = ((size_t)((f * g.Hp + key_y) * g.Wp + key_x) * g.H + h) * D + hf * (D / 2);
 #pragma unroll
-      for (int t = 0; t < C::NT; ++t) {
+      for (int t = 0; t < NTH; ++t) {
         store4(dk + row + 16 * t + 4 * quad, dka[t][0] * scale, dka[t][1] * scale, dka[t][2] * scale,
                dka[t][3] * scale);
         store4(dv + row + 16 * t + 4 * quad, dva[t][0], dva[t][1], dva[t][2], dva[t][3]);
       }
     }
+  };
+
+  // dV^T += dO^T P and dK^T += Q^T dS for this wave's half, with P / dS of the item
+  // in ring entry e left by the pair's producer in xch[par]
+  auto apply = [&](char* e, int par) {
+    Frag<u16> pb, db;
+    load_frag(pb, (const u16*)(xch[par][fslot][0] + lane * 16));
+    load_frag(db, (const u16*)(xch[par][fslot][1] + lane * 16));
+    // A slots j < 4: rows 4 quad + j of row tile 0; j >= 4: the same rows of row tile 1
+    const int trow = 4 * quad + (r16 >> 2);
+#pragma unroll
+    for (int tt = 0; tt < NTH; ++tt) {
+      const int t = hf * NTH + tt;
+      const int off = sw(trow, ((t & 3) * 16 + 4 * (r16 & 3)) * 2);
+      Frag<u16> ao, aq;
+      {
+        const char* base = tile(e, 1, t >> 2) + off;
+        const shortx4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)base);
+        const shortx4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(base + 16 * 128));
+        const shortx4v both[2] = {lo, hi};
+        __builtin_memcpy(&ao.v, both, 16);
+      }
+      {
+        const char* base = tile(e, 0, t >> 2) + off;
+        const shortx4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)base);
+        const shortx4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(base + 16 * 128));
+        const shortx4v both[2] = {lo, hi};
+        __builtin_memcpy(&aq.v, both, 16);
+      }
+      dva[tt] = mma(ao, pb, dva[tt]);
+      dka[tt] = mma(aq, db, dka[tt]);
+      __asm__ __volatile__("" ::: "memory");
+    }
+  };
+
+  // S = Q K^T, dP = dO V^T of row tile hf against this wave's frame, then P and dS of
+  // its queries 16 hf + 4 quad + i, which are slots 4 hf + i of the pair's B
+  // fragments in xch[par] (8 of their 16 bytes per lane)
+  auto produce = [&](char* e, int par) {
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+    const char* kv = kvs[fslot];
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      const int off = sw(16 * hf + r16, (c & 1) * 64 + quad * 16);
+      const int koff = (c >> 1) * 2048 + sw(r16, (c & 1) * 64 + quad * 16);
+      Frag<u16> a, b;
+      load_frag(a, (const u16*)(tile(e, 0, c >> 1) + off));
+      load_frag(b, (const u16*)(kv + koff));
+      sc = mma(a, b, sc);
+      load_frag(a, (const u16*)(tile(e, 1, c >> 1) + off));
+      load_frag(b, (const u16*)(kv + C::NPH * 2048 + koff));
+      dp = mma(a, b, dp);
+    }
+    const int q0 = 16 * hf + 4 * quad;
+    const int4 sa = *reinterpret_cast<const int4*>(e + C::META + q0 * 8);
+    const int4 sb = *reinterpret_cast<const int4*>(e + C::META + q0 * 8 + 16);
+    const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 8 * KV_Q + q0 * 4);
+    const float4 de = *reinterpret_cast<const float4*>(e + C::META + 12 * KV_Q + q0 * 4);
+    const int sy[4] = {sa.x, sa.z, sb.x, sb.z}, sx[4] = {sa.y, sa.w, sb.y, sb.w};
+    const float lq[4] = {ls.x, ls.y, ls.z, ls.w}, dq[4] = {de.x, de.y, de.z, de.w};
+    shortx4v pb, db;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = (unsigned)(key_y - sy[i]) < (unsigned)g.ky && (unsigned)(key_x - sx[i]) < (unsigned)g.kx;
+      const float pe = ok ? __builtin_amdgcn_exp2f(sc[i] * sl2 - lq[i] * LOG2E) : 0.f;
+      pb[i] = __builtin_bit_cast(short, static_cast<__bf16>(pe));
+      db[i] = __builtin_bit_cast(short, static_cast<__bf16>(pe * (dp[i] - dq[i])));
+    }
+    *reinterpret_cast<shortx4v*>(xch[par][fslot][0] + lane * 16 + hf * 8) = pb;
+    *reinterpret_cast<shortx4v*>(xch[par][fslot][1] + lane * 16 + hf * 8) = db;
   };
 
   // Three cursors over the same entry stream: token loads (pc, 2 PD + 1 ahead),
@@ -266,6 +347,7 @@ __global__ __launch_bounds__(64 * NW) void k_dkdv_tube(const u16* __restrict__ q
   __syncthreads();
 
   int issued = 0;
+  bool prev_item = false;  // the previous entry was an item whose dV / dK are still to apply
   for (int st = -C::PD; cc.tau <= tau_hi; ++st) {
     if (ic.tau <= tau_hi) {
       issue(ic, issued, ring[issued % C::NBUF]);
@@ -284,93 +366,34 @@ __global__ __launch_bounds__(64 * NW) void k_dkdv_tube(const u16* __restrict__ q
       lds_barrier();
       continue;
     }
+    // ---- the previous item's dV / dK (before a frame can be written out below)
+    if (prev_item) apply(ring[(st - 1) % C::NBUF], (st - 1) & 1);
     char* e = ring[st % C::NBUF];
     if (cc.j < 0) {
-      // ---- a frame enters: its owner writes the frame it leaves and takes K / V
+      // ---- a frame enters: its pair writes the frame it leaves and takes K / V
       const int f = cc.tau + kt + cc.j;
-      if (wave == f % kt) {
+      if (fslot == f % kt) {
         if (cur_f >= 0) {
           finalize(cur_f);
 #pragma unroll
-          for (int t = 0; t < C::NT; ++t) {
+          for (int t = 0; t < NTH; ++t) {
             dka[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             dva[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
         }
-#pragma unroll
-        for (int c = 0; c < C::NC; ++c) {
-          const int off = sw(r16, (c & 1) * 64 + quad * 16);
-          load_frag(kf[c], (const u16*)(tile(e, 0, c >> 1) + off));
-          load_frag(vf[c], (const u16*)(tile(e, 1, c >> 1) + off));
+        // the frame's K and V rows (first 2 KB of each phase tile of the entry) into
+        // the pair's copy; each wave copies half
+        for (int i = hf * 64 + lane; i < C::KV / 16; i += 128) {
+          const int ti = i / 128, o = (i % 128) * 16;
+          *reinterpret_cast<uint4*>(kvs[fslot] + ti * 2048 + o) = *reinterpret_cast<const uint4*>(e + ti * C::TILE + o);
         }
         cur_f = f;
       }
+      prev_item = false;
     } else {
-      // ---- an item: 2 row tiles of 16 queries against this wave's frame of the key block
-      f32x4_t sc[2], dp[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        sc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        dp[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int off = sw(16 * r + r16, (c & 1) * 64 + quad * 16);
-          Frag<u16> a;
-          load_frag(a, (const u16*)(tile(e, 0, c >> 1) + off));
-          sc[r] = mma(a, kf[c], sc[r]);
-          load_frag(a, (const u16*)(tile(e, 1, c >> 1) + off));
-          dp[r] = mma(a, vf[c], dp[r]);
-        }
-      }
-      // P and dS of queries 16 r + 4 quad + i (slots 4 r + i of the B fragments)
-      float pv[8], dsv[8];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int q0 = 16 * r + 4 * quad;
-        const int4 sa = *reinterpret_cast<const int4*>(e + C::META + q0 * 8);
-        const int4 sb = *reinterpret_cast<const int4*>(e + C::META + q0 * 8 + 16);
-        const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 8 * KV_Q + q0 * 4);
-        const float4 de = *reinterpret_cast<const float4*>(e + C::META + 12 * KV_Q + q0 * 4);
-        const int sy[4] = {sa.x, sa.z, sb.x, sb.z}, sx[4] = {sa.y, sa.w, sb.y, sb.w};
-        const float lq[4] = {ls.x, ls.y, ls.z, ls.w}, dq[4] = {de.x, de.y, de.z, de.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = (unsigned)(key_y - sy[i]) < (unsigned)g.ky && (unsigned)(key_x - sx[i]) < (unsigned)g.kx;
-          const float pe = __builtin_amdgcn_exp2f(sc[r][i] * sl2 - lq[i] * LOG2E);
-          pv[4 * r + i] = ok ? pe : 0.f;
-          dsv[4 * r + i] = pv[4 * r + i] * (dp[r][i] - dq[i]);
-        }
-      }
-      Frag<u16> pb, db;
-      set_frag(pb, pv);
-      set_frag(db, dsv);
-      // dV^T += dO^T P and dK^T += Q^T dS over the 32 queries: A slots j < 4 are rows
-      // 4 quad + j of row tile 0, slots j >= 4 the same rows of row tile 1 (transposed)
-      const int trow = 4 * quad + (r16 >> 2);
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t) {
-        const int off = sw(trow, ((t & 3) * 16 + 4 * (r16 & 3)) * 2);
-        Frag<u16> ao, aq;
-        {
-          const char* base = tile(e, 1, t >> 2) + off;
-          const shortx4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)base);
-          const shortx4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(base + 16 * 128));
-          const shortx4v both[2] = {lo, hi};
-          __builtin_memcpy(&ao.v, both, 16);
-        }
-        {
-          const char* base = tile(e, 0, t >> 2) + off;
-          const shortx4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)base);
-          const shortx4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(base + 16 * 128));
-          const shortx4v both[2] = {lo, hi};
-          __builtin_memcpy(&aq.v, both, 16);
-        }
-        dva[t] = mma(ao, pb, dva[t]);
-        dka[t] = mma(aq, db, dka[t]);
-      }
+      // ---- an item: each wave of a pair forms P and dS of one row tile
+      produce(e, st & 1);
+      prev_item = true;
     }
     // entry st + 1 must have landed; entries st + 2 .. issued - 1 may stay in flight
     if (issued - st - 2 == C::PD - 1)
@@ -379,6 +402,11 @@ __global__ __launch_bounds__(64 * NW) void k_dkdv_tube(const u16* __restrict__ q
       wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
     lds_barrier();
     advance(cc);
+    if (cc.tau > tau_hi && prev_item) {
+      // the last entry was an item: apply it (its ring slot is not reused any more)
+      apply(ring[st % C::NBUF], st & 1);
+      prev_item = false;
+    }
   }
   finalize(cur_f);
 }
@@ -396,13 +424,13 @@ hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int NW>
+template <int D, int KT>
 static hipError_t dkdv_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
   const int nkb = kv_item_columns(g);
   const int nchunk = (g.F + DKDV_TS - 1) / DKDV_TS;
   const long long total = (long long)nkb * nchunk * g.H;
   KvItems it{p.kv_off, p.kv_ids, p.kv_st};
-  k_dkdv_tube<D, NW><<<(unsigned)total, 64 * NW, 0, s>>>((const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
+  k_dkdv_tube<D, KT><<<(unsigned)total, 128 * KT, 0, s>>>((const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
                                                        (const u16*)a.dout, a.lse, p.delta, (u16*)a.dk, (u16*)a.dv, g,
                                                        it, a.scale * LOG2E, a.scale);
   return hipGetLastError();
