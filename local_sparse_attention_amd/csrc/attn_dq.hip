@@ -201,6 +201,10 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           ++issued;
         }
         const char* tb = ring[st % C::NBUF];
+        // with one slot per wave, a wave whose slot holds no tile this frame skips its
+        // MFMA work (a uniform branch) and leaves the SIMD to its partner
+        const bool busy = NS > 1 || fend[0] >= f;
+        if (busy) {
         // ---- dP^T += V dO^T (ph < NPH) or S^T += K Q^T (ph >= NPH) over this column phase
         if constexpr (ph == 0 || ph == C::NPH) {
 #pragma unroll
@@ -270,6 +274,9 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
               }
             }
           }
+        }
+        }  // busy
+        if constexpr (ph == C::NPH2 - 1) {
           // ---- tiles whose last frame this was: write dQ = scale dQ^T^T
 #pragma unroll
           for (int s = 0; s < NS; ++s) {

@@ -164,7 +164,11 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
           ++issued;
         }
         const char* tb = ring[st % C::NBUF];
+        // with one slot per wave, a wave whose slot holds no tile this frame skips its
+        // MFMA and softmax work (a uniform branch) and leaves the SIMD to its partner
+        const bool busy = NS > 1 || fend[0] >= f;
         if constexpr (ph < C::NPH) {
+          if (busy) {
           // ---- S^T += K Q^T over this column phase
           if constexpr (ph == 0) {
 #pragma unroll
@@ -226,9 +230,11 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
               l_run[s] += ps;
             }
           }
+          }
         } else {
           // ---- O^T += V^T P^T over this column phase
           constexpr int vph = ph - C::NPH;
+          if (busy) {
 #pragma unroll
           for (int c = 0; c < C::NPAIR; ++c) {
 #pragma unroll
@@ -245,6 +251,7 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
                 oacc[s][ot + dt] = mma(a, pf[s][c], oacc[s][ot + dt]);
               }
             }
+          }
           }
           if constexpr (ph == C::NPH2 - 1) {
             // ---- tiles whose last frame this was: normalise and write
