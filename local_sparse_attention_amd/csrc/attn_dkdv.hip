@@ -366,8 +366,12 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
       lds_barrier();
       continue;
     }
+    // a pair whose frame lies outside [t0, t1) computes sums nobody writes: skip
+    // (both waves of the pair agree, and the frame cannot change between an item's
+    // two steps)
+    const bool kept = cur_f >= t0 && cur_f < t1;
     // ---- the previous item's dV / dK (before a frame can be written out below)
-    if (prev_item) apply(ring[(st - 1) % C::NBUF], (st - 1) & 1);
+    if (prev_item && kept) apply(ring[(st - 1) % C::NBUF], (st - 1) & 1);
     char* e = ring[st % C::NBUF];
     if (cc.j < 0) {
       // ---- a frame enters: its pair writes the frame it leaves and takes K / V
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
       prev_item = false;
     } else {
       // ---- an item: each wave of a pair forms P and dS of one row tile
-      produce(e, st & 1);
+      if (kept) produce(e, st & 1);
       prev_item = true;
     }
     // entry st + 1 must have landed; entries st + 2 .. issued - 1 may stay in flight
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
       wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
     lds_barrier();
     advance(cc);
-    if (cc.tau > tau_hi && prev_item) {
+    if (cc.tau > tau_hi && prev_item && cur_f >= t0 && cur_f < t1) {
       // the last entry was an item: apply it (its ring slot is not reused any more)
       apply(ring[st % C::NBUF], st & 1);
       prev_item = false;
