@@ -2,18 +2,19 @@
 // "3D Deformable Slide Attention": the gradient of the windowed softmax attention,
 // dV = P^T dO and dK = scale * dS^T Q with dS = P * (dP - rowsum(dO * O))).
 //
-// A workgroup owns one 4 x 4 key block column (kby, kbx) of one head and a chunk
-// of frames, and holds the dK / dV of its keys in registers: wave w owns the frames
-// t = w (mod kt), so while the queries of start slice tau stream past, the kt
-// waves hold exactly the kt frames tau .. tau+kt-1 those queries read.  A frame's
-// sums are complete once slice t has gone by; its owner writes them and moves on
-// to frame t + kt.  Every key gets its sums from one workgroup, in a fixed order:
-// no atomics, and the result does not depend on timing.
+// A workgroup owns one 4 x 4 key block column (kby, kbx) of one head and a run
+// of frames, and holds the dK / dV of its keys in registers: wave pair s owns the
+// frames t = s (mod kt), so while the queries of start slice tau stream past, the
+// kt pairs hold exactly the kt frames tau .. tau+kt-1 those queries read.  A
+// frame's sums are complete once slice t has gone by; its owner writes them and
+// moves on to frame t + kt.  Every key gets its sums from one workgroup, in a
+// fixed order: no atomics, and the result does not depend on timing.
 //
 // The queries of a slice that can reach the key block (start cells in the blob box
 // of the column) are packed into items of KV_Q = 32 by a prep pass.  Items and,
 // once per slice, the K / V rows of the frame that enters, stream through an LDS
-// ring with direct global->LDS loads, PD entries ahead of the MFMAs.
+// ring with direct global->LDS loads, PD entries ahead of the MFMAs, issued by
+// loader waves of their own.
 //
 // Per item and wave (2 row tiles of 16 queries x the 16 keys of its frame), bf16
 // MFMA 16x16x32:
@@ -101,8 +102,7 @@ struct DkdvCfg {
   static constexpr int SINK = META + 16 * KV_Q;      // 16 bytes nobody reads: target of the padding loads
   static constexpr int ENTRY = SINK + 16;
   static constexpr int NL = 2 * NPH * (TILE / 1024) + 3;  // direct loads per entry
-  static constexpr int NBUF = D == 128 ? (KT >= 7 ? 4 : 5) : 8;  // ring entries (LDS: ring, P / dS, K / V copies)
-  static constexpr int KV = 2 * NPH * 2048;          // K and V rows of one frame's key block
+  static constexpr int NBUF = D == 128 ? 7 : 8;   // ring entries (LDS: ring and P / dS)
   static constexpr int PD = NBUF - 2;                // entries in flight (the previous one stays readable)
   static constexpr int NIDS = PD + 2;                // token ring (loaded 2 PD + 1 entries ahead)
   static constexpr int NC = D / 32, NT = D / 16;
@@ -120,15 +120,19 @@ struct Cursor {
   int tau, j, n, base;  // n items in the slice, the first is item `base`
 };
 
-constexpr int DKDV_TS = 32;  // frames per workgroup
+// Frames per workgroup: at most DKDV_TS_MAX.  A long run along time keeps the
+// columns that share queries in step with each other (L2 reuse) and spends few
+// steps on the kt - 1 slices a chunk shares with the one before it.
+constexpr int DKDV_TS_MAX = 256;
+constexpr int DKDV_LW = 2;   // loader waves per workgroup
 
 template <int D, int KT>
-__global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ q, const u16* __restrict__ k,
+__global__ __launch_bounds__(128 * KT + 64 * DKDV_LW) void k_dkdv_tube(const u16* __restrict__ q, const u16* __restrict__ k,
                                                        const u16* __restrict__ v, const u16* __restrict__ dout,
                                                        const float* __restrict__ lse,
                                                        const float* __restrict__ delta, u16* __restrict__ dk,
-                                                       u16* __restrict__ dv, Geom g, KvItems it, float sl2,
-                                                       float scale) {
+                                                       u16* __restrict__ dv, Geom g, KvItems it, int ts,
+                                                       float sl2, float scale) {
   using C = DkdvCfg<D, KT>;
   constexpr int kt = KT;
   // Two waves per frame in flight: wave 2 s + hf holds K / V of the frames
@@ -137,36 +141,44 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
   // P and dS in LDS; in the next step both apply dV^T += dO^T P and dK^T += Q^T dS
   // over all 32 queries to their half.  The ring therefore keeps the previous entry
   // (prefetch distance NBUF - 2).
-  constexpr int NW = 2 * KT;
+  // DKDV_LW more waves issue every global->LDS load (and wait for them): the
+  // compute waves never wait on an LDS token read or on memory, only at the
+  // barrier that closes each step.
+  constexpr int NWC = 2 * KT, NW = NWC + DKDV_LW;
   constexpr int NTH = C::NT / 2;  // d tiles per half
   __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::ENTRY];
   __shared__ __attribute__((aligned(16))) char xch[2][KT][2][64 * 16];  // [step parity][frame slot][P, dS]
-  __shared__ __attribute__((aligned(1024))) char kvs[KT][C::KV];          // K, V rows of each pair's frame
 
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
-  const int nchunk = (g.F + DKDV_TS - 1) / DKDV_TS;
+  const int nchunk = (g.F + ts - 1) / ts;
   int L = xcd_remap(blockIdx.x, nkb * nchunk * g.H);
   const int h = L / (nkb * nchunk);
   L -= h * nkb * nchunk;
   const int chunk = L / nkb, kb = L - chunk * nkb;
   const int kby = kb / nkbx, kbx = kb - kby * nkbx;
-  const int t0 = chunk * DKDV_TS, t1 = min(t0 + DKDV_TS, g.F);  // frames written here
+  const int t0 = chunk * ts, t1 = min(t0 + ts, g.F);  // frames written here
   const int tau_lo = max(t0 - kt + 1, 0), tau_hi = min(t1 - 1, g.Lt - 1);
 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int fslot = wave >> 1, hf = wave & 1;
-  // every wave issues MY_LOADS loads per entry (the count is padded with one-lane
-  // loads), so the steady-state wait is a single immediate
-  constexpr int MY_LOADS = (C::NL + NW - 1) / NW;
+  const bool loader = wave >= NWC;
+  const int fslot = wave >> 1, hf = wave & 1;  // (compute waves)
+  const int lw = wave - NWC;                   // (loader waves)
+  // every loader wave issues MY_LOADS loads per entry (the count is padded with
+  // one-lane loads), so the steady-state wait is a single immediate
+  constexpr int MY_LOADS = (C::NL + DKDV_LW - 1) / DKDV_LW;
   // Nothing in the loop below reads memory through the scalar unit: a scalar load
   // in flight makes every LDS wait a full lgkmcnt(0) wait, which would put its
   // latency in front of the MFMAs.  The slice boundaries of this workgroup go to
   // LDS once; item tokens arrive by direct loads into a small ring, 2 PD + 1
   // entries ahead of use.
-  __shared__ int s_off[DKDV_TS + 8 + 1];
+  __shared__ int s_off[DKDV_TS_MAX + 8 + 1];
   __shared__ int s_ids[C::NIDS][KV_Q];
   for (int i = tid; i <= tau_hi - tau_lo + 1; i += 64 * NW) s_off[i] = it.off[(size_t)kb * g.Lt + tau_lo + i];
+  // The in-loop apply runs its MFMAs with P = dS = 0 when it has nothing to add,
+  // so every ring byte it may read must hold a finite value from the start.
+  for (int i = tid; i < C::NBUF * C::ENTRY / 16; i += 64 * NW)
+    reinterpret_cast<uint4*>(&ring[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 
   // this lane's key (key r16 of the block) for the window test
@@ -192,58 +204,6 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
     }
   };
 
-  // ---- direct loads of entry x (at cursor c) into ring slot e; an item's tokens
-  // are in s_ids[x % NIDS]
-  auto issue = [&](const Cursor& c, int x, char* e) {
-    if (c.j < 0) {
-      const int f = c.tau + kt + c.j;
-#pragma unroll
-      for (int jj = 0; jj < MY_LOADS; ++jj) {
-        const int j = wave + NW * jj;
-        if (j < 4 * C::NPH) {
-          // the 16 key rows fill the first 2 KB of each phase tile
-          const int ti = j >> 1, hh = j & 1, tensor = ti / C::NPH, ph = ti - tensor * C::NPH;
-          const int row = 8 * hh + (lane >> 3), ch = (lane & 7) ^ (row & 7);
-          const int y = 4 * kby + (row >> 2), x = 4 * kbx + (row & 3);
-          const int tok = (y < g.Hp && x < g.Wp) ? (f * g.Hp + y) * g.Wp + x : 0;
-          const u16* src = (tensor ? v : k) + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8;
-          dma16(src, e + ti * C::TILE + hh * 1024);
-        } else if (lane == 0) {
-          dma4(lse, e + C::SINK);  // keeps the per-entry load count uniform
-        }
-      }
-    } else {
-      const int item = c.base + c.j;
-      const int* ids = s_ids[x % C::NIDS];
-      constexpr int NR = 2 * C::NPH * (C::TILE / 1024);  // row loads: 8 rows of 128 B each
-#pragma unroll
-      for (int jj = 0; jj < MY_LOADS; ++jj) {
-        const int j = wave + NW * jj;
-        if (j < NR) {
-          const int ti = j / (C::TILE / 1024), part = j % (C::TILE / 1024);
-          const int tensor = ti / C::NPH, ph = ti - tensor * C::NPH;
-          const int row = 8 * part + (lane >> 3), ch = (lane & 7) ^ (row & 7);
-          const int tok = ids[row];
-          const u16* src = (tensor ? dout : q) + ((size_t)tok * g.H + h) * D + ph * 64 + ch * 8;
-          dma16(src, e + ti * C::TILE + part * 1024);
-        } else if (j == NR) {
-          if (lane < KV_Q / 2) dma16(it.st + (size_t)item * KV_Q + 2 * lane, e + C::META);
-        } else if (j < C::NL) {
-          if (lane < KV_Q) {
-            const float* src = (j == NR + 1 ? lse : delta) + (size_t)h * g.N + ids[lane];
-            dma4(src, e + C::META + 8 * KV_Q + (j == NR + 1 ? 0 : 4 * KV_Q));
-          }
-        } else if (lane == 0) {
-          dma4(lse, e + C::SINK);  // padding of the load count
-        }
-      }
-    }
-  };
-  // tokens of entry x (items only), by the last wave
-  auto issue_ids = [&](const Cursor& c, int x) {
-    if (c.j >= 0 && wave == NW - 1 && lane < KV_Q) dma4(it.ids + (size_t)(c.base + c.j) * KV_Q + lane, s_ids[x % C::NIDS]);
-  };
-
   // tile offsets: Q / dO (item) or K / V (frame) of phase ph
   auto tile = [&](char* e, int tensor, int ph) { return e + (tensor * C::NPH + ph) * C::TILE; };
 
@@ -254,6 +214,7 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
     dva[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   int cur_f = -1;
+  Frag<u16> kf[C::NC], vf[C::NC];  // K / V of the pair's frame (B fragments of S and dP)
 
   auto finalize = [&](int f) {
     if (f >= t0 && f < t1 && key_y < g.Hp && key_x < g.Wp) {
@@ -269,10 +230,21 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
 
   // dV^T += dO^T P and dK^T += Q^T dS for this wave's half, with P / dS of the item
   // in ring entry e left by the pair's producer in xch[par]
-  auto apply = [&](char* e, int par) {
+  auto apply = [&](char* e, int par, bool on) {
     Frag<u16> pb, db;
     load_frag(pb, (const u16*)(xch[par][fslot][0] + lane * 16));
     load_frag(db, (const u16*)(xch[par][fslot][1] + lane * 16));
+    {
+      // off: the MFMAs still run, with P = dS = 0 (no branch around the accumulators)
+      const unsigned m = on ? ~0u : 0u;
+      uint4 wp, wd;
+      __builtin_memcpy(&wp, &pb.v, 16);
+      __builtin_memcpy(&wd, &db.v, 16);
+      wp.x &= m, wp.y &= m, wp.z &= m, wp.w &= m;
+      wd.x &= m, wd.y &= m, wd.z &= m, wd.w &= m;
+      __builtin_memcpy(&pb.v, &wp, 16);
+      __builtin_memcpy(&db.v, &wd, 16);
+    }
     // A slots j < 4: rows 4 quad + j of row tile 0; j >= 4: the same rows of row tile 1
     const int trow = 4 * quad + (r16 >> 2);
 #pragma unroll
@@ -305,18 +277,14 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
   // fragments in xch[par] (8 of their 16 bytes per lane)
   auto produce = [&](char* e, int par) {
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-    const char* kv = kvs[fslot];
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) {
       const int off = sw(16 * hf + r16, (c & 1) * 64 + quad * 16);
-      const int koff = (c >> 1) * 2048 + sw(r16, (c & 1) * 64 + quad * 16);
-      Frag<u16> a, b;
+      Frag<u16> a;
       load_frag(a, (const u16*)(tile(e, 0, c >> 1) + off));
-      load_frag(b, (const u16*)(kv + koff));
-      sc = mma(a, b, sc);
+      sc = mma(a, kf[c], sc);
       load_frag(a, (const u16*)(tile(e, 1, c >> 1) + off));
-      load_frag(b, (const u16*)(kv + C::NPH * 2048 + koff));
-      dp = mma(a, b, dp);
+      dp = mma(a, vf[c], dp);
     }
     const int q0 = 16 * hf + 4 * quad;
     const int4 sa = *reinterpret_cast<const int4*>(e + C::META + q0 * 8);
@@ -329,7 +297,8 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = (unsigned)(key_y - sy[i]) < (unsigned)g.ky && (unsigned)(key_x - sx[i]) < (unsigned)g.kx;
-      const float pe = ok ? __builtin_amdgcn_exp2f(sc[i] * sl2 - lq[i] * LOG2E) : 0.f;
+      // outside the window the exponent is -inf (exp2 gives 0, no branch)
+      const float pe = __builtin_amdgcn_exp2f(ok ? sc[i] * sl2 - lq[i] * LOG2E : -__builtin_inff());
       pb[i] = __builtin_bit_cast(short, static_cast<__bf16>(pe));
       db[i] = __builtin_bit_cast(short, static_cast<__bf16>(pe * (dp[i] - dq[i])));
     }
@@ -338,44 +307,127 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
   };
 
   // Three cursors over the same entry stream: token loads (pc, 2 PD + 1 ahead),
-  // row loads (ic, PD ahead) and the MFMAs (cc).  Steps st < 0 only fill the
-  // pipeline.
-  Cursor pc = start_cursor(), ic = start_cursor(), cc = start_cursor();
-  int npc = 0;
-  for (; npc <= C::PD && pc.tau <= tau_hi; ++npc, advance(pc)) issue_ids(pc, npc);
-  wait_vmcnt(0);
-  __syncthreads();
+  // row loads (ic, PD ahead) and the MFMAs (cc).  Every wave runs PD + (entries)
+  // steps, each closed by one barrier.
+  Cursor cc = start_cursor();
+  if (loader) {
+    // Loader wave LWI issues loads LWI, LWI + DKDV_LW, ... of every entry; with the
+    // index a compile-time constant each load is a handful of instructions.
+    static_for<0, DKDV_LW>([&](auto LWC) {
+      constexpr int LWI = decltype(LWC)::value;
+      if (lw != LWI) return;
+      // column of the 16-byte chunk this lane loads: rows 8 p + (lane >> 3) are
+      // stored swizzled (chunk (lane & 7) ^ (row & 7)), the same for every part p
+      const int lane_el = ((lane & 7) ^ (lane >> 3)) * 8;
+      constexpr int PARTS = C::TILE / 1024;  // 1 KB parts of a tile: 8 rows of 128 B
+      constexpr int NR = 2 * C::NPH * PARTS;  // row loads of an item
+      static_assert(PARTS % DKDV_LW == 0, "loader waves split the parts evenly");
+      auto issue = [&](const Cursor& c, int x, char* e) {
+        if (c.j < 0) {
+          // a frame: its 16 key rows fill the first 2 KB of each phase tile
+          const int f = c.tau + kt + c.j;
+          static_for<0, MY_LOADS>([&](auto JJ) {
+            constexpr int j = LWI + DKDV_LW * decltype(JJ)::value;
+            if constexpr (j < 4 * C::NPH) {
+              constexpr int ti = j >> 1, hh = j & 1, tensor = ti / C::NPH, ph = ti % C::NPH;
+              const int row = 8 * hh + (lane >> 3);
+              const int y = 4 * kby + (row >> 2), x = 4 * kbx + (row & 3);
+              const int tok = (y < g.Hp && x < g.Wp) ? (f * g.Hp + y) * g.Wp + x : 0;
+              const u16* src = (tensor ? v : k) + ((size_t)tok * g.H + h) * D + ph * 64 + lane_el;
+              dma16(src, e + ti * C::TILE + hh * 1024);
+            } else {
+              if (lane == 0) dma4(lse, e + C::SINK);  // keeps the per-entry load count uniform
+            }
+          });
+        } else {
+          const int item = c.base + c.j;
+          const int* ids = s_ids[x % C::NIDS];
+          // the tokens first: every direct load below clobbers memory for the
+          // compiler, which would otherwise read (and wait for) each token again
+          constexpr int NQ = PARTS / DKDV_LW;  // parts LWI + DKDV_LW qq
+          size_t rowoff[NQ];
+#pragma unroll
+          for (int qq = 0; qq < NQ; ++qq)
+            rowoff[qq] = ((size_t)ids[8 * (LWI + DKDV_LW * qq) + (lane >> 3)] * g.H + h) * D + lane_el;
+          const size_t meta_off = (size_t)h * g.N + ids[lane & (KV_Q - 1)];
+          static_for<0, MY_LOADS>([&](auto JJ) {
+            constexpr int jj = decltype(JJ)::value, j = LWI + DKDV_LW * jj;
+            if constexpr (j < NR) {
+              constexpr int ti = j / PARTS, part = j % PARTS, tensor = ti / C::NPH, ph = ti % C::NPH;
+              dma16((tensor ? dout : q) + rowoff[jj % NQ] + ph * 64, e + ti * C::TILE + part * 1024);
+            } else if constexpr (j == NR) {
+              if (lane < KV_Q / 2) dma16(it.st + (size_t)item * KV_Q + 2 * lane, e + C::META);
+            } else if constexpr (j < C::NL) {
+              if (lane < KV_Q)
+                dma4((j == NR + 1 ? lse : delta) + meta_off, e + C::META + 8 * KV_Q + (j == NR + 1 ? 0 : 4 * KV_Q));
+            } else {
+              if (lane == 0) dma4(lse, e + C::SINK);  // padding of the load count
+            }
+          });
+        }
+      };
+      // tokens of entry x (items only), by the last loader wave
+      auto issue_ids = [&](const Cursor& c, int x) {
+        if constexpr (LWI == DKDV_LW - 1)
+          if (c.j >= 0 && lane < KV_Q) dma4(it.ids + (size_t)(c.base + c.j) * KV_Q + lane, s_ids[x % C::NIDS]);
+      };
 
-  int issued = 0;
-  bool prev_item = false;  // the previous entry was an item whose dV / dK are still to apply
-  for (int st = -C::PD; cc.tau <= tau_hi; ++st) {
-    if (ic.tau <= tau_hi) {
-      issue(ic, issued, ring[issued % C::NBUF]);
-      ++issued;
-      advance(ic);
-    }
-    if (pc.tau <= tau_hi) {
-      issue_ids(pc, npc);
-      ++npc;
-      advance(pc);
-    }
-    if (st < 0) {
-      // (token loads only add to the count of loads issued later: the wait is exact
-      // or stricter)
-      wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
-      lds_barrier();
-      continue;
-    }
-    // a pair whose frame lies outside [t0, t1) computes sums nobody writes: skip
-    // (both waves of the pair agree, and the frame cannot change between an item's
-    // two steps)
-    const bool kept = cur_f >= t0 && cur_f < t1;
-    // ---- the previous item's dV / dK (before a frame can be written out below)
-    if (prev_item && kept) apply(ring[(st - 1) % C::NBUF], (st - 1) & 1);
-    char* e = ring[st % C::NBUF];
-    if (cc.j < 0) {
-      // ---- a frame enters: its pair writes the frame it leaves and takes K / V
-      const int f = cc.tau + kt + cc.j;
+      Cursor pc = start_cursor(), ic = start_cursor();
+      int npc = 0;
+      for (; npc <= C::PD && pc.tau <= tau_hi; ++npc, advance(pc)) issue_ids(pc, npc);
+      wait_vmcnt(0);
+      __syncthreads();
+      int issued = 0;
+      auto issue_next = [&]() {
+        if (ic.tau <= tau_hi) {
+          issue(ic, issued, ring[issued % C::NBUF]);
+          ++issued;
+          advance(ic);
+        }
+        if (pc.tau <= tau_hi) {
+          issue_ids(pc, npc);
+          ++npc;
+          advance(pc);
+        }
+      };
+      // fill the pipeline: entries 0 .. PD - 1 (token loads only add to the count
+      // of loads issued later, so the waits are exact or stricter)
+      for (int st = -C::PD; st < 0; ++st) {
+        issue_next();
+        wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
+        lds_barrier();
+      }
+      for (int st = 0; cc.tau <= tau_hi; ++st) {
+        issue_next();
+        // entry st + 1 must have landed; entries st + 2 .. issued - 1 may stay in flight
+        if (issued - st - 2 == C::PD - 1)
+          wait_vmcnt_c<MY_LOADS * (C::PD - 1)>();
+        else
+          wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
+        lds_barrier();
+        advance(cc);
+      }
+    });
+    return;
+  }
+
+  __syncthreads();
+  for (int st = -C::PD; st < 0; ++st) lds_barrier();
+  // Slice by slice: the frames that enter (kt for the first slice, then one), then
+  // the items.  The item loop changes only the accumulators, by MFMA, and the frame
+  // steps sit outside it, which keeps the sums and the K / V fragments in fixed
+  // registers while items stream past.
+  int st = 0;      // entry
+  int nprev = 0;   // items of the previous slice (its last one is still to apply)
+  bool kept = false;
+  for (int tau = tau_lo; tau <= tau_hi; ++tau) {
+    const int n = slice_off(tau + 1) - slice_off(tau);
+    const int nf = tau == tau_lo ? kt : 1;
+    for (int jf = 0; jf < nf; ++jf, ++st) {
+      // ---- the previous slice's last item, then a frame enters: its pair writes
+      // the frame it leaves and takes K / V
+      if (jf == 0 && nprev > 0 && kept) apply(ring[(st - 1) % C::NBUF], (st - 1) & 1, true);
+      const int f = tau + kt - nf + jf;
       if (fslot == f % kt) {
         if (cur_f >= 0) {
           finalize(cur_f);
@@ -385,33 +437,37 @@ __global__ __launch_bounds__(128 * KT) void k_dkdv_tube(const u16* __restrict__ 
             dva[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
         }
-        // the frame's K and V rows (first 2 KB of each phase tile of the entry) into
-        // the pair's copy; each wave copies half
-        for (int i = hf * 64 + lane; i < C::KV / 16; i += 128) {
-          const int ti = i / 128, o = (i % 128) * 16;
-          *reinterpret_cast<uint4*>(kvs[fslot] + ti * 2048 + o) = *reinterpret_cast<const uint4*>(e + ti * C::TILE + o);
+        // the frame's K and V rows (first 2 KB of each phase tile of the entry) as
+        // MFMA B fragments: key r16, head-dim slots 32 c + 8 quad .. + 7
+        char* e = ring[st % C::NBUF];
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) {
+          const int koff = sw(r16, (c & 1) * 64 + quad * 16);
+          load_frag(kf[c], (const u16*)(tile(e, 0, c >> 1) + koff));
+          load_frag(vf[c], (const u16*)(tile(e, 1, c >> 1) + koff));
         }
         cur_f = f;
       }
-      prev_item = false;
-    } else {
-      // ---- an item: each wave of a pair forms P and dS of one row tile
-      if (kept) produce(e, st & 1);
-      prev_item = true;
+      lds_barrier();
     }
-    // entry st + 1 must have landed; entries st + 2 .. issued - 1 may stay in flight
-    if (issued - st - 2 == C::PD - 1)
-      wait_vmcnt_c<MY_LOADS * (C::PD - 1)>();
-    else
-      wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
-    lds_barrier();
-    advance(cc);
-    if (cc.tau > tau_hi && prev_item && cur_f >= t0 && cur_f < t1) {
-      // the last entry was an item: apply it (its ring slot is not reused any more)
-      apply(ring[st % C::NBUF], st & 1);
-      prev_item = false;
+    // a pair whose frame lies outside [t0, t1) computes sums nobody writes: skip
+    kept = cur_f >= t0 && cur_f < t1;
+    // ---- the items: each wave of a pair forms P and dS of one row tile; in the next
+    // step both apply them
+    if (n > 0) {
+      if (kept) produce(ring[st % C::NBUF], st & 1);
+      lds_barrier();
+      ++st;
+      for (int j = 1; j < n; ++j, ++st) {
+        apply(ring[(st + C::NBUF - 1) % C::NBUF], (st - 1) & 1, kept);
+        if (kept) produce(ring[st % C::NBUF], st & 1);
+        lds_barrier();
+      }
     }
+    nprev = n;
   }
+  // the last item (its ring slot is not reused any more)
+  if (nprev > 0 && kept) apply(ring[(st - 1) % C::NBUF], (st - 1) & 1, true);
   finalize(cur_f);
 }
 
@@ -431,12 +487,15 @@ hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s) {
 template <int D, int KT>
 static hipError_t dkdv_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
   const int nkb = kv_item_columns(g);
-  const int nchunk = (g.F + DKDV_TS - 1) / DKDV_TS;
+  // the longest chunk that still leaves at least 512 workgroups (two per compute unit)
+  int ts = min(g.F, DKDV_TS_MAX);
+  while (ts > 8 && (long long)nkb * g.H * ((g.F + ts - 1) / ts) < 512) ts = (ts + 1) / 2;
+  const int nchunk = (g.F + ts - 1) / ts;
   const long long total = (long long)nkb * nchunk * g.H;
   KvItems it{p.kv_off, p.kv_ids, p.kv_st};
-  k_dkdv_tube<D, KT><<<(unsigned)total, 128 * KT, 0, s>>>((const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
-                                                       (const u16*)a.dout, a.lse, p.delta, (u16*)a.dk, (u16*)a.dv, g,
-                                                       it, a.scale * LOG2E, a.scale);
+  k_dkdv_tube<D, KT><<<(unsigned)total, 128 * KT + 64 * DKDV_LW, 0, s>>>(
+      (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, a.lse, p.delta, (u16*)a.dk, (u16*)a.dv, g,
+      it, ts, a.scale * LOG2E, a.scale);
   return hipGetLastError();
 }
 
