@@ -87,7 +87,6 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // tile loads per wave and step, the same for every wave (padding loads)
   constexpr int MY_LOADS = (C::NLOADS + DQ_NW - 1) / DQ_NW;
-  constexpr int NREM = C::NLOADS % DQ_NW;
   __shared__ int s_sink[4];
 
   int roff[C::NC / C::NPH], toff[C::NT / C::NPH];
@@ -152,9 +151,13 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           }
         }
       }
-      issue_key_tile_loop<D, NBX, C::NB, C::NBPAD, DQ_NW>(ring[x % C::NBUF], ph < C::NPH ? v : k, g, by, bx, h, f,
-                                                          ph % C::NPH, wave, lane);
-      if (NREM != 0 && wave >= NREM && lane == 0) dma4(k, s_sink);
+      // this wave's tile loads, with its index a compile-time constant
+      const u16* src = (ph < C::NPH ? v : k) + (ph % C::NPH) * 64 + h * D + lane_chunk_el(lane);
+      static_for<0, DQ_NW>([&](auto WC) {
+        constexpr int WI = decltype(WC)::value;
+        if (wave == WI)
+          issue_key_tile_w<D, NBX, C::NB, C::NBPAD, DQ_NW, WI>(ring[x % C::NBUF], src, g, by, bx, f, lane, k, s_sink);
+      });
     };
     int issued = 0;
     for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
@@ -201,6 +204,12 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           ++issued;
         }
         const char* tb = ring[st % C::NBUF];
+        // opaque per step: keeps the compiler from precomputing every fragment
+        // address of every ring slot outside the loop
+#pragma unroll
+        for (int c = 0; c < C::NC / C::NPH; ++c) __asm__ __volatile__("" : "+v"(roff[c]));
+#pragma unroll
+        for (int t = 0; t < C::NT / C::NPH; ++t) __asm__ __volatile__("" : "+v"(toff[t]));
         // with one slot per wave, a wave whose slot holds no tile this frame skips its
         // MFMA work (a uniform branch) and leaves the SIMD to its partner
         const bool busy = NS > 1 || fend[0] >= f;

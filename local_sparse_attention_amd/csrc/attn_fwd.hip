@@ -41,10 +41,11 @@ struct FwdCfg {
 #define DSA3D_FWD_NS 1
 #endif
 constexpr int FWD_NS = DSA3D_FWD_NS;
-constexpr int FWD_NW = QS_SLOTS / FWD_NS;
+constexpr int FWD_NW = QS_SLOTS / FWD_NS;  // compute waves
+constexpr int FWD_LW = 2;                  // loader waves
 
 template <int D, int NBY, int NBX>
-__global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restrict__ q, const u16* __restrict__ k,
+__global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16* __restrict__ q, const u16* __restrict__ k,
                                                            const u16* __restrict__ v, u16* __restrict__ out,
                                                            float* __restrict__ lse, Geom g, Prep p, float sl2) {
   using C = FwdCfg<D, NBY, NBX>;
@@ -61,11 +62,66 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
   (void)chunk;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // tile loads per wave and step: the same for every wave (waves past the remainder
-  // add one padding load), so the steady-state wait is one immediate
-  constexpr int MY_LOADS = (C::NLOADS + FWD_NW - 1) / FWD_NW;
-  constexpr int NREM = C::NLOADS % FWD_NW;
-  __shared__ int s_sink[4];
+  constexpr int NW = FWD_NW + FWD_LW;
+  // FWD_LW loader waves issue every direct load (key tiles, Q rows) and wait for
+  // them; the compute waves only meet them at the barrier that closes each step.
+  // Tile loads per loader wave and step: the same for each, so the steady-state
+  // wait is one immediate.
+  static_assert(C::NLOADS % FWD_LW == 0, "tile loads split evenly over the loader waves");
+  constexpr int MY_LOADS = C::NLOADS / FWD_LW;
+  const bool loader = wave >= FWD_NW;
+  const int lw = wave - FWD_NW;
+
+  const int* sp = p.qs + p.qs_off[w];
+  const int npass = sp[0];
+  sp += 1;
+  if (loader) {
+    for (int pass = 0; pass < npass; ++pass) {
+      load_pass(T, sp, p, tid, 64 * NW);
+      const int nf = __builtin_amdgcn_readfirstlane(T.hdr[0]);
+      const int nsteps = nf * C::NPH2;
+      static_for<0, FWD_LW>([&](auto LWC) {
+        constexpr int LWI = decltype(LWC)::value;
+        if (lw != LWI) return;
+        const int lane_el = lane_chunk_el(lane);
+        // step x: phase x % NPH2 of frame index x / NPH2; K phases first, then V.  Q
+        // rows of the tiles that start at a frame go out just before its first tile
+        // loads, so the wait that covers those covers them too.
+        auto issue_step = [&](int x) {
+          const int fi = x / C::NPH2, ph = x - fi * C::NPH2;
+          const int f = __builtin_amdgcn_readfirstlane(T.frames[fi]);
+          if (ph == 0) {
+#pragma unroll
+            for (int sl = LWI; sl < QS_SLOTS; sl += FWD_LW) {
+              const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
+              if (t >= 0) issue_rows<D>(stage[sl], q, T.ids[t], g, h, lane);
+            }
+          }
+          issue_key_tile_w<D, NBX, C::NB, C::NBPAD, FWD_LW, LWI>(
+              ring[x % C::NBUF], (ph < C::NPH ? k : v) + (ph % C::NPH) * 64 + h * D + lane_el, g, by, bx, f, lane, k,
+              stage[0]);  // (no padding: the loads split evenly)
+        };
+        int issued = 0;
+        for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
+        wait_vmcnt(0);
+        __syncthreads();
+        for (int st = 0; st < nsteps; ++st) {
+          if (issued < nsteps) {
+            issue_step(issued);
+            ++issued;
+          }
+          // step st + 1 (and the Q rows issued before it) must have landed; later
+          // steps may stay in flight (Q rows only make the count stricter)
+          if (issued - st - 2 == C::PD - 1)
+            wait_vmcnt_c<MY_LOADS * (C::PD - 1)>();
+          else
+            wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
+          lds_barrier();
+        }
+      });
+    }
+    return;
+  }
 
   // per-lane LDS offsets of the fragments inside a phase tile (block 0)
   int roff[C::NC / C::NPH], toff[C::NT / C::NPH];
@@ -77,8 +133,6 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
   // slot state (slots 2 wave, 2 wave + 1)
   Frag<u16> qf[NS][C::NC];
   f32x4_t oacc[NS][C::NT];
-  f32x4_t sacc[NS][C::NB];
-  Frag<u16> pf[NS][C::NPAIR];
   float ybias[NS][NBY], xbias[NS][NBX][4];
   float m_run[NS], l_run[NS];
   int qn[NS], fend[NS];
@@ -100,38 +154,15 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
     fend[s] = -1;
   }
 
-  const int* sp = p.qs + p.qs_off[w];
-  const int npass = sp[0];
-  sp += 1;
   for (int pass = 0; pass < npass; ++pass) {
-    load_pass(T, sp, p, tid, 64 * FWD_NW);
+    load_pass(T, sp, p, tid, 64 * NW);
     const int nf = __builtin_amdgcn_readfirstlane(T.hdr[0]);
-
-    const int nsteps = nf * C::NPH2;
-    // step x: phase x % NPH2 of frame index x / NPH2; K phases first, then V.  Q rows
-    // of the tiles that start at a frame go out just before its first tile loads,
-    // so the wait that covers those covers them too.
-    auto issue_step = [&](int x) {
-      const int fi = x / C::NPH2, ph = x - fi * C::NPH2;
-      const int f = __builtin_amdgcn_readfirstlane(T.frames[fi]);
-      if (ph == 0) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][NS * wave + s]);
-          if (t >= 0) issue_rows<D>(stage[NS * wave + s], q, T.ids[t], g, h, lane);
-        }
-      }
-      issue_key_tile_loop<D, NBX, C::NB, C::NBPAD, FWD_NW>(ring[x % C::NBUF], ph < C::NPH ? k : v, g, by, bx, h, f,
-                                                           ph % C::NPH, wave, lane);
-      if (NREM != 0 && wave >= NREM && lane == 0) dma4(k, s_sink);
-    };
-    int issued = 0;
-    for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
-    wait_vmcnt(0);
-    __syncthreads();
-
+    __syncthreads();  // the loader waves' pipeline fill
     for (int fi = 0; fi < nf; ++fi) {
       const int f = __builtin_amdgcn_readfirstlane(T.frames[fi]);
+      // scores and P of this frame (not carried from one frame to the next)
+      f32x4_t sacc[NS][C::NB];
+      Frag<u16> pf[NS][C::NPAIR];
       // ---- activations: Q fragments, window biases, fresh softmax state
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -159,11 +190,14 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
       static_for<0, C::NPH2>([&](auto PHC) {
         constexpr int ph = decltype(PHC)::value;
         const int st = fi * C::NPH2 + ph;
-        if (issued < nsteps) {
-          issue_step(issued);
-          ++issued;
-        }
         const char* tb = ring[st % C::NBUF];
+        // opaque per step: keeps the compiler from precomputing every fragment
+        // address of every ring slot outside the loop (more registers than a third
+        // wave per SIMD leaves)
+#pragma unroll
+        for (int c = 0; c < C::NC / C::NPH; ++c) __asm__ __volatile__("" : "+v"(roff[c]));
+#pragma unroll
+        for (int t = 0; t < C::NT / C::NPH; ++t) __asm__ __volatile__("" : "+v"(toff[t]));
         // with one slot per wave, a wave whose slot holds no tile this frame skips its
         // MFMA and softmax work (a uniform branch) and leaves the SIMD to its partner
         const bool busy = NS > 1 || fend[0] >= f;
@@ -272,12 +306,6 @@ __global__ __launch_bounds__(64 * FWD_NW) void k_forward_qs(const u16* __restric
             }
           }
         }
-        // step st + 1 (and the Q rows issued before it) must have landed; later
-        // steps may stay in flight (Q rows only make the count stricter)
-        if (issued - st - 2 == C::PD - 1)
-          wait_vmcnt_c<MY_LOADS * (C::PD - 1)>();
-        else
-          wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
         lds_barrier();
       });
     }
@@ -294,7 +322,7 @@ bool fwd_qs_eligible(const Geom& g, int dtype, int D) {
 template <int D, int NBY, int NBX>
 static hipError_t fwd_qs_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
   const long long total = (long long)qs_items(g) * g.H;
-  k_forward_qs<D, NBY, NBX><<<(unsigned)total, 64 * FWD_NW, 0, s>>>(
+  k_forward_qs<D, NBY, NBX><<<(unsigned)total, 64 * (FWD_NW + FWD_LW), 0, s>>>(
       (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.out, a.lse_out, g, p, a.scale * LOG2E);
   return hipGetLastError();
 }

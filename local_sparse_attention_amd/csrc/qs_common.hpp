@@ -103,15 +103,46 @@ __device__ __forceinline__ void issue_key_tile_loop(char* dst, const u16* src, c
   }
 }
 
+// Loads WI, WI + NW, WI + 2 NW, ... of the 2 NLB 1 KB loads of one column phase
+// of the key tile of frame f (layout as in issue_key_tile), for the wave that is
+// number WI (a compile-time constant: each load is then a few instructions) of NW
+// issuing waves.  Every such wave issues ceil(2 NLB / NW) loads; the missing ones
+// are one-lane loads of pad_src into sink, so all waves count the same.  src
+// points at the tensor's element (token 0, head h, column phase ph, the lane's
+// 16-byte chunk (l & 7) ^ ((l >> 3) & 7)).
+template <int D, int NBX, int NBLK, int NLB, int NW, int WI>
+__device__ __forceinline__ void issue_key_tile_w(char* dst, const u16* src, const Geom& g, int by, int bx, int f,
+                                                 int lane, const void* pad_src, void* sink) {
+  const int ly = lane >> 5, lx = (lane >> 3) & 3;
+  const int fbase = f * g.Hp * g.Wp;
+  static_for<0, (2 * NLB + NW - 1) / NW>([&](auto JJ) {
+    constexpr int j = WI + NW * decltype(JJ)::value;
+    if constexpr (j < 2 * NLB) {
+      constexpr int b = j >> 1, bi = b / NBX, bj = b % NBX;
+      const int y = 4 * by + 4 * bi + 2 * (j & 1) + ly, x = 4 * bx + 4 * bj + lx;
+      const int tok = (b < NBLK && y < g.Hp && x < g.Wp) ? fbase + y * g.Wp + x : fbase;
+      dma16(src + (size_t)tok * g.H * D, dst + j * 1024);
+    } else {
+      if (lane == 0) dma4(pad_src, sink);
+    }
+  });
+}
+
+// The lane's element offset inside a row for issue_key_tile_w and issue_rows.
+__device__ __forceinline__ int lane_chunk_el(int lane) { return ((lane & 7) ^ ((lane >> 3) & 7)) * 8; }
+
 // Direct loads of the 16 rows (tokens ids[0..15]) of a [N][H][D] bf16 tensor into a
 // staged row tile: NPH phases of 16 x 128 bytes, swizzled like the key tiles.
 template <int D>
 __device__ __forceinline__ void issue_rows(char* dst, const u16* src, const int* ids, const Geom& g, int h, int lane) {
+  // both tokens first: every direct load clobbers memory for the compiler, which
+  // would otherwise read (and wait for) the token again before each load
+  const u16* r0 = src + ((size_t)ids[lane >> 3] * g.H + h) * D + lane_chunk_el(lane);
+  const u16* r1 = src + ((size_t)ids[8 + (lane >> 3)] * g.H + h) * D + lane_chunk_el(lane);
 #pragma unroll
   for (int j = 0; j < 2 * (D / 64); ++j) {
     const int ph = j >> 1, hh = j & 1;
-    const int row = 8 * hh + (lane >> 3), ch = (lane & 7) ^ (row & 7);
-    dma16(src + ((size_t)ids[row] * g.H + h) * D + ph * 64 + ch * 8, dst + ph * 2048 + hh * 1024);
+    dma16((hh ? r1 : r0) + ph * 64, dst + ph * 2048 + hh * 1024);
   }
 }
 
