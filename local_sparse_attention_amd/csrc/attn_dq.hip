@@ -16,32 +16,45 @@
 
 namespace dsa3d {
 
-// Delta[h][n] = sum_d dO[n][h][d] O[n][h][d] (fp32), D / 8 lanes per row.
+// Delta[h][n] = sum_d dO[n][h][d] O[n][h][d] (fp32), D / 8 lanes per row.  Each
+// lane group takes DELTA_U rows per trip with all their loads issued before the
+// first use, so enough bytes are in flight to stream O and dO at HBM rate.
+constexpr int DELTA_U = 4;
 template <int D>
 __global__ __launch_bounds__(256) void k_delta(const u16* __restrict__ o, const u16* __restrict__ dout,
                                                float* __restrict__ delta, int N, int H) {
   constexpr int LPR = D / 8, RPW = 64 / LPR;  // lanes per row, rows per wave
   const int lane = threadIdx.x & 63, sub = lane % LPR;
   const long long rows = (long long)N * H;
-  for (long long r0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW; r0 < rows;
-       r0 += (long long)gridDim.x * 4 * RPW) {
-    const long long r = r0 + lane / LPR;
-    float s = 0.f;
-    if (r < rows) {
-      const uint4 a = *reinterpret_cast<const uint4*>(o + r * D + sub * 8);
-      const uint4 b = *reinterpret_cast<const uint4*>(dout + r * D + sub * 8);
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+  const long long step = (long long)gridDim.x * 4 * RPW * DELTA_U;
+  for (long long r0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW * DELTA_U; r0 < rows; r0 += step) {
+    uint4 a[DELTA_U], b[DELTA_U];
+#pragma unroll
+    for (int u = 0; u < DELTA_U; ++u) {
+      const long long r = r0 + u * RPW + lane / LPR;
+      if (r < rows) {
+        a[u] = *reinterpret_cast<const uint4*>(o + r * D + sub * 8);
+        b[u] = *reinterpret_cast<const uint4*>(dout + r * D + sub * 8);
+      } else {
+        a[u] = b[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < DELTA_U; ++u) {
+      const long long r = r0 + u * RPW + lane / LPR;
+      const uint32_t av[4] = {a[u].x, a[u].y, a[u].z, a[u].w}, bv[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
+      float s = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s += __uint_as_float(av[i] << 16) * __uint_as_float(bv[i] << 16);
         s += __uint_as_float(av[i] & 0xffff0000u) * __uint_as_float(bv[i] & 0xffff0000u);
       }
-    }
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m, 64);
-    if (r < rows && sub == 0) {
-      const long long n = r / H, h = r - n * H;
-      delta[h * N + n] = s;
+      for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m, 64);
+      if (r < rows && sub == 0) {
+        const long long n = r / H, h = r - n * H;
+        delta[h * N + n] = s;
+      }
     }
   }
 }
@@ -331,8 +344,8 @@ static hipError_t dq_qs_dispatch(const AttnArgs& a, const Geom& g, const Prep& p
 
 hipError_t launch_delta(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
   const long long rows = (long long)g.N * g.H;
-  const int rpb = 4 * (64 / (D / 8));
-  const unsigned blocks = (unsigned)min((rows + rpb - 1) / rpb, 8192LL);
+  const int rpb = 4 * (64 / (D / 8)) * DELTA_U;
+  const unsigned blocks = (unsigned)min((rows + rpb - 1) / rpb, 4096LL);
   if (D == 64)
     k_delta<64><<<blocks, 256, 0, s>>>((const u16*)a.o, (const u16*)a.dout, p.delta, g.N, g.H);
   else

@@ -131,26 +131,41 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* keys, int n,
 }
 
 // In-place exclusive scan of n values by one block of 1024 threads.
+// In-place exclusive scan (one workgroup): chunks of 4096, four consecutive values
+// per thread (coalesced), wave scans by lane shuffles, a running carry.
 __global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n) {
-  __shared__ uint32_t part[1024];
-  const int tid = threadIdx.x;
-  const int seg = (n + 1023) / 1024;
-  const int beg = min(tid * seg, n), end = min(beg + seg, n);
-  uint32_t s = 0;
-  for (int i = beg; i < end; ++i) s += data[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const uint32_t u = tid >= d ? part[tid - d] : 0u;
+  __shared__ uint32_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t carry = 0;
+  for (int base = 0; base < n; base += 4096) {
+    const int i0 = base + 4 * tid;
+    uint32_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = i0 + j < n ? data[i0 + j] : 0u;
+    const uint32_t t = v[0] + v[1] + v[2] + v[3];
+    uint32_t inc = t;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += y;
+    }
+    if (lane == 63) wsum[wave] = inc;
     __syncthreads();
-    part[tid] += u;
-    __syncthreads();
-  }
-  uint32_t run = part[tid] - s;
-  for (int i = beg; i < end; ++i) {
-    const uint32_t x = data[i];
-    data[i] = run;
-    run += x;
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const uint32_t x = wsum[w];
+      before += w < wave ? x : 0u;
+      total += x;
+    }
+    uint32_t run = carry + before + inc - t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (i0 + j < n) data[i0 + j] = run;
+      run += v[j];
+    }
+    carry += total;
+    __syncthreads();  // wsum is rewritten by the next chunk
   }
 }
 
