@@ -34,8 +34,8 @@ __global__ __launch_bounds__(256) void k_tile_fill(const int* __restrict__ perm,
   tq_st[(size_t)g * 16 + j] = st;
 }
 
-// Runs the greedy schedule of work item w (blob column, chunk); writes it when
-// out != nullptr and returns its size in ints.
+// Runs the greedy schedule of work item w (blob column, chunk) and writes it to out;
+// returns its size in ints.
 __device__ int build_schedule(const Geom& g, const int* __restrict__ goff, int w, int* out) {
   const int nbc = g.nby * g.nbx;
   const int chunk = w / nbc, bc = w - chunk * nbc;
@@ -102,9 +102,22 @@ __device__ int build_schedule(const Geom& g, const int* __restrict__ goff, int w
   return size;
 }
 
+// Room for the schedule of work item w: every pass schedules at least one tile and
+// holds 2 + (frames <= QS_TS + kt - 1) + 4 per tile ints, so 1 + tiles (QS_TS + kt
+// + 5) bounds it (the sum over items stays within qs_ints()).
 __global__ __launch_bounds__(64) void k_sched_count(Geom g, const int* __restrict__ goff, int nw, int* __restrict__ off) {
   const int w = blockIdx.x * 64 + threadIdx.x;
-  if (w < nw) off[w] = build_schedule(g, goff, w, nullptr);
+  if (w >= nw) return;
+  const int nbc = g.nby * g.nbx;
+  const int chunk = w / nbc, bc = w - chunk * nbc;
+  const int by = bc / g.nbx, bx = bc - by * g.nbx;
+  const int c0 = chunk * QS_TS, ns = min(QS_TS, g.Lt - c0);
+  int tiles = 0;
+  for (int i = 0; i < ns; ++i) {
+    const int b = ((c0 + i) * g.nby + by) * g.nbx + bx;
+    tiles += goff[b + 1] - goff[b];
+  }
+  off[w] = 1 + tiles * (QS_TS + g.kt + 5);
 }
 
 __global__ __launch_bounds__(64) void k_sched_fill(Geom g, const int* __restrict__ goff, int nw,
