@@ -64,11 +64,20 @@ def _dtype_code(a):
     raise TypeError(f"oracle inputs are float32, float64 or bf16 bits (uint16), got {a.dtype}")
 
 
+def _check_window(grid, window):
+    # The window is centred (odd extents) and lies inside the grid once its start is
+    # clamped, which needs each extent to be at most the grid's.
+    for g, k in zip(grid, window):
+        if not (1 <= k <= g and k % 2 == 1):
+            raise ValueError(f"window {tuple(window)} must be odd and fit the grid {tuple(grid)}")
+
+
 def _cfg(q, grid, window, scale):
     F, Hp, Wp = grid
     kt, ky, kx = window
     N, H, D = q.shape
     assert N == F * Hp * Wp and D <= 256
+    _check_window(grid, window)
     return _Cfg(F, Hp, Wp, H, D, kt, ky, kx, float(scale), _dtype_code(q))
 
 
@@ -81,6 +90,7 @@ def window_starts(offsets, grid, window):
     off = _c(offsets, np.int32)
     N = grid[0] * grid[1] * grid[2]
     assert off.shape == (N, 3)
+    _check_window(grid, window)
     out = np.empty((N, 3), dtype=np.int32)
     _load().oracle_window_starts(off.ctypes.data, *grid, *window, out.ctypes.data)
     return out

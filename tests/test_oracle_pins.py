@@ -309,3 +309,17 @@ def test_bf16_inputs_are_read_exactly():
     g_f = oracle.backward(widen(qb), widen(kb), widen(vb), widen(dob), off, grid, window, 0.5)
     for a, b in zip(g_b, g_f):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("window", [(3, 9, 9), (3, 4, 3), (5, 3, 3)])
+def test_window_must_be_odd_and_fit_the_grid(window):
+    """A window wider than the grid (or of even extent) has no centred, clamped
+    placement: the oracle refuses it, like the library's DSA3D_ERR_WINDOW."""
+    grid = (4, 8, 8)
+    N = 4 * 8 * 8
+    q = np.zeros((N, 1, 64), np.float32)
+    off = np.zeros((N, 3), np.int32)
+    with pytest.raises(ValueError):
+        oracle.window_starts(off, grid, window)
+    with pytest.raises(ValueError):
+        oracle.forward(q, q, q, off, grid, window, 1.0)

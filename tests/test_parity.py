@@ -89,6 +89,10 @@ EDGE = [
     W("kt5-9x9-drift", 14, 21, 26, 2, 128, 5, 9, 9, "bf16", ("blocks", 8, 3.0, True, 8.0)),
     W("kt7-5x3-f32", 9, 11, 7, 2, 64, 7, 5, 3, "f32", ("round_normal", 2.0, 5)),
     W("crowded-slices", 8, 12, 12, 2, 128, 3, 9, 9, "bf16", ("uniform", -9, 9)),
+    # few key-block columns x heads: the key-centric backward splits time into runs of
+    # 5 (8 runs) and 8 frames (4 runs, kt = 7 > half a run)
+    W("many-runs-kt3", 40, 9, 10, 2, 128, 3, 9, 9, "bf16", ("blocks", 4, 2.0, True, 4.0)),
+    W("many-runs-kt7", 30, 8, 8, 2, 64, 7, 5, 5, "bf16", ("round_normal", 2.0, 4)),
 ]
 
 
