@@ -16,32 +16,36 @@
 
 namespace dsa3d {
 
-// Delta[h][n] = sum_d dO[n][h][d] O[n][h][d] (fp32), D / 8 lanes per row.  Each
-// lane group takes DELTA_U rows per trip with all their loads issued before the
-// first use, so enough bytes are in flight to stream O and dO at HBM rate.
+// Delta[h][n] = sum_d dO[n][h][d] O[n][h][d] (fp32), D / 8 lanes per row.  A wave
+// takes 64 consecutive tokens of one head, DELTA_U row groups per trip with all their
+// loads issued before the first use, so that enough bytes are in flight to stream O
+// and dO at HBM rate and the results go out as whole lines of delta[h][.].
 constexpr int DELTA_U = 4;
 template <int D>
 __global__ __launch_bounds__(256) void k_delta(const u16* __restrict__ o, const u16* __restrict__ dout,
                                                float* __restrict__ delta, int N, int H) {
-  constexpr int LPR = D / 8, RPW = 64 / LPR;  // lanes per row, rows per wave
-  const int lane = threadIdx.x & 63, sub = lane % LPR;
-  const long long rows = (long long)N * H;
-  const long long step = (long long)gridDim.x * 4 * RPW * DELTA_U;
-  for (long long r0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW * DELTA_U; r0 < rows; r0 += step) {
+  constexpr int LPR = D / 8, RPW = 64 / LPR;  // lanes per row, rows per wave and group
+  const int lane = threadIdx.x & 63, sub = lane % LPR, rr = lane / LPR;
+  const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nchunk = (N + 63) / 64;
+  if (wv >= (long long)nchunk * H) return;
+  const int h = (int)(wv / nchunk), n0 = (int)(wv - (long long)h * nchunk) * 64;
+  for (int g0 = 0; g0 < 64 / RPW; g0 += DELTA_U) {
     uint4 a[DELTA_U], b[DELTA_U];
 #pragma unroll
     for (int u = 0; u < DELTA_U; ++u) {
-      const long long r = r0 + u * RPW + lane / LPR;
-      if (r < rows) {
-        a[u] = *reinterpret_cast<const uint4*>(o + r * D + sub * 8);
-        b[u] = *reinterpret_cast<const uint4*>(dout + r * D + sub * 8);
+      const int n = n0 + (g0 + u) * RPW + rr;
+      if (n < N) {
+        const size_t row = ((size_t)n * H + h) * D + sub * 8;
+        a[u] = *reinterpret_cast<const uint4*>(o + row);
+        b[u] = *reinterpret_cast<const uint4*>(dout + row);
       } else {
         a[u] = b[u] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
 #pragma unroll
     for (int u = 0; u < DELTA_U; ++u) {
-      const long long r = r0 + u * RPW + lane / LPR;
+      const int n = n0 + (g0 + u) * RPW + rr;
       const uint32_t av[4] = {a[u].x, a[u].y, a[u].z, a[u].w}, bv[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
       float s = 0.f;
 #pragma unroll
@@ -51,10 +55,7 @@ __global__ __launch_bounds__(256) void k_delta(const u16* __restrict__ o, const 
       }
 #pragma unroll
       for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m, 64);
-      if (r < rows && sub == 0) {
-        const long long n = r / H, h = r - n * H;
-        delta[h * N + n] = s;
-      }
+      if (n < N && sub == 0) delta[(size_t)h * N + n] = s;
     }
   }
 }
@@ -343,9 +344,8 @@ static hipError_t dq_qs_dispatch(const AttnArgs& a, const Geom& g, const Prep& p
 }
 
 hipError_t launch_delta(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
-  const long long rows = (long long)g.N * g.H;
-  const int rpb = 4 * (64 / (D / 8)) * DELTA_U;
-  const unsigned blocks = (unsigned)min((rows + rpb - 1) / rpb, 4096LL);
+  const long long waves = (long long)((g.N + 63) / 64) * g.H;
+  const unsigned blocks = (unsigned)((waves + 3) / 4);
   if (D == 64)
     k_delta<64><<<blocks, 256, 0, s>>>((const u16*)a.o, (const u16*)a.dout, p.delta, g.N, g.H);
   else
