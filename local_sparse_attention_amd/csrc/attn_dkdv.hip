@@ -126,8 +126,8 @@ struct Cursor {
 constexpr int DKDV_TS_MAX = 256;
 constexpr int DKDV_LW = 2;   // loader waves per workgroup
 
-template <int D, int KT>
-__global__ __launch_bounds__(128 * KT + 64 * DKDV_LW) void k_dkdv_tube(const u16* __restrict__ q, const u16* __restrict__ k,
+template <int D, int KT, int FPG>
+__global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k_dkdv_tube(const u16* __restrict__ q, const u16* __restrict__ k,
                                                        const u16* __restrict__ v, const u16* __restrict__ dout,
                                                        const float* __restrict__ lse,
                                                        const float* __restrict__ delta, u16* __restrict__ dk,
@@ -135,16 +135,20 @@ __global__ __launch_bounds__(128 * KT + 64 * DKDV_LW) void k_dkdv_tube(const u16
                                                        float sl2, float scale) {
   using C = DkdvCfg<D, KT>;
   constexpr int kt = KT;
-  // Two waves per frame in flight: wave 2 s + hf holds K / V of the frames
-  // t = s (mod kt) and the dK / dV columns [hf D / 2, (hf + 1) D / 2) of their keys.
-  // For each item, wave hf of a pair forms S, dP, P and dS of row tile hf and leaves
-  // P and dS in LDS; in the next step both apply dV^T += dO^T P and dK^T += Q^T dS
-  // over all 32 queries to their half.  The ring therefore keeps the previous entry
-  // (prefetch distance NBUF - 2).
+  // Frame slots s = 0 .. kt-1 (slot s holds the frames t = s (mod kt)) in groups of
+  // FPG: wave pair p (waves 2 p, 2 p + 1) owns slots p FPG .. p FPG + FPG - 1 (the
+  // last pair may own fewer), with K / V of their frames and the dK / dV columns
+  // [hf D / 2, (hf + 1) D / 2) of their keys, hf = wave & 1.  For each item, wave hf
+  // of a pair forms S, dP, P and dS of row tile hf for each of its slots (one read
+  // of the Q / dO rows for all of them) and leaves P and dS in LDS; in the next step
+  // both apply dV^T += dO^T P and dK^T += Q^T dS over all 32 queries to their half
+  // of every slot (one transposed read of dO / Q for all of them).  The ring
+  // therefore keeps the previous entry (prefetch distance NBUF - 2).
   // DKDV_LW more waves issue every global->LDS load (and wait for them): the
   // compute waves never wait on an LDS token read or on memory, only at the
   // barrier that closes each step.
-  constexpr int NWC = 2 * KT, NW = NWC + DKDV_LW;
+  constexpr int NG = (KT + FPG - 1) / FPG;  // wave pairs
+  constexpr int NWC = 2 * NG, NW = NWC + DKDV_LW;
   constexpr int NTH = C::NT / 2;  // d tiles per half
   __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::ENTRY];
   __shared__ __attribute__((aligned(16))) char xch[2][KT][2][64 * 16];  // [step parity][frame slot][P, dS]
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(128 * KT + 64 * DKDV_LW) void k_dkdv_tube(const u16
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool loader = wave >= NWC;
-  const int fslot = wave >> 1, hf = wave & 1;  // (compute waves)
+  const int grp = wave >> 1, hf = wave & 1;  // (compute waves)
   const int lw = wave - NWC;                   // (loader waves)
   // every loader wave issues MY_LOADS loads per entry (the count is padded with
   // one-lane loads), so the steady-state wait is a single immediate
@@ -206,105 +210,6 @@ __global__ __launch_bounds__(128 * KT + 64 * DKDV_LW) void k_dkdv_tube(const u16
 
   // tile offsets: Q / dO (item) or K / V (frame) of phase ph
   auto tile = [&](char* e, int tensor, int ph) { return e + (tensor * C::NPH + ph) * C::TILE; };
-
-  f32x4_t dka[NTH], dva[NTH];
-#pragma unroll
-  for (int t = 0; t < NTH; ++t) {
-    dka[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    dva[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  int cur_f = -1;
-  Frag<u16> kf[C::NC], vf[C::NC];  // K / V of the pair's frame (B fragments of S and dP)
-
-  auto finalize = [&](int f) {
-    if (f >= t0 && f < t1 && key_y < g.Hp && key_x < g.Wp) {
-      const size_t row = ((size_t)((f * g.Hp + key_y) * g.Wp + key_x) * g.H + h) * D + hf * (D / 2);
-#pragma unroll
-      for (int t = 0; t < NTH; ++t) {
-        store4(dk + row + 16 * t + 4 * quad, dka[t][0] * scale, dka[t][1] * scale, dka[t][2] * scale,
-               dka[t][3] * scale);
-        store4(dv + row + 16 * t + 4 * quad, dva[t][0], dva[t][1], dva[t][2], dva[t][3]);
-      }
-    }
-  };
-
-  // dV^T += dO^T P and dK^T += Q^T dS for this wave's half, with P / dS of the item
-  // in ring entry e left by the pair's producer in xch[par]
-  auto apply = [&](char* e, int par, bool on) {
-    Frag<u16> pb, db;
-    load_frag(pb, (const u16*)(xch[par][fslot][0] + lane * 16));
-    load_frag(db, (const u16*)(xch[par][fslot][1] + lane * 16));
-    {
-      // off: the MFMAs still run, with P = dS = 0 (no branch around the accumulators)
-      const unsigned m = on ? ~0u : 0u;
-      uint4 wp, wd;
-      __builtin_memcpy(&wp, &pb.v, 16);
-      __builtin_memcpy(&wd, &db.v, 16);
-      wp.x &= m, wp.y &= m, wp.z &= m, wp.w &= m;
-      wd.x &= m, wd.y &= m, wd.z &= m, wd.w &= m;
-      __builtin_memcpy(&pb.v, &wp, 16);
-      __builtin_memcpy(&db.v, &wd, 16);
-    }
-    // A slots j < 4: rows 4 quad + j of row tile 0; j >= 4: the same rows of row tile 1
-    const int trow = 4 * quad + (r16 >> 2);
-#pragma unroll
-    for (int tt = 0; tt < NTH; ++tt) {
-      const int t = hf * NTH + tt;
-      const int off = sw(trow, ((t & 3) * 16 + 4 * (r16 & 3)) * 2);
-      Frag<u16> ao, aq;
-      {
-        const char* base = tile(e, 1, t >> 2) + off;
-        const shortx4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)base);
-        const shortx4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(base + 16 * 128));
-        const shortx4v both[2] = {lo, hi};
-        __builtin_memcpy(&ao.v, both, 16);
-      }
-      {
-        const char* base = tile(e, 0, t >> 2) + off;
-        const shortx4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)base);
-        const shortx4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(base + 16 * 128));
-        const shortx4v both[2] = {lo, hi};
-        __builtin_memcpy(&aq.v, both, 16);
-      }
-      dva[tt] = mma(ao, pb, dva[tt]);
-      dka[tt] = mma(aq, db, dka[tt]);
-      __asm__ __volatile__("" ::: "memory");
-    }
-  };
-
-  // S = Q K^T, dP = dO V^T of row tile hf against this wave's frame, then P and dS of
-  // its queries 16 hf + 4 quad + i, which are slots 4 hf + i of the pair's B
-  // fragments in xch[par] (8 of their 16 bytes per lane)
-  auto produce = [&](char* e, int par) {
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c) {
-      const int off = sw(16 * hf + r16, (c & 1) * 64 + quad * 16);
-      Frag<u16> a;
-      load_frag(a, (const u16*)(tile(e, 0, c >> 1) + off));
-      sc = mma(a, kf[c], sc);
-      load_frag(a, (const u16*)(tile(e, 1, c >> 1) + off));
-      dp = mma(a, vf[c], dp);
-    }
-    const int q0 = 16 * hf + 4 * quad;
-    const int4 sa = *reinterpret_cast<const int4*>(e + C::META + q0 * 8);
-    const int4 sb = *reinterpret_cast<const int4*>(e + C::META + q0 * 8 + 16);
-    const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 8 * KV_Q + q0 * 4);
-    const float4 de = *reinterpret_cast<const float4*>(e + C::META + 12 * KV_Q + q0 * 4);
-    const int sy[4] = {sa.x, sa.z, sb.x, sb.z}, sx[4] = {sa.y, sa.w, sb.y, sb.w};
-    const float lq[4] = {ls.x, ls.y, ls.z, ls.w}, dq[4] = {de.x, de.y, de.z, de.w};
-    shortx4v pb, db;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = (unsigned)(key_y - sy[i]) < (unsigned)g.ky && (unsigned)(key_x - sx[i]) < (unsigned)g.kx;
-      // outside the window the exponent is -inf (exp2 gives 0, no branch)
-      const float pe = __builtin_amdgcn_exp2f(ok ? sc[i] * sl2 - lq[i] * LOG2E : -__builtin_inff());
-      pb[i] = __builtin_bit_cast(short, static_cast<__bf16>(pe));
-      db[i] = __builtin_bit_cast(short, static_cast<__bf16>(pe * (dp[i] - dq[i])));
-    }
-    *reinterpret_cast<shortx4v*>(xch[par][fslot][0] + lane * 16 + hf * 8) = pb;
-    *reinterpret_cast<shortx4v*>(xch[par][fslot][1] + lane * 16 + hf * 8) = db;
-  };
 
   // Three cursors over the same entry stream: token loads (pc, 2 PD + 1 ahead),
   // row loads (ic, PD ahead) and the MFMAs (cc).  Every wave runs PD + (entries)
@@ -413,62 +318,182 @@ __global__ __launch_bounds__(128 * KT + 64 * DKDV_LW) void k_dkdv_tube(const u16
 
   __syncthreads();
   for (int st = -C::PD; st < 0; ++st) lds_barrier();
-  // Slice by slice: the frames that enter (kt for the first slice, then one), then
-  // the items.  The item loop changes only the accumulators, by MFMA, and the frame
-  // steps sit outside it, which keeps the sums and the K / V fragments in fixed
-  // registers while items stream past.
-  int st = 0;      // entry
-  int nprev = 0;   // items of the previous slice (its last one is still to apply)
-  bool kept = false;
-  for (int tau = tau_lo; tau <= tau_hi; ++tau) {
-    const int n = slice_off(tau + 1) - slice_off(tau);
-    const int nf = tau == tau_lo ? kt : 1;
-    for (int jf = 0; jf < nf; ++jf, ++st) {
-      // ---- the previous slice's last item, then a frame enters: its pair writes
-      // the frame it leaves and takes K / V
-      if (jf == 0 && nprev > 0 && kept) apply(ring[(st - 1) % C::NBUF], (st - 1) & 1, true);
-      const int f = tau + kt - nf + jf;
-      if (fslot == f % kt) {
-        if (cur_f >= 0) {
-          finalize(cur_f);
+
+  // The compute loop, for a pair that owns NSG slots (a compile-time count).
+  auto run = [&](auto NSGC) {
+    constexpr int NSG = decltype(NSGC)::value;
+    const int s0 = grp * FPG;  // first slot of this pair
+    f32x4_t dka[NSG][NTH], dva[NSG][NTH];
 #pragma unroll
-          for (int t = 0; t < NTH; ++t) {
-            dka[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            dva[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
-        }
-        // the frame's K and V rows (first 2 KB of each phase tile of the entry) as
-        // MFMA B fragments: key r16, head-dim slots 32 c + 8 quad .. + 7
-        char* e = ring[st % C::NBUF];
+    for (int i = 0; i < NSG; ++i)
 #pragma unroll
-        for (int c = 0; c < C::NC; ++c) {
-          const int koff = sw(r16, (c & 1) * 64 + quad * 16);
-          load_frag(kf[c], (const u16*)(tile(e, 0, c >> 1) + koff));
-          load_frag(vf[c], (const u16*)(tile(e, 1, c >> 1) + koff));
-        }
-        cur_f = f;
+      for (int t = 0; t < NTH; ++t) {
+        dka[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        dva[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-      lds_barrier();
-    }
-    // a pair whose frame lies outside [t0, t1) computes sums nobody writes: skip
-    kept = cur_f >= t0 && cur_f < t1;
-    // ---- the items: each wave of a pair forms P and dS of one row tile; in the next
-    // step both apply them
-    if (n > 0) {
-      if (kept) produce(ring[st % C::NBUF], st & 1);
-      lds_barrier();
-      ++st;
-      for (int j = 1; j < n; ++j, ++st) {
-        apply(ring[(st + C::NBUF - 1) % C::NBUF], (st - 1) & 1, kept);
-        if (kept) produce(ring[st % C::NBUF], st & 1);
+    int cur_f[NSG];
+#pragma unroll
+    for (int i = 0; i < NSG; ++i) cur_f[i] = -1;
+    Frag<u16> kf[NSG][C::NC], vf[NSG][C::NC];  // K / V of each slot's frame (B fragments of S and dP)
+
+    auto finalize = [&](int i) {
+      const int f = cur_f[i];
+      if (f >= t0 && f < t1 && key_y < g.Hp && key_x < g.Wp) {
+        const size_t row = ((size_t)((f * g.Hp + key_y) * g.Wp + key_x) * g.H + h) * D + hf * (D / 2);
+#pragma unroll
+        for (int t = 0; t < NTH; ++t) {
+          store4(dk + row + 16 * t + 4 * quad, dka[i][t][0] * scale, dka[i][t][1] * scale, dka[i][t][2] * scale,
+                 dka[i][t][3] * scale);
+          store4(dv + row + 16 * t + 4 * quad, dva[i][t][0], dva[i][t][1], dva[i][t][2], dva[i][t][3]);
+        }
+      }
+    };
+
+    // dV^T += dO^T P and dK^T += Q^T dS for this wave's half of every slot, with P /
+    // dS of the item in ring entry e left by the pair's producers in xch[par].  (A
+    // slot whose frame is outside [t0, t1) gets sums nobody writes.)
+    auto apply = [&](char* e, int par) {
+      Frag<u16> pb[NSG], db[NSG];
+#pragma unroll
+      for (int i = 0; i < NSG; ++i) {
+        load_frag(pb[i], (const u16*)(xch[par][s0 + i][0] + lane * 16));
+        load_frag(db[i], (const u16*)(xch[par][s0 + i][1] + lane * 16));
+      }
+      // A slots j < 4: rows 4 quad + j of row tile 0; j >= 4: the same rows of row tile 1
+      const int trow = 4 * quad + (r16 >> 2);
+#pragma unroll
+      for (int tt = 0; tt < NTH; ++tt) {
+        const int t = hf * NTH + tt;
+        const int off = sw(trow, ((t & 3) * 16 + 4 * (r16 & 3)) * 2);
+        Frag<u16> ao, aq;
+        {
+          const char* base = tile(e, 1, t >> 2) + off;
+          const shortx4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)base);
+          const shortx4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(base + 16 * 128));
+          const shortx4v both[2] = {lo, hi};
+          __builtin_memcpy(&ao.v, both, 16);
+        }
+        {
+          const char* base = tile(e, 0, t >> 2) + off;
+          const shortx4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)base);
+          const shortx4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(base + 16 * 128));
+          const shortx4v both[2] = {lo, hi};
+          __builtin_memcpy(&aq.v, both, 16);
+        }
+#pragma unroll
+        for (int i = 0; i < NSG; ++i) {
+          dva[i][tt] = mma(ao, pb[i], dva[i][tt]);
+          dka[i][tt] = mma(aq, db[i], dka[i][tt]);
+        }
+        __asm__ __volatile__("" ::: "memory");
+      }
+    };
+
+    // S = Q K^T, dP = dO V^T of row tile hf against each slot's frame, then P and dS
+    // of its queries 16 hf + 4 quad + i, which are slots 4 hf + i of the pair's B
+    // fragments in xch[par] (8 of their 16 bytes per lane)
+    auto produce = [&](char* e, int par) {
+      f32x4_t sc[NSG], dp[NSG];
+#pragma unroll
+      for (int i = 0; i < NSG; ++i) sc[i] = dp[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        const int off = sw(16 * hf + r16, (c & 1) * 64 + quad * 16);
+        Frag<u16> a;
+        load_frag(a, (const u16*)(tile(e, 0, c >> 1) + off));
+#pragma unroll
+        for (int i = 0; i < NSG; ++i) sc[i] = mma(a, kf[i][c], sc[i]);
+        load_frag(a, (const u16*)(tile(e, 1, c >> 1) + off));
+#pragma unroll
+        for (int i = 0; i < NSG; ++i) dp[i] = mma(a, vf[i][c], dp[i]);
+      }
+      const int q0 = 16 * hf + 4 * quad;
+      const int4 sa = *reinterpret_cast<const int4*>(e + C::META + q0 * 8);
+      const int4 sb = *reinterpret_cast<const int4*>(e + C::META + q0 * 8 + 16);
+      const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 8 * KV_Q + q0 * 4);
+      const float4 de = *reinterpret_cast<const float4*>(e + C::META + 12 * KV_Q + q0 * 4);
+      const int sy[4] = {sa.x, sa.z, sb.x, sb.z}, sx[4] = {sa.y, sa.w, sb.y, sb.w};
+      const float lq[4] = {ls.x, ls.y, ls.z, ls.w}, dq[4] = {de.x, de.y, de.z, de.w};
+#pragma unroll
+      for (int i = 0; i < NSG; ++i) {
+        shortx4v pb, db;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool ok = (unsigned)(key_y - sy[j]) < (unsigned)g.ky && (unsigned)(key_x - sx[j]) < (unsigned)g.kx;
+          // outside the window the exponent is -inf (exp2 gives 0, no branch)
+          const float pe = __builtin_amdgcn_exp2f(ok ? sc[i][j] * sl2 - lq[j] * LOG2E : -__builtin_inff());
+          pb[j] = __builtin_bit_cast(short, static_cast<__bf16>(pe));
+          db[j] = __builtin_bit_cast(short, static_cast<__bf16>(pe * (dp[i][j] - dq[j])));
+        }
+        *reinterpret_cast<shortx4v*>(xch[par][s0 + i][0] + lane * 16 + hf * 8) = pb;
+        *reinterpret_cast<shortx4v*>(xch[par][s0 + i][1] + lane * 16 + hf * 8) = db;
+      }
+    };
+
+    // Slice by slice: the frames that enter (kt for the first slice, then one), then
+    // the items.  The item loop changes only the accumulators, by MFMA, and the frame
+    // steps sit outside it, which keeps the sums and the K / V fragments in fixed
+    // registers while items stream past.
+    int st = 0;     // entry
+    int nprev = 0;  // items of the previous slice (its last one is still to apply)
+    for (int tau = tau_lo; tau <= tau_hi; ++tau) {
+      const int n = slice_off(tau + 1) - slice_off(tau);
+      const int nf = tau == tau_lo ? kt : 1;
+      for (int jf = 0; jf < nf; ++jf, ++st) {
+        // ---- the previous slice's last item, then a frame enters: the pair that
+        // owns its slot writes the frame the slot leaves and takes K / V
+        if (jf == 0 && nprev > 0) apply(ring[(st - 1) % C::NBUF], (st - 1) & 1);
+        const int f = tau + kt - nf + jf;
+        const int sf = f % kt;
+        static_for<0, NSG>([&](auto IC) {
+          constexpr int i = decltype(IC)::value;
+          if (sf == s0 + i) {
+            if (cur_f[i] >= 0) {
+              finalize(i);
+#pragma unroll
+              for (int t = 0; t < NTH; ++t) {
+                dka[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                dva[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              }
+            }
+            // the frame's K and V rows (first 2 KB of each phase tile of the entry)
+            // as MFMA B fragments: key r16, head-dim slots 32 c + 8 quad .. + 7
+            char* e = ring[st % C::NBUF];
+#pragma unroll
+            for (int c = 0; c < C::NC; ++c) {
+              const int koff = sw(r16, (c & 1) * 64 + quad * 16);
+              load_frag(kf[i][c], (const u16*)(tile(e, 0, c >> 1) + koff));
+              load_frag(vf[i][c], (const u16*)(tile(e, 1, c >> 1) + koff));
+            }
+            cur_f[i] = f;
+          }
+        });
         lds_barrier();
       }
+      // ---- the items: each wave of a pair forms P and dS of one row tile; in the next
+      // step both apply them
+      if (n > 0) {
+        produce(ring[st % C::NBUF], st & 1);
+        lds_barrier();
+        ++st;
+        for (int j = 1; j < n; ++j, ++st) {
+          apply(ring[(st + C::NBUF - 1) % C::NBUF], (st - 1) & 1);
+          produce(ring[st % C::NBUF], st & 1);
+          lds_barrier();
+        }
+      }
+      nprev = n;
     }
-    nprev = n;
-  }
-  // the last item (its ring slot is not reused any more)
-  if (nprev > 0 && kept) apply(ring[(st - 1) % C::NBUF], (st - 1) & 1, true);
-  finalize(cur_f);
+    // the last item (its ring slot is not reused any more)
+    if (nprev > 0) apply(ring[(st - 1) % C::NBUF], (st - 1) & 1);
+#pragma unroll
+    for (int i = 0; i < NSG; ++i) finalize(i);
+  };
+  constexpr int LAST = KT - (NG - 1) * FPG;  // slots of the last pair
+  if (LAST != FPG && grp == NG - 1)
+    run(std::integral_constant<int, LAST>{});
+  else
+    run(std::integral_constant<int, FPG>{});
 }
 
 bool dkdv_tube_eligible(const Geom& g, int dtype, int D) {
@@ -484,8 +509,25 @@ hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Frame slots per wave pair: two where the registers allow it (kt = 3, 5: the
+// workgroup has 2 ceil(kt / 2) + 2 waves, at most two per SIMD, so a wave may hold
+// the K / V fragments and dK / dV sums of two frames), one for kt = 7 (sixteen
+// waves, four per SIMD, 128 registers a wave) and kt = 1.
+#ifndef DSA3D_DKDV_FPG3
+#define DSA3D_DKDV_FPG3 2
+#endif
+#ifndef DSA3D_DKDV_FPG5
+#define DSA3D_DKDV_FPG5 2
+#endif
+template <int KT>
+constexpr int dkdv_fpg() {
+  return KT == 3 ? DSA3D_DKDV_FPG3 : KT == 5 ? DSA3D_DKDV_FPG5 : 1;
+}
+
 template <int D, int KT>
 static hipError_t dkdv_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
+  constexpr int FPG = dkdv_fpg<KT>();
+  constexpr int NG = (KT + FPG - 1) / FPG;
   const int nkb = kv_item_columns(g);
   // the longest chunk that still leaves at least 512 workgroups (two per compute unit)
   int ts = min(g.F, DKDV_TS_MAX);
@@ -493,7 +535,7 @@ static hipError_t dkdv_impl(const AttnArgs& a, const Geom& g, const Prep& p, hip
   const int nchunk = (g.F + ts - 1) / ts;
   const long long total = (long long)nkb * nchunk * g.H;
   KvItems it{p.kv_off, p.kv_ids, p.kv_st};
-  k_dkdv_tube<D, KT><<<(unsigned)total, 128 * KT + 64 * DKDV_LW, 0, s>>>(
+  k_dkdv_tube<D, KT, FPG><<<(unsigned)total, 128 * NG + 64 * DKDV_LW, 0, s>>>(
       (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, a.lse, p.delta, (u16*)a.dk, (u16*)a.dv, g,
       it, ts, a.scale * LOG2E, a.scale);
   return hipGetLastError();
