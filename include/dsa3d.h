@@ -43,6 +43,10 @@
  *   Determinism      Outputs are bitwise identical for identical inputs (no
  *                    floating-point atomics; the dk/dv reduction visits queries
  *                    in a fixed order).
+ *   Finite inputs    q, k, v and dout are expected to be finite.  The kernels
+ *                    multiply whole 16-token tiles, with zero weights outside a
+ *                    query's window, so an inf or NaN in one row can reach the
+ *                    outputs of other queries (keys) of the same tile.
  */
 #ifndef DSA3D_H
 #define DSA3D_H
