@@ -23,12 +23,11 @@ namespace dsa3d {
 template <int D, int NBY, int NBX>
 struct FwdCfg {
   static constexpr int NB = NBY * NBX;              // key blocks of a frame tile
-  static constexpr int NBPAD = (NB + 1) & ~1;       // whole 32-key pairs for the V pass
-  static constexpr int NPAIR = NBPAD / 2;
+  static constexpr int NPAIR = (NB + 1) / 2;        // 32-key pairs of the V pass (the last may be one block)
   static constexpr int NPH = D / 64;                // 128-byte column phases per K (or V) row
   static constexpr int NPH2 = 2 * NPH;              // ring steps per frame
-  static constexpr int TILE = NBPAD * 16 * 128;     // one phase tile
-  static constexpr int NLOADS = NBPAD * 2;          // 1 KB direct loads per phase tile (pad block too)
+  static constexpr int TILE = NB * 16 * 128;        // one phase tile
+  static constexpr int NLOADS = NB * 2;             // 1 KB direct loads per phase tile
   static constexpr int NBUF = 5, PD = NBUF - 1;     // ring depth, steps loaded ahead
   static constexpr int NC = D / 32, NT = D / 16;
   static constexpr int QTILE = 16 * 128;            // one phase of a staged row tile
@@ -97,7 +96,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
               if (t >= 0) issue_rows<D>(stage[sl], q, T.ids[t], g, h, lane);
             }
           }
-          issue_key_tile_w<D, NBX, C::NB, C::NBPAD, FWD_LW, LWI>(
+          issue_key_tile_w<D, NBX, C::NB, C::NB, FWD_LW, LWI>(
               ring[x % C::NBUF], (ph < C::NPH ? k : v) + (ph % C::NPH) * 64 + h * D + lane_el, g, by, bx, f, lane, k,
               stage[0]);  // (no padding: the loads split evenly)
         };
@@ -250,7 +249,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
               float ps = 0.f;
               static_for<0, C::NPAIR>([&](auto CC) {
                 constexpr int c = decltype(CC)::value;
-                constexpr bool odd = 2 * c + 1 < C::NB;  // else the pad block: P = 0
+                constexpr bool odd = 2 * c + 1 < C::NB;  // else a single block: its pair half is 0
                 float pr[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -273,9 +272,12 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
           for (int c = 0; c < C::NPAIR; ++c) {
 #pragma unroll
             for (int dt = 0; dt < C::NT / C::NPH; ++dt) {
+              // a single last block reads itself again as the pair's second half (its
+              // P there is 0)
               const char* pa = tb + (2 * c) * 2048 + toff[dt];
+              const char* pb = 2 * c + 1 < C::NB ? pa + 2048 : pa;
               const shortx4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
-              const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
+              const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pb);
               Frag<u16> a;
               const shortx4_t both[2] = {lo, hi};
               __builtin_memcpy(&a.v, both, 16);
