@@ -5,7 +5,8 @@
 //
 // Same work decomposition as the forward (attn_fwd.hip): a workgroup sweeps the
 // frames of one start blob column, every frame's key tile goes through an LDS ring
-// once and serves the QS_SLOTS row tiles in flight, 2 per wave, always computed.
+// once and serves the QS_SLOTS row tiles in flight, one per wave (a wave whose
+// slot holds no tile this frame skips its MFMA work).
 // A frame takes four ring steps (D = 128): V columns 0-63 and 64-127 (dP^T =
 // V dO^T), then K columns 0-63 and 64-127 (S^T = K Q^T); at the last one P^T and
 // dS^T follow and dQ^T += K^T dS^T reads both K steps transposed, so the ring keeps

@@ -5,11 +5,11 @@
 // it, and sweeps the frames its row tiles read (the pass schedule built by
 // qsched.hip).  Every frame's key tile -- the (4 + ky - 1) x (4 + kx - 1) keys
 // anchored at (4 by, 4 bx), in NBY x NBX blocks of 4 x 4 -- is staged once into an
-// LDS ring with direct global->LDS loads and read by all QS_SLOTS row tiles in
-// flight (2 per wave), which belong to the kt slices that read that frame.
+// LDS ring with direct global->LDS loads (issued by two loader waves) and read by
+// all QS_SLOTS row tiles in flight (one per compute wave), which belong to the kt
+// slices that read that frame.
 //
-// Per frame and wave, for both of its slots (always, busy or idle: no branch on
-// the MFMA path):
+// Per frame and busy slot (a wave whose slot holds no tile this frame skips it):
 //   S^T = K Q^T        16x16x32 bf16 MFMA, K rows from LDS, Q^T held in registers
 //   mask to the query's own window (additive 0 / -inf biases set at activation),
 //   online softmax in the log2 domain, P kept as bf16 fragments
@@ -33,9 +33,11 @@ struct FwdCfg {
   static constexpr int QTILE = 16 * 128;            // one phase of a staged row tile
 };
 
-// Row-tile slots per wave: with one, the QS_SLOTS slots take 8 waves (2 per SIMD),
-// so one wave's LDS and scalar work issues beside the other's VALU and MFMA work;
-// with two, a K / V fragment read from LDS feeds the MFMAs of both slots.
+// Row-tile slots per compute wave: with one (the default), the QS_SLOTS slots take
+// 8 waves (2 per SIMD, plus the loaders), so one wave's LDS and scalar work issues
+// beside the other's VALU and MFMA work; with two, a K / V fragment read from LDS
+// feeds the MFMAs of both slots, but four waves hide latency poorly (measured
+// slower).
 #ifndef DSA3D_FWD_NS
 #define DSA3D_FWD_NS 1
 #endif
