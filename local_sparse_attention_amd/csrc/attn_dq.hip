@@ -114,6 +114,7 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
   f32x4_t dqa[NS][C::NT];
   f32x4_t sacc[NS][C::NB], dpa[NS][C::NB];
   Frag<u16> dsf[NS][C::NPAIR];
+  shortx4_t dsl[NS];  // dS^T of the unpaired last key block (odd NB), 4 keys per lane
   float ybias[NS][NBY], xbias[NS][NBX][4];
   float lse2[NS], dlt[NS];
   int qn[NS], fend[NS];
@@ -266,14 +267,20 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
             };
             static_for<0, C::NPAIR>([&](auto CC) {
               constexpr int c = decltype(CC)::value;
-              constexpr bool odd = 2 * c + 1 < C::NB;  // else the pad block: dS = 0
-              float d8[8];
+              if constexpr (2 * c + 1 < C::NB) {
+                float d8[8];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                d8[i] = ds_of(2 * c, i);
-                d8[i + 4] = odd ? ds_of(odd ? 2 * c + 1 : 0, i) : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                  d8[i] = ds_of(2 * c, i);
+                  d8[i + 4] = ds_of(2 * c + 1, i);
+                }
+                set_frag(dsf[s][c], d8);
+              } else {
+                __bf16 d4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d4[i] = static_cast<__bf16>(ds_of(2 * c, i));
+                __builtin_memcpy(&dsl[s], d4, 8);
               }
-              set_frag(dsf[s][c], d8);
             });
           }
           // ---- dQ^T += K^T dS^T: this step's K columns and the previous step's
@@ -285,15 +292,20 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
 #pragma unroll
               for (int dt = 0; dt < C::NT / C::NPH; ++dt) {
                 const char* pa = kt_ + (2 * c) * 2048 + toff[dt];
+                const int ot = kp * (C::NT / C::NPH) + dt;
                 const shortx4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
-                const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
-                Frag<u16> a;
-                const shortx4_t both[2] = {lo, hi};
-                __builtin_memcpy(&a.v, both, 16);
+                if (2 * c + 1 < C::NB) {
+                  const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
+                  Frag<u16> a;
+                  const shortx4_t both[2] = {lo, hi};
+                  __builtin_memcpy(&a.v, both, 16);
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                  const int ot = kp * (C::NT / C::NPH) + dt;
-                  dqa[s][ot] = mma(a, dsf[s][c], dqa[s][ot]);
+                  for (int s = 0; s < NS; ++s) dqa[s][ot] = mma(a, dsf[s][c], dqa[s][ot]);
+                } else {
+                  // a single 16-key block: a 16-deep product, half the transposed reads
+#pragma unroll
+                  for (int s = 0; s < NS; ++s)
+                    dqa[s][ot] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, dsl[s], dqa[s][ot], 0, 0, 0);
                 }
               }
             }

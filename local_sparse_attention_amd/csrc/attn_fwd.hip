@@ -164,6 +164,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
       // scores and P of this frame (not carried from one frame to the next)
       f32x4_t sacc[NS][C::NB];
       Frag<u16> pf[NS][C::NPAIR];
+      shortx4_t pl[NS];  // P^T of the unpaired last key block (odd NB), 4 keys per lane
       // ---- activations: Q fragments, window biases, fresh softmax state
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -251,15 +252,25 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
               float ps = 0.f;
               static_for<0, C::NPAIR>([&](auto CC) {
                 constexpr int c = decltype(CC)::value;
-                constexpr bool odd = 2 * c + 1 < C::NB;  // else a single block: its pair half is 0
-                float pr[8];
+                if constexpr (2 * c + 1 < C::NB) {
+                  float pr[8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  pr[i] = __builtin_amdgcn_exp2f(sacc[s][2 * c][i] - mref);
-                  pr[i + 4] = odd ? __builtin_amdgcn_exp2f(sacc[s][odd ? 2 * c + 1 : 0][i] - mref) : 0.f;
-                  ps += pr[i] + pr[i + 4];
+                  for (int i = 0; i < 4; ++i) {
+                    pr[i] = __builtin_amdgcn_exp2f(sacc[s][2 * c][i] - mref);
+                    pr[i + 4] = __builtin_amdgcn_exp2f(sacc[s][2 * c + 1][i] - mref);
+                    ps += pr[i] + pr[i + 4];
+                  }
+                  set_frag(pf[s][c], pr);
+                } else {
+                  __bf16 p4[4];
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    const float pr = __builtin_amdgcn_exp2f(sacc[s][2 * c][i] - mref);
+                    ps += pr;
+                    p4[i] = static_cast<__bf16>(pr);
+                  }
+                  __builtin_memcpy(&pl[s], p4, 8);
                 }
-                set_frag(pf[s][c], pr);
               });
               ps = quad_sum(ps);
               l_run[s] += ps;
@@ -274,19 +285,21 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
           for (int c = 0; c < C::NPAIR; ++c) {
 #pragma unroll
             for (int dt = 0; dt < C::NT / C::NPH; ++dt) {
-              // a single last block reads itself again as the pair's second half (its
-              // P there is 0)
+              constexpr int ot = vph * (C::NT / C::NPH);
               const char* pa = tb + (2 * c) * 2048 + toff[dt];
-              const char* pb = 2 * c + 1 < C::NB ? pa + 2048 : pa;
               const shortx4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
-              const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pb);
-              Frag<u16> a;
-              const shortx4_t both[2] = {lo, hi};
-              __builtin_memcpy(&a.v, both, 16);
+              if (2 * c + 1 < C::NB) {
+                const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
+                Frag<u16> a;
+                const shortx4_t both[2] = {lo, hi};
+                __builtin_memcpy(&a.v, both, 16);
 #pragma unroll
-              for (int s = 0; s < NS; ++s) {
-                constexpr int ot = vph * (C::NT / C::NPH);
-                oacc[s][ot + dt] = mma(a, pf[s][c], oacc[s][ot + dt]);
+                for (int s = 0; s < NS; ++s) oacc[s][ot + dt] = mma(a, pf[s][c], oacc[s][ot + dt]);
+              } else {
+                // a single last block: a 16-deep product
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+                  oacc[s][ot + dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, pl[s], oacc[s][ot + dt], 0, 0, 0);
               }
             }
           }
