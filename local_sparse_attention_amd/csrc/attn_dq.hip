@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
   shortx4_t dsl[NS];  // dS^T of the unpaired last key block (odd NB), 4 keys per lane
   float ybias[NS][NBY], xbias[NS][NBX][4];
   float lse2[NS], dlt[NS];
-  int qn[NS], fend[NS];
+  int qn[NS], fend[NS], rt[NS];  // rt: the row's slice (it sees frames rt .. rt + kt - 1)
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
 #pragma unroll
@@ -137,6 +137,7 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
     dlt[s] = 0.f;
     qn[s] = -1;
     fend[s] = -1;
+    rt[s] = 0;
   }
 
   const int* sp = p.qs + p.qs_off[w];
@@ -205,7 +206,8 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
             for (int i = 0; i < 4; ++i)
               xbias[s][j][i] = (unsigned)(4 * bx + 4 * j + i - st.y) < (unsigned)g.kx ? 0.f : -INFINITY;
           qn[s] = st.x >= 0 ? T.ids[t][r16] : -1;
-          fend[s] = __builtin_amdgcn_readfirstlane(T.tau[t]) + g.kt - 1;
+          fend[s] = __builtin_amdgcn_readfirstlane(T.tlast[t]) + g.kt - 1;
+          rt[s] = __builtin_amdgcn_readfirstlane(T.tau[t]) + T.dt[t][r16];
 #pragma unroll
           for (int tt = 0; tt < C::NT; ++tt) dqa[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
@@ -261,8 +263,14 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           // ---- P^T and dS^T on the window, as bf16 pairs of key blocks
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
+            // a row whose slice does not read this frame (a tile of several slices)
+            // has P = 0 there; lse folds into the row bias (exact: biases are 0 or -inf)
+            const float tb = (unsigned)(f - rt[s]) < (unsigned)g.kt ? 0.f : -INFINITY;
+            float yb[NBY];
+#pragma unroll
+            for (int i = 0; i < NBY; ++i) yb[i] = (ybias[s][i] + tb) - lse2[s];
             auto ds_of = [&](int b, int i) {
-              const float x = sacc[s][b][i] * sl2 + (ybias[s][b / NBX] + xbias[s][b % NBX][i]) - lse2[s];
+              const float x = sacc[s][b][i] * sl2 + (yb[b / NBX] + xbias[s][b % NBX][i]);
               return __builtin_amdgcn_exp2f(x) * (dpa[s][b][i] - dlt[s]);
             };
             static_for<0, C::NPAIR>([&](auto CC) {

@@ -15,7 +15,9 @@
 //   online softmax in the log2 domain, P kept as bf16 fragments
 //   O^T += V^T P^T     V^T by transposed LDS reads (ds_read_b64_tr_b16)
 // A slot's row tile is activated at its first frame (Q rows staged by direct
-// loads issued with the frame's first tile loads) and written out after its kt-th.
+// loads issued with the frame's first tile loads) and written out after its last
+// (the kt-th; later for a tile of several slices, whose rows each see only the kt
+// frames of their own slice and no keys in the others).
 #include "qs_common.hpp"
 
 namespace dsa3d {
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
   f32x4_t oacc[NS][C::NT];
   float ybias[NS][NBY], xbias[NS][NBX][4];
   float m_run[NS], l_run[NS];
-  int qn[NS], fend[NS];
+  int qn[NS], fend[NS], rt[NS];  // rt: the row's slice (it sees frames rt .. rt + kt - 1)
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
 #pragma unroll
@@ -153,6 +155,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
     l_run[s] = 0.f;
     qn[s] = -1;
     fend[s] = -1;
+    rt[s] = 0;
   }
 
   for (int pass = 0; pass < npass; ++pass) {
@@ -184,7 +187,8 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
             for (int i = 0; i < 4; ++i)
               xbias[s][j][i] = (unsigned)(4 * bx + 4 * j + i - st.y) < (unsigned)g.kx ? 0.f : -INFINITY;
           qn[s] = st.x >= 0 ? T.ids[t][r16] : -1;
-          fend[s] = __builtin_amdgcn_readfirstlane(T.tau[t]) + g.kt - 1;
+          fend[s] = __builtin_amdgcn_readfirstlane(T.tlast[t]) + g.kt - 1;
+          rt[s] = __builtin_amdgcn_readfirstlane(T.tau[t]) + T.dt[t][r16];
           m_run[s] = -INFINITY;  // the first rescale (alpha = 0) clears O and l
         }
       }
@@ -226,19 +230,26 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
             // ---- window mask, online softmax (log2 domain), P as bf16 pairs
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
+              // a row whose slice does not read this frame (a tile of several slices)
+              // sees none of its keys
+              const float tb = (unsigned)(f - rt[s]) < (unsigned)g.kt ? 0.f : -INFINITY;
+              float yb[NBY];
+#pragma unroll
+              for (int i = 0; i < NBY; ++i) yb[i] = ybias[s][i] + tb;
               float cm = -INFINITY;
 #pragma unroll
               for (int b = 0; b < C::NB; ++b)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  const float x = sacc[s][b][i] * sl2 + (ybias[s][b / NBX] + xbias[s][b % NBX][i]);
+                  const float x = sacc[s][b][i] * sl2 + (yb[b / NBX] + xbias[s][b % NBX][i]);
                   sacc[s][b][i] = x;
                   cm = fmaxf(cm, x);
                 }
               cm = quad_max(cm);
               // The reference max moves only when a score exceeds it by more than
-              // 2^8 (or on a tile's first frame, m = -inf): P <= 256 otherwise, and
-              // O and l need no rescale.
+              // 2^8 (or on a row's first frame with keys, m = -inf): P <= 256
+              // otherwise, and O and l need no rescale.  A row that has seen no key
+              // yet keeps m = -inf (alpha = 0 clears its O and l until it does).
               if (__ballot(cm > m_run[s] + 8.f)) {
                 const float mn = fmaxf(m_run[s], cm);
                 const float mref = (mn == -INFINITY) ? 0.f : mn;
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
                 l_run[s] *= alpha;
 #pragma unroll
                 for (int t = 0; t < C::NT; ++t) oacc[s][t] *= alpha;
-                m_run[s] = mref;
+                m_run[s] = mn;
               }
               const float mref = m_run[s] == -INFINITY ? 0.f : m_run[s];
               float ps = 0.f;

@@ -25,8 +25,11 @@ struct Prep {
   int* kv_ids;         // [max_kv_items * KV_Q] query tokens, KV_Q per item
   int2* kv_st;         // [max_kv_items * KV_Q] (sy, sx) window starts
   // query-side frame-sweeping kernels (qs_geometry() only)
+  int* qt_off;         // [qs_items + 1]: row tiles of work item w are qt[qt_off[w] .. qt_off[w+1])
+  int* qt;             // [max_groups * QT_INTS] row tile descriptors (see qsched.hip)
   int* tq_ids;         // [max_groups * 16] row tile query tokens
   int2* tq_st;         // [max_groups * 16] row tile (sy, sx) window starts
+  signed char* tq_dt;  // [max_groups * 16] row's slice minus the tile's first slice
   int* qs_off;         // [qs_items + 1] schedule of work item w at qs + qs_off[w]
   int* qs;             // schedules (see qsched.hip)
   int* perm;           // = the vals buffer the sort ends in
@@ -57,8 +60,11 @@ inline size_t max_kv_items(const Geom& g) {
 }
 
 // Query-side schedules: a work item is one start blob column and QS_TS slices;
-// QS_SLOTS row tiles in flight, at most QS_MAXT per pass.
-constexpr int QS_TS = 32, QS_SLOTS = 8, QS_MAXT = 64;
+// QS_SLOTS row tiles in flight, at most QS_MAXT per pass.  A row tile holds the
+// queries of one slice, or the leftover queries (fewer than 16 each) of up to
+// QS_SPAN consecutive slices; its descriptor is QT_INTS ints.
+constexpr int QS_TS = 32, QS_SLOTS = 8, QS_MAXT = 64, QS_SPAN = 2;
+constexpr int QT_INTS = 2 + 3 * QS_SPAN;
 __host__ __device__ inline bool qs_geometry(const Geom& g) { return g.kt >= 3 && g.kt <= 16 && g.ky <= 9 && g.kx <= 9; }
 __host__ __device__ inline int qs_items(const Geom& g) { return g.nby * g.nbx * ((g.Lt + QS_TS - 1) / QS_TS); }
 // A pass holds 2 + (frames <= QS_TS + kt - 1) + 4 ints per tile and schedules at

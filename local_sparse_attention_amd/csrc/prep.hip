@@ -60,8 +60,11 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   q.kv_ids = kv ? (int*)take(max_kv_items(g) * KV_Q * 4) : nullptr;
   q.kv_st = kv ? (int2*)take(max_kv_items(g) * KV_Q * sizeof(int2)) : nullptr;
   const bool qsg = qs_geometry(g);
+  q.qt_off = qsg ? (int*)take(((size_t)qs_items(g) + 1) * 4) : nullptr;
+  q.qt = qsg ? (int*)take((size_t)max_groups * QT_INTS * 4) : nullptr;
   q.tq_ids = qsg ? (int*)take((size_t)max_groups * 16 * 4) : nullptr;
   q.tq_st = qsg ? (int2*)take((size_t)max_groups * 16 * sizeof(int2)) : nullptr;
+  q.tq_dt = qsg ? (signed char*)take((size_t)max_groups * 16) : nullptr;
   q.qs_off = qsg ? (int*)take(((size_t)qs_items(g) + 1) * 4) : nullptr;
   q.qs = qsg ? (int*)take(qs_ints(g, max_groups) * 4) : nullptr;
   q.perm = q.vals[passes & 1];

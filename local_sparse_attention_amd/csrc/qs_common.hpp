@@ -11,7 +11,9 @@ namespace dsa3d {
 struct QsPass {
   int ids[QS_MAXT][16];             // query tokens of each tile of the pass
   int2 st[QS_MAXT][16];             // their window starts (sy, sx)
-  int tau[QS_MAXT];                 // slice of each tile
+  signed char dt[QS_MAXT][16];      // their slices minus the tile's first slice
+  int tau[QS_MAXT];                 // first slice of each tile
+  int tlast[QS_MAXT];               // last slice of each tile
   short act[QS_TS + 16][QS_SLOTS];  // tile activated at (frame index, slot), or -1
   int frames[QS_TS + 16];           // frames swept by the pass
   int hdr[2];                       // frame count, tile count
@@ -34,8 +36,10 @@ __device__ __forceinline__ void load_pass(QsPass& T, const int*& sp, const Prep&
     const int gi = tl[4 * t];
     T.ids[t][j] = p.tq_ids[(size_t)gi * 16 + j];
     T.st[t][j] = p.tq_st[(size_t)gi * 16 + j];
+    T.dt[t][j] = p.tq_dt[(size_t)gi * 16 + j];
     if (j == 0) {
       T.tau[t] = tl[4 * t + 1];
+      T.tlast[t] = p.qt[(size_t)gi * QT_INTS + 1];
       T.act[tl[4 * t + 3]][tl[4 * t + 2]] = (short)t;
     }
   }

@@ -1,54 +1,139 @@
 // Query-side work lists shared by the frame-sweeping forward and dQ kernels
 // (head-independent: built once per call, used by every head).
 //
-// Row tiles: the queries of one start blob slice (1 x 4 x 4 start cells of the
-// lattice of the 3D Deformable Slide Attention section) in groups of 16, as listed
-// by groups / goff.  tq_ids / tq_st hold each tile's query tokens and window
-// starts (sy, sx), padded to 16 with token 0 and a start no key matches.
+// Row tiles: a work item is one start blob column (by, bx) and QS_TS consecutive
+// slices (1 x 4 x 4 start cells of the lattice of the 3D Deformable Slide
+// Attention section).  Each slice's blob contributes its full groups of 16
+// queries as tiles of their own; the leftover group of a slice (fewer than 16
+// queries) joins the open leftover tile of an earlier slice of the item when the
+// queries fit in 16 and that tile's first slice is less than QS_SPAN slices back,
+// else it opens a new one.  A tile of slices tau0 .. tlast reads the frames
+// tau0 .. tlast + kt - 1; each row sees only the kt frames of its own slice
+// (tq_dt = its slice - tau0), the kernels mask the others.  Descriptor (QT_INTS
+// ints): tau0, tlast, then per part (first index into perm, count, slice - tau0),
+// unused parts with count 0.  Tiles are listed in order of tau0.  tq_ids / tq_st
+// hold each tile's query tokens and window starts (sy, sx), padded to 16 with
+// token 0 and a start no key matches.
 //
-// Schedules: a workgroup owns one start blob column (by, bx) and QS_TS consecutive
-// slices.  Its row tiles get one of QS_SLOTS slots for the kt frames they read;
-// greedy, in slice order, a tile takes the slot that has been free the longest
+// Schedules: a work item's row tiles get one of QS_SLOTS slots for the frames they
+// read; greedy, in tile order, a tile takes the slot that has been free the longest
 // (a slot is free again once its tile has read its last frame).  Tiles that find
 // no free slot at their first frame wait for a further pass over the frames.
 // Each pass lists the frames it sweeps (the union of its tiles' frame ranges, in
-// order) and its tiles as (tile, slice, slot, index of the slice's frame in the list).
+// order) and its tiles as (tile, tau0, slot, index of frame tau0 in the list).
 #include "internal.hpp"
 
 namespace dsa3d {
 
-__global__ __launch_bounds__(256) void k_tile_fill(const int* __restrict__ perm, const int4* __restrict__ starts,
-                                                   const int2* __restrict__ groups, const int* __restrict__ ngroups,
-                                                   int* __restrict__ tq_ids, int2* __restrict__ tq_st) {
-  const int g = blockIdx.x * 16 + (threadIdx.x >> 4), j = threadIdx.x & 15;
-  if (g >= *ngroups) return;
-  const int2 gr = groups[g];
-  int id = 0;
-  int2 st = make_int2(-(1 << 29), -(1 << 29));
-  if (j < gr.y) {
-    id = perm[gr.x + j];
-    const int4 s = starts[id];
-    st = make_int2(s.y, s.z);
-  }
-  tq_ids[(size_t)g * 16 + j] = id;
-  tq_st[(size_t)g * 16 + j] = st;
-}
-
-// Runs the greedy schedule of work item w (blob column, chunk) and writes it to out;
-// returns its size in ints.
-__device__ int build_schedule(const Geom& g, const int* __restrict__ goff, int w, int* out) {
+// Row tiles of work item w (see above): writes their descriptors to out (if not
+// null) and returns their count, which is at most the item's group count.
+__device__ int item_tiles(const Geom& g, const int* __restrict__ goff, const int2* __restrict__ groups, int w,
+                          int* out) {
   const int nbc = g.nby * g.nbx;
   const int chunk = w / nbc, bc = w - chunk * nbc;
   const int by = bc / g.nbx, bx = bc - by * g.nbx;
   const int c0 = chunk * QS_TS, ns = min(QS_TS, g.Lt - c0);
-  int done[QS_TS];
+  auto put = [&](int t, int tau, int begin, int cnt) {
+    int* d = out + (size_t)t * QT_INTS;
+    d[0] = tau;
+    d[1] = tau;
+    d[2] = begin;
+    d[3] = cnt;
+    d[4] = 0;
+    for (int q = 1; q < QS_SPAN; ++q) d[3 + 3 * q] = 0;
+  };
+  int n = 0, open = -1, acc = 0, s0 = 0, np = 0;
+  for (int i = 0; i < ns; ++i) {
+    const int tau = c0 + i, b = (tau * g.nby + by) * g.nbx + bx;
+    const int gb = goff[b], ng = goff[b + 1] - gb;
+    if (ng == 0) continue;
+    const int2 last = groups[gb + ng - 1];
+    const int nfull = last.y == GROUP_Q ? ng : ng - 1;
+    for (int k = 0; k < nfull; ++k, ++n)
+      if (out) put(n, tau, groups[gb + k].x, GROUP_Q);
+    if (last.y == GROUP_Q) continue;
+    if (open >= 0 && acc + last.y <= GROUP_Q && tau - s0 < QS_SPAN) {
+      if (out) {
+        int* d = out + (size_t)open * QT_INTS;
+        d[1] = tau;
+        d[2 + 3 * np] = last.x;
+        d[3 + 3 * np] = last.y;
+        d[4 + 3 * np] = tau - s0;
+      }
+      ++np;
+      acc += last.y;
+    } else {
+      if (out) put(n, tau, last.x, last.y);
+      open = n++;
+      s0 = tau;
+      acc = last.y;
+      np = 1;
+    }
+  }
+  return n;
+}
+
+__global__ __launch_bounds__(64) void k_qtile_count(Geom g, const int* __restrict__ goff,
+                                                    const int2* __restrict__ groups, int nw, int* __restrict__ qt_off) {
+  const int w = blockIdx.x * 64 + threadIdx.x;
+  if (w < nw) qt_off[w] = item_tiles(g, goff, groups, w, nullptr);
+  if (w == nw) qt_off[w] = 0;
+}
+
+__global__ __launch_bounds__(64) void k_qtile_fill(Geom g, const int* __restrict__ goff,
+                                                   const int2* __restrict__ groups, int nw,
+                                                   const int* __restrict__ qt_off, int* __restrict__ qt) {
+  const int w = blockIdx.x * 64 + threadIdx.x;
+  if (w < nw) item_tiles(g, goff, groups, w, qt + (size_t)qt_off[w] * QT_INTS);
+}
+
+// Rows of the tiles: 16 lanes per tile, row j from the part that holds it.
+__global__ __launch_bounds__(256) void k_tile_fill(const int* __restrict__ perm, const int4* __restrict__ starts,
+                                                   const int* __restrict__ qt, const int* __restrict__ ntiles,
+                                                   int* __restrict__ tq_ids, int2* __restrict__ tq_st,
+                                                   signed char* __restrict__ tq_dt) {
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4), j = threadIdx.x & 15;
+  if (t >= *ntiles) return;
+  const int* d = qt + (size_t)t * QT_INTS;
+  int id = 0, dt = 0, r = j;
+  int2 st = make_int2(-(1 << 29), -(1 << 29));
+  for (int q = 0; q < QS_SPAN; ++q) {
+    const int cnt = d[3 + 3 * q];
+    if (r >= 0 && r < cnt) {
+      id = perm[d[2 + 3 * q] + r];
+      const int4 s = starts[id];
+      st = make_int2(s.y, s.z);
+      dt = d[4 + 3 * q];
+    }
+    r -= cnt;
+  }
+  tq_ids[(size_t)t * 16 + j] = id;
+  tq_st[(size_t)t * 16 + j] = st;
+  tq_dt[(size_t)t * 16 + j] = (signed char)dt;
+}
+
+// Runs the greedy schedule of work item w (its tiles: qt[qt_off[w] ..], in order of
+// first slice) and writes it to out; returns its size in ints.
+__device__ int build_schedule(const Geom& g, const int* __restrict__ qt, const int* __restrict__ qt_off, int w,
+                              int* out) {
+  const int nbc = g.nby * g.nbx;
+  const int chunk = w / nbc;
+  const int c0 = chunk * QS_TS, ns = min(QS_TS, g.Lt - c0);
+  const int t0 = qt_off[w], ntiles = qt_off[w + 1] - t0;
+  // sfirst[i]: first tile (of the item) whose first slice is c0 + i; done[i]: tiles
+  // of that slice scheduled so far (cleared in a loop of its own with a constant
+  // bound: folded into the loop above, the guarded clear became an indexed register
+  // write at index ns, one past the array)
+  int sfirst[QS_TS + 1], done[QS_TS];
   for (int i = 0; i < QS_TS; ++i) done[i] = 0;
-  auto blob_of = [&](int tau) { return (tau * g.nby + by) * g.nbx + bx; };
+  for (int i = 0, t = 0; i <= ns; ++i) {
+    while (t < ntiles && qt[(size_t)(t0 + t) * QT_INTS] < c0 + i) ++t;
+    sfirst[i] = t;
+  }
   int size = 1, npass = 0;
   for (;;) {
     int free_at[QS_SLOTS];
     for (int s = 0; s < QS_SLOTS; ++s) free_at[s] = -(1 << 29);
-    // first pass over the slices: count frames and tiles; second: write
     int nf = 0, nt = 0, fmax = -1;
     int* hdr = out ? out + size : nullptr;
     int* frames = hdr ? hdr + 2 : nullptr;
@@ -56,30 +141,26 @@ __device__ int build_schedule(const Geom& g, const int* __restrict__ goff, int w
     // so collect them first into a bounded local list
     int tg[QS_MAXT], tt[QS_MAXT], tslot[QS_MAXT], tfi[QS_MAXT];
     for (int i = 0; i < ns && nt < QS_MAXT; ++i) {
-      const int tau = c0 + i, b = blob_of(tau);
-      const int first = goff[b], ntl = goff[b + 1] - first;
+      const int tau = c0 + i, ntl = sfirst[i + 1] - sfirst[i];
       while (done[i] < ntl && nt < QS_MAXT) {
         int best = -1;
         for (int s = 0; s < QS_SLOTS; ++s)
           if (free_at[s] <= tau && (best < 0 || free_at[s] < free_at[best])) best = s;
         if (best < 0) break;
-        int fi;
-        if (tau > fmax) {
-          fi = nf;
-        } else {
-          fi = nf - 1 - (fmax - tau);
-        }
-        for (int f = max(tau, fmax + 1); f < tau + g.kt; ++f) {
+        const int ti = t0 + sfirst[i] + done[i];
+        const int tlast = qt[(size_t)ti * QT_INTS + 1];
+        const int fi = tau > fmax ? nf : nf - 1 - (fmax - tau);
+        for (int f = max(tau, fmax + 1); f < tlast + g.kt; ++f) {
           if (frames) frames[nf] = f;
           ++nf;
         }
-        fmax = max(fmax, tau + g.kt - 1);
-        tg[nt] = first + done[i];
+        fmax = max(fmax, tlast + g.kt - 1);
+        tg[nt] = ti;
         tt[nt] = tau;
         tslot[nt] = best;
         tfi[nt] = fi;
         ++nt;
-        free_at[best] = tau + g.kt;
+        free_at[best] = tlast + g.kt;
         ++done[i];
       }
     }
@@ -104,35 +185,31 @@ __device__ int build_schedule(const Geom& g, const int* __restrict__ goff, int w
 
 // Room for the schedule of work item w: every pass schedules at least one tile and
 // holds 2 + (frames <= QS_TS + kt - 1) + 4 per tile ints, so 1 + tiles (QS_TS + kt
-// + 5) bounds it (the sum over items stays within qs_ints()).
-__global__ __launch_bounds__(64) void k_sched_count(Geom g, const int* __restrict__ goff, int nw, int* __restrict__ off) {
+// + 5) bounds it (the sum over items stays within qs_ints(): tiles <= groups).
+__global__ __launch_bounds__(64) void k_sched_count(Geom g, const int* __restrict__ qt_off, int nw,
+                                                    int* __restrict__ off) {
   const int w = blockIdx.x * 64 + threadIdx.x;
   if (w >= nw) return;
-  const int nbc = g.nby * g.nbx;
-  const int chunk = w / nbc, bc = w - chunk * nbc;
-  const int by = bc / g.nbx, bx = bc - by * g.nbx;
-  const int c0 = chunk * QS_TS, ns = min(QS_TS, g.Lt - c0);
-  int tiles = 0;
-  for (int i = 0; i < ns; ++i) {
-    const int b = ((c0 + i) * g.nby + by) * g.nbx + bx;
-    tiles += goff[b + 1] - goff[b];
-  }
-  off[w] = 1 + tiles * (QS_TS + g.kt + 5);
+  off[w] = 1 + (qt_off[w + 1] - qt_off[w]) * (QS_TS + g.kt + 5);
 }
 
-__global__ __launch_bounds__(64) void k_sched_fill(Geom g, const int* __restrict__ goff, int nw,
-                                                   const int* __restrict__ off, int* __restrict__ sched) {
+__global__ __launch_bounds__(64) void k_sched_fill(Geom g, const int* __restrict__ qt, const int* __restrict__ qt_off,
+                                                   int nw, const int* __restrict__ off, int* __restrict__ sched) {
   const int w = blockIdx.x * 64 + threadIdx.x;
-  if (w < nw) build_schedule(g, goff, w, sched + off[w]);
+  if (w < nw) build_schedule(g, qt, qt_off, w, sched + off[w]);
 }
 
 hipError_t launch_qsched(const Geom& g, const Prep& p, hipStream_t s) {
-  k_tile_fill<<<(unsigned)((p.max_groups + 15) / 16), 256, 0, s>>>(p.perm, p.starts, p.groups, p.ngroups, p.tq_ids,
-                                                                   p.tq_st);
   const int nw = qs_items(g);
-  k_sched_count<<<(unsigned)((nw + 63) / 64), 64, 0, s>>>(g, p.goff, nw, p.qs_off);
+  const unsigned wb = (unsigned)((nw + 1 + 63) / 64);
+  k_qtile_count<<<wb, 64, 0, s>>>(g, p.goff, p.groups, nw, p.qt_off);
+  if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.qt_off), nw + 1, s) != hipSuccess) return hipGetLastError();
+  k_qtile_fill<<<wb, 64, 0, s>>>(g, p.goff, p.groups, nw, p.qt_off, p.qt);
+  k_tile_fill<<<(unsigned)((p.max_groups + 15) / 16), 256, 0, s>>>(p.perm, p.starts, p.qt, p.qt_off + nw, p.tq_ids,
+                                                                   p.tq_st, p.tq_dt);
+  k_sched_count<<<wb, 64, 0, s>>>(g, p.qt_off, nw, p.qs_off);
   if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.qs_off), nw + 1, s) != hipSuccess) return hipGetLastError();
-  k_sched_fill<<<(unsigned)((nw + 63) / 64), 64, 0, s>>>(g, p.goff, nw, p.qs_off, p.qs);
+  k_sched_fill<<<wb, 64, 0, s>>>(g, p.qt, p.qt_off, nw, p.qs_off, p.qs);
   return hipGetLastError();
 }
 

@@ -17,6 +17,11 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def nan_like(t):
+    """An output buffer shaped like t, filled with NaN (unwritten elements stay visible)."""
+    return torch.full_like(t, float("nan"))
+
+
 def to_host_f64(t):
     if t.dtype == torch.bfloat16:
         return synth.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)

@@ -13,7 +13,7 @@ import torch
 import oracle
 from local_sparse_attention_amd import configs, synth
 
-from _gpu_helpers import assert_close, assert_lse_close, border_and_random_rows, gather_rows, to_dev
+from _gpu_helpers import assert_close, assert_lse_close, border_and_random_rows, gather_rows, nan_like, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +27,11 @@ def run_sampled(dsa3d, name):
     inp = synth.make_inputs(wl)
     q, k, v, do, off = (to_dev(inp[x]) for x in ("q", "k", "v", "dout", "offsets"))
     print(f"case {wl.name}: forward + backward on the GPU", flush=True)
-    out, lse = dsa3d.forward(q, k, v, off, grid, window, wl.scale)
-    dq, dk, dv = dsa3d.backward(q, k, v, off, out, lse, do, grid, window, wl.scale)
+    # outputs start as NaN: an element the library leaves unwritten fails the checks
+    out, lse = dsa3d.forward(q, k, v, off, grid, window, wl.scale, out=nan_like(q),
+                             lse=torch.full((q.shape[1], q.shape[0]), float("nan"), device=q.device))
+    dq, dk, dv = dsa3d.backward(q, k, v, off, out, lse, do, grid, window, wl.scale, dq=nan_like(q), dk=nan_like(q),
+                                dv=nan_like(q))
     torch.cuda.synchronize()
 
     nq, nk = SAMPLES[name]

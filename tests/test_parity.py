@@ -12,7 +12,7 @@ import oracle
 from local_sparse_attention_amd import configs, synth
 from local_sparse_attention_amd.configs import Workload
 
-from _gpu_helpers import assert_close, assert_lse_close, to_dev, to_host_f64
+from _gpu_helpers import assert_close, assert_lse_close, nan_like, to_dev, to_host_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -32,11 +32,14 @@ def run_case(dsa3d, wl, inp, backward=True):
     grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
     print(f"case {wl.name} grid={grid} window={window} H={wl.heads} D={wl.head_dim} {wl.dtype}", flush=True)
     q, k, v, off = (to_dev(inp[x]) for x in ("q", "k", "v", "offsets"))
-    out, lse = dsa3d.forward(q, k, v, off, grid, window, wl.scale)
+    # outputs start as NaN: an element the library leaves unwritten fails the comparison
+    out, lse = dsa3d.forward(q, k, v, off, grid, window, wl.scale, out=nan_like(q),
+                             lse=torch.full((q.shape[1], q.shape[0]), float("nan"), device=q.device))
     res = {"out": out, "lse": lse}
     if backward:
         do = to_dev(inp["dout"])
-        res["dq"], res["dk"], res["dv"] = dsa3d.backward(q, k, v, off, out, lse, do, grid, window, wl.scale)
+        res["dq"], res["dk"], res["dv"] = dsa3d.backward(q, k, v, off, out, lse, do, grid, window, wl.scale,
+                                                         dq=nan_like(q), dk=nan_like(q), dv=nan_like(q))
     torch.cuda.synchronize()
     return res
 
