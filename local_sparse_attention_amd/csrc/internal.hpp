@@ -63,7 +63,7 @@ inline size_t max_kv_items(const Geom& g) {
 // QS_SLOTS row tiles in flight, at most QS_MAXT per pass.  A row tile holds the
 // queries of one slice, or the leftover queries (fewer than 16 each) of up to
 // QS_SPAN consecutive slices; its descriptor is QT_INTS ints.
-constexpr int QS_TS = 32, QS_SLOTS = 8, QS_MAXT = 64, QS_SPAN = 2;
+constexpr int QS_TS = 32, QS_SLOTS = 8, QS_MAXT = 64, QS_SPAN = 3;
 constexpr int QT_INTS = 2 + 3 * QS_SPAN;
 __host__ __device__ inline bool qs_geometry(const Geom& g) { return g.kt >= 3 && g.kt <= 16 && g.ky <= 9 && g.kx <= 9; }
 __host__ __device__ inline int qs_items(const Geom& g) { return g.nby * g.nbx * ((g.Lt + QS_TS - 1) / QS_TS); }
