@@ -133,19 +133,40 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* keys, int n,
   ghist[(size_t)tid * nblk + blockIdx.x] = h[tid];
 }
 
-// In-place exclusive scan of n values by one block of 1024 threads.
-// In-place exclusive scan (one workgroup): chunks of 4096, four consecutive values
-// per thread (coalesced), wave scans by lane shuffles, a running carry.
+// In-place exclusive scan (one workgroup of 1024 threads): chunks of 16384 values,
+// sixteen consecutive values per thread (four 16-byte loads), wave scans by lane
+// shuffles, a running carry; the next chunk's loads are issued before this chunk's
+// scan, so one chunk's latency hides behind the other's work.
+constexpr int SCAN_PER = 16, SCAN_CHUNK = 1024 * SCAN_PER;
+__device__ __forceinline__ void scan_load(const uint32_t* data, int n, int i0, uint32_t (&v)[SCAN_PER]) {
+  if (i0 + SCAN_PER <= n) {
+#pragma unroll
+    for (int j = 0; j < SCAN_PER / 4; ++j) {
+      const uint4 u = reinterpret_cast<const uint4*>(data + i0)[j];
+      v[4 * j] = u.x;
+      v[4 * j + 1] = u.y;
+      v[4 * j + 2] = u.z;
+      v[4 * j + 3] = u.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SCAN_PER; ++j) v[j] = i0 + j < n ? data[i0 + j] : 0u;
+  }
+}
 __global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n) {
   __shared__ uint32_t wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t carry = 0;
-  for (int base = 0; base < n; base += 4096) {
-    const int i0 = base + 4 * tid;
-    uint32_t v[4];
+  uint32_t v[SCAN_PER], nx[SCAN_PER];
+  scan_load(data, n, SCAN_PER * tid, nx);
+  for (int base = 0; base < n; base += SCAN_CHUNK) {
+    const int i0 = base + SCAN_PER * tid;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = i0 + j < n ? data[i0 + j] : 0u;
-    const uint32_t t = v[0] + v[1] + v[2] + v[3];
+    for (int j = 0; j < SCAN_PER; ++j) v[j] = nx[j];
+    if (base + SCAN_CHUNK < n) scan_load(data, n, i0 + SCAN_CHUNK, nx);
+    uint32_t t = 0;
+#pragma unroll
+    for (int j = 0; j < SCAN_PER; ++j) t += v[j];
     uint32_t inc = t;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -162,10 +183,22 @@ __global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n) {
       total += x;
     }
     uint32_t run = carry + before + inc - t;
+    if (i0 + SCAN_PER <= n) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (i0 + j < n) data[i0 + j] = run;
-      run += v[j];
+      for (int j = 0; j < SCAN_PER / 4; ++j) {
+        uint4 u;
+        u.x = run; run += v[4 * j];
+        u.y = run; run += v[4 * j + 1];
+        u.z = run; run += v[4 * j + 2];
+        u.w = run; run += v[4 * j + 3];
+        reinterpret_cast<uint4*>(data + i0)[j] = u;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SCAN_PER; ++j) {
+        if (i0 + j < n) data[i0 + j] = run;
+        run += v[j];
+      }
     }
     carry += total;
     __syncthreads();  // wsum is rewritten by the next chunk

@@ -112,23 +112,29 @@ __global__ __launch_bounds__(256) void k_tile_fill(const int* __restrict__ perm,
   tq_dt[(size_t)t * 16 + j] = (signed char)dt;
 }
 
-// Runs the greedy schedule of work item w (its tiles: qt[qt_off[w] ..], in order of
-// first slice) and writes it to out; returns its size in ints.
-__device__ int build_schedule(const Geom& g, const int* __restrict__ qt, const int* __restrict__ qt_off, int w,
-                              int* out) {
+// Runs the greedy schedule of work item w, whose ntiles tiles (global indices t0 ..,
+// in order of first slice) have first / last slices tiles.tau0(i) / tiles.tlast(i),
+// and writes it to out; returns its size in ints.  work: 4 QS_MAXT ints of scratch
+// (LDS in the kernel), written by all nlanes lanes alike and copied out by lane
+// lane of nlanes; tiles.uni(x) marks a value as the same in every lane, so that a
+// whole wave runs the pass on the scalar unit.
+template <typename Tiles>
+__device__ int build_schedule(const Geom& g, int w, int t0, int ntiles, const Tiles& tiles, int* out, int* work,
+                              int lane, int nlanes) {
   const int nbc = g.nby * g.nbx;
   const int chunk = w / nbc;
   const int c0 = chunk * QS_TS, ns = min(QS_TS, g.Lt - c0);
-  const int t0 = qt_off[w], ntiles = qt_off[w + 1] - t0;
-  // sfirst[i]: first tile (of the item) whose first slice is c0 + i; done[i]: tiles
-  // of that slice scheduled so far (cleared in a loop of its own with a constant
-  // bound: folded into the loop above, the guarded clear became an indexed register
-  // write at index ns, one past the array)
-  int sfirst[QS_TS + 1], done[QS_TS];
-  for (int i = 0; i < QS_TS; ++i) done[i] = 0;
-  for (int i = 0, t = 0; i <= ns; ++i) {
-    while (t < ntiles && qt[(size_t)(t0 + t) * QT_INTS] < c0 + i) ++t;
-    sfirst[i] = t;
+  // cur[i] .. lim[i]: the tiles (of the item) whose first slice is c0 + i that are
+  // still to be scheduled.  Both arrays are cleared in a loop of their own with a
+  // constant bound and written only at indices below ns: a guarded clear folded into
+  // a loop that runs to ns became an indexed register write at index ns, one past
+  // the array.
+  int cur[QS_TS], lim[QS_TS];
+  for (int i = 0; i < QS_TS; ++i) cur[i] = lim[i] = 0;
+  for (int i = 0, t = 0; i < ns; ++i) {
+    cur[i] = t;
+    while (t < ntiles && tiles.tau0(t) < c0 + i + 1) ++t;
+    lim[i] = t;
   }
   int size = 1, npass = 0;
   for (;;) {
@@ -138,30 +144,30 @@ __device__ int build_schedule(const Geom& g, const int* __restrict__ qt, const i
     int* hdr = out ? out + size : nullptr;
     int* frames = hdr ? hdr + 2 : nullptr;
     // tiles are written after the frames, whose count is known only at the end,
-    // so collect them first into a bounded local list
-    int tg[QS_MAXT], tt[QS_MAXT], tslot[QS_MAXT], tfi[QS_MAXT];
+    // so collect them first into a bounded list: (tile, slice, slot, frame index)
+    int* tl4 = work;
     for (int i = 0; i < ns && nt < QS_MAXT; ++i) {
-      const int tau = c0 + i, ntl = sfirst[i + 1] - sfirst[i];
-      while (done[i] < ntl && nt < QS_MAXT) {
+      const int tau = c0 + i;
+      while (cur[i] < lim[i] && nt < QS_MAXT) {
         int best = -1;
         for (int s = 0; s < QS_SLOTS; ++s)
           if (free_at[s] <= tau && (best < 0 || free_at[s] < free_at[best])) best = s;
         if (best < 0) break;
-        const int ti = t0 + sfirst[i] + done[i];
-        const int tlast = qt[(size_t)ti * QT_INTS + 1];
+        const int ti = cur[i];
+        const int tlast = tiles.tlast(ti);
         const int fi = tau > fmax ? nf : nf - 1 - (fmax - tau);
         for (int f = max(tau, fmax + 1); f < tlast + g.kt; ++f) {
           if (frames) frames[nf] = f;
           ++nf;
         }
         fmax = max(fmax, tlast + g.kt - 1);
-        tg[nt] = ti;
-        tt[nt] = tau;
-        tslot[nt] = best;
-        tfi[nt] = fi;
+        tl4[4 * nt + 0] = t0 + ti;
+        tl4[4 * nt + 1] = tau;
+        tl4[4 * nt + 2] = best;
+        tl4[4 * nt + 3] = fi;
         ++nt;
         free_at[best] = tlast + g.kt;
-        ++done[i];
+        ++cur[i];
       }
     }
     if (nt == 0) break;
@@ -169,12 +175,7 @@ __device__ int build_schedule(const Geom& g, const int* __restrict__ qt, const i
       hdr[0] = nf;
       hdr[1] = nt;
       int* tl = frames + nf;
-      for (int t = 0; t < nt; ++t) {
-        tl[4 * t + 0] = tg[t];
-        tl[4 * t + 1] = tt[t];
-        tl[4 * t + 2] = tslot[t];
-        tl[4 * t + 3] = tfi[t];
-      }
+      for (int t = lane; t < 4 * nt; t += nlanes) tl[t] = tl4[t];
     }
     size += 2 + nf + 4 * nt;
     ++npass;
@@ -182,6 +183,21 @@ __device__ int build_schedule(const Geom& g, const int* __restrict__ qt, const i
   if (out) out[0] = npass;
   return size;
 }
+
+// Tile slices of a work item read from the descriptors in global memory, or from
+// a copy in LDS.
+struct TilesGlobal {
+  const int* qt;  // descriptors of the item's first tile
+  __device__ int tau0(int i) const { return qt[(size_t)i * QT_INTS]; }
+  __device__ int tlast(int i) const { return qt[(size_t)i * QT_INTS + 1]; }
+  __device__ int uni(int x) const { return __builtin_amdgcn_readfirstlane(x); }
+};
+struct TilesLds {
+  const int2* c;  // (tau0, tlast) per tile
+  __device__ int tau0(int i) const { return __builtin_amdgcn_readfirstlane(c[i].x); }
+  __device__ int tlast(int i) const { return __builtin_amdgcn_readfirstlane(c[i].y); }
+  __device__ int uni(int x) const { return __builtin_amdgcn_readfirstlane(x); }
+};
 
 // Room for the schedule of work item w: every pass schedules at least one tile and
 // holds 2 + (frames <= QS_TS + kt - 1) + 4 per tile ints, so 1 + tiles (QS_TS + kt
@@ -193,10 +209,31 @@ __global__ __launch_bounds__(64) void k_sched_count(Geom g, const int* __restric
   off[w] = 1 + (qt_off[w + 1] - qt_off[w]) * (QS_TS + g.kt + 5);
 }
 
-__global__ __launch_bounds__(64) void k_sched_fill(Geom g, const int* __restrict__ qt, const int* __restrict__ qt_off,
-                                                   int nw, const int* __restrict__ off, int* __restrict__ sched) {
-  const int w = blockIdx.x * 64 + threadIdx.x;
-  if (w < nw) build_schedule(g, qt, qt_off, w, sched + off[w]);
+// One wave per work item: the wave copies the item's tile slices to LDS (when they
+// fit), then runs the greedy pass on them with every value uniform (scalar
+// instructions; the stores carry one value for all lanes).
+constexpr int SCHED_WAVES = 4, SCHED_CACHE = 1024;
+__global__ __launch_bounds__(64 * SCHED_WAVES) void k_sched_fill(Geom g, const int* __restrict__ qt,
+                                                                 const int* __restrict__ qt_off, int nw,
+                                                                 const int* __restrict__ off, int* __restrict__ sched) {
+  __shared__ int2 cache[SCHED_WAVES][SCHED_CACHE];
+  __shared__ int work[SCHED_WAVES][4 * QS_MAXT];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int w = blockIdx.x * SCHED_WAVES + wv;
+  const bool live = w < nw;
+  const int t0 = live ? qt_off[w] : 0, ntiles = live ? qt_off[w + 1] - t0 : 0;
+  const bool cached = ntiles <= SCHED_CACHE;
+  if (cached)
+    for (int i = lane; i < ntiles; i += 64)
+      cache[wv][i] = make_int2(qt[(size_t)(t0 + i) * QT_INTS], qt[(size_t)(t0 + i) * QT_INTS + 1]);
+  __syncthreads();
+  if (live) {
+    if (cached)
+      build_schedule(g, w, t0, ntiles, TilesLds{cache[wv]}, sched + off[w], work[wv], lane, 64);
+    else
+      build_schedule(g, w, t0, ntiles, TilesGlobal{qt + (size_t)t0 * QT_INTS}, sched + off[w], work[wv], lane,
+                     64);
+  }
 }
 
 hipError_t launch_qsched(const Geom& g, const Prep& p, hipStream_t s) {
@@ -209,7 +246,8 @@ hipError_t launch_qsched(const Geom& g, const Prep& p, hipStream_t s) {
                                                                    p.tq_st, p.tq_dt);
   k_sched_count<<<wb, 64, 0, s>>>(g, p.qt_off, nw, p.qs_off);
   if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.qs_off), nw + 1, s) != hipSuccess) return hipGetLastError();
-  k_sched_fill<<<wb, 64, 0, s>>>(g, p.qt, p.qt_off, nw, p.qs_off, p.qs);
+  k_sched_fill<<<(unsigned)((nw + SCHED_WAVES - 1) / SCHED_WAVES), 64 * SCHED_WAVES, 0, s>>>(g, p.qt, p.qt_off, nw,
+                                                                                          p.qs_off, p.qs);
   return hipGetLastError();
 }
 
