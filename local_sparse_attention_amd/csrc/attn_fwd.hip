@@ -86,7 +86,9 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
       static_for<0, FWD_LW>([&](auto LWC) {
         constexpr int LWI = decltype(LWC)::value;
         if (lw != LWI) return;
-        const int lane_el = lane_chunk_el(lane);
+        KeyTileLoads<D, NBX, C::NB, C::NB, FWD_LW, LWI> kl;
+        kl.init(g, h, by, bx, lane);
+        const size_t frame_el = (size_t)g.Hp * g.Wp * g.H * D;
         // step x: phase x % NPH2 of frame index x / NPH2; K phases first, then V.  Q
         // rows of the tiles that start at a frame go out just before its first tile
         // loads, so the wait that covers those covers them too.
@@ -100,9 +102,8 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
               if (t >= 0) issue_rows<D>(stage[sl], q, T.ids[t], g, h, lane);
             }
           }
-          issue_key_tile_w<D, NBX, C::NB, C::NB, FWD_LW, LWI>(
-              ring[x % C::NBUF], (ph < C::NPH ? k : v) + (ph % C::NPH) * 64 + h * D + lane_el, g, by, bx, f, lane, k,
-              stage[0]);  // (no padding: the loads split evenly)
+          kl.issue(ring[x % C::NBUF], (ph < C::NPH ? k : v) + f * frame_el + (ph % C::NPH) * 64, lane, k,
+                   stage[0]);  // (no padding: the loads split evenly)
         };
         int issued = 0;
         for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);
@@ -340,11 +341,13 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
   }
 }
 
-// bf16 rows of 64 or 128, windows whose key tile spans at most 3 x 3 blocks, and
+// bf16 rows of 64 or 128, windows whose key tile spans at most 3 x 3 blocks,
 // 3 <= kt <= 16 (a slot's next Q rows load while its current tile reads its last
-// frames; a pass lists at most QS_TS + kt - 1 frames).
+// frames; a pass lists at most QS_TS + kt - 1 frames), and frames of under 4 GiB
+// per tensor (32-bit load offsets inside a frame).
 bool fwd_qs_eligible(const Geom& g, int dtype, int D) {
-  return dtype == 1 && (D == 64 || D == 128) && qs_geometry(g);
+  return dtype == 1 && (D == 64 || D == 128) && qs_geometry(g) &&
+         (unsigned long long)g.Hp * g.Wp * g.H * D * 2 < (1ull << 32);
 }
 
 template <int D, int NBY, int NBX>

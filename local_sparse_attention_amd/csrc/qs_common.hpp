@@ -132,6 +132,44 @@ __device__ __forceinline__ void issue_key_tile_w(char* dst, const u16* src, cons
   });
 }
 
+// The loads WI, WI + NW, ... of issue_key_tile_w with their frame-independent
+// part precomputed: off[i] is the lane's byte offset, inside one frame of the
+// [N][H][D] tensor and from column 0 of head h, of load WI + NW i (0 for loads
+// beyond the tile).  issue() then costs no vector instructions per load.  Needs
+// Hp Wp H D 2 < 2^32 (byte offsets inside a frame fit 32 bits).
+template <int D, int NBX, int NBLK, int NLB, int NW, int WI>
+struct KeyTileLoads {
+  static constexpr int N = (2 * NLB + NW - 1) / NW;
+  uint32_t off[N];
+  __device__ __forceinline__ void init(const Geom& g, int h, int by, int bx, int lane) {
+    const int ly = lane >> 5, lx = (lane >> 3) & 3;
+    const uint32_t lane_b = (uint32_t)(h * D + (((lane & 7) ^ ((lane >> 3) & 7)) * 8)) * 2u;
+    static_for<0, N>([&](auto JJ) {
+      constexpr int i = decltype(JJ)::value, j = WI + NW * i;
+      if constexpr (j < 2 * NLB) {
+        constexpr int b = j >> 1, bi = b / NBX, bj = b % NBX;
+        const int y = 4 * by + 4 * bi + 2 * (j & 1) + ly, x = 4 * bx + 4 * bj + lx;
+        const bool in = b < NBLK && y < g.Hp && x < g.Wp;
+        off[i] = (in ? (uint32_t)(y * g.Wp + x) * (uint32_t)(g.H * D) * 2u : 0u) + lane_b;
+      } else {
+        off[i] = 0u;
+      }
+    });
+  }
+  // frame_base: the tensor's element (token (f, 0, 0), head 0, column phase start)
+  __device__ __forceinline__ void issue(char* dst, const u16* frame_base, int lane, const void* pad_src,
+                                        void* sink) const {
+    static_for<0, N>([&](auto JJ) {
+      constexpr int i = decltype(JJ)::value, j = WI + NW * i;
+      if constexpr (j < 2 * NLB) {
+        dma16_s(frame_base, off[i], dst + j * 1024);
+      } else {
+        if (lane == 0) dma4(pad_src, sink);
+      }
+    });
+  }
+};
+
 // The lane's element offset inside a row for issue_key_tile_w and issue_rows.
 __device__ __forceinline__ int lane_chunk_el(int lane) { return ((lane & 7) ^ ((lane >> 3) & 7)) * 8; }
 

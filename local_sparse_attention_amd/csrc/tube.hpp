@@ -31,6 +31,14 @@ __device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
   __asm__ __volatile__("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
 }
 
+// The same load with a wave-uniform 64-bit base (SGPRs) and a per-lane 32-bit byte
+// offset: the address needs no vector arithmetic (the base of a frame goes in
+// scalar registers, the lane's offset inside the frame is computed once).
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const void* lds_base) {
+  const unsigned m0 = (unsigned)(size_t)(const __attribute__((address_space(3))) char*)lds_base;
+  __asm__ __volatile__("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
 // Workgroup barrier for the pipelined loop: the LDS reads and writes of this wave
 // are complete, the direct loads are covered by the preceding vmcnt wait.
 // (__syncthreads() would also wait for every outstanding global access.)
