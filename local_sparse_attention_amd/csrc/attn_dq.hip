@@ -140,6 +140,9 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
     rt[s] = 0;
   }
 
+  KeyTileLoadsW<D, NBX, C::NB, C::NBPAD, DQ_NW> kl;
+  kl.init(g, h, by, bx, lane, wave);
+  const size_t frame_el = (size_t)g.Hp * g.Wp * g.H * D;
   const int* sp = p.qs + p.qs_off[w];
   const int npass = sp[0];
   sp += 1;
@@ -168,13 +171,8 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           }
         }
       }
-      // this wave's tile loads, with its index a compile-time constant
-      const u16* src = (ph < C::NPH ? v : k) + (ph % C::NPH) * 64 + h * D + lane_chunk_el(lane);
-      static_for<0, DQ_NW>([&](auto WC) {
-        constexpr int WI = decltype(WC)::value;
-        if (wave == WI)
-          issue_key_tile_w<D, NBX, C::NB, C::NBPAD, DQ_NW, WI>(ring[x % C::NBUF], src, g, by, bx, f, lane, k, s_sink);
-      });
+      // this wave's tile loads (offsets inside a frame computed once)
+      kl.issue(ring[x % C::NBUF], (ph < C::NPH ? v : k) + f * frame_el + (ph % C::NPH) * 64, lane, k, s_sink);
     };
     int issued = 0;
     for (; issued < C::PD && issued < nsteps; ++issued) issue_step(issued);

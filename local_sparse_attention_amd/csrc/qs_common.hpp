@@ -170,6 +170,39 @@ struct KeyTileLoads {
   }
 };
 
+// KeyTileLoads for issuing wave wi (wave-uniform, known at run time): load
+// wi + NW i, i < N.  The missing loads of the last round are one-lane loads of
+// pad_src into sink, so every wave counts the same.
+template <int D, int NBX, int NBLK, int NLB, int NW>
+struct KeyTileLoadsW {
+  static constexpr int N = (2 * NLB + NW - 1) / NW;
+  uint32_t off[N];
+  int wi;
+  __device__ __forceinline__ void init(const Geom& g, int h, int by, int bx, int lane, int wave) {
+    wi = wave;
+    const int ly = lane >> 5, lx = (lane >> 3) & 3;
+    const uint32_t lane_b = (uint32_t)(h * D + (((lane & 7) ^ ((lane >> 3) & 7)) * 8)) * 2u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int j = wi + NW * i, b = j >> 1, bi = b / NBX, bj = b - bi * NBX;
+      const int y = 4 * by + 4 * bi + 2 * (j & 1) + ly, x = 4 * bx + 4 * bj + lx;
+      const bool in = j < 2 * NLB && b < NBLK && y < g.Hp && x < g.Wp;
+      off[i] = (in ? (uint32_t)(y * g.Wp + x) * (uint32_t)(g.H * D) * 2u : 0u) + lane_b;
+    }
+  }
+  __device__ __forceinline__ void issue(char* dst, const u16* frame_base, int lane, const void* pad_src,
+                                        void* sink) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int j = wi + NW * i;
+      if (j < 2 * NLB)
+        dma16_s(frame_base, off[i], dst + j * 1024);
+      else if (lane == 0)
+        dma4(pad_src, sink);
+    }
+  }
+};
+
 // The lane's element offset inside a row for issue_key_tile_w and issue_rows.
 __device__ __forceinline__ int lane_chunk_el(int lane) { return ((lane & 7) ^ ((lane >> 3) & 7)) * 8; }
 
