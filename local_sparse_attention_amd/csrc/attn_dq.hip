@@ -211,12 +211,46 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
         }
       }
 
+      // what this frame's issues need, read once here rather than behind a wait in
+      // each step: the next frame, and the rows of the tile that starts there in this
+      // wave's slot (its Q / dO rows, lse and Delta go out PD steps before it)
+      const bool has_next = fi + 1 < nf;
+      const int fnext = has_next ? __builtin_amdgcn_readfirstlane(T.frames[fi + 1]) : 0;
+      const int tnext = has_next && NS == 1 ? __builtin_amdgcn_readfirstlane((int)T.act[fi + 1][wave]) : -1;
+      int ntok0 = 0, ntok1 = 0, ntokl = 0;
+      if (tnext >= 0) {
+        ntok0 = T.ids[tnext][lane >> 3];
+        ntok1 = T.ids[tnext][8 + (lane >> 3)];
+        ntokl = T.ids[tnext][lane & 15];
+      }
+
       static_for<0, C::NPH2>([&](auto PHC) {
         constexpr int ph = decltype(PHC)::value;
         constexpr int kph = ph - C::NPH;  // K column phase (ph >= NPH)
         const int st = fi * C::NPH2 + ph;
         if (issued < nsteps) {
-          issue_step(issued);
+          if constexpr (NS == 1) {
+            // issued == st + PD: its frame and phase are known here
+            constexpr int phx = (ph + C::PD) % C::NPH2;
+            constexpr bool in_next = ph + C::PD >= C::NPH2;
+            static_assert(C::PD < 2 * C::NPH2, "an issue reaches at most one frame ahead");
+            const int fx = in_next ? fnext : f;
+            if constexpr (phx == 0) {
+              if (tnext >= 0) {
+                char* sg = stage[wave];
+                issue_rows_tok<D>(sg, q, ntok0, ntok1, g, h, lane);
+                issue_rows_tok<D>(sg + C::RTILE, dout, ntok0, ntok1, g, h, lane);
+                if (lane < 16) {
+                  dma4(lse + (size_t)h * g.N + ntokl, sg + 2 * C::RTILE);
+                  dma4(delta + (size_t)h * g.N + ntokl, sg + 2 * C::RTILE + 64);
+                }
+              }
+            }
+            kl.issue(ring[issued % C::NBUF], (phx < C::NPH ? v : k) + fx * frame_el + (phx % C::NPH) * 64, lane, k,
+                     s_sink);
+          } else {
+            issue_step(issued);
+          }
           ++issued;
         }
         const char* tb = ring[st % C::NBUF];

@@ -208,17 +208,23 @@ __device__ __forceinline__ int lane_chunk_el(int lane) { return ((lane & 7) ^ ((
 
 // Direct loads of the 16 rows (tokens ids[0..15]) of a [N][H][D] bf16 tensor into a
 // staged row tile: NPH phases of 16 x 128 bytes, swizzled like the key tiles.
+// tok0 / tok1: the tokens of rows lane >> 3 and 8 + (lane >> 3).
 template <int D>
-__device__ __forceinline__ void issue_rows(char* dst, const u16* src, const int* ids, const Geom& g, int h, int lane) {
-  // both tokens first: every direct load clobbers memory for the compiler, which
-  // would otherwise read (and wait for) the token again before each load
-  const u16* r0 = src + ((size_t)ids[lane >> 3] * g.H + h) * D + lane_chunk_el(lane);
-  const u16* r1 = src + ((size_t)ids[8 + (lane >> 3)] * g.H + h) * D + lane_chunk_el(lane);
+__device__ __forceinline__ void issue_rows_tok(char* dst, const u16* src, int tok0, int tok1, const Geom& g, int h,
+                                               int lane) {
+  const u16* r0 = src + ((size_t)tok0 * g.H + h) * D + lane_chunk_el(lane);
+  const u16* r1 = src + ((size_t)tok1 * g.H + h) * D + lane_chunk_el(lane);
 #pragma unroll
   for (int j = 0; j < 2 * (D / 64); ++j) {
     const int ph = j >> 1, hh = j & 1;
     dma16((hh ? r1 : r0) + ph * 64, dst + ph * 2048 + hh * 1024);
   }
+}
+template <int D>
+__device__ __forceinline__ void issue_rows(char* dst, const u16* src, const int* ids, const Geom& g, int h, int lane) {
+  // both tokens first: every direct load clobbers memory for the compiler, which
+  // would otherwise read (and wait for) the token again before each load
+  issue_rows_tok<D>(dst, src, ids[lane >> 3], ids[8 + (lane >> 3)], g, h, lane);
 }
 
 }  // namespace dsa3d
