@@ -179,12 +179,16 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
     wait_vmcnt(0);
     __syncthreads();
 
+    // the frame and this wave's activating tile, carried from the read one frame
+    // ahead below (one slot per wave)
+    int f_cur = nf > 0 ? __builtin_amdgcn_readfirstlane(T.frames[0]) : 0;
+    int t_cur = nf > 0 && NS == 1 ? __builtin_amdgcn_readfirstlane((int)T.act[0][wave]) : -1;
     for (int fi = 0; fi < nf; ++fi) {
-      const int f = __builtin_amdgcn_readfirstlane(T.frames[fi]);
+      const int f = f_cur;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int sl = NS * wave + s;
-        const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
+        const int t = NS == 1 ? t_cur : __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
         if (t >= 0) {
 #pragma unroll
           for (int c = 0; c < C::NC; ++c) {
@@ -374,6 +378,8 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           wait_vmcnt(MY_LOADS * max(issued - st - 2, 0));
         lds_barrier();
       });
+      f_cur = fnext;
+      t_cur = tnext;
     }
   }
 }
