@@ -183,38 +183,54 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
     // ahead below (one slot per wave)
     int f_cur = nf > 0 ? __builtin_amdgcn_readfirstlane(T.frames[0]) : 0;
     int t_cur = nf > 0 && NS == 1 ? __builtin_amdgcn_readfirstlane((int)T.act[0][wave]) : -1;
+    // The dQ^T products of the last K step's own columns run one step late, in the
+    // next frame's first (light) step, whose ring still holds that tile: pend says
+    // they are due (with dS^T kept in dsf / dsl), pf is their frame.  A tile's dQ row
+    // is written once they are done.
+    bool pend = false;
+    int pf = -1;
+    auto flush = [&](const char* kt_) {
+      if (pend) {
+#pragma unroll
+        for (int c = 0; c < C::NPAIR; ++c) {
+#pragma unroll
+          for (int dt = 0; dt < C::NT / C::NPH; ++dt) {
+            const char* pa = kt_ + (2 * c) * 2048 + toff[dt];
+            const int ot = (C::NPH - 1) * (C::NT / C::NPH) + dt;
+            const shortx4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
+            if (2 * c + 1 < C::NB) {
+              const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
+              Frag<u16> a;
+              const shortx4_t both[2] = {lo, hi};
+              __builtin_memcpy(&a.v, both, 16);
+#pragma unroll
+              for (int s = 0; s < NS; ++s) dqa[s][ot] = mma(a, dsf[s][c], dqa[s][ot]);
+            } else {
+#pragma unroll
+              for (int s = 0; s < NS; ++s)
+                dqa[s][ot] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, dsl[s], dqa[s][ot], 0, 0, 0);
+            }
+          }
+        }
+        // ---- tiles whose last frame that was: write dQ = scale dQ^T^T
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          if (pf == fend[s]) {
+            if (qn[s] >= 0) {
+              u16* row = dq + ((size_t)qn[s] * g.H + h) * D;
+#pragma unroll
+              for (int t = 0; t < C::NT; ++t)
+                store4(row + t * 16 + quad * 4, dqa[s][t][0] * scale, dqa[s][t][1] * scale, dqa[s][t][2] * scale,
+                       dqa[s][t][3] * scale);
+            }
+            fend[s] = -1;
+          }
+        }
+        pend = false;
+      }
+    };
     for (int fi = 0; fi < nf; ++fi) {
       const int f = f_cur;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int sl = NS * wave + s;
-        const int t = NS == 1 ? t_cur : __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
-        if (t >= 0) {
-#pragma unroll
-          for (int c = 0; c < C::NC; ++c) {
-            const int off = (c >> 1) * 2048 + sw(r16, (c & 1) * 64 + quad * 16);
-            load_frag(qf[s][c], (const u16*)(stage[sl] + off));
-            load_frag(dof[s][c], (const u16*)(stage[sl] + C::RTILE + off));
-          }
-          lse2[s] = reinterpret_cast<const float*>(stage[sl] + 2 * C::RTILE)[r16] * LOG2E;
-          dlt[s] = reinterpret_cast<const float*>(stage[sl] + 2 * C::RTILE + 64)[r16];
-          const int2 st = T.st[t][r16];
-#pragma unroll
-          for (int i = 0; i < NBY; ++i)
-            ybias[s][i] = (unsigned)(4 * by + 4 * i + quad - st.x) < (unsigned)g.ky ? 0.f : -INFINITY;
-#pragma unroll
-          for (int j = 0; j < NBX; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              xbias[s][j][i] = (unsigned)(4 * bx + 4 * j + i - st.y) < (unsigned)g.kx ? 0.f : -INFINITY;
-          qn[s] = st.x >= 0 ? T.ids[t][r16] : -1;
-          fend[s] = __builtin_amdgcn_readfirstlane(T.tlast[t]) + g.kt - 1;
-          rt[s] = __builtin_amdgcn_readfirstlane(T.tau[t]) + T.dt[t][r16];
-#pragma unroll
-          for (int tt = 0; tt < C::NT; ++tt) dqa[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-
       // what this frame's issues need, read once here rather than behind a wait in
       // each step: the next frame, and the rows of the tile that starts there in this
       // wave's slot (its Q / dO rows, lse and Delta go out PD steps before it)
@@ -264,6 +280,40 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
         for (int c = 0; c < C::NC / C::NPH; ++c) __asm__ __volatile__("" : "+v"(roff[c]));
 #pragma unroll
         for (int t = 0; t < C::NT / C::NPH; ++t) __asm__ __volatile__("" : "+v"(toff[t]));
+        if constexpr (ph == 0) {
+          // the previous frame's late dQ^T products (its last K tile is the previous
+          // ring slot), then the tiles that start with this frame
+          flush(ring[(st + C::NBUF - 1) % C::NBUF]);
+    #pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const int sl = NS * wave + s;
+            const int t = NS == 1 ? t_cur : __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
+            if (t >= 0) {
+    #pragma unroll
+              for (int c = 0; c < C::NC; ++c) {
+                const int off = (c >> 1) * 2048 + sw(r16, (c & 1) * 64 + quad * 16);
+                load_frag(qf[s][c], (const u16*)(stage[sl] + off));
+                load_frag(dof[s][c], (const u16*)(stage[sl] + C::RTILE + off));
+              }
+              lse2[s] = reinterpret_cast<const float*>(stage[sl] + 2 * C::RTILE)[r16] * LOG2E;
+              dlt[s] = reinterpret_cast<const float*>(stage[sl] + 2 * C::RTILE + 64)[r16];
+              const int2 st = T.st[t][r16];
+    #pragma unroll
+              for (int i = 0; i < NBY; ++i)
+                ybias[s][i] = (unsigned)(4 * by + 4 * i + quad - st.x) < (unsigned)g.ky ? 0.f : -INFINITY;
+    #pragma unroll
+              for (int j = 0; j < NBX; ++j)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  xbias[s][j][i] = (unsigned)(4 * bx + 4 * j + i - st.y) < (unsigned)g.kx ? 0.f : -INFINITY;
+              qn[s] = st.x >= 0 ? T.ids[t][r16] : -1;
+              fend[s] = __builtin_amdgcn_readfirstlane(T.tlast[t]) + g.kt - 1;
+              rt[s] = __builtin_amdgcn_readfirstlane(T.tau[t]) + T.dt[t][r16];
+    #pragma unroll
+              for (int tt = 0; tt < C::NT; ++tt) dqa[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+        }
         // with one slot per wave, a wave whose slot holds no tile this frame skips its
         // MFMA work (a uniform branch) and leaves the SIMD to its partner
         const bool busy = NS > 1 || fend[0] >= f;
@@ -327,10 +377,13 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
               }
             });
           }
-          // ---- dQ^T += K^T dS^T: this step's K columns and the previous step's
+          // ---- dQ^T += K^T dS^T over the earlier K steps' columns now (their tiles
+          // leave the ring next step), over this step's own columns one step late
+          pend = true;
+          pf = f;
 #pragma unroll
-          for (int kp = 0; kp < C::NPH; ++kp) {
-            const char* kt_ = (kp == C::NPH - 1) ? tb : ring[(st - (C::NPH - 1 - kp)) % C::NBUF];
+          for (int kp = 0; kp < C::NPH - 1; ++kp) {
+            const char* kt_ = ring[(st - (C::NPH - 1 - kp)) % C::NBUF];
 #pragma unroll
             for (int c = 0; c < C::NPAIR; ++c) {
 #pragma unroll
@@ -356,22 +409,6 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           }
         }
         }  // busy
-        if constexpr (ph == C::NPH2 - 1) {
-          // ---- tiles whose last frame this was: write dQ = scale dQ^T^T
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            if (f == fend[s]) {
-              if (qn[s] >= 0) {
-                u16* row = dq + ((size_t)qn[s] * g.H + h) * D;
-#pragma unroll
-                for (int t = 0; t < C::NT; ++t)
-                  store4(row + t * 16 + quad * 4, dqa[s][t][0] * scale, dqa[s][t][1] * scale, dqa[s][t][2] * scale,
-                         dqa[s][t][3] * scale);
-              }
-              fend[s] = -1;
-            }
-          }
-        }
         if (issued - st - 2 == C::PD - 1)
           wait_vmcnt_c<MY_LOADS * (C::PD - 1)>();
         else
@@ -381,6 +418,8 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
       f_cur = fnext;
       t_cur = tnext;
     }
+    // the pass's last K tile is still in the ring (no loads follow)
+    if (nf > 0) flush(ring[(nf * C::NPH2 - 1) % C::NBUF]);
   }
 }
 
