@@ -28,6 +28,7 @@
 namespace dsa3d {
 
 typedef short shortx4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 // Blob rows (or columns) of start cells whose windows reach key block kb along an
 // axis with window k, lattice length L: cells [4 kb - k + 1, 4 kb + 3] clipped.
@@ -416,17 +417,17 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
       const float lq[4] = {ls.x, ls.y, ls.z, ls.w}, dq[4] = {de.x, de.y, de.z, de.w};
 #pragma unroll
       for (int i = 0; i < NSG; ++i) {
-        shortx4v pb, db;
+        f32x4_t pe, ds;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bool ok = (unsigned)(key_y - sy[j]) < (unsigned)g.ky && (unsigned)(key_x - sx[j]) < (unsigned)g.kx;
           // outside the window the exponent is -inf (exp2 gives 0, no branch)
-          const float pe = __builtin_amdgcn_exp2f(ok ? sc[i][j] * sl2 - lq[j] * LOG2E : -__builtin_inff());
-          pb[j] = __builtin_bit_cast(short, static_cast<__bf16>(pe));
-          db[j] = __builtin_bit_cast(short, static_cast<__bf16>(pe * (dp[i][j] - dq[j])));
+          pe[j] = __builtin_amdgcn_exp2f(ok ? sc[i][j] * sl2 - lq[j] * LOG2E : -__builtin_inff());
+          ds[j] = pe[j] * (dp[i][j] - dq[j]);
         }
-        *reinterpret_cast<shortx4v*>(xch[par][s0 + i][0] + lane * 16 + hf * 8) = pb;
-        *reinterpret_cast<shortx4v*>(xch[par][s0 + i][1] + lane * 16 + hf * 8) = db;
+        // bf16 (round to nearest even), two values per conversion instruction
+        *reinterpret_cast<bf16x4_t*>(xch[par][s0 + i][0] + lane * 16 + hf * 8) = __builtin_convertvector(pe, bf16x4_t);
+        *reinterpret_cast<bf16x4_t*>(xch[par][s0 + i][1] + lane * 16 + hf * 8) = __builtin_convertvector(ds, bf16x4_t);
       }
     };
 

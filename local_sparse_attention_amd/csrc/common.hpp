@@ -114,12 +114,9 @@ __device__ __forceinline__ void gather_frag<float>(Frag<float>& f, const float* 
 
 // Store 4 consecutive output elements from fp32.
 __device__ __forceinline__ void store4(u16* p, float a, float b, float c, float d) {
-  const __bf16 v0 = static_cast<__bf16>(a), v1 = static_cast<__bf16>(b), v2 = static_cast<__bf16>(c),
-               v3 = static_cast<__bf16>(d);
-  uint2 u;
-  u.x = static_cast<uint32_t>(__builtin_bit_cast(u16, v0)) | (static_cast<uint32_t>(__builtin_bit_cast(u16, v1)) << 16);
-  u.y = static_cast<uint32_t>(__builtin_bit_cast(u16, v2)) | (static_cast<uint32_t>(__builtin_bit_cast(u16, v3)) << 16);
-  *reinterpret_cast<uint2*>(p) = u;
+  // round to nearest even, two values per conversion instruction
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<bf16x4*>(p) = __builtin_convertvector((f32x4_t{a, b, c, d}), bf16x4);
 }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
