@@ -28,7 +28,6 @@
 namespace dsa3d {
 
 typedef short shortx4v __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 // Blob rows (or columns) of start cells whose windows reach key block kb along an
 // axis with window k, lattice length L: cells [4 kb - k + 1, 4 kb + 3] clipped.
@@ -394,9 +393,16 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
     // of its queries 16 hf + 4 quad + i, which are slots 4 hf + i of the pair's B
     // fragments in xch[par] (8 of their 16 bytes per lane)
     auto produce = [&](char* e, int par) {
+      const int q0 = 16 * hf + 4 * quad;
+      const float4 de = *reinterpret_cast<const float4*>(e + C::META + 12 * KV_Q + q0 * 4);
+      // dP - Delta: the products accumulate onto -Delta of the lane's four queries
+      const f32x4_t ndq = f32x4_t{-de.x, -de.y, -de.z, -de.w};
       f32x4_t sc[NSG], dp[NSG];
 #pragma unroll
-      for (int i = 0; i < NSG; ++i) sc[i] = dp[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NSG; ++i) {
+        sc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        dp[i] = ndq;
+      }
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
         const int off = sw(16 * hf + r16, (c & 1) * 64 + quad * 16);
@@ -408,22 +414,25 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
 #pragma unroll
         for (int i = 0; i < NSG; ++i) dp[i] = mma(a, vf[i][c], dp[i]);
       }
-      const int q0 = 16 * hf + 4 * quad;
       const int4 sa = *reinterpret_cast<const int4*>(e + C::META + q0 * 8);
       const int4 sb = *reinterpret_cast<const int4*>(e + C::META + q0 * 8 + 16);
       const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 8 * KV_Q + q0 * 4);
-      const float4 de = *reinterpret_cast<const float4*>(e + C::META + 12 * KV_Q + q0 * 4);
       const int sy[4] = {sa.x, sa.z, sb.x, sb.z}, sx[4] = {sa.y, sa.w, sb.y, sb.w};
-      const float lq[4] = {ls.x, ls.y, ls.z, ls.w}, dq[4] = {de.x, de.y, de.z, de.w};
+      const float lq[4] = {ls.x, ls.y, ls.z, ls.w};
+      // per query: -lse (log2 units) inside the window, -inf outside (exp2 gives 0)
+      float qb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        qb[j] = (unsigned)(key_y - sy[j]) < (unsigned)g.ky && (unsigned)(key_x - sx[j]) < (unsigned)g.kx
+                    ? -lq[j] * LOG2E
+                    : -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < NSG; ++i) {
         f32x4_t pe, ds;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bool ok = (unsigned)(key_y - sy[j]) < (unsigned)g.ky && (unsigned)(key_x - sx[j]) < (unsigned)g.kx;
-          // outside the window the exponent is -inf (exp2 gives 0, no branch)
-          pe[j] = __builtin_amdgcn_exp2f(ok ? sc[i][j] * sl2 - lq[j] * LOG2E : -__builtin_inff());
-          ds[j] = pe[j] * (dp[i][j] - dq[j]);
+          pe[j] = __builtin_amdgcn_exp2f(sc[i][j] * sl2 + qb[j]);
+          ds[j] = pe[j] * dp[i][j];
         }
         // bf16 (round to nearest even), two values per conversion instruction
         *reinterpret_cast<bf16x4_t*>(xch[par][s0 + i][0] + lane * 16 + hf * 8) = __builtin_convertvector(pe, bf16x4_t);

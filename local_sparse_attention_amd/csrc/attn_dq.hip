@@ -324,8 +324,8 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int b = 0; b < C::NB; ++b) {
-              if constexpr (ph == 0)
-                dpa[s][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              if constexpr (ph == 0)  // dP - Delta: the products accumulate onto -Delta
+                dpa[s][b] = f32x4_t{-dlt[s], -dlt[s], -dlt[s], -dlt[s]};
               else
                 sacc[s][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
             for (int i = 0; i < NBY; ++i) yb[i] = (ybias[s][i] + tb) - lse2[s];
             auto ds_of = [&](int b, int i) {
               const float x = sacc[s][b][i] * sl2 + (yb[b / NBX] + xbias[s][b % NBX][i]);
-              return __builtin_amdgcn_exp2f(x) * (dpa[s][b][i] - dlt[s]);
+              return __builtin_amdgcn_exp2f(x) * dpa[s][b][i];
             };
             static_for<0, C::NPAIR>([&](auto CC) {
               constexpr int c = decltype(CC)::value;
@@ -370,10 +370,10 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
                 }
                 set_frag(dsf[s][c], d8);
               } else {
-                __bf16 d4[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) d4[i] = static_cast<__bf16>(ds_of(2 * c, i));
-                __builtin_memcpy(&dsl[s], d4, 8);
+                const bf16x4_t d4 =
+                    __builtin_convertvector((f32x4_t{ds_of(2 * c, 0), ds_of(2 * c, 1), ds_of(2 * c, 2), ds_of(2 * c, 3)}),
+                                            bf16x4_t);
+                __builtin_memcpy(&dsl[s], &d4, 8);
               }
             });
           }

@@ -232,11 +232,14 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
               // a row whose slice does not read this frame (a tile of several slices)
-              // sees none of its keys
+              // sees none of its keys.  Scores are taken relative to the current
+              // reference max mref (0 before the row's first key), which folds into
+              // the biases.
               const float tb = (unsigned)(f - rt[s]) < (unsigned)g.kt ? 0.f : -INFINITY;
+              const float mref0 = m_run[s] == -INFINITY ? 0.f : m_run[s];
               float yb[NBY];
 #pragma unroll
-              for (int i = 0; i < NBY; ++i) yb[i] = ybias[s][i] + tb;
+              for (int i = 0; i < NBY; ++i) yb[i] = ybias[s][i] + (tb - mref0);
               float cm = -INFINITY;
 #pragma unroll
               for (int b = 0; b < C::NB; ++b)
@@ -251,16 +254,18 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
               // 2^8 (or on a row's first frame with keys, m = -inf): P <= 256
               // otherwise, and O and l need no rescale.  A row that has seen no key
               // yet keeps m = -inf (alpha = 0 clears its O and l until it does).
-              if (__ballot(cm > m_run[s] + 8.f)) {
-                const float mn = fmaxf(m_run[s], cm);
+              if (__ballot(cm > (m_run[s] == -INFINITY ? -INFINITY : 8.f))) {
+                const float mn = fmaxf(m_run[s], cm + mref0);
                 const float mref = (mn == -INFINITY) ? 0.f : mn;
                 const float alpha = __builtin_amdgcn_exp2f(m_run[s] - mref);
                 l_run[s] *= alpha;
 #pragma unroll
                 for (int t = 0; t < C::NT; ++t) oacc[s][t] *= alpha;
                 m_run[s] = mn;
+                const float d = mref0 - mref;
+#pragma unroll
+                for (int b = 0; b < C::NB; ++b) sacc[s][b] += d;
               }
-              const float mref = m_run[s] == -INFINITY ? 0.f : m_run[s];
               float ps = 0.f;
               static_for<0, C::NPAIR>([&](auto CC) {
                 constexpr int c = decltype(CC)::value;
@@ -268,20 +273,20 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
                   float pr[8];
 #pragma unroll
                   for (int i = 0; i < 4; ++i) {
-                    pr[i] = __builtin_amdgcn_exp2f(sacc[s][2 * c][i] - mref);
-                    pr[i + 4] = __builtin_amdgcn_exp2f(sacc[s][2 * c + 1][i] - mref);
+                    pr[i] = __builtin_amdgcn_exp2f(sacc[s][2 * c][i]);
+                    pr[i + 4] = __builtin_amdgcn_exp2f(sacc[s][2 * c + 1][i]);
                     ps += pr[i] + pr[i + 4];
                   }
                   set_frag(pf[s][c], pr);
                 } else {
-                  __bf16 p4[4];
+                  f32x4_t e;
 #pragma unroll
                   for (int i = 0; i < 4; ++i) {
-                    const float pr = __builtin_amdgcn_exp2f(sacc[s][2 * c][i] - mref);
-                    ps += pr;
-                    p4[i] = static_cast<__bf16>(pr);
+                    e[i] = __builtin_amdgcn_exp2f(sacc[s][2 * c][i]);
+                    ps += e[i];
                   }
-                  __builtin_memcpy(&pl[s], p4, 8);
+                  const bf16x4_t p4 = __builtin_convertvector(e, bf16x4_t);
+                  __builtin_memcpy(&pl[s], &p4, 8);
                 }
               });
               ps = quad_sum(ps);

@@ -88,6 +88,8 @@ __device__ __forceinline__ void set_frag(Frag<float>& f, const float* x) {
   for (int j = 0; j < 8; ++j) f.v[j] = x[j];
 }
 
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float to_f32(u16 b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float frag_elem(const Frag<u16>& f, int j) { return static_cast<float>(f.v[j]); }
