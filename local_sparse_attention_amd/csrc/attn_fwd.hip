@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
                   sacc[s][b][i] = x;
                   cm = fmaxf(cm, x);
                 }
-              cm = quad_max(cm);
+              cm = quad_max_rs(cm);
               // The reference max moves only when a score exceeds it by more than
               // 2^8 (or on a row's first frame with keys, m = -inf): P <= 256
               // otherwise, and O and l need no rescale.  A row that has seen no key
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
                   __builtin_memcpy(&pl[s], &p4, 8);
                 }
               });
-              ps = quad_sum(ps);
+              ps = quad_sum_rs(ps);
               l_run[s] += ps;
             }
           }

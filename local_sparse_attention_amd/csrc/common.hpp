@@ -143,6 +143,27 @@ __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor
 __device__ __forceinline__ float quad_max(float v) { return xor_max(xor_max(v, 16), 32); }
 __device__ __forceinline__ float quad_sum(float v) { return xor_sum(xor_sum(v, 16), 32); }
 
+// The same reductions by row swaps (v_permlane16_swap / v_permlane32_swap: VALU
+// instructions, no LDS round trip).  Every lane of the wave must be active.
+__device__ __forceinline__ float2 swap_rows16(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return float2{__uint_as_float(a[0]), __uint_as_float(a[1])};  // rows (2r, 2r + 1), both lanes
+}
+__device__ __forceinline__ float2 swap_rows32(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return float2{__uint_as_float(a[0]), __uint_as_float(a[1])};  // halves (0, 1), both lanes
+}
+__device__ __forceinline__ float quad_max_rs(float v) {
+  float2 a = swap_rows16(v);
+  a = swap_rows32(fmaxf(a.x, a.y));
+  return fmaxf(a.x, a.y);
+}
+__device__ __forceinline__ float quad_sum_rs(float v) {
+  float2 a = swap_rows16(v);
+  a = swap_rows32(a.x + a.y);
+  return a.x + a.y;
+}
+
 // Min / max over lanes 0..15 of each 16-lane row (all rows hold the same data).
 __device__ __forceinline__ int row16_min(int v) {
 #pragma unroll
