@@ -298,17 +298,33 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
           // ---- O^T += V^T P^T over this column phase
           constexpr int vph = ph - C::NPH;
           if (busy) {
+          constexpr int NDT = C::NT / C::NPH;
+          // one address per column tile, opaque, so that every read of the step takes
+          // its block offset in the instruction and no address is rewritten between reads
+          typedef __attribute__((address_space(3))) char lds_char;
+          lds_char* vb[NDT];
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            vb[dt] = (lds_char*)(tb + toff[dt]);
+            __asm__ __volatile__("" : "+v"(vb[dt]));
+          }
 #pragma unroll
           for (int c = 0; c < C::NPAIR; ++c) {
+            constexpr int ot = vph * (C::NT / C::NPH);
+            // the pair's transposed reads for all its column tiles first, then its MFMAs
+            shortx4_t lo[NDT], hi[NDT];
 #pragma unroll
-            for (int dt = 0; dt < C::NT / C::NPH; ++dt) {
-              constexpr int ot = vph * (C::NT / C::NPH);
-              const char* pa = tb + (2 * c) * 2048 + toff[dt];
-              const shortx4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
+            for (int dt = 0; dt < NDT; ++dt) {
+              lds_char* pa = vb[dt] + (2 * c) * 2048;
+              lo[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
+              if (2 * c + 1 < C::NB) hi[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
               if (2 * c + 1 < C::NB) {
-                const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
                 Frag<u16> a;
-                const shortx4_t both[2] = {lo, hi};
+                const shortx4_t both[2] = {lo[dt], hi[dt]};
                 __builtin_memcpy(&a.v, both, 16);
 #pragma unroll
                 for (int s = 0; s < NS; ++s) oacc[s][ot + dt] = mma(a, pf[s][c], oacc[s][ot + dt]);
@@ -316,7 +332,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
                 // a single last block: a 16-deep product
 #pragma unroll
                 for (int s = 0; s < NS; ++s)
-                  oacc[s][ot + dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, pl[s], oacc[s][ot + dt], 0, 0, 0);
+                  oacc[s][ot + dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo[dt], pl[s], oacc[s][ot + dt], 0, 0, 0);
               }
             }
           }
