@@ -198,6 +198,8 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
         constexpr int ph = decltype(PHC)::value;
         const int st = fi * C::NPH2 + ph;
         const char* tb = ring[st % C::NBUF];
+        typedef __attribute__((address_space(3))) char lds_char;
+        typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
         // opaque per step: keeps the compiler from precomputing every fragment
         // address of every ring slot outside the loop (more registers than a third
         // wave per SIMD leaves)
@@ -217,14 +219,30 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
 #pragma unroll
               for (int b = 0; b < C::NB; ++b) sacc[s][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
+          // K fragments in groups of KG blocks: the group's reads together (from fixed
+          // base addresses, one per column group, set before the first read; block
+          // offsets in the instruction), then its MFMAs
+          lds_char* kb[C::NC / C::NPH];
+#pragma unroll
+          for (int c = 0; c < C::NC / C::NPH; ++c) kb[c] = (lds_char*)(tb + roff[c]);
+          static_assert(C::NC / C::NPH == 2, "two column groups per step");
+          __asm__ __volatile__("" : "+v"(kb[0]), "+v"(kb[1]));
 #pragma unroll
           for (int c = 0; c < C::NC / C::NPH; ++c) {
+            constexpr int KG = 4;
 #pragma unroll
-            for (int b = 0; b < C::NB; ++b) {
-              Frag<u16> a;
-              load_frag(a, (const u16*)(tb + b * 2048 + roff[c]));
+            for (int b0 = 0; b0 < C::NB; b0 += KG) {
+              Frag<u16> a[KG];
 #pragma unroll
-              for (int s = 0; s < NS; ++s) sacc[s][b] = mma(a, qf[s][ph * (C::NC / C::NPH) + c], sacc[s][b]);
+              for (int j = 0; j < KG; ++j)
+                if (b0 + j < C::NB) a[j].v = *(const lds_bf16x8_t*)(kb[c] + (b0 + j) * 2048);
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int j = 0; j < KG; ++j)
+                if (b0 + j < C::NB)
+#pragma unroll
+                  for (int s = 0; s < NS; ++s)
+                    sacc[s][b0 + j] = mma(a[j], qf[s][ph * (C::NC / C::NPH) + c], sacc[s][b0 + j]);
             }
           }
           if constexpr (ph == C::NPH - 1) {
@@ -301,13 +319,11 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
           constexpr int NDT = C::NT / C::NPH;
           // one address per column tile, opaque, so that every read of the step takes
           // its block offset in the instruction and no address is rewritten between reads
-          typedef __attribute__((address_space(3))) char lds_char;
           lds_char* vb[NDT];
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            vb[dt] = (lds_char*)(tb + toff[dt]);
-            __asm__ __volatile__("" : "+v"(vb[dt]));
-          }
+          for (int dt = 0; dt < NDT; ++dt) vb[dt] = (lds_char*)(tb + toff[dt]);
+          static_assert(NDT == 4, "four column tiles per step");
+          __asm__ __volatile__("" : "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]));
 #pragma unroll
           for (int c = 0; c < C::NPAIR; ++c) {
             constexpr int ot = vph * (C::NT / C::NPH);
