@@ -61,6 +61,9 @@ __global__ __launch_bounds__(256) void k_delta(const u16* __restrict__ o, const 
   }
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+
 template <int D, int NBY, int NBX>
 struct DqCfg {
   static constexpr int NB = NBY * NBX;
@@ -189,29 +192,47 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
     // is written once they are done.
     bool pend = false;
     int pf = -1;
-    auto flush = [&](const char* kt_) {
-      if (pend) {
+    // dQ^T += K^T dS^T over the columns of K column phase kp (the tile at kt_): per
+    // key-block pair, its transposed reads for all column tiles together (from base
+    // addresses fixed before the first read, block offsets in the instruction), then
+    // its MFMAs; a single last block is a 16-deep product with half the reads
+    auto dqt_products = [&](const char* kt_, int kp) {
+      constexpr int NDT = C::NT / C::NPH;
+      static_assert(NDT == 4, "four column tiles per phase");
+      lds_char* vb[NDT];
 #pragma unroll
-        for (int c = 0; c < C::NPAIR; ++c) {
+      for (int dt = 0; dt < NDT; ++dt) vb[dt] = (lds_char*)(kt_ + toff[dt]);
+      __asm__ __volatile__("" : "+v"(vb[0]), "+v"(vb[1]), "+v"(vb[2]), "+v"(vb[3]));
 #pragma unroll
-          for (int dt = 0; dt < C::NT / C::NPH; ++dt) {
-            const char* pa = kt_ + (2 * c) * 2048 + toff[dt];
-            const int ot = (C::NPH - 1) * (C::NT / C::NPH) + dt;
-            const shortx4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
-            if (2 * c + 1 < C::NB) {
-              const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
-              Frag<u16> a;
-              const shortx4_t both[2] = {lo, hi};
-              __builtin_memcpy(&a.v, both, 16);
+      for (int c = 0; c < C::NPAIR; ++c) {
+        shortx4_t lo[NDT], hi[NDT];
 #pragma unroll
-              for (int s = 0; s < NS; ++s) dqa[s][ot] = mma(a, dsf[s][c], dqa[s][ot]);
-            } else {
+        for (int dt = 0; dt < NDT; ++dt) {
+          lds_char* pa = vb[dt] + (2 * c) * 2048;
+          lo[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
+          if (2 * c + 1 < C::NB) hi[dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-              for (int s = 0; s < NS; ++s)
-                dqa[s][ot] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, dsl[s], dqa[s][ot], 0, 0, 0);
-            }
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int ot = kp * NDT + dt;
+          if (2 * c + 1 < C::NB) {
+            Frag<u16> a;
+            const shortx4_t both[2] = {lo[dt], hi[dt]};
+            __builtin_memcpy(&a.v, both, 16);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) dqa[s][ot] = mma(a, dsf[s][c], dqa[s][ot]);
+          } else {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+              dqa[s][ot] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo[dt], dsl[s], dqa[s][ot], 0, 0, 0);
           }
         }
+      }
+    };
+    auto flush = [&](const char* kt_) {
+      if (pend) {
+        dqt_products(kt_, C::NPH - 1);
         // ---- tiles whose last frame that was: write dQ = scale dQ^T^T
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -330,18 +351,35 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
                 sacc[s][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
         }
+        // V (or K) fragments in groups of KG blocks: the group's reads together (from
+        // base addresses fixed before the first read, block offsets in the
+        // instruction), then its MFMAs
+        lds_char* kb[C::NC / C::NPH];
+#pragma unroll
+        for (int c = 0; c < C::NC / C::NPH; ++c) kb[c] = (lds_char*)(tb + roff[c]);
+        static_assert(C::NC / C::NPH == 2, "two column groups per step");
+        __asm__ __volatile__("" : "+v"(kb[0]), "+v"(kb[1]));
 #pragma unroll
         for (int c = 0; c < C::NC / C::NPH; ++c) {
+          constexpr int KG = 4;
 #pragma unroll
-          for (int b = 0; b < C::NB; ++b) {
-            Frag<u16> a;
-            load_frag(a, (const u16*)(tb + b * 2048 + roff[c]));
+          for (int b0 = 0; b0 < C::NB; b0 += KG) {
+            Frag<u16> a[KG];
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              if constexpr (ph < C::NPH)
-                dpa[s][b] = mma(a, dof[s][ph * (C::NC / C::NPH) + c], dpa[s][b]);
-              else
-                sacc[s][b] = mma(a, qf[s][kph * (C::NC / C::NPH) + c], sacc[s][b]);
+            for (int j = 0; j < KG; ++j)
+              if (b0 + j < C::NB) a[j].v = *(const lds_bf16x8_t*)(kb[c] + (b0 + j) * 2048);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < KG; ++j) {
+              if (b0 + j >= C::NB) continue;
+              const int b = b0 + j;
+#pragma unroll
+              for (int s = 0; s < NS; ++s) {
+                if constexpr (ph < C::NPH)
+                  dpa[s][b] = mma(a[j], dof[s][ph * (C::NC / C::NPH) + c], dpa[s][b]);
+                else
+                  sacc[s][b] = mma(a[j], qf[s][kph * (C::NC / C::NPH) + c], sacc[s][b]);
+              }
             }
           }
         }
@@ -382,31 +420,7 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
           pend = true;
           pf = f;
 #pragma unroll
-          for (int kp = 0; kp < C::NPH - 1; ++kp) {
-            const char* kt_ = ring[(st - (C::NPH - 1 - kp)) % C::NBUF];
-#pragma unroll
-            for (int c = 0; c < C::NPAIR; ++c) {
-#pragma unroll
-              for (int dt = 0; dt < C::NT / C::NPH; ++dt) {
-                const char* pa = kt_ + (2 * c) * 2048 + toff[dt];
-                const int ot = kp * (C::NT / C::NPH) + dt;
-                const shortx4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pa);
-                if (2 * c + 1 < C::NB) {
-                  const shortx4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pa + 2048));
-                  Frag<u16> a;
-                  const shortx4_t both[2] = {lo, hi};
-                  __builtin_memcpy(&a.v, both, 16);
-#pragma unroll
-                  for (int s = 0; s < NS; ++s) dqa[s][ot] = mma(a, dsf[s][c], dqa[s][ot]);
-                } else {
-                  // a single 16-key block: a 16-deep product, half the transposed reads
-#pragma unroll
-                  for (int s = 0; s < NS; ++s)
-                    dqa[s][ot] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, dsl[s], dqa[s][ot], 0, 0, 0);
-                }
-              }
-            }
-          }
+          for (int kp = 0; kp < C::NPH - 1; ++kp) dqt_products(ring[(st - (C::NPH - 1 - kp)) % C::NBUF], kp);
         }
         }  // busy
         if (issued - st - 2 == C::PD - 1)
