@@ -28,6 +28,8 @@
 namespace dsa3d {
 
 typedef short shortx4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 
 // Blob rows (or columns) of start cells whose windows reach key block kb along an
 // axis with window k, lattice length L: cells [4 kb - k + 1, 4 kb + 3] clipped.
@@ -394,7 +396,11 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
     // fragments in xch[par] (8 of their 16 bytes per lane)
     auto produce = [&](char* e, int par) {
       const int q0 = 16 * hf + 4 * quad;
+      // the queries' starts, lse and Delta first: they do not depend on the products
       const float4 de = *reinterpret_cast<const float4*>(e + C::META + 12 * KV_Q + q0 * 4);
+      const int4 sa = *reinterpret_cast<const int4*>(e + C::META + q0 * 8);
+      const int4 sb = *reinterpret_cast<const int4*>(e + C::META + q0 * 8 + 16);
+      const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 8 * KV_Q + q0 * 4);
       // dP - Delta: the products accumulate onto -Delta of the lane's four queries
       const f32x4_t ndq = f32x4_t{-de.x, -de.y, -de.z, -de.w};
       f32x4_t sc[NSG], dp[NSG];
@@ -403,20 +409,27 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
         sc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         dp[i] = ndq;
       }
+      // every Q and dO fragment of the row tile read together (two base addresses,
+      // fixed before the first read; tensor and phase offsets in the instruction),
+      // then the MFMAs
+      lds_char* fb[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) fb[c] = (lds_char*)(e + sw(16 * hf + r16, c * 64 + quad * 16));
+      __asm__ __volatile__("" : "+v"(fb[0]), "+v"(fb[1]));
+      Frag<u16> aq[C::NC], ao[C::NC];
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
-        const int off = sw(16 * hf + r16, (c & 1) * 64 + quad * 16);
-        Frag<u16> a;
-        load_frag(a, (const u16*)(tile(e, 0, c >> 1) + off));
-#pragma unroll
-        for (int i = 0; i < NSG; ++i) sc[i] = mma(a, kf[i][c], sc[i]);
-        load_frag(a, (const u16*)(tile(e, 1, c >> 1) + off));
-#pragma unroll
-        for (int i = 0; i < NSG; ++i) dp[i] = mma(a, vf[i][c], dp[i]);
+        aq[c].v = *(const lds_bf16x8_t*)(fb[c & 1] + (0 * C::NPH + (c >> 1)) * C::TILE);
+        ao[c].v = *(const lds_bf16x8_t*)(fb[c & 1] + (1 * C::NPH + (c >> 1)) * C::TILE);
       }
-      const int4 sa = *reinterpret_cast<const int4*>(e + C::META + q0 * 8);
-      const int4 sb = *reinterpret_cast<const int4*>(e + C::META + q0 * 8 + 16);
-      const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 8 * KV_Q + q0 * 4);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+#pragma unroll
+        for (int i = 0; i < NSG; ++i) sc[i] = mma(aq[c], kf[i][c], sc[i]);
+#pragma unroll
+        for (int i = 0; i < NSG; ++i) dp[i] = mma(ao[c], vf[i][c], dp[i]);
+      }
       const int sy[4] = {sa.x, sa.z, sb.x, sb.z}, sx[4] = {sa.y, sa.w, sb.y, sb.w};
       const float lq[4] = {ls.x, ls.y, ls.z, ls.w};
       // per query: -lse (log2 units) inside the window, -inf outside (exp2 gives 0)
