@@ -174,20 +174,18 @@ def main():
     bevs = [hip.events(4) for _ in range(args.steps)]
 
     def step(fev=None, bev=None):
-        rc = lib.dsa3d_forward_timed(ptr(dev["q"]), ptr(dev["k"]), ptr(dev["v"]), ptr(dev["offsets"]), *grid,
-                                     wl.heads, wl.head_dim, *window, wl.scale, dtc, ptr(out), ptr(lse), ptr(ws),
-                                     ws.numel(), sp, fev)
+        rc = lib.dsa3d_forward_ex(ptr(dev["q"]), ptr(dev["k"]), ptr(dev["v"]), ptr(dev["offsets"]), *grid,
+                                  wl.heads, wl.head_dim, *window, wl.scale, dtc, ptr(out), ptr(lse), ptr(ws),
+                                  ws.numel(), sp, 0, fev)
         assert rc == 0, dsa3d.status_string(rc)
-        rc = lib.dsa3d_backward_timed(ptr(dev["q"]), ptr(dev["k"]), ptr(dev["v"]), ptr(dev["offsets"]), ptr(out),
-                                      ptr(lse), ptr(dev["dout"]), *grid, wl.heads, wl.head_dim, *window, wl.scale,
-                                      dtc, ptr(dq), ptr(dk), ptr(dv), ptr(ws), ws.numel(), sp,
-                                      bev)
+        rc = lib.dsa3d_backward_ex(ptr(dev["q"]), ptr(dev["k"]), ptr(dev["v"]), ptr(dev["offsets"]), ptr(out),
+                                   ptr(lse), ptr(dev["dout"]), *grid, wl.heads, wl.head_dim, *window, wl.scale,
+                                   dtc, ptr(dq), ptr(dk), ptr(dv), ptr(ws), ws.numel(), sp, 0, bev)
         assert rc == 0, dsa3d.status_string(rc)
 
     evp = ctypes.POINTER(ctypes.c_void_p)
-    lib.dsa3d_forward_timed.argtypes = lib.dsa3d_forward.argtypes + [evp]
-    lib.dsa3d_backward_timed.argtypes = lib.dsa3d_backward.argtypes + [evp]
-    lib.dsa3d_forward_timed.restype = lib.dsa3d_backward_timed.restype = ctypes.c_int
+    lib.dsa3d_forward_ex.argtypes = lib.dsa3d_forward.argtypes + [ctypes.c_uint, evp]
+    lib.dsa3d_backward_ex.argtypes = lib.dsa3d_backward.argtypes + [ctypes.c_uint, evp]
 
     for _ in range(args.warmup):
         step()

@@ -28,7 +28,10 @@
  *                    workspace 16-byte aligned.  Inputs are only read.  Outputs
  *                    are fully overwritten (dk, dv are not accumulated into).
  *   Limits           head_dim 64 or 128; each window dimension odd, >= 1 and not
- *                    larger than the grid dimension; N < 2^30; 1 <= heads <= 65535.
+ *                    larger than the grid dimension; N < 2^30; fewer than 2^27
+ *                    blobs of 1 x 4 x 4 start cells, i.e.
+ *                    (F-kt+1) * ceil((Hp-ky+1)/4) * ceil((Wp-kx+1)/4) < 2^27;
+ *                    1 <= heads <= 65535.
  *   Memory           The library allocates nothing and keeps no state between
  *                    calls.  Scratch space is the caller's `workspace` of at least
  *                    dsa3d_workspace_bytes(...) bytes; concurrent calls need
@@ -36,8 +39,11 @@
  *   Streams          Work is enqueued on `stream` (0 = the null stream) and the
  *                    call returns without synchronising.
  *   Errors           All arguments are checked before anything is enqueued: a
- *                    negative status means nothing was launched.
- *                    DSA3D_ERR_LAUNCH reports a failed launch.  Faults inside a
+ *                    validation error (every negative status except
+ *                    DSA3D_ERR_LAUNCH) means nothing was launched.
+ *                    DSA3D_ERR_LAUNCH reports a failed launch; kernels of the same
+ *                    call that were launched before it may already be on the
+ *                    stream, so the outputs are then undefined.  Faults inside a
  *                    kernel surface at the caller's next synchronisation.  The
  *                    library never prints, raises or aborts.
  *   Determinism      Outputs are bitwise identical for identical inputs (no
@@ -67,12 +73,21 @@ enum {
   DSA3D_ERR_NULL = -1,      /* a required pointer is null */
   DSA3D_ERR_DTYPE = -2,     /* dtype is not DSA3D_F32 / DSA3D_BF16 */
   DSA3D_ERR_HEAD_DIM = -3,  /* head_dim is not 64 or 128 */
-  DSA3D_ERR_GRID = -4,      /* F, Hp, Wp < 1, N too large, or heads out of range */
+  DSA3D_ERR_GRID = -4,      /* F, Hp, Wp < 1, N or the start-cell count too large, or heads out of range */
   DSA3D_ERR_WINDOW = -5,    /* a window dimension is even, < 1 or larger than the grid */
   DSA3D_ERR_ALIGN = -6,     /* a tensor or the workspace is not 16-byte aligned */
   DSA3D_ERR_WORKSPACE = -7, /* workspace_bytes is smaller than dsa3d_workspace_bytes() */
   DSA3D_ERR_LAUNCH = -8,    /* a kernel launch failed */
-  DSA3D_ERR_SCALE = -9      /* scale is not finite */
+  DSA3D_ERR_SCALE = -9,     /* scale is not finite */
+  DSA3D_ERR_FLAGS = -10     /* flags holds a bit not defined below */
+};
+
+/* Bits of the `flags` argument of dsa3d_forward_ex / dsa3d_backward_ex. */
+enum {
+  /* Run the per-group kernels, which serve every valid geometry, even where the
+     frame-sweeping kernels would be chosen.  Results agree within the stated
+     tolerances; used by the tests to cover both kernel families on one input. */
+  DSA3D_FLAG_GENERIC_KERNELS = 1
 };
 
 /* Bytes of workspace needed by dsa3d_forward (backward = 0) or dsa3d_backward
@@ -105,22 +120,23 @@ int dsa3d_backward(const void* q, const void* k, const void* v, const int32_t* o
                    int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
 
-/* Profiling variants: the same work as dsa3d_forward / dsa3d_backward, plus
+/* Extended variants: the same work as dsa3d_forward / dsa3d_backward, with
+   `flags` (DSA3D_FLAG_* bits; 0 = the plain call) and optional phase events:
    hipEventRecord(events[i], stream) at the phase boundaries, so the caller can
    time each kernel on the stream it runs on.  `events` holds caller-created
    events: forward 3 ([0] before the bucketing of queries by window start and the
    work lists, [1] before the attention kernel, [2] after it); backward 4 ([0]
    before the bucketing, the work lists and the Delta = rowsum(dO * O) pass, [1]
    before the dQ kernel, [2] before the dK/dV kernel, [3] after it).  A null
-   `events` gives the untimed call. */
-int dsa3d_forward_timed(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
-                        int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out,
-                        float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                        const hipEvent_t* events);
-int dsa3d_backward_timed(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
-                         const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim,
-                         int kt, int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream, const hipEvent_t* events);
+   `events` records nothing. */
+int dsa3d_forward_ex(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
+                     int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream, unsigned flags,
+                     const hipEvent_t* events);
+int dsa3d_backward_ex(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
+                      const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
+                      int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, unsigned flags, const hipEvent_t* events);
 
 /* Static string for a status code. */
 const char* dsa3d_status_string(int status);

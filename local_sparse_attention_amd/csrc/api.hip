@@ -10,13 +10,6 @@ using namespace dsa3d;
 
 namespace {
 
-// Set DSA3D_GENERIC_KERNELS=1 to run the per-group kernels for every geometry
-// (used by the tests to cover both kernel families on the same inputs).
-bool generic_only() {
-  const char* e = getenv("DSA3D_GENERIC_KERNELS");
-  return e && e[0] == '1';
-}
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool odd_in(int k, int G) { return k >= 1 && (k & 1) == 1 && k <= G; }
@@ -26,6 +19,9 @@ int check_geom(int F, int Hp, int Wp, int heads, int kt, int ky, int kx) {
   const long long N = (long long)F * Hp * Wp;
   if (N >= (1LL << 30)) return DSA3D_ERR_GRID;
   if (!odd_in(kt, F) || !odd_in(ky, Hp) || !odd_in(kx, Wp)) return DSA3D_ERR_WINDOW;
+  // start cells are numbered blob by blob (1 x 4 x 4 cells each) in 32-bit sort keys
+  const long long blobs = (long long)(F - kt + 1) * ((Hp - ky + 1 + 3) / 4) * ((Wp - kx + 1 + 3) / 4);
+  if (blobs * 16 >= (1LL << 31)) return DSA3D_ERR_GRID;
   return DSA3D_OK;
 }
 
@@ -39,6 +35,42 @@ int check_common(int F, int Hp, int Wp, int heads, int head_dim, int kt, int ky,
 }
 
 }  // namespace
+
+namespace dsa3d {
+
+int check_forward_args(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
+                       int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, const void* out,
+                       const float* lse) {
+  if (!q || !k || !v || !offsets || !out || !lse) return DSA3D_ERR_NULL;
+  const int st = check_common(F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype);
+  if (st != DSA3D_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(offsets) & 3u))
+    return DSA3D_ERR_ALIGN;
+  return DSA3D_OK;
+}
+
+int run_forward(const void* q, const void* k, const void* v, const int32_t* offsets, const Geom& g, int head_dim,
+                float scale, int dtype, void* out, float* lse, char* workspace, hipStream_t stream, unsigned flags,
+                const hipEvent_t* events) {
+  Prep p;
+  workspace_layout(g, false, workspace, &p);
+  if (events) hipEventRecord(events[0], stream);
+  if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && fwd_qs_eligible(g, dtype, head_dim);
+  if (qs && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (events) hipEventRecord(events[1], stream);
+  AttnArgs a = {};
+  a.q = q; a.k = k; a.v = v;
+  a.out = out; a.lse_out = lse;
+  a.scale = scale;
+  const hipError_t e = qs ? launch_forward_qs(head_dim, a, g, p, stream)
+                          : launch_forward_v1(dtype, head_dim, a, g, p, stream);
+  if (events) hipEventRecord(events[2], stream);
+  return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
+}
+
+}  // namespace dsa3d
 
 extern "C" {
 
@@ -59,47 +91,35 @@ int dsa3d_window_starts(const int32_t* offsets, int F, int Hp, int Wp, int kt, i
   return launch_window_starts(offsets, g, starts, stream) == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
 
-int dsa3d_forward_timed(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
-                        int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out,
-                        float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                        const hipEvent_t* events) {
-  if (!q || !k || !v || !offsets || !out || !lse || !workspace) return DSA3D_ERR_NULL;
-  const int st = check_common(F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype);
+int dsa3d_forward_ex(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
+                     int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream, unsigned flags,
+                     const hipEvent_t* events) {
+  if (!workspace) return DSA3D_ERR_NULL;
+  const int st = check_forward_args(q, k, v, offsets, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype, out, lse);
   if (st != DSA3D_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||
-      (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(offsets) & 3u))
-    return DSA3D_ERR_ALIGN;
+  if (flags & ~(unsigned)DSA3D_FLAG_GENERIC_KERNELS) return DSA3D_ERR_FLAGS;
+  if (!aligned16(workspace)) return DSA3D_ERR_ALIGN;
   const Geom g = make_geom(F, Hp, Wp, heads, kt, ky, kx);
   if (workspace_bytes < workspace_layout(g, false, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
-  Prep p;
-  workspace_layout(g, false, static_cast<char*>(workspace), &p);
-  if (events) hipEventRecord(events[0], stream);
-  if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  const bool qs = !generic_only() && fwd_qs_eligible(g, dtype, head_dim);
-  if (qs && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  if (events) hipEventRecord(events[1], stream);
-  AttnArgs a = {};
-  a.q = q; a.k = k; a.v = v;
-  a.out = out; a.lse_out = lse;
-  a.scale = scale;
-  const hipError_t e = qs ? launch_forward_qs(head_dim, a, g, p, stream)
-                          : launch_forward_v1(dtype, head_dim, a, g, p, stream);
-  if (events) hipEventRecord(events[2], stream);
-  return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
+  return run_forward(q, k, v, offsets, g, head_dim, scale, dtype, out, lse, static_cast<char*>(workspace), stream,
+                     flags, events);
 }
 
 int dsa3d_forward(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
                   int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out, float* lse,
                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return dsa3d_forward_timed(q, k, v, offsets, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype, out, lse,
-                             workspace, workspace_bytes, stream, nullptr);
+  return dsa3d_forward_ex(q, k, v, offsets, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype, out, lse, workspace,
+                          workspace_bytes, stream, 0u, nullptr);
 }
 
-int dsa3d_backward_timed(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
-                         const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim,
-                         int kt, int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream, const hipEvent_t* events) {
+int dsa3d_backward_ex(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
+                      const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
+                      int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, unsigned flags,
+                      const hipEvent_t* events) {
   if (!q || !k || !v || !offsets || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return DSA3D_ERR_NULL;
+  if (flags & ~(unsigned)DSA3D_FLAG_GENERIC_KERNELS) return DSA3D_ERR_FLAGS;
   const int st = check_common(F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype);
   if (st != DSA3D_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
@@ -112,8 +132,8 @@ int dsa3d_backward_timed(const void* q, const void* k, const void* v, const int3
   workspace_layout(g, true, static_cast<char*>(workspace), &p);
   if (events) hipEventRecord(events[0], stream);
   if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  const bool kv_tube = !generic_only() && dkdv_tube_eligible(g, dtype, head_dim);
-  const bool qs = !generic_only() && dq_qs_eligible(g, dtype, head_dim);
+  const bool kv_tube = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dkdv_tube_eligible(g, dtype, head_dim);
+  const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dq_qs_eligible(g, dtype, head_dim);
   if (kv_tube && launch_kv_items(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   if (qs && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   AttnArgs a = {};
@@ -138,8 +158,8 @@ int dsa3d_backward(const void* q, const void* k, const void* v, const int32_t* o
                    const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
                    int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, void* workspace,
                    size_t workspace_bytes, hipStream_t stream) {
-  return dsa3d_backward_timed(q, k, v, offsets, out, lse, dout, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype,
-                              dq, dk, dv, workspace, workspace_bytes, stream, nullptr);
+  return dsa3d_backward_ex(q, k, v, offsets, out, lse, dout, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype, dq,
+                           dk, dv, workspace, workspace_bytes, stream, 0u, nullptr);
 }
 
 const char* dsa3d_status_string(int status) {
@@ -148,12 +168,13 @@ const char* dsa3d_status_string(int status) {
     case DSA3D_ERR_NULL: return "a required pointer is null";
     case DSA3D_ERR_DTYPE: return "dtype must be DSA3D_F32 (0) or DSA3D_BF16 (1)";
     case DSA3D_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
-    case DSA3D_ERR_GRID: return "grid must be >= 1 per axis with N < 2^30, and 1 <= heads <= 65535";
+    case DSA3D_ERR_GRID: return "grid must be >= 1 per axis with N < 2^30 (and < 2^27 blobs of start cells), and 1 <= heads <= 65535";
     case DSA3D_ERR_WINDOW: return "each window dimension must be odd, >= 1 and not larger than the grid";
     case DSA3D_ERR_ALIGN: return "tensors and workspace must be 16-byte aligned (lse, offsets 4-byte)";
     case DSA3D_ERR_WORKSPACE: return "workspace is smaller than dsa3d_workspace_bytes()";
     case DSA3D_ERR_LAUNCH: return "a kernel launch failed";
     case DSA3D_ERR_SCALE: return "scale must be finite";
+    case DSA3D_ERR_FLAGS: return "unknown bits in flags";
     default: return "unknown status";
   }
 }

@@ -106,4 +106,13 @@ bool dkdv_tube_eligible(const Geom& g, int dtype, int D);
 hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s);
 hipError_t launch_dkdv_tube(int D, const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s);
 
+// Host-side argument checks of the forward (everything but the workspace) and its
+// launch sequence once the arguments are known to be valid (api.hip).
+int check_forward_args(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
+                       int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, const void* out,
+                       const float* lse);
+int run_forward(const void* q, const void* k, const void* v, const int32_t* offsets, const Geom& g, int head_dim,
+                float scale, int dtype, void* out, float* lse, char* workspace, hipStream_t stream, unsigned flags,
+                const hipEvent_t* events);
+
 }  // namespace dsa3d

@@ -89,9 +89,9 @@ __device__ __forceinline__ int4 query_start(const int32_t* off, const Geom& g, i
   const int plane = g.Hp * g.Wp;
   const int t = n / plane, rem = n - t * plane, y = rem / g.Wp, x = rem - y * g.Wp;
   int4 s;
-  s.x = clamp_start(t, off[3 * n + 0], g.kt, g.F);
-  s.y = clamp_start(y, off[3 * n + 1], g.ky, g.Hp);
-  s.z = clamp_start(x, off[3 * n + 2], g.kx, g.Wp);
+  s.x = clamp_start(t, off[3 * (size_t)n + 0], g.kt, g.F);
+  s.y = clamp_start(y, off[3 * (size_t)n + 1], g.ky, g.Hp);
+  s.z = clamp_start(x, off[3 * (size_t)n + 2], g.kx, g.Wp);
   s.w = 0;
   return s;
 }
@@ -100,9 +100,9 @@ __global__ __launch_bounds__(256) void k_window_starts(const int32_t* off, Geom 
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= g.N) return;
   const int4 s = query_start(off, g, n);
-  starts3[3 * n + 0] = s.x;
-  starts3[3 * n + 1] = s.y;
-  starts3[3 * n + 2] = s.z;
+  starts3[3 * (size_t)n + 0] = s.x;
+  starts3[3 * (size_t)n + 1] = s.y;
+  starts3[3 * (size_t)n + 2] = s.z;
 }
 
 __global__ __launch_bounds__(256) void k_starts_keys(const int32_t* off, Geom g, int4* starts, uint32_t* keys) {

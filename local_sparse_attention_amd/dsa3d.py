@@ -24,21 +24,28 @@ class DSA3DError(RuntimeError):
     pass
 
 
+FLAG_GENERIC_KERNELS = 1  # DSA3D_FLAG_GENERIC_KERNELS
+
+
 def load():
     global _lib
     if _lib is None:
         if not os.path.exists(LIBPATH):
             raise DSA3DError(f"{LIBPATH} is missing: build it with __graft_entry__.build()")
         lib = ctypes.CDLL(LIBPATH)
-        i32, vp, sz, f32 = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+        i32, u32, vp, sz, f32 = ctypes.c_int, ctypes.c_uint, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
         lib.dsa3d_workspace_bytes.argtypes = [i32] * 8
         lib.dsa3d_workspace_bytes.restype = sz
         lib.dsa3d_window_starts.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp]
         lib.dsa3d_window_starts.restype = i32
-        lib.dsa3d_forward.argtypes = [vp, vp, vp, vp] + [i32] * 8 + [f32, i32, vp, vp, vp, sz, vp]
-        lib.dsa3d_forward.restype = i32
-        lib.dsa3d_backward.argtypes = [vp] * 7 + [i32] * 8 + [f32, i32, vp, vp, vp, vp, sz, vp]
-        lib.dsa3d_backward.restype = i32
+        fwd = [vp, vp, vp, vp] + [i32] * 8 + [f32, i32, vp, vp, vp, sz, vp]
+        bwd = [vp] * 7 + [i32] * 8 + [f32, i32, vp, vp, vp, vp, sz, vp]
+        lib.dsa3d_forward.argtypes = fwd
+        lib.dsa3d_backward.argtypes = bwd
+        lib.dsa3d_forward_ex.argtypes = fwd + [u32, vp]
+        lib.dsa3d_backward_ex.argtypes = bwd + [u32, vp]
+        for f in ("dsa3d_forward", "dsa3d_backward", "dsa3d_forward_ex", "dsa3d_backward_ex"):
+            getattr(lib, f).restype = i32
         lib.dsa3d_status_string.argtypes = [i32]
         lib.dsa3d_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -62,9 +69,21 @@ def _dtype_code(t):
     raise DSA3DError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
 
 
-def _dev(t, name):
+def _want(t, name, shape, dtype):
+    """Shape and dtype of an argument (checked before anything touches the GPU)."""
+    if not isinstance(t, torch.Tensor):
+        raise DSA3DError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise DSA3DError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise DSA3DError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _dev(t, name, device=None):
     if not t.is_cuda:
         raise DSA3DError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise DSA3DError(f"{name} is on {t.device}, the other tensors on {device}")
     if not t.is_contiguous():
         raise DSA3DError(f"{name} must be contiguous")
     return t.data_ptr()
@@ -86,6 +105,7 @@ def workspace(grid, heads, window, backward, device="cuda"):
 def window_starts(offsets, grid, window):
     """int32 [N, 3] window starts (st, sy, sx) computed on the GPU."""
     N = grid[0] * grid[1] * grid[2]
+    _want(offsets, "offsets", (N, 3), torch.int32)
     starts = torch.empty((N, 3), dtype=torch.int32, device=offsets.device)
     _check(load().dsa3d_window_starts(_dev(offsets, "offsets"), *grid, *window, starts.data_ptr(), _stream()),
            "dsa3d_window_starts")
@@ -93,45 +113,72 @@ def window_starts(offsets, grid, window):
 
 
 def _shape(q, grid):
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise DSA3DError("q must be a [N, heads, head_dim] tensor")
     N, H, D = q.shape
     if N != grid[0] * grid[1] * grid[2]:
         raise DSA3DError(f"q has {N} tokens, grid {grid} has {grid[0] * grid[1] * grid[2]}")
+    _dtype_code(q)
     return N, H, D
 
 
-def forward(q, k, v, offsets, grid, window, scale=None, out=None, lse=None, ws=None):
-    """Returns (out [N, H, D], lse [H, N] float32)."""
+def _workspace_arg(ws, grid, H, window, backward, device):
+    if ws is None:
+        return workspace(grid, H, window, backward, device)
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise DSA3DError("ws must be a 1-D uint8 tensor")
+    return ws
+
+
+def forward(q, k, v, offsets, grid, window, scale=None, out=None, lse=None, ws=None, generic=False):
+    """Returns (out [N, H, D], lse [H, N] float32).  generic=True runs the per-group
+    kernels (DSA3D_FLAG_GENERIC_KERNELS) whatever the geometry."""
     N, H, D = _shape(q, grid)
     for t, name in ((k, "k"), (v, "v")):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise DSA3DError(f"{name} must match q in shape and dtype")
+        _want(t, name, q.shape, q.dtype)
+    _want(offsets, "offsets", (N, 3), torch.int32)
+    if out is not None:
+        _want(out, "out", q.shape, q.dtype)
+    if lse is not None:
+        _want(lse, "lse", (H, N), torch.float32)
     if scale is None:
         scale = D ** -0.5
+    dev = q.device
+    ptrs = [_dev(t, n, dev) for t, n in ((q, "q"), (k, "k"), (v, "v"), (offsets, "offsets"))]
     out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    ws = workspace(grid, H, window, False, q.device) if ws is None else ws
-    _check(load().dsa3d_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(offsets, "offsets"), *grid, H, D,
-                                *window, float(scale), _dtype_code(q), _dev(out, "out"), _dev(lse, "lse"),
-                                _dev(ws, "workspace"), ws.numel(), _stream()), "dsa3d_forward")
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    ws = _workspace_arg(ws, grid, H, window, False, dev)
+    flags = FLAG_GENERIC_KERNELS if generic else 0
+    _check(load().dsa3d_forward_ex(*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q), _dev(out, "out", dev),
+                                   _dev(lse, "lse", dev), _dev(ws, "workspace", dev), ws.numel(), _stream(), flags,
+                                   None), "dsa3d_forward")
     return out, lse
 
 
-def backward(q, k, v, offsets, out, lse, dout, grid, window, scale=None, dq=None, dk=None, dv=None, ws=None):
+def backward(q, k, v, offsets, out, lse, dout, grid, window, scale=None, dq=None, dk=None, dv=None, ws=None,
+             generic=False):
     """Returns (dq, dk, dv), each [N, H, D] in q's dtype."""
     N, H, D = _shape(q, grid)
     for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise DSA3DError(f"{name} must match q in shape and dtype")
+        _want(t, name, q.shape, q.dtype)
+    _want(offsets, "offsets", (N, 3), torch.int32)
+    _want(lse, "lse", (H, N), torch.float32)
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t is not None:
+            _want(t, name, q.shape, q.dtype)
     if scale is None:
         scale = D ** -0.5
+    dev = q.device
+    ptrs = [_dev(t, n, dev) for t, n in ((q, "q"), (k, "k"), (v, "v"), (offsets, "offsets"), (out, "out"),
+                                         (lse, "lse"), (dout, "dout"))]
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    ws = workspace(grid, H, window, True, q.device) if ws is None else ws
-    _check(load().dsa3d_backward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(offsets, "offsets"),
-                                 _dev(out, "out"), _dev(lse, "lse"), _dev(dout, "dout"), *grid, H, D, *window,
-                                 float(scale), _dtype_code(q), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"),
-                                 _dev(ws, "workspace"), ws.numel(), _stream()), "dsa3d_backward")
+    ws = _workspace_arg(ws, grid, H, window, True, dev)
+    flags = FLAG_GENERIC_KERNELS if generic else 0
+    _check(load().dsa3d_backward_ex(*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q), _dev(dq, "dq", dev),
+                                    _dev(dk, "dk", dev), _dev(dv, "dv", dev), _dev(ws, "workspace", dev), ws.numel(),
+                                    _stream(), flags, None), "dsa3d_backward")
     return dq, dk, dv
 
 

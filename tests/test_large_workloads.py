@@ -1,7 +1,17 @@
 """Parity at the full sizes of the 720p-like, full-width and 256-frame workloads, in the
-launch configuration the benchmark times: sampled outputs (grid corners, edge centres and
-random rows) against the oracle computed row by row, plus properties that hold at any
-size, checked over every output.
+launch configuration the benchmark times.
+
+- 720p-like (grid 32 x 45 x 80, 16 heads x 128, window 3 x 9 x 9): every element of O, LSE,
+  dQ, dK and dV against the full oracle.
+- 5 x 9 x 9 window over 100 frames (grid 100 x 32 x 32, 8 heads x 128, drifting offsets):
+  every element as well.  Its 96 start slices make three query-side work items of 32
+  slices, and its 64 key-block columns x 8 heads = 512 workgroups keep the key-centric
+  dK/dV pass at one run over all 100 frames, as at the 256-frame workload.
+- full-width (64 x 68 x 120, 64 heads) and 256-frame (256 x 68 x 120, 16 heads x 128,
+  window 5 x 9 x 9): every (query, head) row of the start slices on both sides of each
+  query-side work-item boundary (slices 31 | 32, and 63 | 64 at 256 frames), grid
+  corners and edge centres, and random rows, against the oracle computed row by row;
+  plus properties that hold at any size, checked over every output.
 
 Properties (P = softmax weights of a query, rows sum to one; dS rows sum to zero):
   sum_j dV[j,h] = sum_n dO[n,h]        sum_j dK[j,h] = 0        all outputs finite.
@@ -12,19 +22,20 @@ import torch
 
 import oracle
 from local_sparse_attention_amd import configs, synth
+from local_sparse_attention_amd.configs import Workload
 
-from _gpu_helpers import assert_close, assert_lse_close, border_and_random_rows, gather_rows, nan_like, to_dev
+from _gpu_helpers import (assert_close, assert_lse_close, border_and_random_rows, gather_rows, nan_like, to_dev,
+                          to_host_f64)
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {"C3": (1024, 256), "C4": (512, 96), "C5": (512, 96)}
+SAMPLES = {"C4": (512, 96), "C5": (512, 96)}
+# query-side work items are 32 start slices (the frame-sweeping kernels' QS_TS)
+ITEM_SLICES = 32
 
 
-def run_sampled(dsa3d, name):
-    wl = configs.ALL[name]
+def run_gpu(dsa3d, wl, inp):
     grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
-    print(f"case {wl.name}: generating inputs N={wl.N} H={wl.heads} D={wl.head_dim}", flush=True)
-    inp = synth.make_inputs(wl)
     q, k, v, do, off = (to_dev(inp[x]) for x in ("q", "k", "v", "dout", "offsets"))
     print(f"case {wl.name}: forward + backward on the GPU", flush=True)
     # outputs start as NaN: an element the library leaves unwritten fails the checks
@@ -33,23 +44,11 @@ def run_sampled(dsa3d, name):
     dq, dk, dv = dsa3d.backward(q, k, v, off, out, lse, do, grid, window, wl.scale, dq=nan_like(q), dk=nan_like(q),
                                 dv=nan_like(q))
     torch.cuda.synchronize()
+    return do, out, lse, dq, dk, dv
 
-    nq, nk = SAMPLES[name]
-    qrows = border_and_random_rows(grid, wl.heads, nq, seed=1)
-    krows = border_and_random_rows(grid, wl.heads, nk, seed=2)
-    args = (inp["q"], inp["k"], inp["v"])
-    print(f"case {wl.name}: oracle on {len(qrows)} query rows and {len(krows)} key rows", flush=True)
-    o_ref, lse_ref = oracle.forward_rows(*args, inp["offsets"], grid, window, wl.scale, qrows)
-    assert_close(gather_rows(out, qrows), o_ref, wl.dtype, "out")
-    lse_g = lse.T.reshape(-1)[torch.as_tensor(qrows, device=lse.device)].cpu().numpy()
-    assert_lse_close(lse_g, lse_ref)
-    dq_ref = oracle.backward_q_rows(*args, inp["dout"], inp["offsets"], grid, window, wl.scale, qrows)
-    assert_close(gather_rows(dq, qrows), dq_ref, wl.dtype, "dq")
-    dk_ref, dv_ref = oracle.backward_kv_rows(*args, inp["dout"], inp["offsets"], grid, window, wl.scale, krows)
-    assert_close(gather_rows(dk, krows), dk_ref, wl.dtype, "dk")
-    assert_close(gather_rows(dv, krows), dv_ref, wl.dtype, "dv")
 
-    # properties over every output, per head, in float64 on the device
+def check_properties(wl, do, out, lse, dq, dk, dv):
+    """Properties over every output, per head, in float64 on the device."""
     N = wl.N
     dv_sum = dv.double().sum(0)
     do_sum = do.double().sum(0)
@@ -66,15 +65,90 @@ def run_sampled(dsa3d, name):
     assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()
 
 
-def test_720p_like_workload(dsa3d_gpu):
-    run_sampled(dsa3d_gpu, "C3")
+def run_full(dsa3d, wl):
+    """Every output element against the full oracle."""
+    grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
+    print(f"case {wl.name}: generating inputs N={wl.N} H={wl.heads} D={wl.head_dim}", flush=True)
+    inp = synth.make_inputs(wl)
+    do, out, lse, dq, dk, dv = run_gpu(dsa3d, wl, inp)
+    check_properties(wl, do, out, lse, dq, dk, dv)
+    args = (inp["q"], inp["k"], inp["v"])
+    print(f"case {wl.name}: full oracle forward", flush=True)
+    o_ref, lse_ref = oracle.forward(*args, inp["offsets"], grid, window, wl.scale)
+    errs = {"out": assert_close(to_host_f64(out), o_ref, wl.dtype, "out"),
+            "lse": assert_lse_close(lse.cpu().numpy(), lse_ref)}
+    del o_ref, lse_ref
+    print(f"case {wl.name}: full oracle backward", flush=True)
+    refs = oracle.backward(*args, inp["dout"], inp["offsets"], grid, window, wl.scale)
+    for name, gpu, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        errs[name] = assert_close(to_host_f64(gpu), ref, wl.dtype, name)
+    print("max abs err", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+
+
+def boundary_rows(wl, offsets, boundaries=2):
+    """Rows r = n*H + h (every head) of the queries whose window starts in a slice next to
+    one of the first `boundaries` query-side work-item boundaries."""
+    grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
+    st = oracle.window_starts(offsets, grid, window)[:, 0]
+    Lt = wl.F - wl.kt + 1
+    slices = [s for b in range(ITEM_SLICES, Lt, ITEM_SLICES)[:boundaries] for s in (b - 1, b)]
+    toks = np.nonzero(np.isin(st, slices))[0].astype(np.int64)
+    rows = (toks[:, None] * wl.heads + np.arange(wl.heads)[None, :]).ravel()
+    return slices, rows
+
+
+def run_sampled(dsa3d, name):
+    wl = configs.ALL[name]
+    grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
+    print(f"case {wl.name}: generating inputs N={wl.N} H={wl.heads} D={wl.head_dim}", flush=True)
+    inp = synth.make_inputs(wl)
+    do, out, lse, dq, dk, dv = run_gpu(dsa3d, wl, inp)
+
+    nq, nk = SAMPLES[name]
+    slices, brows = boundary_rows(wl, inp["offsets"])
+    qrows = np.unique(np.concatenate([border_and_random_rows(grid, wl.heads, nq, seed=1), brows]))
+    krows = border_and_random_rows(grid, wl.heads, nk, seed=2)
+    args = (inp["q"], inp["k"], inp["v"])
+    print(f"case {wl.name}: oracle on {len(qrows)} query rows ({len(brows)} in start slices {slices}) and "
+          f"{len(krows)} key rows", flush=True)
+    o_ref, lse_ref = oracle.forward_rows(*args, inp["offsets"], grid, window, wl.scale, qrows)
+    assert_close(gather_rows(out, qrows), o_ref, wl.dtype, "out")
+    lse_g = lse.T.reshape(-1)[torch.as_tensor(qrows, device=lse.device)].cpu().numpy()
+    assert_lse_close(lse_g, lse_ref)
+    del o_ref
+    dq_ref = oracle.backward_q_rows(*args, inp["dout"], inp["offsets"], grid, window, wl.scale, qrows)
+    assert_close(gather_rows(dq, qrows), dq_ref, wl.dtype, "dq")
+    del dq_ref
+    dk_ref, dv_ref = oracle.backward_kv_rows(*args, inp["dout"], inp["offsets"], grid, window, wl.scale, krows)
+    assert_close(gather_rows(dk, krows), dk_ref, wl.dtype, "dk")
+    assert_close(gather_rows(dv, krows), dv_ref, wl.dtype, "dv")
+    check_properties(wl, do, out, lse, dq, dk, dv)
+
+
+@pytest.mark.timeout(900)
+def test_720p_like_workload_every_element(dsa3d_gpu):
+    run_full(dsa3d_gpu, configs.C3)
+
+
+LONG_5x9x9 = Workload("kt5-9x9-drift-100f", 100, 32, 32, 8, 128, 5, 9, 9, "bf16", True, 4, 1.0,
+                      ("blocks", 8, 3.0, True, 8.0))
+
+
+@pytest.mark.timeout(900)
+def test_5x9x9_window_three_work_items_every_element(dsa3d_gpu):
+    wl = LONG_5x9x9
+    assert (wl.F - wl.kt + 1) // ITEM_SLICES == 3
+    assert ((wl.Hp + 3) // 4) * ((wl.Wp + 3) // 4) * wl.heads == 512
+    run_full(dsa3d_gpu, wl)
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_full_width_workload(dsa3d_gpu):
     run_sampled(dsa3d_gpu, "C4")
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_256_frame_workload(dsa3d_gpu):
     run_sampled(dsa3d_gpu, "C5")

@@ -18,35 +18,34 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(params=["default", "generic"])
-def kernels(request, monkeypatch):
+def kernels(request):
     """Run each case through the default kernels (frame-sweeping where the window allows)
-    and through the per-group kernels that serve every geometry."""
-    if request.param == "generic":
-        monkeypatch.setenv("DSA3D_GENERIC_KERNELS", "1")
-    else:
-        monkeypatch.delenv("DSA3D_GENERIC_KERNELS", raising=False)
-    return request.param
+    and through the per-group kernels that serve every geometry (DSA3D_FLAG_GENERIC_KERNELS)."""
+    return request.param == "generic"
 
 
-def run_case(dsa3d, wl, inp, backward=True):
+def run_case(dsa3d, wl, inp, backward=True, generic=False):
     grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
-    print(f"case {wl.name} grid={grid} window={window} H={wl.heads} D={wl.head_dim} {wl.dtype}", flush=True)
+    print(f"case {wl.name} grid={grid} window={window} H={wl.heads} D={wl.head_dim} {wl.dtype} "
+          f"generic={generic}", flush=True)
     q, k, v, off = (to_dev(inp[x]) for x in ("q", "k", "v", "offsets"))
     # outputs start as NaN: an element the library leaves unwritten fails the comparison
     out, lse = dsa3d.forward(q, k, v, off, grid, window, wl.scale, out=nan_like(q),
-                             lse=torch.full((q.shape[1], q.shape[0]), float("nan"), device=q.device))
+                             lse=torch.full((q.shape[1], q.shape[0]), float("nan"), device=q.device),
+                             generic=generic)
     res = {"out": out, "lse": lse}
     if backward:
         do = to_dev(inp["dout"])
         res["dq"], res["dk"], res["dv"] = dsa3d.backward(q, k, v, off, out, lse, do, grid, window, wl.scale,
-                                                         dq=nan_like(q), dk=nan_like(q), dv=nan_like(q))
+                                                         dq=nan_like(q), dk=nan_like(q), dv=nan_like(q),
+                                                         generic=generic)
     torch.cuda.synchronize()
     return res
 
 
-def check_full(dsa3d, wl, inp=None, backward=True):
+def check_full(dsa3d, wl, inp=None, backward=True, generic=False):
     inp = inp if inp is not None else synth.make_inputs(wl, with_dout=backward)
-    res = run_case(dsa3d, wl, inp, backward)
+    res = run_case(dsa3d, wl, inp, backward, generic)
     grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
     o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["offsets"], grid, window, wl.scale)
     errs = {"out": assert_close(to_host_f64(res["out"]), o_ref, wl.dtype, "out"),
@@ -60,16 +59,16 @@ def check_full(dsa3d, wl, inp=None, backward=True):
 
 
 def test_tiny_fp32_workload(dsa3d_gpu, kernels):
-    check_full(dsa3d_gpu, configs.C1)
+    check_full(dsa3d_gpu, configs.C1, generic=kernels)
 
 
 def test_bf16_forward_workload(dsa3d_gpu, kernels):
-    check_full(dsa3d_gpu, configs.C2, backward=False)
+    check_full(dsa3d_gpu, configs.C2, backward=False, generic=kernels)
 
 
 def test_bf16_forward_workload_backward_too(dsa3d_gpu, kernels):
     # the forward workload's shapes through the backward as well (dO from its stream)
-    check_full(dsa3d_gpu, configs.C2.with_frames(6), backward=True)
+    check_full(dsa3d_gpu, configs.C2.with_frames(6), backward=True, generic=kernels)
 
 
 def W(name, F, Hp, Wp, H, D, kt, ky, kx, dtype, offsets, seed=11, scale=1.0):
@@ -101,7 +100,7 @@ EDGE = [
 
 @pytest.mark.parametrize("wl", EDGE, ids=[w.name for w in EDGE])
 def test_edge_cases(dsa3d_gpu, wl, kernels):
-    check_full(dsa3d_gpu, wl)
+    check_full(dsa3d_gpu, wl, generic=kernels)
 
 
 def test_huge_offsets_pile_on_borders(dsa3d_gpu, kernels):
@@ -112,7 +111,7 @@ def test_huge_offsets_pile_on_borders(dsa3d_gpu, kernels):
     g = np.random.default_rng(0)
     big = np.array([-(2**31), -(10**9), -40, 40, 10**9, 2**31 - 1], dtype=np.int64)
     inp["offsets"] = big[g.integers(0, len(big), size=inp["offsets"].shape)].astype(np.int32)
-    check_full(dsa3d_gpu, wl, inp)
+    check_full(dsa3d_gpu, wl, inp, generic=kernels)
 
 
 def test_window_starts_bit_exact(dsa3d_gpu):
@@ -128,11 +127,11 @@ def test_window_starts_bit_exact(dsa3d_gpu):
 def test_deterministic_across_calls_and_streams(dsa3d_gpu, kernels):
     wl = configs.C3.with_frames(6)
     inp = synth.make_inputs(wl)
-    a = run_case(dsa3d_gpu, wl, inp)
-    b = run_case(dsa3d_gpu, wl, inp)
+    a = run_case(dsa3d_gpu, wl, inp, generic=kernels)
+    b = run_case(dsa3d_gpu, wl, inp, generic=kernels)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        c = run_case(dsa3d_gpu, wl, inp)
+        c = run_case(dsa3d_gpu, wl, inp, generic=kernels)
     s.synchronize()
     for name in a:
         assert torch.equal(a[name].view(torch.int16) if a[name].dtype == torch.bfloat16 else a[name],

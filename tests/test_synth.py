@@ -13,15 +13,13 @@ from local_sparse_attention_amd import configs, synth
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def test_values_do_not_depend_on_thread_count():
+def test_values_do_not_depend_on_thread_count(tmp_path):
     a = synth.normal(7, 2, (4096, 3), "f32")
     code = ("import sys; sys.path.insert(0, %r); import numpy as np; from local_sparse_attention_amd import synth;"
             "np.save(sys.argv[1], synth.normal(7, 2, (4096, 3), 'f32'))" % ROOT)
-    path = os.path.join(ROOT, "_work", "synth_1thread.npy")
-    os.makedirs(os.path.dirname(path), exist_ok=True)
+    path = str(tmp_path / "synth_1thread.npy")
     subprocess.run([sys.executable, "-c", code, path], check=True, env={**os.environ, "OMP_NUM_THREADS": "1"})
     assert np.array_equal(np.load(path), a)
-    os.remove(path)
 
 
 def test_normal_distribution_and_streams():
