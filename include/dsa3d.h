@@ -79,7 +79,9 @@ enum {
   DSA3D_ERR_WORKSPACE = -7, /* workspace_bytes is smaller than dsa3d_workspace_bytes() */
   DSA3D_ERR_LAUNCH = -8,    /* a kernel launch failed */
   DSA3D_ERR_SCALE = -9,     /* scale is not finite */
-  DSA3D_ERR_FLAGS = -10     /* flags holds a bit not defined below */
+  DSA3D_ERR_FLAGS = -10,    /* flags holds a bit not defined below */
+  DSA3D_ERR_SCRATCH = -11   /* dsa3d_forward_static: the geometry needs more scratch than
+                               DSA3D_STATIC_SCRATCH_BYTES */
 };
 
 /* Bits of the `flags` argument of dsa3d_forward_ex / dsa3d_backward_ex. */
@@ -137,6 +139,28 @@ int dsa3d_backward_ex(const void* q, const void* k, const void* v, const int32_t
                       const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
                       int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, unsigned flags, const hipEvent_t* events);
+
+/* Size of the library's static scratch array (one per GPU), used by
+   dsa3d_forward_static only. */
+#define DSA3D_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)
+
+/* The forward of dsa3d_forward without a workspace, for callers that cannot
+   allocate device memory: code under HIP graph capture, tight serving loops and
+   harnesses that forbid hipMalloc.  The call allocates nothing (no hipMalloc,
+   hipFree or allocating library routine): its scratch is a file-scope device array
+   of DSA3D_STATIC_SCRATCH_BYTES in the library, one copy per GPU, held until the
+   process ends.  Arguments, outputs, results and errors are those of dsa3d_forward;
+   in addition it returns DSA3D_ERR_SCRATCH (nothing launched) when
+   dsa3d_workspace_bytes(F, Hp, Wp, heads, kt, ky, kx, 0) exceeds
+   DSA3D_STATIC_SCRATCH_BYTES (about 84 bytes per token: N up to ~790,000).  The
+   work runs on the current device (`stream` must belong to it); the first call on
+   a device looks up that device's copy of the array.  Every call on one GPU shares
+   its array, so calls that overlap on one GPU (other streams, other host threads)
+   race and must be serialised by the caller; back-to-back calls on one stream are
+   safe (every byte read is written earlier in the same call). */
+int dsa3d_forward_static(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
+                         int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out,
+                         float* lse, hipStream_t stream);
 
 /* Static string for a status code. */
 const char* dsa3d_status_string(int status);

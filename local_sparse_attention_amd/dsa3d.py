@@ -44,7 +44,8 @@ def load():
         lib.dsa3d_backward.argtypes = bwd
         lib.dsa3d_forward_ex.argtypes = fwd + [u32, vp]
         lib.dsa3d_backward_ex.argtypes = bwd + [u32, vp]
-        for f in ("dsa3d_forward", "dsa3d_backward", "dsa3d_forward_ex", "dsa3d_backward_ex"):
+        lib.dsa3d_forward_static.argtypes = [vp, vp, vp, vp] + [i32] * 8 + [f32, i32, vp, vp, vp]
+        for f in ("dsa3d_forward", "dsa3d_backward", "dsa3d_forward_ex", "dsa3d_backward_ex", "dsa3d_forward_static"):
             getattr(lib, f).restype = i32
         lib.dsa3d_status_string.argtypes = [i32]
         lib.dsa3d_status_string.restype = ctypes.c_char_p
@@ -152,6 +153,30 @@ def forward(q, k, v, offsets, grid, window, scale=None, out=None, lse=None, ws=N
     _check(load().dsa3d_forward_ex(*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q), _dev(out, "out", dev),
                                    _dev(lse, "lse", dev), _dev(ws, "workspace", dev), ws.numel(), _stream(), flags,
                                    None), "dsa3d_forward")
+    return out, lse
+
+
+def forward_static(q, k, v, offsets, grid, window, scale=None, out=None, lse=None):
+    """The forward through dsa3d_forward_static: no workspace, the library's static scratch
+    array instead (geometries up to DSA3D_STATIC_SCRATCH_BYTES of scratch).  Returns
+    (out, lse); out and lse are allocated here only when not given."""
+    N, H, D = _shape(q, grid)
+    for t, name in ((k, "k"), (v, "v")):
+        _want(t, name, q.shape, q.dtype)
+    _want(offsets, "offsets", (N, 3), torch.int32)
+    if out is not None:
+        _want(out, "out", q.shape, q.dtype)
+    if lse is not None:
+        _want(lse, "lse", (H, N), torch.float32)
+    if scale is None:
+        scale = D ** -0.5
+    dev = q.device
+    ptrs = [_dev(t, n, dev) for t, n in ((q, "q"), (k, "k"), (v, "v"), (offsets, "offsets"))]
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(load().dsa3d_forward_static(*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q),
+                                       _dev(out, "out", dev), _dev(lse, "lse", dev), _stream()),
+           "dsa3d_forward_static")
     return out, lse
 
 

@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "dsa3d.h")
 
 OK, ERR_NULL, ERR_DTYPE, ERR_HEAD_DIM, ERR_GRID, ERR_WINDOW, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_SCALE = (
     0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
-ERR_FLAGS = -10
+ERR_FLAGS, ERR_SCRATCH = -10, -11
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +41,7 @@ def test_exports_every_declared_function(lib):
 
 def test_status_strings(lib):
     for code in (OK, ERR_NULL, ERR_DTYPE, ERR_HEAD_DIM, ERR_GRID, ERR_WINDOW, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH,
-                 ERR_SCALE, ERR_FLAGS):
+                 ERR_SCALE, ERR_FLAGS, ERR_SCRATCH):
         s = dsa3d.status_string(code)
         assert s and s != "unknown status"
     assert dsa3d.status_string(-100) == "unknown status"
