@@ -47,8 +47,13 @@ def _load():
         lib.oracle_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_backward_q_rows.argtypes = [P, vp, vp, vp, vp, vp, i64, vp, vp]
         lib.oracle_backward_kv_rows.argtypes = [P, vp, vp, vp, vp, vp, i64, vp, vp, vp]
+        lib.oracle_forward_heads.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        lib.oracle_backward_heads.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_sampled_forward.argtypes = [P, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
+        lib.oracle_sampled_backward.argtypes = [P, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp]
         for f in ("oracle_window_starts", "oracle_forward", "oracle_forward_rows", "oracle_backward",
-                  "oracle_backward_q_rows", "oracle_backward_kv_rows"):
+                  "oracle_backward_q_rows", "oracle_backward_kv_rows", "oracle_forward_heads",
+                  "oracle_backward_heads", "oracle_sampled_forward", "oracle_sampled_backward"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -166,3 +171,86 @@ def backward_kv_rows(q, k, v, dout, offsets, grid, window, scale, rows):
                                     do.ctypes.data, off.ctypes.data, len(rows), rows.ctypes.data, dk.ctypes.data,
                                     dv.ctypes.data)
     return dk, dv
+
+
+# ---- per-head integer offsets ---------------------------------------------------------
+
+def forward_heads(q, k, v, offsets_heads, grid, window, scale):
+    """Per-head offsets int32 [H][N][3]: O [N][H][D], LSE [H][N] (float64)."""
+    q, k, v, off = _c(q), _c(k), _c(v), _c(offsets_heads, np.int32)
+    cfg = _cfg(q, grid, window, scale)
+    N, H, D = q.shape
+    assert off.shape == (H, N, 3)
+    out = np.empty((N, H, D), dtype=np.float64)
+    lse = np.empty((H, N), dtype=np.float64)
+    _load().oracle_forward_heads(ctypes.byref(cfg), q.ctypes.data, k.ctypes.data, v.ctypes.data, off.ctypes.data,
+                                 out.ctypes.data, lse.ctypes.data)
+    return out, lse
+
+
+def backward_heads(q, k, v, dout, offsets_heads, grid, window, scale):
+    q, k, v, do, off = _c(q), _c(k), _c(v), _c(dout), _c(offsets_heads, np.int32)
+    cfg = _cfg(q, grid, window, scale)
+    N, H, D = q.shape
+    assert off.shape == (H, N, 3) and do.dtype == q.dtype
+    dq, dk, dv = (np.empty(q.shape, dtype=np.float64) for _ in range(3))
+    _load().oracle_backward_heads(ctypes.byref(cfg), q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+                                  off.ctypes.data, dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    return dq, dk, dv
+
+
+# ---- sampled windows (real offsets, trilinear sampling) ---------------------------------
+MODES = {"box": 0, "free": 1}
+
+
+def _sampled_offsets(offsets, N, H, K, mode):
+    """Broadcast the offsets to the canonical shape of the mode, box (N, H, 3) or free
+    (N, H, K, 3), and return (float64 array, element strides (sn, sh, ss))."""
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.float64))
+    if off.ndim != (3 if mode == "box" else 4):
+        raise ValueError(f"{mode} offsets must be broadcastable to (N, H, 3) / (N, H, K, 3), got {off.shape}")
+    if mode == "box":
+        full = np.broadcast_to(off, (N, H, 3))
+        sn, sh, ss = full.strides[0] // 8, full.strides[1] // 8, 0
+    else:
+        full = np.broadcast_to(off, (N, H, K, 3))
+        sn, sh, ss = full.strides[0] // 8, full.strides[1] // 8, full.strides[2] // 8
+    assert full.strides[-1] == 8
+    return off, (sn, sh, ss)
+
+
+def sampled_forward(q, k, v, offsets, grid, window, scale, mode):
+    """Sampled windows (see oracle.c).  offsets: float, broadcastable to (N, H, 3) in box
+    mode or (N, H, K, 3) in free mode.  Returns O [N][H][D], LSE [H][N] (float64)."""
+    q, k, v = _c(q), _c(k), _c(v)
+    cfg = _cfg(q, grid, window, scale)
+    N, H, D = q.shape
+    K = window[0] * window[1] * window[2]
+    off, (sn, sh, ss) = _sampled_offsets(offsets, N, H, K, mode)
+    out = np.empty((N, H, D), dtype=np.float64)
+    lse = np.empty((H, N), dtype=np.float64)
+    _load().oracle_sampled_forward(ctypes.byref(cfg), q.ctypes.data, k.ctypes.data, v.ctypes.data, off.ctypes.data,
+                                   sn, sh, ss, MODES[mode], out.ctypes.data, lse.ctypes.data)
+    return out, lse
+
+
+def sampled_backward(q, k, v, dout, offsets, grid, window, scale, mode):
+    """dq, dk, dv [N][H][D] and doffsets in the shape of `offsets` (the gradient of each
+    given entry: summed over the heads / samples that share it)."""
+    q, k, v, do = _c(q), _c(k), _c(v), _c(dout)
+    assert do.dtype == q.dtype
+    cfg = _cfg(q, grid, window, scale)
+    N, H, D = q.shape
+    K = window[0] * window[1] * window[2]
+    off, (sn, sh, ss) = _sampled_offsets(offsets, N, H, K, mode)
+    dq, dk, dv = (np.empty(q.shape, dtype=np.float64) for _ in range(3))
+    full_shape = (N, H, 3) if mode == "box" else (N, H, K, 3)
+    g = np.empty(full_shape, dtype=np.float64)
+    _load().oracle_sampled_backward(ctypes.byref(cfg), q.ctypes.data, k.ctypes.data, v.ctypes.data, do.ctypes.data,
+                                    off.ctypes.data, sn, sh, ss, MODES[mode], dq.ctypes.data, dk.ctypes.data,
+                                    dv.ctypes.data, g.ctypes.data)
+    # sum over the axes along which the given offsets are shared
+    shape = off.shape
+    axes = tuple(i for i, s in enumerate(shape) if s == 1 and full_shape[i] != 1)
+    doff = g.sum(axis=axes, keepdims=True) if axes else g
+    return dq, dk, dv, doff.reshape(shape)
