@@ -140,6 +140,23 @@ int dsa3d_backward_ex(const void* q, const void* k, const void* v, const int32_t
                       int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, unsigned flags, const hipEvent_t* events);
 
+/* Per-head offsets.  The section learns offsets for each token and each attention
+   head; here each head h has its own integer offsets, offsets_heads int32
+   [heads][N][3] (head h's (dt, dy, dx) of token n at offsets_heads + 3 * (h * N + n)),
+   and head h of out / lse (forward) or of dq / dk / dv (backward) is exactly what
+   dsa3d_forward / dsa3d_backward compute for that head with those offsets.  Every
+   other argument, the workspace size (dsa3d_workspace_bytes with the same
+   arguments), the flags, tolerances, determinism and errors are those of the
+   *_ex calls.  The window starts, buckets and work lists are built per head, one
+   head after the other in stream order on the one workspace. */
+int dsa3d_forward_heads(const void* q, const void* k, const void* v, const int32_t* offsets_heads, int F, int Hp,
+                        int Wp, int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out,
+                        float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream, unsigned flags);
+int dsa3d_backward_heads(const void* q, const void* k, const void* v, const int32_t* offsets_heads, const void* out,
+                         const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
+                         int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, unsigned flags);
+
 /* Size of the library's static scratch array (one per GPU), used by
    dsa3d_forward_static only. */
 #define DSA3D_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)

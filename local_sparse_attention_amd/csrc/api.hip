@@ -70,6 +70,56 @@ int run_forward(const void* q, const void* k, const void* v, const int32_t* offs
   return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
 
+int check_backward_args(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
+                        const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
+                        int ky, int kx, float scale, int dtype, const void* dq, const void* dk, const void* dv) {
+  if (!q || !k || !v || !offsets || !out || !lse || !dout || !dq || !dk || !dv) return DSA3D_ERR_NULL;
+  const int st = check_common(F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype);
+  if (st != DSA3D_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(lse) & 3u) ||
+      (reinterpret_cast<uintptr_t>(offsets) & 3u))
+    return DSA3D_ERR_ALIGN;
+  return DSA3D_OK;
+}
+
+static AttnArgs backward_args(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                              const void* dout, float scale, void* dq, void* dk, void* dv) {
+  AttnArgs a = {};
+  a.q = q; a.k = k; a.v = v;
+  a.o = out; a.dout = dout; a.lse = lse;
+  a.out = dq; a.dk = dk; a.dv = dv;
+  a.scale = scale;
+  return a;
+}
+
+int run_backward(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
+                 const float* lse, const void* dout, const Geom& g, int head_dim, float scale, int dtype, void* dq,
+                 void* dk, void* dv, char* workspace, hipStream_t stream, unsigned flags, const hipEvent_t* events,
+                 bool delta_ready) {
+  Prep p;
+  workspace_layout(g, true, workspace, &p);
+  if (events) hipEventRecord(events[0], stream);
+  if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  const bool kv_tube = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dkdv_tube_eligible(g, dtype, head_dim);
+  const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dq_qs_eligible(g, dtype, head_dim);
+  if (kv_tube && launch_kv_items(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (qs && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  const AttnArgs a = backward_args(q, k, v, out, lse, dout, scale, dq, dk, dv);
+  // Delta = rowsum(dO * O) of every head for both kernels (the per-group dQ kernel makes
+  // its own head's)
+  if (qs && !delta_ready && launch_delta(head_dim, a, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (events) hipEventRecord(events[1], stream);
+  if (qs ? launch_dq_qs(head_dim, a, g, p, stream) != hipSuccess
+         : launch_backward_dq_v1(dtype, head_dim, a, g, p, stream) != hipSuccess)
+    return DSA3D_ERR_LAUNCH;
+  if (events) hipEventRecord(events[2], stream);
+  const hipError_t e = kv_tube ? launch_dkdv_tube(head_dim, a, g, p, stream)
+                               : launch_backward_dkdv_v1(dtype, head_dim, a, g, p, stream);
+  if (events) hipEventRecord(events[3], stream);
+  return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
+}
+
 }  // namespace dsa3d
 
 extern "C" {
@@ -118,40 +168,16 @@ int dsa3d_backward_ex(const void* q, const void* k, const void* v, const int32_t
                       int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv,
                       void* workspace, size_t workspace_bytes, hipStream_t stream, unsigned flags,
                       const hipEvent_t* events) {
-  if (!q || !k || !v || !offsets || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return DSA3D_ERR_NULL;
-  if (flags & ~(unsigned)DSA3D_FLAG_GENERIC_KERNELS) return DSA3D_ERR_FLAGS;
-  const int st = check_common(F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype);
+  if (!workspace) return DSA3D_ERR_NULL;
+  const int st = check_backward_args(q, k, v, offsets, out, lse, dout, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale,
+                                     dtype, dq, dk, dv);
   if (st != DSA3D_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(lse) & 3u) ||
-      (reinterpret_cast<uintptr_t>(offsets) & 3u))
-    return DSA3D_ERR_ALIGN;
+  if (flags & ~(unsigned)DSA3D_FLAG_GENERIC_KERNELS) return DSA3D_ERR_FLAGS;
+  if (!aligned16(workspace)) return DSA3D_ERR_ALIGN;
   const Geom g = make_geom(F, Hp, Wp, heads, kt, ky, kx);
   if (workspace_bytes < workspace_layout(g, true, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
-  Prep p;
-  workspace_layout(g, true, static_cast<char*>(workspace), &p);
-  if (events) hipEventRecord(events[0], stream);
-  if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  const bool kv_tube = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dkdv_tube_eligible(g, dtype, head_dim);
-  const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dq_qs_eligible(g, dtype, head_dim);
-  if (kv_tube && launch_kv_items(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  if (qs && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  AttnArgs a = {};
-  a.q = q; a.k = k; a.v = v;
-  a.o = out; a.dout = dout; a.lse = lse;
-  a.out = dq; a.dk = dk; a.dv = dv;
-  a.scale = scale;
-  // Delta = rowsum(dO * O) for both kernels (the per-group dQ kernel makes its own)
-  if (qs && launch_delta(head_dim, a, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  if (events) hipEventRecord(events[1], stream);
-  if (qs ? launch_dq_qs(head_dim, a, g, p, stream) != hipSuccess
-         : launch_backward_dq_v1(dtype, head_dim, a, g, p, stream) != hipSuccess)
-    return DSA3D_ERR_LAUNCH;
-  if (events) hipEventRecord(events[2], stream);
-  const hipError_t e = kv_tube ? launch_dkdv_tube(head_dim, a, g, p, stream)
-                               : launch_backward_dkdv_v1(dtype, head_dim, a, g, p, stream);
-  if (events) hipEventRecord(events[3], stream);
-  return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
+  return run_backward(q, k, v, offsets, out, lse, dout, g, head_dim, scale, dtype, dq, dk, dv,
+                      static_cast<char*>(workspace), stream, flags, events, false);
 }
 
 int dsa3d_backward(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
@@ -160,6 +186,58 @@ int dsa3d_backward(const void* q, const void* k, const void* v, const int32_t* o
                    size_t workspace_bytes, hipStream_t stream) {
   return dsa3d_backward_ex(q, k, v, offsets, out, lse, dout, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype, dq,
                            dk, dv, workspace, workspace_bytes, stream, 0u, nullptr);
+}
+
+int dsa3d_forward_heads(const void* q, const void* k, const void* v, const int32_t* offsets, int F, int Hp, int Wp,
+                        int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream, unsigned flags) {
+  if (!workspace) return DSA3D_ERR_NULL;
+  const int st = check_forward_args(q, k, v, offsets, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale, dtype, out, lse);
+  if (st != DSA3D_OK) return st;
+  if (flags & ~(unsigned)DSA3D_FLAG_GENERIC_KERNELS) return DSA3D_ERR_FLAGS;
+  if (!aligned16(workspace)) return DSA3D_ERR_ALIGN;
+  Geom g = make_geom(F, Hp, Wp, heads, kt, ky, kx);
+  if (workspace_bytes < workspace_layout(g, false, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
+  // one head at a time: its own window starts, buckets and work lists (the workspace is
+  // reused in stream order), then the attention kernels on that head only
+  for (int h = 0; h < heads; ++h) {
+    g.h0 = h;
+    g.nh = 1;
+    const int r = run_forward(q, k, v, offsets + (size_t)3 * g.N * h, g, head_dim, scale, dtype, out, lse,
+                              static_cast<char*>(workspace), stream, flags, nullptr);
+    if (r != DSA3D_OK) return r;
+  }
+  return DSA3D_OK;
+}
+
+int dsa3d_backward_heads(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
+                         const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
+                         int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, unsigned flags) {
+  if (!workspace) return DSA3D_ERR_NULL;
+  const int st = check_backward_args(q, k, v, offsets, out, lse, dout, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale,
+                                     dtype, dq, dk, dv);
+  if (st != DSA3D_OK) return st;
+  if (flags & ~(unsigned)DSA3D_FLAG_GENERIC_KERNELS) return DSA3D_ERR_FLAGS;
+  if (!aligned16(workspace)) return DSA3D_ERR_ALIGN;
+  Geom g = make_geom(F, Hp, Wp, heads, kt, ky, kx);
+  if (workspace_bytes < workspace_layout(g, true, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
+  // Delta of every head once (it does not depend on the offsets)
+  const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dq_qs_eligible(g, dtype, head_dim);
+  if (qs) {
+    Prep p;
+    workspace_layout(g, true, static_cast<char*>(workspace), &p);
+    const AttnArgs a = backward_args(q, k, v, out, lse, dout, scale, dq, dk, dv);
+    if (launch_delta(head_dim, a, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  }
+  for (int h = 0; h < heads; ++h) {
+    g.h0 = h;
+    g.nh = 1;
+    const int r = run_backward(q, k, v, offsets + (size_t)3 * g.N * h, out, lse, dout, g, head_dim, scale, dtype, dq,
+                               dk, dv, static_cast<char*>(workspace), stream, flags, nullptr, true);
+    if (r != DSA3D_OK) return r;
+  }
+  return DSA3D_OK;
 }
 
 const char* dsa3d_status_string(int status) {

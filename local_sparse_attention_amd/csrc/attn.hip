@@ -118,7 +118,7 @@ __global__ __launch_bounds__(64) void k_forward(const T* __restrict__ q, const T
   __shared__ int4 lpos[CHUNK];
 
   if ((int)blockIdx.x >= *p.ngroups) return;
-  const int h = blockIdx.y, lane = threadIdx.x, r16 = lane & 15, quad = lane >> 4;
+  const int h = g.h0 + (int)blockIdx.y, lane = threadIdx.x, r16 = lane & 15, quad = lane >> 4;
   const GroupInfo gi = group_info(g, p, blockIdx.x, lane);
 
   Frag<T> qf[TL::NC];
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(64) void k_backward_dq(const T* __restrict__ q, con
   __shared__ int4 lpos[CHUNK];
 
   if ((int)blockIdx.x >= *p.ngroups) return;
-  const int h = blockIdx.y, lane = threadIdx.x, r16 = lane & 15, quad = lane >> 4;
+  const int h = g.h0 + (int)blockIdx.y, lane = threadIdx.x, r16 = lane & 15, quad = lane >> 4;
   const GroupInfo gi = group_info(g, p, blockIdx.x, lane);
 
   Frag<T> qf[TL::NC], dof[TL::NC];
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(64) void k_backward_dkdv(const T* __restrict__ q, c
   __shared__ int4 lst[CHUNK];
   __shared__ float llse[CHUNK], ldel[CHUNK];
 
-  const int h = blockIdx.y, lane = threadIdx.x, r16 = lane & 15, quad = lane >> 4;
+  const int h = g.h0 + (int)blockIdx.y, lane = threadIdx.x, r16 = lane & 15, quad = lane >> 4;
   // key blob -> this lane's key (lane & 15)
   const int kby = (g.Hp + 3) / 4, kbx = (g.Wp + 3) / 4;
   const int b = blockIdx.x;
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(64) void k_backward_dkdv(const T* __restrict__ q, c
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 static hipError_t fwd_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
-  dim3 grid(p.max_groups, g.H);
+  dim3 grid(p.max_groups, g.nh);
   k_forward<T, D><<<grid, 64, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse_out, g, p,
                                       a.scale * LOG2E);
   return hipGetLastError();
@@ -452,7 +452,7 @@ static hipError_t fwd_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipS
 
 template <typename T, int D>
 static hipError_t dq_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
-  dim3 grid_q(p.max_groups, g.H);
+  dim3 grid_q(p.max_groups, g.nh);
   k_backward_dq<T, D><<<grid_q, 64, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.o,
                                             (const T*)a.dout, a.lse, (T*)a.out, p.delta, g, p, a.scale * LOG2E,
                                             a.scale);
@@ -462,7 +462,7 @@ static hipError_t dq_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipSt
 template <typename T, int D>
 static hipError_t dkdv_impl_v1(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
   const int nkb = g.F * ((g.Hp + 3) / 4) * ((g.Wp + 3) / 4);
-  dim3 grid_k(nkb, g.H);
+  dim3 grid_k(nkb, g.nh);
   k_backward_dkdv<T, D><<<grid_k, 64, 0, s>>>((const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
                                               a.lse, p.delta, (T*)a.dk, (T*)a.dv, g, p, a.scale * LOG2E, a.scale);
   return hipGetLastError();

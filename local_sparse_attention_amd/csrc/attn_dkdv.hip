@@ -157,9 +157,10 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
 
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
   const int nchunk = (g.F + ts - 1) / ts;
-  int L = xcd_remap(blockIdx.x, nkb * nchunk * g.H);
-  const int h = L / (nkb * nchunk);
-  L -= h * nkb * nchunk;
+  int L = xcd_remap(blockIdx.x, nkb * nchunk * g.nh);
+  const int hl = L / (nkb * nchunk);
+  L -= hl * nkb * nchunk;
+  const int h = g.h0 + hl;
   const int chunk = L / nkb, kb = L - chunk * nkb;
   const int kby = kb / nkbx, kbx = kb - kby * nkbx;
   const int t0 = chunk * ts, t1 = min(t0 + ts, g.F);  // frames written here
@@ -554,9 +555,9 @@ static hipError_t dkdv_impl(const AttnArgs& a, const Geom& g, const Prep& p, hip
   const int nkb = kv_item_columns(g);
   // the longest chunk that still leaves at least 512 workgroups (two per compute unit)
   int ts = min(g.F, DKDV_TS_MAX);
-  while (ts > 8 && (long long)nkb * g.H * ((g.F + ts - 1) / ts) < 512) ts = (ts + 1) / 2;
+  while (ts > 8 && (long long)nkb * g.nh * ((g.F + ts - 1) / ts) < 512) ts = (ts + 1) / 2;
   const int nchunk = (g.F + ts - 1) / ts;
-  const long long total = (long long)nkb * nchunk * g.H;
+  const long long total = (long long)nkb * nchunk * g.nh;
   KvItems it{p.kv_off, p.kv_ids, p.kv_st};
   k_dkdv_tube<D, KT, FPG><<<(unsigned)total, 128 * NG + 64 * DKDV_LW, 0, s>>>(
       (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, a.lse, p.delta, (u16*)a.dk, (u16*)a.dv, g,

@@ -97,8 +97,8 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
   __shared__ QsPass T;
 
   const int nbc = g.nby * g.nbx, nw = qs_items(g);
-  int L = xcd_remap(blockIdx.x, nw * g.H);
-  const int h = L / nw, w = L - h * nw;
+  int L = xcd_remap(blockIdx.x, nw * g.nh);
+  const int hl = L / nw, w = L - hl * nw, h = g.h0 + hl;
   const int bc = w % nbc;
   const int by = bc / g.nbx, bx = bc - by * g.nbx;
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, quad = lane >> 4;
@@ -441,7 +441,7 @@ bool dq_qs_eligible(const Geom& g, int dtype, int D) { return fwd_qs_eligible(g,
 
 template <int D, int NBY, int NBX>
 static hipError_t dq_qs_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
-  const long long total = (long long)qs_items(g) * g.H;
+  const long long total = (long long)qs_items(g) * g.nh;
   k_dq_qs<D, NBY, NBX><<<(unsigned)total, 64 * DQ_NW, 0, s>>>((const u16*)a.q, (const u16*)a.k, (const u16*)a.v,
                                                               (const u16*)a.dout, a.lse, p.delta, (u16*)a.out, g, p,
                                                               a.scale * LOG2E, a.scale);

@@ -58,8 +58,8 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
   __shared__ QsPass T;
 
   const int nbc = g.nby * g.nbx, nw = qs_items(g);
-  int L = xcd_remap(blockIdx.x, nw * g.H);
-  const int h = L / nw, w = L - h * nw;
+  int L = xcd_remap(blockIdx.x, nw * g.nh);
+  const int hl = L / nw, w = L - hl * nw, h = g.h0 + hl;
   const int chunk = w / nbc, bc = w - chunk * nbc;
   const int by = bc / g.nbx, bx = bc - by * g.nbx;
   (void)chunk;
@@ -389,7 +389,7 @@ bool fwd_qs_eligible(const Geom& g, int dtype, int D) {
 
 template <int D, int NBY, int NBX>
 static hipError_t fwd_qs_impl(const AttnArgs& a, const Geom& g, const Prep& p, hipStream_t s) {
-  const long long total = (long long)qs_items(g) * g.H;
+  const long long total = (long long)qs_items(g) * g.nh;
   k_forward_qs<D, NBY, NBX><<<(unsigned)total, 64 * (FWD_NW + FWD_LW), 0, s>>>(
       (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.out, a.lse_out, g, p, a.scale * LOG2E);
   return hipGetLastError();

@@ -25,7 +25,8 @@ struct Geom {
   int kt, ky, kx;    // window
   int Lt, Ly, Lx;    // start lattice: G - k + 1 per axis
   int nby, nbx;      // start blobs per lattice row / column (Lt blobs along t)
-  int H;             // heads
+  int H;             // heads (the row stride of [N][H][D] tensors)
+  int h0, nh;        // heads an attention launch covers: h0 .. h0 + nh - 1
   int N;             // tokens
   int nblobs;        // Lt * nby * nbx
   int keyspace;      // nblobs * BLOB_CELLS

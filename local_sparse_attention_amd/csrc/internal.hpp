@@ -115,4 +115,13 @@ int run_forward(const void* q, const void* k, const void* v, const int32_t* offs
                 float scale, int dtype, void* out, float* lse, char* workspace, hipStream_t stream, unsigned flags,
                 const hipEvent_t* events);
 
+int check_backward_args(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
+                        const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
+                        int ky, int kx, float scale, int dtype, const void* dq, const void* dk, const void* dv);
+// delta_ready: Delta of every head is already in the workspace (per-head calls)
+int run_backward(const void* q, const void* k, const void* v, const int32_t* offsets, const void* out,
+                 const float* lse, const void* dout, const Geom& g, int head_dim, float scale, int dtype, void* dq,
+                 void* dk, void* dv, char* workspace, hipStream_t stream, unsigned flags, const hipEvent_t* events,
+                 bool delta_ready);
+
 }  // namespace dsa3d

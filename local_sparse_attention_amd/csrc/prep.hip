@@ -21,6 +21,8 @@ Geom make_geom(int F, int Hp, int Wp, int H, int kt, int ky, int kx) {
   g.nby = (g.Ly + BLOB_Y - 1) / BLOB_Y;
   g.nbx = (g.Lx + BLOB_X - 1) / BLOB_X;
   g.H = H;
+  g.h0 = 0;
+  g.nh = H;
   g.N = F * Hp * Wp;
   g.nblobs = g.Lt * g.nby * g.nbx;
   g.keyspace = g.nblobs * BLOB_CELLS;

@@ -45,7 +45,10 @@ def load():
         lib.dsa3d_forward_ex.argtypes = fwd + [u32, vp]
         lib.dsa3d_backward_ex.argtypes = bwd + [u32, vp]
         lib.dsa3d_forward_static.argtypes = [vp, vp, vp, vp] + [i32] * 8 + [f32, i32, vp, vp, vp]
-        for f in ("dsa3d_forward", "dsa3d_backward", "dsa3d_forward_ex", "dsa3d_backward_ex", "dsa3d_forward_static"):
+        lib.dsa3d_forward_heads.argtypes = fwd + [u32]
+        lib.dsa3d_backward_heads.argtypes = bwd + [u32]
+        for f in ("dsa3d_forward", "dsa3d_backward", "dsa3d_forward_ex", "dsa3d_backward_ex", "dsa3d_forward_static",
+                  "dsa3d_forward_heads", "dsa3d_backward_heads"):
             getattr(lib, f).restype = i32
         lib.dsa3d_status_string.argtypes = [i32]
         lib.dsa3d_status_string.restype = ctypes.c_char_p
@@ -131,13 +134,20 @@ def _workspace_arg(ws, grid, H, window, backward, device):
     return ws
 
 
+def _offsets_shape(offsets, N, H):
+    """(N, 3) shared by the heads, or (H, N, 3) per head."""
+    return (H, N, 3) if isinstance(offsets, torch.Tensor) and offsets.dim() == 3 else (N, 3)
+
+
 def forward(q, k, v, offsets, grid, window, scale=None, out=None, lse=None, ws=None, generic=False):
-    """Returns (out [N, H, D], lse [H, N] float32).  generic=True runs the per-group
+    """Returns (out [N, H, D], lse [H, N] float32).  offsets: int32 [N, 3] shared by the
+    heads, or [H, N, 3] per head (dsa3d_forward_heads).  generic=True runs the per-group
     kernels (DSA3D_FLAG_GENERIC_KERNELS) whatever the geometry."""
     N, H, D = _shape(q, grid)
     for t, name in ((k, "k"), (v, "v")):
         _want(t, name, q.shape, q.dtype)
-    _want(offsets, "offsets", (N, 3), torch.int32)
+    per_head = _offsets_shape(offsets, N, H) == (H, N, 3)
+    _want(offsets, "offsets", _offsets_shape(offsets, N, H), torch.int32)
     if out is not None:
         _want(out, "out", q.shape, q.dtype)
     if lse is not None:
@@ -150,9 +160,12 @@ def forward(q, k, v, offsets, grid, window, scale=None, out=None, lse=None, ws=N
     lse = torch.empty((H, N), dtype=torch.float32, device=dev) if lse is None else lse
     ws = _workspace_arg(ws, grid, H, window, False, dev)
     flags = FLAG_GENERIC_KERNELS if generic else 0
-    _check(load().dsa3d_forward_ex(*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q), _dev(out, "out", dev),
-                                   _dev(lse, "lse", dev), _dev(ws, "workspace", dev), ws.numel(), _stream(), flags,
-                                   None), "dsa3d_forward")
+    args = (*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q), _dev(out, "out", dev), _dev(lse, "lse", dev),
+            _dev(ws, "workspace", dev), ws.numel(), _stream(), flags)
+    if per_head:
+        _check(load().dsa3d_forward_heads(*args), "dsa3d_forward_heads")
+    else:
+        _check(load().dsa3d_forward_ex(*args, None), "dsa3d_forward")
     return out, lse
 
 
@@ -182,11 +195,12 @@ def forward_static(q, k, v, offsets, grid, window, scale=None, out=None, lse=Non
 
 def backward(q, k, v, offsets, out, lse, dout, grid, window, scale=None, dq=None, dk=None, dv=None, ws=None,
              generic=False):
-    """Returns (dq, dk, dv), each [N, H, D] in q's dtype."""
+    """Returns (dq, dk, dv), each [N, H, D] in q's dtype.  offsets as in forward()."""
     N, H, D = _shape(q, grid)
     for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
         _want(t, name, q.shape, q.dtype)
-    _want(offsets, "offsets", (N, 3), torch.int32)
+    per_head = _offsets_shape(offsets, N, H) == (H, N, 3)
+    _want(offsets, "offsets", _offsets_shape(offsets, N, H), torch.int32)
     _want(lse, "lse", (H, N), torch.float32)
     for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         if t is not None:
@@ -201,9 +215,12 @@ def backward(q, k, v, offsets, out, lse, dout, grid, window, scale=None, dq=None
     dv = torch.empty_like(q) if dv is None else dv
     ws = _workspace_arg(ws, grid, H, window, True, dev)
     flags = FLAG_GENERIC_KERNELS if generic else 0
-    _check(load().dsa3d_backward_ex(*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q), _dev(dq, "dq", dev),
-                                    _dev(dk, "dk", dev), _dev(dv, "dv", dev), _dev(ws, "workspace", dev), ws.numel(),
-                                    _stream(), flags, None), "dsa3d_backward")
+    args = (*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q), _dev(dq, "dq", dev), _dev(dk, "dk", dev),
+            _dev(dv, "dv", dev), _dev(ws, "workspace", dev), ws.numel(), _stream(), flags)
+    if per_head:
+        _check(load().dsa3d_backward_heads(*args), "dsa3d_backward_heads")
+    else:
+        _check(load().dsa3d_backward_ex(*args, None), "dsa3d_backward")
     return dq, dk, dv
 
 
