@@ -80,8 +80,11 @@ enum {
   DSA3D_ERR_LAUNCH = -8,    /* a kernel launch failed */
   DSA3D_ERR_SCALE = -9,     /* scale is not finite */
   DSA3D_ERR_FLAGS = -10,    /* flags holds a bit not defined below */
-  DSA3D_ERR_SCRATCH = -11   /* dsa3d_forward_static: the geometry needs more scratch than
+  DSA3D_ERR_SCRATCH = -11,  /* dsa3d_forward_static: the geometry needs more scratch than
                                DSA3D_STATIC_SCRATCH_BYTES */
+  DSA3D_ERR_MODE = -12,     /* sampled windows: mode is not DSA3D_SAMPLE_BOX / DSA3D_SAMPLE_FREE */
+  DSA3D_ERR_LAYOUT = -13    /* sampled windows: offset strides negative, overlapping, or a
+                               per-sample stride in box mode */
 };
 
 /* Bits of the `flags` argument of dsa3d_forward_ex / dsa3d_backward_ex. */
@@ -156,6 +159,62 @@ int dsa3d_backward_heads(const void* q, const void* k, const void* v, const int3
                          const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
                          int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, void* workspace,
                          size_t workspace_bytes, hipStream_t stream, unsigned flags);
+
+/* ---- Sampled windows: real offsets, trilinear sampling ------------------------
+   The section samples keys and values from XW_k and XW_v at real positions by
+   trilinear interpolation (its implementation paragraph: grid_sample, bilinear
+   mode, 5-D tensors) and takes the softmax over the kt x kh x kw samples:
+     z_j  = scale * <q[n,h,:], K~_j>,  K~_j = trilinear sample of k[., h, :] at P_j
+     out[n,h,:] = sum_j softmax(z)_j * V~_j,  lse = log sum_j exp(z_j)
+   A sample at P (token units along t, y, x) blends the 8 grid rows
+   floor(P) + {0,1}^3 with weights prod_d (bit_d ? f_d : 1 - f_d), f = P - floor(P);
+   rows outside the grid are zero (grid_sample's default padding; integer positions
+   are grid points).  Where sample j = (u, v, w) (lexicographic, u over kt) of the
+   query at p = (t, y, x) sits, for its offset o (float32 (dt, dy, dx)):
+     DSA3D_SAMPLE_BOX   one offset per (query, head), shared by its samples:
+                        P_j = s + (u, v, w), s_d = min(max(p_d + o_d - (k_d-1)/2, 0),
+                        G_d - k_d) (real); integer offsets give exactly the windows of
+                        dsa3d_forward; each k_d <= G_d.
+     DSA3D_SAMPLE_FREE  P_j = p + (u, v, w) - (k - 1)/2 + o_j, each sample its own
+                        offset (the section's per-sample offsets), zero padded.
+   Offsets: float32, three consecutive values per entry, entry (n, h, j) at
+   offsets + n * stride_token + h * stride_head + j * stride_sample (element
+   strides; 0 = shared: [N][3] shared by heads and samples is (3, 0, 0), [H][N][3]
+   per head is (3, 3N, 0), [N][H][K][3] per sample is (3HK, 3K, 3)).  Entries not
+   shared must not overlap; box mode needs stride_sample == 0 (DSA3D_ERR_LAYOUT).
+   Windows: odd extents, kt * ky * kx <= 4096.  q, k, v, out, dout, dq, dk, dv, lse:
+   as for dsa3d_forward / dsa3d_backward (fp32 or bf16, head_dim 64 or 128).
+   Arithmetic is fp32 throughout (bf16 inputs widened, outputs rounded to nearest
+   even).  Results are bitwise deterministic. */
+#define DSA3D_SAMPLE_BOX 0
+#define DSA3D_SAMPLE_FREE 1
+
+/* Workspace bytes of dsa3d_sampled_backward (backward = 1; the forward needs none and
+   reports 256); 0 for an invalid geometry or one past the backward's limits
+   (N * heads * kt*ky*kx < 2^31 samples, heads * (F+1)(Hp+1)(Wp+1) < 2^31 cells).
+   About 36 bytes per sample in free mode, 24 in box mode. */
+size_t dsa3d_sampled_workspace_bytes(int F, int Hp, int Wp, int heads, int kt, int ky, int kx, int mode,
+                                     int backward);
+
+/* Forward over sampled windows: out [N][heads][head_dim], lse [heads][N]. */
+int dsa3d_sampled_forward(const void* q, const void* k, const void* v, const float* offsets, long long stride_token,
+                          long long stride_head, long long stride_sample, int mode, int F, int Hp, int Wp, int heads,
+                          int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out, float* lse,
+                          hipStream_t stream);
+
+/* Backward: dq, dk, dv and doffsets, the gradient of the offsets, written in the
+   layout of `offsets` (same strides; an entry shared by several heads or samples
+   gets the sum of their gradients, in a fixed order).  The gradient of a sample
+   position flows through the interpolation weights (at integer coordinates the
+   one-sided derivative of floor-based weights); in box mode also through the clamp
+   (1 where p_d + o_d - (k_d-1)/2 lies strictly inside (0, G_d - k_d), else 0).
+   dk and dv are gathered per key from its samples (sorted by base cell, fixed
+   order): no atomics. */
+int dsa3d_sampled_backward(const void* q, const void* k, const void* v, const float* offsets, long long stride_token,
+                           long long stride_head, long long stride_sample, int mode, const void* out,
+                           const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
+                           int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, float* doffsets,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Size of the library's static scratch array (one per GPU), used by
    dsa3d_forward_static only. */

@@ -253,6 +253,8 @@ const char* dsa3d_status_string(int status) {
     case DSA3D_ERR_LAUNCH: return "a kernel launch failed";
     case DSA3D_ERR_SCALE: return "scale must be finite";
     case DSA3D_ERR_FLAGS: return "unknown bits in flags";
+    case DSA3D_ERR_MODE: return "mode must be DSA3D_SAMPLE_BOX (0) or DSA3D_SAMPLE_FREE (1)";
+    case DSA3D_ERR_LAYOUT: return "offset strides must be >= 0 and not overlap (box mode: stride_sample 0)";
     case DSA3D_ERR_SCRATCH: return "the geometry needs more scratch than the static array holds (DSA3D_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }

@@ -47,6 +47,12 @@ hipError_t launch_window_starts(const int32_t* off, const Geom& g, int32_t* star
 hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, hipStream_t s);
 // In-place exclusive scan of n uint32 values (one workgroup).
 hipError_t launch_scan_excl(uint32_t* data, int n, hipStream_t s);
+// Stable LSD radix sort of n (key, value) pairs, 8 bits a pass from bit 0, values
+// starting as the item index: ping-pong buffers, ghist holds 256 * ceil(n / RADIX_TILE)
+// words.  Returns the buffer index (0 or 1) that holds the result, -1 on a launch error.
+int radix_sort(uint32_t* keys[2], int* vals[2], uint32_t* ghist, int n, int passes, hipStream_t s);
+// cell_ptr[c] = number of sorted keys below c, c = 0 .. keyspace.
+hipError_t launch_cell_ptr(const uint32_t* sorted_keys, int n, int keyspace, int* cell_ptr, hipStream_t s);
 
 // Key-centric dK/dV: windows whose key blocks reach at most 3 x 3 start blobs
 // (ky, kx <= 9) and kt <= 8 (one wave per frame in flight).

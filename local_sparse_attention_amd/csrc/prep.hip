@@ -297,6 +297,24 @@ hipError_t launch_window_starts(const int32_t* off, const Geom& g, int32_t* star
   return hipGetLastError();
 }
 
+int radix_sort(uint32_t* keys[2], int* vals[2], uint32_t* ghist, int n, int passes, hipStream_t s) {
+  const int nb = (int)(((long long)n + RADIX_TILE - 1) / RADIX_TILE);
+  int cur = 0;
+  for (int pass = 0; pass < passes; ++pass) {
+    k_radix_hist<<<nb, 256, 0, s>>>(keys[cur], n, 8 * pass, ghist, nb);
+    k_scan_excl<<<1, 1024, 0, s>>>(ghist, 256 * nb);
+    k_radix_scatter<<<nb, 256, 0, s>>>(keys[cur], pass == 0 ? nullptr : vals[cur], n, 8 * pass, ghist, nb,
+                                       keys[cur ^ 1], vals[cur ^ 1]);
+    cur ^= 1;
+  }
+  return hipGetLastError() == hipSuccess ? cur : -1;
+}
+
+hipError_t launch_cell_ptr(const uint32_t* sorted_keys, int n, int keyspace, int* cell_ptr, hipStream_t s) {
+  k_cell_ptr<<<blocks((long long)keyspace + 1, 256), 256, 0, s>>>(sorted_keys, n, keyspace, cell_ptr);
+  return hipGetLastError();
+}
+
 hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, hipStream_t s) {
   const int n = g.N, nb = p.radix_blocks;
   k_starts_keys<<<blocks(n, 256), 256, 0, s>>>(off, g, p.starts, p.keys[0]);

@@ -1,0 +1,681 @@
+// Sampled windows of 3D Deformable Slide Attention (MegaSlide-DiT, section "3D
+// Deformable Slide Attention": keys and values sampled at real offset positions by
+// trilinear interpolation, softmax over the kt x kh x kw samples, Eq. (1) attention
+// term; the implementation paragraph samples with grid_sample, bilinear mode, 5-D).
+//
+// A sample at position P (token units along t, y, x) blends the 8 grid rows
+// floor(P) + {0,1}^3 with weights prod_d (bit_d ? f_d : 1 - f_d), f = P - floor(P);
+// rows outside the grid are zero.  Two ways of placing sample (u, v, w) of the query
+// at p, with offsets o read at element strides (sn, sh, ss) per token, head, sample:
+//   box:  one offset per (query, head); s_d = clamp(p_d + o_d - (k_d - 1)/2, 0, G_d - k_d)
+//         and the sample sits at s + (u, v, w)  (integer offsets: the integer windows);
+//   free: the sample sits at p + (u, v, w) - (k - 1)/2 + its own offset.
+// Positions are kept as integer part plus fraction: the fraction of p + integer + o is
+// o - floor(o), exact in fp32, so the weights do not lose bits at large coordinates.
+//
+// Kernels (all VALU and gathers: with per-sample positions there is no shared key tile
+// for matrix cores to work on):
+//   forward     one wave per (query, head); D/8 lanes per sample (8 elements a lane),
+//               64/(D/8) samples in flight, an online softmax per lane group, groups
+//               merged at the end; writes O and the log-sum-exp.
+//   dQ side     the same mapping: recomputes the weights from the log-sum-exp, Delta =
+//               dO . O, dz = alpha (dO . v~ - Delta); writes dQ, the offset gradient of
+//               every sample (through the interpolation weights) and, per sample, alpha
+//               and scale * dz for the key side.
+//   dK/dV side  deterministic, no atomics: samples are sorted (stable radix sort) by
+//               (head, floor(P)); the wave of key m visits the 8 cells m - {0,1}^3 in a
+//               fixed order and their samples in sorted order, adding w alpha dO and
+//               w scale dz q.
+//   offsets     the per-sample gradients summed over the heads / samples that share an
+//               offset entry, in a fixed order.
+#include <math.h>
+
+#include "dsa3d.h"
+#include "internal.hpp"
+
+namespace dsa3d {
+
+struct SGeom {
+  int F, Hp, Wp;
+  int kt, ky, kx, K;
+  int H, N;
+  int mode;               // DSA3D_SAMPLE_BOX / DSA3D_SAMPLE_FREE
+  long long sn, sh, ss;   // offset strides in floats (0 = shared)
+  float scale;
+};
+
+constexpr int EL = 8;  // row elements per lane
+
+__device__ __forceinline__ void load8(const u16* p, float* x) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* x) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void store8(u16* p, const float* x) {
+  store4(p, x[0], x[1], x[2], x[3]);
+  store4(p + 4, x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void store8(float* p, const float* x) {
+  store4(p, x[0], x[1], x[2], x[3]);
+  store4(p + 4, x[4], x[5], x[6], x[7]);
+}
+
+__device__ __forceinline__ float dot8(const float* a, const float* b) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < EL; ++i) s = fmaf(a[i], b[i], s);
+  return s;
+}
+
+// Sum over the G lanes of a sample group (G a power of two; the masks stay inside it).
+template <int G>
+__device__ __forceinline__ float gsum(float v) {
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Box start along one axis: integer part, fraction, and whether the clamp is inactive
+// (the start then moves with the offset).  |o| <= 2G gives the same start as any larger
+// offset and keeps the integer part in range.
+__device__ __forceinline__ void box_axis(int p, float o, int k, int G, int& si, float& sf, bool& active) {
+  o = fminf(fmaxf(o, -2.f * G), 2.f * G);
+  const float fl = floorf(o);
+  const int xi = p - (k - 1) / 2 + (int)fl;
+  const float xf = o - fl;
+  if (xi < 0) {
+    si = 0; sf = 0.f; active = false;
+  } else if (xi > G - k || (xi == G - k && xf > 0.f)) {
+    si = G - k; sf = 0.f; active = false;
+  } else {
+    si = xi; sf = xf;
+    active = (xi > 0 || xf > 0.f) && xi < G - k;
+  }
+}
+
+struct QPos {
+  int p[3];       // query position
+  int si[3];      // box: start (integer part)
+  float sf[3];    //      start (fraction)
+  bool act[3];    //      clamp inactive
+  const float* o; // offsets of (query, head)
+};
+
+__device__ __forceinline__ QPos query_pos(const SGeom& g, const float* off, int n, int h) {
+  QPos q;
+  const int plane = g.Hp * g.Wp;
+  q.p[0] = n / plane;
+  q.p[1] = (n - q.p[0] * plane) / g.Wp;
+  q.p[2] = n - q.p[0] * plane - q.p[1] * g.Wp;
+  q.o = off + (long long)n * g.sn + (long long)h * g.sh;
+  if (g.mode == DSA3D_SAMPLE_BOX) {
+    box_axis(q.p[0], q.o[0], g.kt, g.F, q.si[0], q.sf[0], q.act[0]);
+    box_axis(q.p[1], q.o[1], g.ky, g.Hp, q.si[1], q.sf[1], q.act[1]);
+    box_axis(q.p[2], q.o[2], g.kx, g.Wp, q.si[2], q.sf[2], q.act[2]);
+  }
+  return q;
+}
+
+// Position of sample j: floor (i) and fraction (f) per axis.
+__device__ __forceinline__ void sample_pos(const SGeom& g, const QPos& q, int j, int* i, float* f) {
+  const int u = j / (g.ky * g.kx), r = j - u * (g.ky * g.kx), v = r / g.kx, w = r - v * g.kx;
+  const int lat[3] = {u, v, w};
+  if (g.mode == DSA3D_SAMPLE_BOX) {
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      i[d] = q.si[d] + lat[d];
+      f[d] = q.sf[d];
+    }
+  } else {
+    const int kk[3] = {g.kt, g.ky, g.kx};
+    const int G[3] = {g.F, g.Hp, g.Wp};
+    const float* o = q.o + (long long)j * g.ss;
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      const float od = fminf(fmaxf(o[d], -2.f * G[d] - kk[d]), 2.f * G[d] + kk[d]);
+      const float fl = floorf(od);
+      i[d] = q.p[d] + lat[d] - (kk[d] - 1) / 2 + (int)fl;
+      f[d] = od - fl;
+    }
+  }
+}
+
+// Corner c (bits t, y, x) of a sample: token (-1 outside the grid) and weight.
+__device__ __forceinline__ int corner_tok(const SGeom& g, const int* i, int c) {
+  const int t = i[0] + ((c >> 2) & 1), y = i[1] + ((c >> 1) & 1), x = i[2] + (c & 1);
+  if ((unsigned)t >= (unsigned)g.F || (unsigned)y >= (unsigned)g.Hp || (unsigned)x >= (unsigned)g.Wp) return -1;
+  return (t * g.Hp + y) * g.Wp + x;
+}
+__device__ __forceinline__ float corner_w(const float* f, int c) {
+  const float a = (c & 4) ? f[0] : 1.f - f[0];
+  const float b = (c & 2) ? f[1] : 1.f - f[1];
+  const float e = (c & 1) ? f[2] : 1.f - f[2];
+  return a * b * e;
+}
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_sampled_fwd(const T* __restrict__ q, const T* __restrict__ k,
+                                                     const T* __restrict__ v, const float* __restrict__ off,
+                                                     T* __restrict__ out, float* __restrict__ lse, SGeom g) {
+  constexpr int G = D / EL, NG = 64 / G;
+  const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wv >= (long long)g.N * g.H) return;
+  const int n = (int)(wv / g.H), h = (int)(wv - (long long)n * g.H);
+  const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
+  const size_t row = ((size_t)n * g.H + h) * D + gl * EL;
+  float qf[EL];
+  load8(q + row, qf);
+  const float sl2 = g.scale * LOG2E;
+  const QPos qp = query_pos(g, off, n, h);
+
+  float m = -INFINITY, l = 0.f, acc[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) acc[e] = 0.f;
+  for (int j = grp; j < g.K; j += NG) {
+    int i[3];
+    float f[3];
+    sample_pos(g, qp, j, i, f);
+    float ks[EL], vs[EL], x[EL];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) ks[e] = vs[e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int tok = corner_tok(g, i, c);
+      const float w = corner_w(f, c);
+      if (tok < 0 || w == 0.f) continue;
+      const size_t r = ((size_t)tok * g.H + h) * D + gl * EL;
+      load8(k + r, x);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) ks[e] = fmaf(w, x[e], ks[e]);
+      load8(v + r, x);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) vs[e] = fmaf(w, x[e], vs[e]);
+    }
+    const float s = gsum<G>(dot8(qf, ks)) * sl2;
+    const float mn = fmaxf(m, s);
+    const float a = exp2f(m - mn), p = exp2f(s - mn);
+    l = l * a + p;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] = fmaf(p, vs[e], acc[e] * a);
+    m = mn;
+  }
+  // merge the lane groups (a fixed tree)
+#pragma unroll
+  for (int mask = G; mask < 64; mask <<= 1) {
+    const float m2 = __shfl_xor(m, mask, 64), l2 = __shfl_xor(l, mask, 64);
+    const float mn = fmaxf(m, m2);
+    const float a1 = m == -INFINITY ? 0.f : exp2f(m - mn), a2 = m2 == -INFINITY ? 0.f : exp2f(m2 - mn);
+    l = l * a1 + l2 * a2;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] = acc[e] * a1 + __shfl_xor(acc[e], mask, 64) * a2;
+    m = mn;
+  }
+  if (grp == 0) {
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] *= inv;
+    store8(out + row, acc);
+    if (gl == 0) lse[(size_t)h * g.N + n] = (m + log2f(l)) * LN2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward, query side: dQ, per-sample coefficients, offset gradients
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_sampled_bwd_q(const T* __restrict__ q, const T* __restrict__ k,
+                                                       const T* __restrict__ v, const T* __restrict__ o,
+                                                       const T* __restrict__ dout, const float* __restrict__ lse,
+                                                       const float* __restrict__ off, T* __restrict__ dq,
+                                                       float* __restrict__ coef_a, float* __restrict__ coef_g,
+                                                       float* __restrict__ gpos, SGeom g) {
+  constexpr int G = D / EL, NG = 64 / G;
+  const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wv >= (long long)g.N * g.H) return;
+  const int n = (int)(wv / g.H), h = (int)(wv - (long long)n * g.H);
+  const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
+  const size_t row = ((size_t)n * g.H + h) * D + gl * EL;
+  float qf[EL], df[EL], x[EL];
+  load8(q + row, qf);
+  load8(dout + row, df);
+  load8(o + row, x);
+  const float delta = gsum<G>(dot8(df, x));
+  const float sl2 = g.scale * LOG2E;
+  const float l2 = lse[(size_t)h * g.N + n] * LOG2E;
+  const QPos qp = query_pos(g, off, n, h);
+  const size_t e0 = ((size_t)h * g.N + n) * g.K;
+
+  float dqa[EL], gb[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < EL; ++e) dqa[e] = 0.f;
+  for (int j = grp; j < g.K; j += NG) {
+    int i[3];
+    float f[3];
+    sample_pos(g, qp, j, i, f);
+    float ks[EL], vs[EL], kd[3][EL], vd[3][EL];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      ks[e] = vs[e] = 0.f;
+      kd[0][e] = kd[1][e] = kd[2][e] = vd[0][e] = vd[1][e] = vd[2][e] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int tok = corner_tok(g, i, c);
+      if (tok < 0) continue;
+      const float pt = (c & 4) ? f[0] : 1.f - f[0], py = (c & 2) ? f[1] : 1.f - f[1],
+                  px = (c & 1) ? f[2] : 1.f - f[2];
+      const float w = pt * py * px;
+      const float dw[3] = {((c & 4) ? 1.f : -1.f) * py * px, ((c & 2) ? 1.f : -1.f) * pt * px,
+                           ((c & 1) ? 1.f : -1.f) * pt * py};
+      const size_t r = ((size_t)tok * g.H + h) * D + gl * EL;
+      load8(k + r, x);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        ks[e] = fmaf(w, x[e], ks[e]);
+        kd[0][e] = fmaf(dw[0], x[e], kd[0][e]);
+        kd[1][e] = fmaf(dw[1], x[e], kd[1][e]);
+        kd[2][e] = fmaf(dw[2], x[e], kd[2][e]);
+      }
+      load8(v + r, x);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        vs[e] = fmaf(w, x[e], vs[e]);
+        vd[0][e] = fmaf(dw[0], x[e], vd[0][e]);
+        vd[1][e] = fmaf(dw[1], x[e], vd[1][e]);
+        vd[2][e] = fmaf(dw[2], x[e], vd[2][e]);
+      }
+    }
+    const float z = gsum<G>(dot8(qf, ks));
+    const float da = gsum<G>(dot8(df, vs));
+    float qk[3], dv_[3];
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      qk[d] = gsum<G>(dot8(qf, kd[d]));
+      dv_[d] = gsum<G>(dot8(df, vd[d]));
+    }
+    const float alpha = exp2f(z * sl2 - l2);
+    const float gz = g.scale * alpha * (da - delta);  // scale * dz
+#pragma unroll
+    for (int e = 0; e < EL; ++e) dqa[e] = fmaf(gz, ks[e], dqa[e]);
+    float gp[3];
+#pragma unroll
+    for (int d = 0; d < 3; ++d) gp[d] = gz * qk[d] + alpha * dv_[d];
+    if (gl == 0) {
+      coef_a[e0 + j] = alpha;
+      coef_g[e0 + j] = gz;
+      if (g.mode == DSA3D_SAMPLE_FREE) {
+        float* gq = gpos + (e0 + j) * 3;
+        gq[0] = gp[0]; gq[1] = gp[1]; gq[2] = gp[2];
+      }
+    }
+    gb[0] += gp[0]; gb[1] += gp[1]; gb[2] += gp[2];
+  }
+#pragma unroll
+  for (int mask = G; mask < 64; mask <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EL; ++e) dqa[e] += __shfl_xor(dqa[e], mask, 64);
+#pragma unroll
+    for (int d = 0; d < 3; ++d) gb[d] += __shfl_xor(gb[d], mask, 64);
+  }
+  if (grp == 0) {
+    store8(dq + row, dqa);
+    if (g.mode == DSA3D_SAMPLE_BOX && gl == 0) {
+      float* gq = gpos + ((size_t)h * g.N + n) * 3;
+#pragma unroll
+      for (int d = 0; d < 3; ++d) gq[d] = qp.act[d] ? gb[d] : 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward, key side
+// ---------------------------------------------------------------------------
+// Sort key of sample e = (h * N + n) * K + j: (head, base cell floor(P) + 1), base cells
+// in [-1, G-1] per axis; samples whose 8 corners all lie outside the grid get the
+// sentinel H * ncell and are never visited.
+__global__ __launch_bounds__(256) void k_sampled_keys(const float* __restrict__ off, SGeom g,
+                                                      uint32_t* __restrict__ keys) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long E = (long long)g.N * g.H * g.K;
+  if (e >= E) return;
+  const int j = (int)(e % g.K);
+  const long long hn = e / g.K;
+  const int n = (int)(hn % g.N), h = (int)(hn / g.N);
+  const QPos qp = query_pos(g, off, n, h);
+  int i[3];
+  float f[3];
+  sample_pos(g, qp, j, i, f);
+  const int ncell = (g.F + 1) * (g.Hp + 1) * (g.Wp + 1);
+  uint32_t key = (uint32_t)g.H * ncell;
+  if (i[0] >= -1 && i[0] < g.F && i[1] >= -1 && i[1] < g.Hp && i[2] >= -1 && i[2] < g.Wp)
+    key = (uint32_t)(h * ncell + ((i[0] + 1) * (g.Hp + 1) + (i[1] + 1)) * (g.Wp + 1) + (i[2] + 1));
+  keys[e] = key;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_sampled_dkdv(const T* __restrict__ q, const T* __restrict__ dout,
+                                                      const float* __restrict__ off, const int* __restrict__ ids,
+                                                      const int* __restrict__ cell_ptr,
+                                                      const float* __restrict__ coef_a,
+                                                      const float* __restrict__ coef_g, T* __restrict__ dk,
+                                                      T* __restrict__ dv, SGeom g) {
+  constexpr int G = D / EL, NG = 64 / G;
+  const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wv >= (long long)g.N * g.H) return;
+  const int m = (int)(wv / g.H), h = (int)(wv - (long long)m * g.H);
+  const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
+  const int plane = g.Hp * g.Wp;
+  const int mt = m / plane, my = (m - mt * plane) / g.Wp, mx = m - mt * plane - my * g.Wp;
+  const int ncell = (g.F + 1) * (g.Hp + 1) * (g.Wp + 1);
+
+  float dka[EL], dva[EL], x[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) dka[e] = dva[e] = 0.f;
+  for (int c = 0; c < 8; ++c) {
+    // samples whose corner c is key m have base cell m - bits(c)
+    const int bt = (c >> 2) & 1, by = (c >> 1) & 1, bx = c & 1;
+    const int cell = h * ncell + ((mt - bt + 1) * (g.Hp + 1) + (my - by + 1)) * (g.Wp + 1) + (mx - bx + 1);
+    const int beg = cell_ptr[cell], end = cell_ptr[cell + 1];
+    for (int it = beg + grp; it < end; it += NG) {
+      const int e = ids[it];
+      const int j = e % g.K;
+      const int n = (e / g.K) % g.N;
+      const QPos qp = query_pos(g, off, n, h);
+      int i[3];
+      float f[3];
+      sample_pos(g, qp, j, i, f);
+      const float w = corner_w(f, c);
+      const float a = w * coef_a[e], gz = w * coef_g[e];
+      const size_t r = ((size_t)n * g.H + h) * D + gl * EL;
+      load8(dout + r, x);
+#pragma unroll
+      for (int t = 0; t < EL; ++t) dva[t] = fmaf(a, x[t], dva[t]);
+      load8(q + r, x);
+#pragma unroll
+      for (int t = 0; t < EL; ++t) dka[t] = fmaf(gz, x[t], dka[t]);
+    }
+  }
+#pragma unroll
+  for (int mask = G; mask < 64; mask <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      dka[e] += __shfl_xor(dka[e], mask, 64);
+      dva[e] += __shfl_xor(dva[e], mask, 64);
+    }
+  }
+  if (grp == 0) {
+    const size_t r = ((size_t)m * g.H + h) * D + gl * EL;
+    store8(dk + r, dka);
+    store8(dv + r, dva);
+  }
+}
+
+// Offset gradients in the caller's layout: entry (n, ho, jo) sums the per-sample (free)
+// or per-(query, head) (box) gradients over the heads (sh == 0) and samples (ss == 0)
+// that share it, heads then samples in ascending order.
+__global__ __launch_bounds__(256) void k_sampled_doff(const float* __restrict__ gpos, float* __restrict__ doff,
+                                                      SGeom g) {
+  const int hb = g.sh == 0 ? 1 : g.H;
+  const int kb = (g.mode == DSA3D_SAMPLE_BOX || g.ss == 0) ? 1 : g.K;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long long)g.N * hb * kb) return;
+  const int jo = (int)(t % kb);
+  const long long r = t / kb;
+  const int ho = (int)(r % hb), n = (int)(r / hb);
+  float s[3] = {0.f, 0.f, 0.f};
+  for (int h = (hb == 1 ? 0 : ho); h < (hb == 1 ? g.H : ho + 1); ++h) {
+    if (g.mode == DSA3D_SAMPLE_BOX) {
+      const float* p = gpos + ((size_t)h * g.N + n) * 3;
+      s[0] += p[0]; s[1] += p[1]; s[2] += p[2];
+    } else {
+      for (int j = (kb == 1 ? 0 : jo); j < (kb == 1 ? g.K : jo + 1); ++j) {
+        const float* p = gpos + (((size_t)h * g.N + n) * g.K + j) * 3;
+        s[0] += p[0]; s[1] += p[1]; s[2] += p[2];
+      }
+    }
+  }
+  float* d = doff + (long long)n * g.sn + (long long)ho * g.sh + (long long)jo * g.ss;
+  d[0] = s[0]; d[1] = s[1]; d[2] = s[2];
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct SampledWs {
+  uint32_t* keys[2];
+  int* vals[2];
+  uint32_t* ghist;
+  int* cell_ptr;
+  float* coef_a;
+  float* coef_g;
+  float* gpos;
+  int passes;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t sampled_layout(const SGeom& g, char* base, SampledWs* w) {
+  const size_t E = (size_t)g.N * g.H * g.K;
+  const size_t nb = (E + RADIX_TILE - 1) / RADIX_TILE;
+  const size_t ncell = (size_t)(g.F + 1) * (g.Hp + 1) * (g.Wp + 1);
+  const size_t keyspace = ncell * g.H;
+  int bits = 1;
+  while (((size_t)1 << bits) <= keyspace) ++bits;  // the sentinel H * ncell sorts last
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  SampledWs s;
+  s.keys[0] = (uint32_t*)take(E * 4);
+  s.keys[1] = (uint32_t*)take(E * 4);
+  s.vals[0] = (int*)take(E * 4);
+  s.vals[1] = (int*)take(E * 4);
+  s.ghist = (uint32_t*)take(256 * nb * 4);
+  s.cell_ptr = (int*)take((keyspace + 1) * 4);
+  s.coef_a = (float*)take(E * 4);
+  s.coef_g = (float*)take(E * 4);
+  s.gpos = (float*)take((g.mode == DSA3D_SAMPLE_BOX ? (size_t)g.N * g.H : E) * 3 * 4);
+  s.passes = (bits + 7) / 8;
+  if (w) *w = s;
+  return off;
+}
+
+static unsigned nblocks(long long n, int per) { return (unsigned)((n + per - 1) / per); }
+
+template <typename T, int D>
+static hipError_t sampled_fwd_impl(const void* q, const void* k, const void* v, const float* off, void* out,
+                                   float* lse, const SGeom& g, hipStream_t s) {
+  k_sampled_fwd<T, D><<<nblocks((long long)g.N * g.H, 4), 256, 0, s>>>(
+      (const T*)q, (const T*)k, (const T*)v, off, (T*)out, lse, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_sampled_forward(int dtype, int D, const void* q, const void* k, const void* v, const float* off,
+                                  void* out, float* lse, const SGeom& g, hipStream_t s) {
+  if (dtype == DSA3D_BF16)
+    return D == 64 ? sampled_fwd_impl<u16, 64>(q, k, v, off, out, lse, g, s)
+                   : sampled_fwd_impl<u16, 128>(q, k, v, off, out, lse, g, s);
+  return D == 64 ? sampled_fwd_impl<float, 64>(q, k, v, off, out, lse, g, s)
+                 : sampled_fwd_impl<float, 128>(q, k, v, off, out, lse, g, s);
+}
+
+template <typename T, int D>
+static hipError_t sampled_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, const float* off, void* dq, void* dk, void* dv, float* doff,
+                                   const SGeom& g, const SampledWs& w, hipStream_t s) {
+  const long long E = (long long)g.N * g.H * g.K;
+  const long long waves = (long long)g.N * g.H;
+  k_sampled_keys<<<nblocks(E, 256), 256, 0, s>>>(off, g, w.keys[0]);
+  uint32_t* keys[2] = {w.keys[0], w.keys[1]};
+  int* vals[2] = {w.vals[0], w.vals[1]};
+  const int cur = radix_sort(keys, vals, w.ghist, (int)E, w.passes, s);
+  if (cur < 0) return hipErrorLaunchFailure;
+  const int ncell = (g.F + 1) * (g.Hp + 1) * (g.Wp + 1);
+  hipError_t e = launch_cell_ptr(keys[cur], (int)E, g.H * ncell, w.cell_ptr, s);
+  if (e != hipSuccess) return e;
+  k_sampled_bwd_q<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)k, (const T*)v, (const T*)o,
+                                                          (const T*)dout, lse, off, (T*)dq, w.coef_a, w.coef_g,
+                                                          w.gpos, g);
+  k_sampled_dkdv<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)dout, off, vals[cur], w.cell_ptr,
+                                                         w.coef_a, w.coef_g, (T*)dk, (T*)dv, g);
+  const long long nout = (long long)g.N * (g.sh == 0 ? 1 : g.H) *
+                         ((g.mode == DSA3D_SAMPLE_BOX || g.ss == 0) ? 1 : g.K);
+  k_sampled_doff<<<nblocks(nout, 256), 256, 0, s>>>(w.gpos, doff, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_sampled_backward(int dtype, int D, const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, const float* off, void* dq, void* dk,
+                                   void* dv, float* doff, const SGeom& g, char* workspace, hipStream_t s) {
+  SampledWs w;
+  sampled_layout(g, workspace, &w);
+  if (dtype == DSA3D_BF16)
+    return D == 64 ? sampled_bwd_impl<u16, 64>(q, k, v, o, dout, lse, off, dq, dk, dv, doff, g, w, s)
+                   : sampled_bwd_impl<u16, 128>(q, k, v, o, dout, lse, off, dq, dk, dv, doff, g, w, s);
+  return D == 64 ? sampled_bwd_impl<float, 64>(q, k, v, o, dout, lse, off, dq, dk, dv, doff, g, w, s)
+                 : sampled_bwd_impl<float, 128>(q, k, v, o, dout, lse, off, dq, dk, dv, doff, g, w, s);
+}
+
+}  // namespace dsa3d
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+using namespace dsa3d;
+
+namespace {
+
+bool odd_pos(int k) { return k >= 1 && (k & 1); }
+
+// Offsets layout: three consecutive floats per entry at element strides (sn, sh, ss)
+// >= 0, 0 meaning shared; the entries that are not shared must not overlap (checked as
+// a strided array: sorted by stride, each level starts past the extent of the one
+// inside it).  Box windows take one offset per (query, head): ss must be 0.
+bool layout_ok(long long sn, long long sh, long long ss, int N, int H, int K, int mode) {
+  if (sn < 3 || sh < 0 || ss < 0) return false;
+  if (mode == DSA3D_SAMPLE_BOX && ss != 0) return false;
+  struct Dim { long long stride, size; } d[3] = {{sn, N}, {sh, sh ? H : 1}, {ss, ss ? K : 1}};
+  for (int a = 0; a < 3; ++a)
+    for (int b = a + 1; b < 3; ++b)
+      if (d[b].stride < d[a].stride) { const Dim t = d[a]; d[a] = d[b]; d[b] = t; }
+  long long extent = 3;  // floats covered by one entry
+  for (int a = 0; a < 3; ++a) {
+    if (d[a].size == 1) continue;
+    if (d[a].stride < extent) return false;
+    extent = d[a].stride * (d[a].size - 1) + extent;
+  }
+  return true;
+}
+
+int check_sampled_geom(int mode, int F, int Hp, int Wp, int heads, int kt, int ky, int kx) {
+  if (mode != DSA3D_SAMPLE_BOX && mode != DSA3D_SAMPLE_FREE) return DSA3D_ERR_MODE;
+  if (F < 1 || Hp < 1 || Wp < 1 || heads < 1 || heads > 65535) return DSA3D_ERR_GRID;
+  if ((long long)F * Hp * Wp >= (1LL << 30)) return DSA3D_ERR_GRID;
+  if (!odd_pos(kt) || !odd_pos(ky) || !odd_pos(kx)) return DSA3D_ERR_WINDOW;
+  if (mode == DSA3D_SAMPLE_BOX && (kt > F || ky > Hp || kx > Wp)) return DSA3D_ERR_WINDOW;
+  if ((long long)kt * ky * kx > 4096) return DSA3D_ERR_WINDOW;
+  return DSA3D_OK;
+}
+
+SGeom make_sgeom(int mode, int F, int Hp, int Wp, int heads, int kt, int ky, int kx, long long sn, long long sh,
+                 long long ss, float scale) {
+  SGeom g;
+  g.F = F; g.Hp = Hp; g.Wp = Wp;
+  g.kt = kt; g.ky = ky; g.kx = kx; g.K = kt * ky * kx;
+  g.H = heads; g.N = F * Hp * Wp;
+  g.mode = mode;
+  g.sn = sn; g.sh = sh; g.ss = ss;
+  g.scale = scale;
+  return g;
+}
+
+int check_sampled(const void* q, const void* k, const void* v, const float* off, long long sn, long long sh,
+                  long long ss, int mode, int F, int Hp, int Wp, int heads, int head_dim, int kt, int ky, int kx,
+                  float scale, int dtype, SGeom* g) {
+  if (!q || !k || !v || !off) return DSA3D_ERR_NULL;
+  if (dtype != DSA3D_F32 && dtype != DSA3D_BF16) return DSA3D_ERR_DTYPE;
+  if (head_dim != 64 && head_dim != 128) return DSA3D_ERR_HEAD_DIM;
+  const int st = check_sampled_geom(mode, F, Hp, Wp, heads, kt, ky, kx);
+  if (st != DSA3D_OK) return st;
+  if (!isfinite(scale)) return DSA3D_ERR_SCALE;
+  if (!layout_ok(sn, sh, ss, F * Hp * Wp, heads, kt * ky * kx, mode)) return DSA3D_ERR_LAYOUT;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15u) return DSA3D_ERR_ALIGN;
+  if ((uintptr_t)off & 3u) return DSA3D_ERR_ALIGN;
+  *g = make_sgeom(mode, F, Hp, Wp, heads, kt, ky, kx, sn, sh, ss, scale);
+  return DSA3D_OK;
+}
+
+// the backward sorts N * H * K samples with 32-bit indices and (H * cells) 32-bit keys
+bool backward_fits(const SGeom& g) {
+  const long long E = (long long)g.N * g.H * g.K;
+  const long long cells = (long long)(g.F + 1) * (g.Hp + 1) * (g.Wp + 1) * g.H;
+  return E < (1LL << 31) && cells < (1LL << 31) - 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa3d_sampled_workspace_bytes(int F, int Hp, int Wp, int heads, int kt, int ky, int kx, int mode,
+                                     int backward) {
+  if (check_sampled_geom(mode, F, Hp, Wp, heads, kt, ky, kx) != DSA3D_OK) return 0;
+  if (!backward) return 256;  // the forward needs no scratch
+  // the layout depends on the geometry and the mode only
+  const SGeom g = make_sgeom(mode, F, Hp, Wp, heads, kt, ky, kx, 3, 0, 0, 1.f);
+  if (!backward_fits(g)) return 0;
+  return sampled_layout(g, nullptr, nullptr);
+}
+
+int dsa3d_sampled_forward(const void* q, const void* k, const void* v, const float* offsets, long long stride_token,
+                          long long stride_head, long long stride_sample, int mode, int F, int Hp, int Wp, int heads,
+                          int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out, float* lse,
+                          hipStream_t stream) {
+  SGeom g;
+  const int st = check_sampled(q, k, v, offsets, stride_token, stride_head, stride_sample, mode, F, Hp, Wp, heads,
+                               head_dim, kt, ky, kx, scale, dtype, &g);
+  if (st != DSA3D_OK) return st;
+  if (!out || !lse) return DSA3D_ERR_NULL;
+  if (((uintptr_t)out & 15u) || ((uintptr_t)lse & 3u)) return DSA3D_ERR_ALIGN;
+  return launch_sampled_forward(dtype, head_dim, q, k, v, offsets, out, lse, g, stream) == hipSuccess
+             ? DSA3D_OK
+             : DSA3D_ERR_LAUNCH;
+}
+
+int dsa3d_sampled_backward(const void* q, const void* k, const void* v, const float* offsets, long long stride_token,
+                           long long stride_head, long long stride_sample, int mode, const void* out,
+                           const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,
+                           int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, float* doffsets,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  SGeom g;
+  const int st = check_sampled(q, k, v, offsets, stride_token, stride_head, stride_sample, mode, F, Hp, Wp, heads,
+                               head_dim, kt, ky, kx, scale, dtype, &g);
+  if (st != DSA3D_OK) return st;
+  if (!out || !lse || !dout || !dq || !dk || !dv || !doffsets || !workspace) return DSA3D_ERR_NULL;
+  if (((uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) &
+      15u)
+    return DSA3D_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)doffsets) & 3u) return DSA3D_ERR_ALIGN;
+  if (!backward_fits(g)) return DSA3D_ERR_GRID;
+  if (workspace_bytes < sampled_layout(g, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
+  return launch_sampled_backward(dtype, head_dim, q, k, v, out, dout, lse, offsets, dq, dk, dv, doffsets, g,
+                                 static_cast<char*>(workspace), stream) == hipSuccess
+             ? DSA3D_OK
+             : DSA3D_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -45,10 +45,16 @@ def load():
         lib.dsa3d_forward_ex.argtypes = fwd + [u32, vp]
         lib.dsa3d_backward_ex.argtypes = bwd + [u32, vp]
         lib.dsa3d_forward_static.argtypes = [vp, vp, vp, vp] + [i32] * 8 + [f32, i32, vp, vp, vp]
+        i64 = ctypes.c_longlong
+        lib.dsa3d_sampled_workspace_bytes.argtypes = [i32] * 9
+        lib.dsa3d_sampled_workspace_bytes.restype = sz
+        lib.dsa3d_sampled_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64] + [i32] * 9 + [f32, i32, vp, vp, vp]
+        lib.dsa3d_sampled_backward.argtypes = ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, vp] + [i32] * 8 +
+                                               [f32, i32, vp, vp, vp, vp, vp, sz, vp])
         lib.dsa3d_forward_heads.argtypes = fwd + [u32]
         lib.dsa3d_backward_heads.argtypes = bwd + [u32]
         for f in ("dsa3d_forward", "dsa3d_backward", "dsa3d_forward_ex", "dsa3d_backward_ex", "dsa3d_forward_static",
-                  "dsa3d_forward_heads", "dsa3d_backward_heads"):
+                  "dsa3d_forward_heads", "dsa3d_backward_heads", "dsa3d_sampled_forward", "dsa3d_sampled_backward"):
             getattr(lib, f).restype = i32
         lib.dsa3d_status_string.argtypes = [i32]
         lib.dsa3d_status_string.restype = ctypes.c_char_p
@@ -222,6 +228,93 @@ def backward(q, k, v, offsets, out, lse, dout, grid, window, scale=None, dq=None
     else:
         _check(load().dsa3d_backward_ex(*args, None), "dsa3d_backward")
     return dq, dk, dv
+
+
+# ---- sampled windows (real offsets, trilinear sampling) ---------------------------------
+SAMPLE_MODES = {"box": 0, "free": 1}
+
+
+def _sampled_layout(offsets, N, H, K, mode):
+    """Element strides (token, head, sample) of float32 offsets broadcastable to (N, H, 3)
+    (box) or (N, H, K, 3) (free); the last axis must be contiguous."""
+    if not isinstance(offsets, torch.Tensor) or offsets.dtype != torch.float32:
+        raise DSA3DError("offsets must be a float32 tensor")
+    want = (N, H, 3) if mode == "box" else (N, H, K, 3)
+    if offsets.dim() != len(want):
+        raise DSA3DError(f"{mode} offsets must have {len(want)} axes, broadcastable to {want}")
+    try:
+        full = offsets.expand(*want)
+    except RuntimeError as e:
+        raise DSA3DError(f"offsets of shape {tuple(offsets.shape)} do not broadcast to {want}") from e
+    st = full.stride()
+    if st[-1] != 1:
+        raise DSA3DError("offsets: the (dt, dy, dx) axis must be contiguous")
+    return st[0], st[1], (st[2] if mode == "free" else 0)
+
+
+def sampled_workspace_bytes(grid, heads, window, mode, backward=True):
+    return int(load().dsa3d_sampled_workspace_bytes(*grid, heads, *window, SAMPLE_MODES[mode], int(bool(backward))))
+
+
+def sampled_forward(q, k, v, offsets, grid, window, mode, scale=None, out=None, lse=None):
+    """Sampled windows (dsa3d_sampled_forward).  mode "box" (one offset per (query, head),
+    offsets broadcastable to [N, H, 3]) or "free" (per-sample offsets broadcastable to
+    [N, H, K, 3]); offsets float32.  Returns (out [N, H, D], lse [H, N] float32)."""
+    N, H, D = _shape(q, grid)
+    if mode not in SAMPLE_MODES:
+        raise DSA3DError(f"mode must be one of {list(SAMPLE_MODES)}")
+    K = window[0] * window[1] * window[2]
+    for t, name in ((k, "k"), (v, "v")):
+        _want(t, name, q.shape, q.dtype)
+    sn, sh, ss = _sampled_layout(offsets, N, H, K, mode)
+    if out is not None:
+        _want(out, "out", q.shape, q.dtype)
+    if lse is not None:
+        _want(lse, "lse", (H, N), torch.float32)
+    if scale is None:
+        scale = D ** -0.5
+    dev = q.device
+    ptrs = [_dev(t, n, dev) for t, n in ((q, "q"), (k, "k"), (v, "v"))]
+    if not offsets.is_cuda or offsets.device != dev:
+        raise DSA3DError("offsets must be on q's GPU")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(load().dsa3d_sampled_forward(*ptrs, offsets.data_ptr(), sn, sh, ss, SAMPLE_MODES[mode], *grid, H, D,
+                                        *window, float(scale), _dtype_code(q), _dev(out, "out", dev),
+                                        _dev(lse, "lse", dev), _stream()), "dsa3d_sampled_forward")
+    return out, lse
+
+
+def sampled_backward(q, k, v, offsets, out, lse, dout, grid, window, mode, scale=None, ws=None):
+    """Returns (dq, dk, dv, doffsets); doffsets has the shape and strides of `offsets`, each
+    entry the gradient summed over the heads / samples that share it."""
+    N, H, D = _shape(q, grid)
+    if mode not in SAMPLE_MODES:
+        raise DSA3DError(f"mode must be one of {list(SAMPLE_MODES)}")
+    K = window[0] * window[1] * window[2]
+    for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _want(t, name, q.shape, q.dtype)
+    _want(lse, "lse", (H, N), torch.float32)
+    sn, sh, ss = _sampled_layout(offsets, N, H, K, mode)
+    if scale is None:
+        scale = D ** -0.5
+    dev = q.device
+    ptrs = [_dev(t, n, dev) for t, n in ((q, "q"), (k, "k"), (v, "v"))]
+    if not offsets.is_cuda or offsets.device != dev:
+        raise DSA3DError("offsets must be on q's GPU")
+    rest = [_dev(t, n, dev) for t, n in ((out, "out"), (lse, "lse"), (dout, "dout"))]
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    doff = torch.empty_strided(offsets.shape, offsets.stride(), dtype=torch.float32, device=dev)
+    if ws is None:
+        n = sampled_workspace_bytes(grid, H, window, mode, True)
+        if n == 0:
+            raise DSA3DError("sampled backward: geometry past the limits (N * heads * K < 2^31)")
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    _check(load().dsa3d_sampled_backward(*ptrs, offsets.data_ptr(), sn, sh, ss, SAMPLE_MODES[mode], *rest, *grid, H,
+                                         D, *window, float(scale), _dtype_code(q), dq.data_ptr(), dk.data_ptr(),
+                                         dv.data_ptr(), doff.data_ptr(), _dev(ws, "workspace", dev), ws.numel(),
+                                         _stream()), "dsa3d_sampled_backward")
+    return dq, dk, dv, doff
 
 
 class DSA3DFunction(torch.autograd.Function):
