@@ -8,8 +8,15 @@ One step = dsa3d_forward + dsa3d_backward over the whole grid.  Prints one JSON 
              and work lists (+ Delta in the backward), then each attention kernel
   value      query-token-heads per second (N * heads / step time)
   roofline   the dominant kernel's algorithmic bytes per launch / its mean duration,
-             timed with HIP events on the library's stream, against 8 TB/s HBM
-  cpu_baseline  the CPU oracle (fp64, OpenMP) on the first 5 frames of the same workload
+             timed with HIP events on the library's stream, against 8 TB/s HBM (and
+             against the measured streaming-read peak)
+  cpu_baseline  the CPU oracle (fp64, OpenMP) on the first 5 frames of the same workload,
+             forward and backward timed separately, with the host CPU model
+  peaks      measured on this GPU: bf16 matrix-core loop, streaming read and copy
+  linear_in_n  the same step on the first 64 and 128 frames (time linear in N)
+  variants   the other forms of the operator on their own workloads, fwd+bwd: per-head
+             integer offsets (256-frame workload), box windows with one real offset per
+             query, free per-sample real offsets (16 x 32 x 32, 3 x 7 x 7)
 """
 import argparse
 import ctypes
@@ -38,6 +45,8 @@ class Hip:
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.restype = ctypes.c_int
 
     def events(self, n):
         arr = (ctypes.c_void_p * n)()
@@ -97,9 +106,20 @@ def measured_traffic(kernel, workload):
         return None
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl_full, frames=5):
     """The oracle on the first `frames` frames of the workload (same heads, head size,
-    window, generator words), fwd + bwd, wall time on this host's cores."""
+    window, generator words), forward and backward timed separately, wall time on this
+    host's cores."""
     import oracle
     from local_sparse_attention_amd import synth
 
@@ -108,13 +128,167 @@ def cpu_baseline(wl_full, frames=5):
     grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
     t0 = time.perf_counter()
     oracle.forward(inp["q"], inp["k"], inp["v"], inp["offsets"], grid, window, wl.scale)
+    t1 = time.perf_counter()
     oracle.backward(inp["q"], inp["k"], inp["v"], inp["dout"], inp["offsets"], grid, window, wl.scale)
-    dt = time.perf_counter() - t0
+    t2 = time.perf_counter()
     cores = len(os.sched_getaffinity(0))
     threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
-    return {"value": wl.N * wl.heads / dt, "unit": "query-token-heads/s", "cores": threads, "kind": "oracle",
+    NH = wl.N * wl.heads
+    return {"value": NH / (t2 - t0), "unit": "query-token-heads/s", "cores": threads, "kind": "oracle",
             "sample": f"first {frames} of {wl_full.F} frames ({wl.N} tokens x {wl.heads} heads), fwd+bwd, "
-                      f"{dt:.1f} s wall"}
+                      f"{t2 - t0:.1f} s wall",
+            "fwd_s": t1 - t0, "bwd_s": t2 - t1, "fwd_value": NH / (t1 - t0), "bwd_value": NH / (t2 - t1),
+            "cpu_model": cpu_model()}
+
+
+def measure_peaks(lib, hip, stream_ptr):
+    """Measured peaks on this GPU: bf16 matrix-core loop, streaming read and copy."""
+    import torch
+
+    lib.dsa3d_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.dsa3d_peak_mfma_bf16.restype = ctypes.c_double
+    lib.dsa3d_peak_mfma32_bf16.argtypes = lib.dsa3d_peak_mfma_bf16.argtypes
+    lib.dsa3d_peak_mfma32_bf16.restype = ctypes.c_double
+    lib.dsa3d_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.dsa3d_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_void_p]
+    ev = hip.events(2)
+    blocks = 256 * 8
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    best = {}
+    for key, fn in (("mfma_16x16x32_tflops", lib.dsa3d_peak_mfma_bf16),
+                    ("mfma_32x32x16_tflops", lib.dsa3d_peak_mfma32_bf16)):
+        for _ in range(3):
+            hip.lib.hipEventRecord(ev[0], stream_ptr)
+            flops = fn(ctypes.c_void_p(out.data_ptr()), blocks, 4096, stream_ptr)
+            hip.lib.hipEventRecord(ev[1], stream_ptr)
+            assert flops > 0
+            best[key] = max(best.get(key, 0.0), flops / (hip.elapsed_ms(ev[0], ev[1]) / 1e3) / 1e12)
+    best["mfma_bf16_tflops"] = max(best["mfma_16x16x32_tflops"], best["mfma_32x32x16_tflops"])
+    nbytes = 4 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        hip.lib.hipEventRecord(ev[0], stream_ptr)
+        assert lib.dsa3d_peak_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), 4096,
+                                   stream_ptr) == 0
+        hip.lib.hipEventRecord(ev[1], stream_ptr)
+        best["read_gbs"] = max(best.get("read_gbs", 0.0), nbytes / (hip.elapsed_ms(ev[0], ev[1]) / 1e3) / 1e9)
+        hip.lib.hipEventRecord(ev[0], stream_ptr)
+        assert lib.dsa3d_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, 4096,
+                                   stream_ptr) == 0
+        hip.lib.hipEventRecord(ev[1], stream_ptr)
+        best["copy_gbs"] = max(best.get("copy_gbs", 0.0), 2 * nbytes / (hip.elapsed_ms(ev[0], ev[1]) / 1e3) / 1e9)
+    del src, dst, sink, out
+    torch.cuda.empty_cache()
+    best["note"] = ("best of 3: 2048 workgroups x 4 waves of independent bf16 MFMA chains (8 of 16x16x32, or 4 of "
+                    "32x32x16); 4 GiB streaming read / copy with 16-byte loads (copy counts read + write bytes)")
+    return best
+
+
+def sampled_flops(wl, fwd=True, bwd=True):
+    """Algorithmic fp32 VALU flops of sampled windows per launch: per (query, head, sample)
+    the forward blends 8 corner rows of K and of V (2 x 16D) and takes q . K~ and
+    alpha V~ (2 x 2D) = 36D; the backward recomputes K~, V~ and their dots (36D), takes
+    dQ += scale dz K~ (2D), the 8 corner dots q . k_c and dO . v_c of the position
+    gradient (32D) and scatters w alpha dO and w scale dz q to the 8 corners (32D) = 102D."""
+    per = (36 if fwd else 0) + (102 if bwd else 0)
+    return float(per) * wl.head_dim * wl.K * wl.N * wl.heads
+
+
+def _timed(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def dev_inputs(wl):
+    import torch
+
+    from local_sparse_attention_amd import synth
+
+    shape = (wl.N, wl.heads, wl.head_dim)
+    t = {}
+    for name, sid in (("q", 0), ("k", 1), ("v", 2), ("dout", 3)):
+        a = synth.normal(wl.seed, sid, shape, wl.dtype, wl.qkv_scale if name != "dout" else 1.0)
+        t[name] = torch.from_numpy(a.view("int16")).cuda().view(torch.bfloat16)
+        del a
+    return t
+
+
+def run_per_head(dsa3d, wl, t, out, lse, g, ws, steps, warmup):
+    """fwd+bwd with per-head integer offsets [H][N][3] on the given workload's tensors."""
+    import torch
+
+    from local_sparse_attention_amd import synth
+
+    grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
+    offh = torch.from_numpy(synth.make_head_offsets(wl)).cuda()
+
+    def step_heads():
+        dsa3d.forward(t["q"], t["k"], t["v"], offh, grid, window, wl.scale, out=out, lse=lse, ws=ws)
+        dsa3d.backward(t["q"], t["k"], t["v"], offh, out, lse, t["dout"], grid, window, wl.scale, dq=g[0], dk=g[1],
+                       dv=g[2], ws=ws)
+
+    ms = _timed(step_heads, steps, warmup)
+    return {"workload": f"{wl.name} with per-head offsets [{wl.heads}][N][3] (head h: the same recipe, seed "
+                        f"+ 1000 h)",
+            "ms_per_step": ms, "value": wl.N * wl.heads / (ms / 1e3), "unit": "query-token-heads/s",
+            "roofline": {"bound": "hbm", "achieved": wl.bytes() / (ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": wl.bytes() / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                         "note": "whole step, algorithmic bytes (as the main line) over the step time"}}
+
+
+def run_sampled(dsa3d, steps, warmup):
+    """fwd+bwd of sampled windows (real offsets): box windows, one offset per query, and
+    free per-sample offsets, each on its own workload."""
+    import torch
+
+    from local_sparse_attention_amd import configs, synth
+
+    res = {}
+    for key, wl, mode in (("box_real_offsets", configs.S_BOX, "box"),
+                          ("free_per_sample_offsets", configs.S_FREE, "free")):
+        grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
+        t = dev_inputs(wl)
+        off = torch.from_numpy(synth.make_real_offsets(wl, mode)).cuda()
+        ws = torch.empty(dsa3d.sampled_workspace_bytes(grid, wl.heads, window, mode, True), dtype=torch.uint8,
+                         device="cuda")
+        box = {}
+
+        def fwd():
+            box["o"] = dsa3d.sampled_forward(t["q"], t["k"], t["v"], off, grid, window, mode, wl.scale)
+
+        def bwd():
+            dsa3d.sampled_backward(t["q"], t["k"], t["v"], off, box["o"][0], box["o"][1], t["dout"], grid, window,
+                                   mode, wl.scale, ws=ws)
+
+        ms_f = _timed(fwd, steps, warmup)
+        ms_b = _timed(bwd, steps, warmup)
+        ms = ms_f + ms_b
+        fl = sampled_flops(wl)
+        res[key] = {
+            "workload": f"{wl.name}: grid {wl.F}x{wl.Hp}x{wl.Wp} (N={wl.N}), {wl.heads} heads x {wl.head_dim}, "
+                        f"window {wl.kt}x{wl.ky}x{wl.kx}, {wl.dtype}, "
+                        + ("one real offset per query" if mode == "box" else "one real offset per sample"),
+            "ms_per_step": ms, "fwd_ms": ms_f, "bwd_ms": ms_b, "value": wl.N * wl.heads / (ms / 1e3),
+            "unit": "query-token-heads/s",
+            "roofline": {"bound": "alu", "achieved": fl / (ms / 1e3) / 1e12, "peak": PEAK_F32_TFLOPS,
+                         "unit": "TFLOP/s", "frac": fl / (ms / 1e3) / 1e12 / PEAK_F32_TFLOPS,
+                         "note": "fp32 VALU flops of the trilinear form (36D fwd + 102D bwd per sample)"}}
+        del t, off, ws, box
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -126,6 +300,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scales the HBM byte counters)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="main line only: no measured peaks, linear-in-N run or operator variants")
+    ap.add_argument("--variants-only", action="store_true",
+                    help="only the operator variants (for profiling their kernels)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards by heads without "
@@ -146,10 +324,25 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
         return
+    if args.variants_only:
+        wl = configs.C5
+        t = dev_inputs(wl)
+        out = torch.empty_like(t["q"])
+        lse = torch.empty((wl.heads, wl.N), dtype=torch.float32, device="cuda")
+        g = [torch.empty_like(t["q"]) for _ in range(3)]
+        ws = dsa3d.workspace((wl.F, wl.Hp, wl.Wp), wl.heads, (wl.kt, wl.ky, wl.kx), True)
+        var = {"per_head_offsets": run_per_head(dsa3d, wl, t, out, lse, g, ws, 3, 1)}
+        del t, out, lse, g, ws
+        torch.cuda.empty_cache()
+        var.update(run_sampled(dsa3d, 3, 1))
+        print(json.dumps({"variants": var}), flush=True)
+        return
     wl = configs.ALL[args.workload]
     grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
     lib = dsa3d.load()
     hip = Hip()
+    log = lambda msg: print(f"[bench] {msg}", file=sys.stderr, flush=True)
+    log(f"generating {wl.name} inputs")
 
     # inputs: generated on the host (seeded), copied once, resident in HBM
     shape = (wl.N, wl.heads, wl.head_dim)
@@ -187,10 +380,12 @@ def main():
     lib.dsa3d_forward_ex.argtypes = lib.dsa3d_forward.argtypes + [ctypes.c_uint, evp]
     lib.dsa3d_backward_ex.argtypes = lib.dsa3d_backward.argtypes + [ctypes.c_uint, evp]
 
+    log("warm-up")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
+    log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(fevs[i], bevs[i])
@@ -223,6 +418,9 @@ def main():
         roof = {"bound": "mfma", "achieved": kf / t_dom / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(KERNEL_OF[dom], wl.name)
+    roof["traffic_note"] = ("bytes between L2 and the memory fabric (FETCH_SIZE x fetch scale + WRITE_SIZE x write "
+                            "scale, both scales from a device copy of known size; fabric reads that hit the "
+                            "Infinity Cache count too), from profiles/traffic.json when it matches the sources")
     roof["kernel"] = KERNEL_OF[dom] if wl.dtype == "bf16" else dom
     roof["kernel_ms"] = phases[dom]
 
@@ -250,9 +448,56 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+
+    if not args.no_extras and wl.name == configs.C5.name:
+        # time linear in N at a fixed window: the same step on the first 64 and 128 frames
+        # (token order is frame-major, so those are prefixes of the same tensors)
+        lin = []
+        for F in (64, 128):
+            wF = wl.with_frames(F)
+            gF = (F, wl.Hp, wl.Wp)
+            log(f"linear-in-N run, {F} frames")
+
+            def stepF():
+                rc = lib.dsa3d_forward_ex(ptr(dev["q"]), ptr(dev["k"]), ptr(dev["v"]), ptr(dev["offsets"]), *gF,
+                                          wl.heads, wl.head_dim, *window, wl.scale, dtc, ptr(out), ptr(lse), ptr(ws),
+                                          ws.numel(), sp, 0, None)
+                assert rc == 0, dsa3d.status_string(rc)
+                rc = lib.dsa3d_backward_ex(ptr(dev["q"]), ptr(dev["k"]), ptr(dev["v"]), ptr(dev["offsets"]),
+                                           ptr(out), ptr(lse), ptr(dev["dout"]), *gF, wl.heads, wl.head_dim, *window,
+                                           wl.scale, dtc, ptr(dq), ptr(dk), ptr(dv), ptr(ws), ws.numel(), sp, 0,
+                                           None)
+                assert rc == 0, dsa3d.status_string(rc)
+
+            stepF()
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            for _ in range(3):
+                stepF()
+            torch.cuda.synchronize()
+            msF = (time.perf_counter() - a) * 1e3 / 3
+            lin.append({"frames": F, "N": wF.N, "ms_per_step": msF, "value": wF.N * wl.heads / (msF / 1e3)})
+        lin.append({"frames": wl.F, "N": wl.N, "ms_per_step": ms_per_step, "value": value})
+        res["linear_in_n"] = lin
+        log("per-head offsets variant")
+        res["variants"] = {"per_head_offsets": run_per_head(dsa3d, wl, dev, out, lse, [dq, dk, dv], ws, 3, 1)}
+
     del dev, out, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
+    if not args.no_extras:
+        log("measured peaks")
+        peaks = measure_peaks(lib, hip, sp)
+        res["peaks_measured"] = peaks
+        if roof["unit"] == "GB/s":
+            roof["measured_peak"] = peaks["read_gbs"]
+        else:
+            roof["measured_peak"] = peaks["mfma_bf16_tflops"]
+        roof["frac_of_measured"] = roof["achieved"] / roof["measured_peak"]
+        res["mfma_frac_of_measured"] = res["useful_tflops"] / peaks["mfma_bf16_tflops"]
+        log("sampled-window variants")
+        res.setdefault("variants", {}).update(run_sampled(dsa3d, 3, 1))
     if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)
 

@@ -75,3 +75,12 @@ C4 = Workload("C4-full-width", 64, 68, 120, 64, 128, 3, 9, 9, "bf16", True, 3, 1
 C5 = Workload("C5-256f", 256, 68, 120, 16, 128, 5, 9, 9, "bf16", True, 4, 1.0, ("blocks", 8, 3.0, True, 8.0))
 
 ALL = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
+
+# Sampled windows (real offsets, trilinear sampling): the pages' 3 x 7 x 7 window on a
+# 16-frame 32 x 32 grid, 8 heads x 128, bf16, a drifting block motion field plus real
+# jitter (synth.make_real_offsets): one offset per query (box windows) or one per
+# sample (free positions).
+S_BOX = Workload("S-box-real-offsets", 16, 32, 32, 8, 128, 3, 7, 7, "bf16", True, 5, 1.0,
+                 ("blocks", 8, 3.0, True, 8.0))
+S_FREE = Workload("S-free-per-sample-offsets", 16, 32, 32, 8, 128, 3, 7, 7, "bf16", True, 6, 1.0,
+                  ("blocks", 8, 3.0, True, 8.0))

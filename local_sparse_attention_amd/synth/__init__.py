@@ -88,3 +88,21 @@ def make_inputs(wl, with_dout=None):
 def bf16_bits_to_f32(a):
     """Exact widening of raw bf16 bits to fp32."""
     return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def make_head_offsets(wl):
+    """int32 [H][N][3] per-head offsets: head h follows the workload's recipe with seed
+    seed + 1000 h."""
+    from dataclasses import replace
+
+    return np.stack([make_offsets(replace(wl, seed=wl.seed + 1000 * h)) for h in range(wl.heads)])
+
+
+def make_real_offsets(wl, mode, jitter=0.5):
+    """float32 real offsets for sampled windows: the workload's integer motion field plus
+    N(0, jitter) per component (stream 7).  mode "box": [N, 1, 3] (one offset per query,
+    shared by the heads); "free": [N, H, K, 3] (every sample its own offset)."""
+    base = make_offsets(wl).astype(np.float32)
+    if mode == "box":
+        return base[:, None, :] + normal(wl.seed, 7, (wl.N, 1, 3), "f32", jitter)
+    return base[:, None, None, :] + normal(wl.seed, 7, (wl.N, wl.heads, wl.K, 3), "f32", jitter)
