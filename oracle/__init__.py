@@ -47,13 +47,16 @@ def _load():
         lib.oracle_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_backward_q_rows.argtypes = [P, vp, vp, vp, vp, vp, i64, vp, vp]
         lib.oracle_backward_kv_rows.argtypes = [P, vp, vp, vp, vp, vp, i64, vp, vp, vp]
+        lib.oracle_dwconv3d_forward.argtypes = [vp, i32, vp, vp] + [i32] * 7 + [vp]
+        lib.oracle_dwconv3d_backward.argtypes = [vp, i32, vp, vp] + [i32] * 7 + [vp, vp, vp]
         lib.oracle_forward_heads.argtypes = [P, vp, vp, vp, vp, vp, vp]
         lib.oracle_backward_heads.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_sampled_forward.argtypes = [P, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
         lib.oracle_sampled_backward.argtypes = [P, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp]
         for f in ("oracle_window_starts", "oracle_forward", "oracle_forward_rows", "oracle_backward",
                   "oracle_backward_q_rows", "oracle_backward_kv_rows", "oracle_forward_heads",
-                  "oracle_backward_heads", "oracle_sampled_forward", "oracle_sampled_backward"):
+                  "oracle_backward_heads", "oracle_sampled_forward", "oracle_sampled_backward",
+                  "oracle_dwconv3d_forward", "oracle_dwconv3d_backward"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -254,3 +257,57 @@ def sampled_backward(q, k, v, dout, offsets, grid, window, scale, mode):
     axes = tuple(i for i, s in enumerate(shape) if s == 1 and full_shape[i] != 1)
     doff = g.sum(axis=axes, keepdims=True) if axes else g
     return dq, dk, dv, doff.reshape(shape)
+
+
+# ---- depthwise 3-D convolution and the offset predictor ---------------------------------
+
+def dwconv3d_forward(x, weight, bias, grid):
+    """Depthwise 3-D convolution (see oracle.c): x [N][C] (float32, float64 or bf16 bits),
+    weight [C][ct][cy][cx], bias [C] or None (float).  Returns y [N][C] float64."""
+    x = _c(x)
+    N, C = x.shape
+    assert N == grid[0] * grid[1] * grid[2]
+    w = _c(weight, np.float64)
+    ct, cy, cx = w.shape[1:]
+    assert w.shape[0] == C and ct % 2 and cy % 2 and cx % 2
+    b = None if bias is None else _c(bias, np.float64)
+    y = np.empty((N, C), dtype=np.float64)
+    _load().oracle_dwconv3d_forward(x.ctypes.data, _dtype_code(x), w.ctypes.data,
+                                    None if b is None else b.ctypes.data, *grid, C, ct, cy, cx, y.ctypes.data)
+    return y
+
+
+def dwconv3d_backward(x, weight, dy, grid):
+    """dx [N][C], dweight [C][ct][cy][cx], dbias [C] (float64) for an output gradient dy."""
+    x = _c(x)
+    N, C = x.shape
+    w = _c(weight, np.float64)
+    ct, cy, cx = w.shape[1:]
+    g = _c(dy, np.float64)
+    dx = np.empty((N, C), dtype=np.float64)
+    dw = np.empty(w.shape, dtype=np.float64)
+    db = np.empty(C, dtype=np.float64)
+    _load().oracle_dwconv3d_backward(x.ctypes.data, _dtype_code(x), w.ctypes.data, g.ctypes.data, *grid, C, ct, cy, cx,
+                                     dx.ctypes.data, dw.ctypes.data, db.ctypes.data)
+    return dx, dw, db
+
+
+def linear_forward(x, weight, bias):
+    """The predictor's pointwise layer (a 1 x 1 x 1 convolution, i.e. a linear map per
+    token): y = x W^T + b, x [M][K], W [O][K], b [O]; float64 (one matrix product)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = x @ np.asarray(weight, dtype=np.float64).T
+    return y if bias is None else y + np.asarray(bias, dtype=np.float64)
+
+
+def linear_backward(x, weight, dy):
+    """dx = dy W, dW = dy^T x, db = sum over rows of dy (float64)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    return dy @ w, dy.T @ x, dy.sum(0)
+
+
+def bf16_to_f64(bits):
+    """bf16 bit patterns (uint16) as float64 values."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

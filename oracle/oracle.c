@@ -25,7 +25,8 @@
  * bf16 bits (fp64 too, for the finite-difference checks); offsets are int32
  * [N][3] in (dt, dy, dx) order.
  *
- * Also here (same section): per-head integer offsets (oracle_forward_heads,
+ * Also here (same section): the depthwise 3-D convolution of Eq. (1)'s first term and
+ * of the offset predictor (oracle_dwconv3d_forward / _backward); per-head integer offsets (oracle_forward_heads,
  * oracle_backward_heads), and sampled windows with real offsets and trilinear
  * sampling, with the gradient of the offsets (oracle_sampled_forward,
  * oracle_sampled_backward; their readings are written above those functions).
@@ -571,5 +572,91 @@ void oracle_sampled_backward(const oracle_cfg* c, const void* q, const void* k, 
     }
     free(P);
     free(p);
+  }
+}
+
+/* ---- depthwise 3-D convolution ------------------------------------------------
+   The first term of Eq. (1), and the first stage of the offset predictor (the
+   implementation paragraph: nn.Conv3d with groups equal to the hidden size, i.e. one
+   ct x cy x cx filter per channel).  Cross-correlation over the T x H' x W' grid with
+   zero padding that keeps the grid ("same"; extents odd):
+     y[n, c] = b[c] + sum_{a, e, f} w[c][a][e][f] x[(t + a - rt, y + e - ry, x + f - rx), c]
+   x is [N][C] (fp32, bf16 bits or fp64, `dtype` as above); w [C][ct][cy][cx], b [C]
+   and y [N][C] are fp64.  Backward: dx[n, c] = sum_{a,e,f} w[c][a][e][f] dy[n - (a - rt,
+   e - ry, f - rx), c], dw[c][a][e][f] = sum_n dy[n, c] x[n + (a - rt, e - ry, f - rx), c],
+   db[c] = sum_n dy[n, c]. */
+
+static double load_elem(int dtype, const void* base, size_t i) {
+  if (dtype == 0) return ((const float*)base)[i];
+  if (dtype == 2) return ((const double*)base)[i];
+  uint32_t b = (uint32_t)((const uint16_t*)base)[i] << 16;
+  float f;
+  memcpy(&f, &b, 4);
+  return f;
+}
+
+void oracle_dwconv3d_forward(const void* x, int dtype, const double* w, const double* b, int F, int Hp, int Wp, int C,
+                             int ct, int cy, int cx, double* y) {
+  const int64_t N = (int64_t)F * Hp * Wp;
+  const int rt = (ct - 1) / 2, ry = (cy - 1) / 2, rx = (cx - 1) / 2;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    const int64_t t = n / ((int64_t)Hp * Wp), yy = (n / Wp) % Hp, xx = n % Wp;
+    for (int c = 0; c < C; ++c) {
+      double s = b ? b[c] : 0.0;
+      for (int a = 0; a < ct; ++a)
+        for (int e = 0; e < cy; ++e)
+          for (int f = 0; f < cx; ++f) {
+            const int64_t ts = t + a - rt, ys = yy + e - ry, xs = xx + f - rx;
+            if (ts < 0 || ts >= F || ys < 0 || ys >= Hp || xs < 0 || xs >= Wp) continue;
+            const int64_t m = (ts * Hp + ys) * Wp + xs;
+            s += w[(((size_t)c * ct + a) * cy + e) * cx + f] * load_elem(dtype, x, (size_t)m * C + c);
+          }
+      y[(size_t)n * C + c] = s;
+    }
+  }
+}
+
+void oracle_dwconv3d_backward(const void* x, int dtype, const double* w, const double* dy, int F, int Hp, int Wp,
+                              int C, int ct, int cy, int cx, double* dx, double* dw, double* db) {
+  const int64_t N = (int64_t)F * Hp * Wp;
+  const int rt = (ct - 1) / 2, ry = (cy - 1) / 2, rx = (cx - 1) / 2;
+  const int taps = ct * cy * cx;
+  /* dx: gather form, every input position collects the outputs whose window holds it */
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    const int64_t t = n / ((int64_t)Hp * Wp), yy = (n / Wp) % Hp, xx = n % Wp;
+    for (int c = 0; c < C; ++c) {
+      double s = 0.0;
+      for (int a = 0; a < ct; ++a)
+        for (int e = 0; e < cy; ++e)
+          for (int f = 0; f < cx; ++f) {
+            const int64_t to = t - (a - rt), yo = yy - (e - ry), xo = xx - (f - rx);
+            if (to < 0 || to >= F || yo < 0 || yo >= Hp || xo < 0 || xo >= Wp) continue;
+            const int64_t m = (to * Hp + yo) * Wp + xo;
+            s += w[(((size_t)c * ct + a) * cy + e) * cx + f] * dy[(size_t)m * C + c];
+          }
+      dx[(size_t)n * C + c] = s;
+    }
+  }
+  /* dw, db: one channel per thread, tokens in order */
+#pragma omp parallel for schedule(static)
+  for (int c = 0; c < C; ++c) {
+    double sb = 0.0;
+    for (int k = 0; k < taps; ++k) dw[(size_t)c * taps + k] = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double g = dy[(size_t)n * C + c];
+      sb += g;
+      const int64_t t = n / ((int64_t)Hp * Wp), yy = (n / Wp) % Hp, xx = n % Wp;
+      for (int a = 0; a < ct; ++a)
+        for (int e = 0; e < cy; ++e)
+          for (int f = 0; f < cx; ++f) {
+            const int64_t ts = t + a - rt, ys = yy + e - ry, xs = xx + f - rx;
+            if (ts < 0 || ts >= F || ys < 0 || ys >= Hp || xs < 0 || xs >= Wp) continue;
+            const int64_t m = (ts * Hp + ys) * Wp + xs;
+            dw[(size_t)c * taps + (a * cy + e) * cx + f] += g * load_elem(dtype, x, (size_t)m * C + c);
+          }
+    }
+    db[c] = sb;
   }
 }
