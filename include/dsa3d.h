@@ -216,6 +216,46 @@ int dsa3d_sampled_backward(const void* q, const void* k, const void* v, const fl
                            int ky, int kx, float scale, int dtype, void* dq, void* dk, void* dv, float* doffsets,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- The DWConv3D term and the offset predictor --------------------------------
+   Eq. (1) adds a 3-D depthwise convolution of X to the attention term, and the
+   offsets are predicted by a depthwise 3-D convolution followed by a linear layer
+   (the implementation paragraph: nn.Conv3d with groups equal to the hidden size, then
+   pointwise convolutions).  Tensors here are [N][C] with C = heads * head_dim (the
+   [N][heads][head_dim] tensors above, seen as one row of C channels per token).
+
+   Depthwise 3-D convolution, one ct x cy x cx filter per channel (odd extents,
+   ct*cy*cx <= 512), cross-correlation with zero padding that keeps the grid:
+     y[n, c] = (accumulate ? y[n, c] : 0) + bias[c]
+               + sum_{a,e,f} weight[c][a][e][f] * x[(t + a - (ct-1)/2, y + e - (cy-1)/2,
+                                                    x + f - (cx-1)/2), c]
+   x, y: dtype, 16-byte aligned, C a multiple of 8; weight fp32 [C][ct][cy][cx]; bias
+   fp32 [C] or null.  accumulate = 1 adds the term into y in place (the attention
+   output plus the convolution term, one rounding), 0 overwrites y.  fp32 arithmetic.
+   Backward: dx (dtype, [N][C]) = the transposed convolution of dy; dweight (fp32,
+   weight's shape) and dbias (fp32 [C], or null to skip) sum over the tokens in a
+   fixed order (per-frame partial sums in the workspace, then frames in order). */
+int dsa3d_dwconv3d_forward(const void* x, const float* weight, const float* bias, int F, int Hp, int Wp, int C, int ct,
+                           int cy, int cx, int dtype, void* y, int accumulate, hipStream_t stream);
+size_t dsa3d_dwconv3d_workspace_bytes(int F, int Hp, int Wp, int C, int ct, int cy, int cx);
+int dsa3d_dwconv3d_backward(const void* x, const float* weight, const void* dy, int F, int Hp, int Wp, int C, int ct,
+                            int cy, int cx, int dtype, void* dx, float* dweight, float* dbias, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Linear (pointwise) layer: y[m][o] = sum_k x[m][k] * weight[o][k] + bias[o], for the
+   predictor's map from C channels to heads * kt*ky*kx * 3 offsets per token (the
+   free-mode offset layout [N][heads][kt*ky*kx][3] when the outputs are ordered (head,
+   sample, axis)).  x [M][Kd] and weight [O][Kd] in dtype (16-byte aligned); y fp32
+   [M][O] (the offsets); bias fp32 [O] or null.  Matrix cores, fp32 accumulation.
+   Backward: dx (dtype [M][Kd]) = dy weight, dweight (fp32 [O][Kd]) = dy^T x, dbias
+   (fp32 [O], or null) = column sums of dy in a fixed order; on the bf16 path dy is
+   rounded to bf16 for the two products.  M*Kd, M*O, Kd*O < 2^31. */
+int dsa3d_linear_forward(const void* x, const void* weight, const float* bias, int M, int Kd, int O, int dtype,
+                         float* y, hipStream_t stream);
+size_t dsa3d_linear_workspace_bytes(int M, int Kd, int O, int dtype);
+int dsa3d_linear_backward(const void* x, const void* weight, const float* dy, int M, int Kd, int O, int dtype,
+                          void* dx, float* dweight, float* dbias, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
 /* Size of the library's static scratch array (one per GPU), used by
    dsa3d_forward_static only. */
 #define DSA3D_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)

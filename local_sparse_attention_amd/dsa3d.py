@@ -51,10 +51,20 @@ def load():
         lib.dsa3d_sampled_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64] + [i32] * 9 + [f32, i32, vp, vp, vp]
         lib.dsa3d_sampled_backward.argtypes = ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, vp] + [i32] * 8 +
                                                [f32, i32, vp, vp, vp, vp, vp, sz, vp])
+        lib.dsa3d_dwconv3d_forward.argtypes = [vp, vp, vp] + [i32] * 8 + [vp, i32, vp]
+        lib.dsa3d_dwconv3d_workspace_bytes.argtypes = [i32] * 7
+        lib.dsa3d_dwconv3d_workspace_bytes.restype = sz
+        lib.dsa3d_dwconv3d_backward.argtypes = [vp, vp, vp] + [i32] * 8 + [vp, vp, vp, vp, sz, vp]
+        lib.dsa3d_linear_forward.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
+        lib.dsa3d_linear_workspace_bytes.argtypes = [i32] * 4
+        lib.dsa3d_linear_workspace_bytes.restype = sz
+        lib.dsa3d_linear_backward.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         lib.dsa3d_forward_heads.argtypes = fwd + [u32]
         lib.dsa3d_backward_heads.argtypes = bwd + [u32]
         for f in ("dsa3d_forward", "dsa3d_backward", "dsa3d_forward_ex", "dsa3d_backward_ex", "dsa3d_forward_static",
-                  "dsa3d_forward_heads", "dsa3d_backward_heads", "dsa3d_sampled_forward", "dsa3d_sampled_backward"):
+                  "dsa3d_forward_heads", "dsa3d_backward_heads", "dsa3d_sampled_forward", "dsa3d_sampled_backward",
+                  "dsa3d_dwconv3d_forward", "dsa3d_dwconv3d_backward", "dsa3d_linear_forward",
+                  "dsa3d_linear_backward"):
             getattr(lib, f).restype = i32
         lib.dsa3d_status_string.argtypes = [i32]
         lib.dsa3d_status_string.restype = ctypes.c_char_p
@@ -315,6 +325,97 @@ def sampled_backward(q, k, v, offsets, out, lse, dout, grid, window, mode, scale
                                          dv.data_ptr(), doff.data_ptr(), _dev(ws, "workspace", dev), ws.numel(),
                                          _stream()), "dsa3d_sampled_backward")
     return dq, dk, dv, doff
+
+
+# ---- the DWConv3D term and the offset predictor ------------------------------------------
+
+def _ptr_or_none(t, name, dev):
+    return None if t is None else _dev(t, name, dev)
+
+
+def dwconv3d_forward(x, weight, bias, grid, out=None, accumulate=False):
+    """Depthwise 3-D convolution of x [N, C] (float32 or bfloat16) with weight float32
+    [C, ct, cy, cx] and bias float32 [C] or None.  accumulate=True adds into `out` (e.g.
+    the attention output seen as [N, C]); otherwise `out` (or a new tensor) is overwritten."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise DSA3DError("x must be a [N, C] tensor")
+    N, C = x.shape
+    if N != grid[0] * grid[1] * grid[2]:
+        raise DSA3DError(f"x has {N} tokens, grid {grid} has {grid[0] * grid[1] * grid[2]}")
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 4 or weight.shape[0] != C:
+        raise DSA3DError("weight must be float32 [C, ct, cy, cx]")
+    _want(weight, "weight", weight.shape, torch.float32)
+    if bias is not None:
+        _want(bias, "bias", (C,), torch.float32)
+    if accumulate and out is None:
+        raise DSA3DError("accumulate needs out")
+    if out is not None:
+        _want(out, "out", x.shape, x.dtype)
+    dev = x.device
+    out = torch.empty_like(x) if out is None else out
+    ct, cy, cx = weight.shape[1:]
+    _check(load().dsa3d_dwconv3d_forward(_dev(x, "x", dev), _dev(weight, "weight", dev), _ptr_or_none(bias, "bias", dev),
+                                         *grid, C, ct, cy, cx, _dtype_code(x), _dev(out, "out", dev), int(accumulate),
+                                         _stream()), "dsa3d_dwconv3d_forward")
+    return out
+
+
+def dwconv3d_backward(x, weight, dy, grid, need_bias=True):
+    """Returns (dx [N, C] in x's dtype, dweight float32 like weight, dbias float32 [C] or None)."""
+    N, C = x.shape
+    _want(dy, "dy", x.shape, x.dtype)
+    _want(weight, "weight", weight.shape, torch.float32)
+    dev = x.device
+    ct, cy, cx = weight.shape[1:]
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(weight)
+    db = torch.empty(C, dtype=torch.float32, device=dev) if need_bias else None
+    n = load().dsa3d_dwconv3d_workspace_bytes(*grid, C, ct, cy, cx)
+    if n == 0:
+        raise DSA3DError("dsa3d_dwconv3d_backward: invalid geometry")
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    _check(load().dsa3d_dwconv3d_backward(_dev(x, "x", dev), _dev(weight, "weight", dev), _dev(dy, "dy", dev), *grid,
+                                          C, ct, cy, cx, _dtype_code(x), dx.data_ptr(), dw.data_ptr(),
+                                          None if db is None else db.data_ptr(), ws.data_ptr(), ws.numel(),
+                                          _stream()), "dsa3d_dwconv3d_backward")
+    return dx, dw, db
+
+
+def linear_forward(x, weight, bias=None):
+    """y float32 [M, O] = x [M, K] weight[O, K]^T + bias (x, weight: float32 or bfloat16)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise DSA3DError("x must be [M, K] and weight [O, K]")
+    M, K = x.shape
+    O = weight.shape[0]
+    _want(weight, "weight", (O, K), x.dtype)
+    if bias is not None:
+        _want(bias, "bias", (O,), torch.float32)
+    dev = x.device
+    y = torch.empty((M, O), dtype=torch.float32, device=dev)
+    _check(load().dsa3d_linear_forward(_dev(x, "x", dev), _dev(weight, "weight", dev), _ptr_or_none(bias, "bias", dev),
+                                       M, K, O, _dtype_code(x), y.data_ptr(), _stream()), "dsa3d_linear_forward")
+    return y
+
+
+def linear_backward(x, weight, dy, need_bias=True):
+    """Returns (dx [M, K] in x's dtype, dweight float32 [O, K], dbias float32 [O] or None)."""
+    M, K = x.shape
+    O = weight.shape[0]
+    _want(weight, "weight", (O, K), x.dtype)
+    _want(dy, "dy", (M, O), torch.float32)
+    dev = x.device
+    dx = torch.empty_like(x)
+    dw = torch.empty((O, K), dtype=torch.float32, device=dev)
+    db = torch.empty(O, dtype=torch.float32, device=dev) if need_bias else None
+    n = load().dsa3d_linear_workspace_bytes(M, K, O, _dtype_code(x))
+    if n == 0:
+        raise DSA3DError("dsa3d_linear_backward: invalid sizes")
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    _check(load().dsa3d_linear_backward(_dev(x, "x", dev), _dev(weight, "weight", dev), _dev(dy, "dy", dev), M, K, O,
+                                        _dtype_code(x), dx.data_ptr(), dw.data_ptr(),
+                                        None if db is None else db.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
+           "dsa3d_linear_backward")
+    return dx, dw, db
 
 
 class DSA3DFunction(torch.autograd.Function):

@@ -283,7 +283,9 @@ def dwconv3d_backward(x, weight, dy, grid):
     N, C = x.shape
     w = _c(weight, np.float64)
     ct, cy, cx = w.shape[1:]
-    g = _c(dy, np.float64)
+    dy = np.asarray(dy)
+    g = bf16_to_f64(dy) if dy.dtype == np.uint16 else _c(dy, np.float64)
+    g = np.ascontiguousarray(g)
     dx = np.empty((N, C), dtype=np.float64)
     dw = np.empty(w.shape, dtype=np.float64)
     db = np.empty(C, dtype=np.float64)

@@ -1,7 +1,8 @@
-"""The C ABI library loads, exports every function include/dsa3d.h declares, sizes its
+"""The C ABI library loads, exports every function include/*.h declares, sizes its
 workspace and rejects bad arguments before launching anything (CPU only: no call here
 reaches the GPU)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,7 +11,7 @@ import pytest
 from local_sparse_attention_amd import dsa3d
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dsa3d.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, ERR_NULL, ERR_DTYPE, ERR_HEAD_DIM, ERR_GRID, ERR_WINDOW, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_SCALE = (
     0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
@@ -26,15 +27,18 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa3d_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(dsa3d_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) >= {"dsa3d_forward", "dsa3d_backward", "dsa3d_window_starts", "dsa3d_workspace_bytes",
-                          "dsa3d_status_string"}
+                          "dsa3d_status_string", "dsa3d_forward_heads", "dsa3d_sampled_forward",
+                          "dsa3d_sampled_backward", "dsa3d_peak_mfma_bf16"}
     for n in names:
         assert hasattr(lib, n), n
 
