@@ -16,7 +16,8 @@ One step = dsa3d_forward + dsa3d_backward over the whole grid.  Prints one JSON 
   linear_in_n  the same step on the first 64 and 128 frames (time linear in N)
   variants   the other forms of the operator on their own workloads, fwd+bwd: per-head
              integer offsets (256-frame workload), box windows with one real offset per
-             query, free per-sample real offsets (16 x 32 x 32, 3 x 7 x 7)
+             query, free per-sample real offsets (16 x 32 x 32, 3 x 7 x 7), the DWConv3D
+             term (256-frame grid) and the offset predictor (16 x 32 x 32)
 """
 import argparse
 import ctypes
@@ -291,6 +292,76 @@ def run_sampled(dsa3d, steps, warmup):
     return res
 
 
+def run_predictor(dsa3d, steps, warmup):
+    """The DWConv3D term of Eq. (1) on the 256-frame grid (hidden 16 x 128 = 2048 channels,
+    3 x 3 x 3 filter: the pages give no size), added into an attention output, forward and
+    backward; and the offset predictor (3 x 3 x 3 depthwise convolution, then the pointwise
+    layer from 1024 channels to 8 heads x 147 samples x 3 offsets) on the 16 x 32 x 32
+    sampled-window workload, forward and backward."""
+    import torch
+
+    from local_sparse_attention_amd import configs
+
+    res = {}
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    wl = configs.C5
+    grid, N, C = (wl.F, wl.Hp, wl.Wp), wl.N, wl.heads * wl.head_dim
+    x = torch.randn((N, C), generator=gen, device="cuda").bfloat16()
+    out = torch.randn((N, C), generator=gen, device="cuda").bfloat16()
+    w = 0.1 * torch.randn((C, 3, 3, 3), generator=gen, device="cuda")
+    b = torch.randn((C,), generator=gen, device="cuda")
+
+    ms_f = _timed(lambda: dsa3d.dwconv3d_forward(x, w, b, grid, out=out, accumulate=True), steps, warmup)
+    dy = out
+    ms_b = _timed(lambda: dsa3d.dwconv3d_backward(x, w, dy, grid), steps, warmup)
+    bf, bb = 3.0 * N * C * 2, 3.0 * N * C * 2
+    res["dwconv3d_term"] = {
+        "workload": f"DWConv3D term on {wl.name} (grid {wl.F}x{wl.Hp}x{wl.Wp}, N={N}, C={C} channels, bf16), "
+                    "3x3x3 filter, added into the attention output",
+        "fwd_ms": ms_f, "bwd_ms": ms_b, "ms_per_step": ms_f + ms_b,
+        "roofline": {"bound": "hbm", "achieved": (bf + bb) / ((ms_f + ms_b) / 1e3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": (bf + bb) / ((ms_f + ms_b) / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "fwd_frac": bf / (ms_f / 1e3) / 1e9 / PEAK_HBM_GBS,
+                     "note": "algorithmic bytes: forward reads x and the attention output and writes the sum "
+                             "(3 N C s), backward reads x and dy and writes dx (3 N C s)"}}
+    del x, out, dy, w, b
+    torch.cuda.empty_cache()
+
+    wl = configs.S_FREE
+    grid, N, C, O = (wl.F, wl.Hp, wl.Wp), wl.N, wl.heads * wl.head_dim, wl.heads * wl.K * 3
+    x = torch.randn((N, C), generator=gen, device="cuda").bfloat16()
+    w1 = 0.1 * torch.randn((C, 3, 3, 3), generator=gen, device="cuda")
+    b1 = torch.randn((C,), generator=gen, device="cuda")
+    w2 = (0.05 * torch.randn((O, C), generator=gen, device="cuda")).bfloat16()
+    b2 = torch.randn((O,), generator=gen, device="cuda")
+    dy = torch.randn((N, O), generator=gen, device="cuda")
+    box = {}
+
+    def fwd():
+        box["h"] = dsa3d.dwconv3d_forward(x, w1, b1, grid)
+        box["y"] = dsa3d.linear_forward(box["h"], w2, b2)
+
+    def bwd():
+        dh, _, _ = dsa3d.linear_backward(box["h"], w2, dy)
+        dsa3d.dwconv3d_backward(x, w1, dh, grid)
+
+    fwd()
+    ms_lf = _timed(lambda: dsa3d.linear_forward(box["h"], w2, b2), steps, warmup)
+    ms_f = _timed(fwd, steps, warmup)
+    ms_b = _timed(bwd, steps, warmup)
+    gemm_fl = 2.0 * N * C * O
+    res["offset_predictor"] = {
+        "workload": f"offset predictor on {wl.name} (N={N}): 3x3x3 depthwise conv over {C} channels, then the "
+                    f"pointwise layer {C} -> {O} ({wl.heads} heads x {wl.K} samples x 3), bf16",
+        "fwd_ms": ms_f, "bwd_ms": ms_b, "ms_per_step": ms_f + ms_b, "linear_fwd_ms": ms_lf,
+        "roofline": {"bound": "mfma", "achieved": gemm_fl / (ms_lf / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": gemm_fl / (ms_lf / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "note": "the pointwise layer's forward product (2 N C O flops) over its own time"}}
+    del x, w1, b1, w2, b2, dy, box
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,6 +406,7 @@ def main():
         del t, out, lse, g, ws
         torch.cuda.empty_cache()
         var.update(run_sampled(dsa3d, 3, 1))
+        var.update(run_predictor(dsa3d, 3, 1))
         print(json.dumps({"variants": var}), flush=True)
         return
     wl = configs.ALL[args.workload]
@@ -496,6 +568,8 @@ def main():
         res["mfma_frac_of_measured"] = res["useful_tflops"] / peaks["mfma_bf16_tflops"]
         log("sampled-window variants")
         res.setdefault("variants", {}).update(run_sampled(dsa3d, 3, 1))
+        log("DWConv3D term and offset predictor")
+        res["variants"].update(run_predictor(dsa3d, 3, 1))
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(wl)

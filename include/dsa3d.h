@@ -192,7 +192,7 @@ int dsa3d_backward_heads(const void* q, const void* k, const void* v, const int3
 /* Workspace bytes of dsa3d_sampled_backward (backward = 1; the forward needs none and
    reports 256); 0 for an invalid geometry or one past the backward's limits
    (N * heads * kt*ky*kx < 2^31 samples, heads * (F+1)(Hp+1)(Wp+1) < 2^31 cells).
-   About 36 bytes per sample in free mode, 24 in box mode. */
+   About 60 bytes per sample in free mode, 48 in box mode. */
 size_t dsa3d_sampled_workspace_bytes(int F, int Hp, int Wp, int heads, int kt, int ky, int kx, int mode,
                                      int backward);
 
@@ -230,7 +230,8 @@ int dsa3d_sampled_backward(const void* q, const void* k, const void* v, const fl
                                                     x + f - (cx-1)/2), c]
    x, y: dtype, 16-byte aligned, C a multiple of 8; weight fp32 [C][ct][cy][cx]; bias
    fp32 [C] or null.  accumulate = 1 adds the term into y in place (the attention
-   output plus the convolution term, one rounding), 0 overwrites y.  fp32 arithmetic.
+   output plus the convolution term, one rounding), 0 overwrites y; y must not overlap
+   x (nor dx overlap dy).  fp32 arithmetic.
    Backward: dx (dtype, [N][C]) = the transposed convolution of dy; dweight (fp32,
    weight's shape) and dbias (fp32 [C], or null to skip) sum over the tokens in a
    fixed order (per-frame partial sums in the workspace, then frames in order). */

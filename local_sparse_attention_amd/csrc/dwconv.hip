@@ -7,15 +7,18 @@
 // Tensors are [N][C] (token n = (t * Hp + y) * Wp + x, channels contiguous).  The
 // stencil is HBM-bound: the kernels keep a block's filters in LDS and take each input
 // row from L1/L2 for the taps that reuse it.
-//   k_dwconv      one thread per (token, 8 channels); forward (optionally adding into y:
+//   k_dwconv      one thread per (4 tokens of a row, 8 channels); forward (optionally adding into y:
 //                 the attention output plus the convolution term in one pass) and, with
 //                 the taps mirrored, the input gradient dx.
-//   k_dwconv_dw   filter and bias gradients, per frame: a block of 32 channels x 8 tap
-//                 groups sums dy[n, c] x[n + shift, c] over one frame's tokens; the frames'
-//                 partial sums are added in frame order by k_dwconv_dw_sum (deterministic,
-//                 no atomics).
+//   k_dwconv_dw   filter and bias gradients: a block sums dy[n, c] x[n + shift, c] over a
+//                 span of one frame's rows for 2048 channels and up to 8 taps; the spans'
+//                 partial sums are added in a fixed order by k_dwconv_dw_sum
+//                 (deterministic, no atomics).
 #include "dsa3d.h"
 #include "internal.hpp"
+#include "tube.hpp"
+
+#include <algorithm>
 
 namespace dsa3d {
 
@@ -26,8 +29,12 @@ struct CGeom {
 };
 
 constexpr int CONV_CB = 64;      // channels per forward block
-constexpr int CONV_TOK = 32;     // tokens per forward block
+constexpr int CONV_TOK = 32;     // token quads (4 tokens of a row) per forward block
 constexpr int CONV_MAX_TAPS = 512;
+
+// 32 bytes of zeros: the row a masked tap reads (8 bf16 or 8 fp32 zero elements), so the
+// load itself yields 0 and needs no select afterwards.
+__device__ __align__(32) const uint4 g_zero_row[2] = {};
 
 __device__ __forceinline__ void ld8(const u16* p, float* x) {
   const uint4 u = *reinterpret_cast<const uint4*>(p);
@@ -53,110 +60,258 @@ __device__ __forceinline__ void st8(float* p, const float* x) {
   store4(p + 4, x[4], x[5], x[6], x[7]);
 }
 
+// Packed tap shift (da, de, df), each biased by 512 into 10 bits.
+__device__ __forceinline__ int pack_shift(int da, int de, int df) {
+  return ((da + 512) << 20) | ((de + 512) << 10) | (df + 512);
+}
+__device__ __forceinline__ void unpack_shift(int s, int& da, int& de, int& df) {
+  da = (s >> 20) - 512;
+  de = ((s >> 10) & 1023) - 512;
+  df = (s & 1023) - 512;
+}
+
 // flip = 0: y = conv(x) + b (+ y when accumulating).  flip = 1: the transpose (taps
-// mirrored, no bias): dx from dy.
+// mirrored, no bias): dx from dy.  A thread takes 8 channels of CONV_Q consecutive tokens
+// of one grid row, so a tap's row test, row address and filter values serve CONV_Q
+// outputs; a tap's CONV_Q loads are issued before their products (a token outside the
+// grid reads a row of zeros).
+constexpr int CONV_Q = 4;
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_dwconv(const T* __restrict__ x, const float* __restrict__ w,
                                                 const float* __restrict__ b, T* __restrict__ y, CGeom g,
                                                 int accumulate, int flip) {
-  extern __shared__ float lw[];  // [taps][CONV_CB]
+  extern __shared__ float lw[];  // [taps][CONV_CB] filters, then [taps] packed shifts
+  int* lsh = reinterpret_cast<int*>(lw + g.taps * CONV_CB);
   const int tid = threadIdx.x;
-  const int c0 = blockIdx.y * CONV_CB;
+  // each XCD takes a contiguous run of quad blocks of one channel block, so the rows of
+  // neighbouring frames and rows that a block's taps reach sit in the same L2
+  const int nqx = (g.Wp + CONV_Q - 1) / CONV_Q;         // quads per grid row
+  const long long nquads = (long long)g.F * g.Hp * nqx;
+  const int nqb = (int)((nquads + CONV_TOK - 1) / CONV_TOK), ncb = (g.C + CONV_CB - 1) / CONV_CB;
+  const int L = xcd_remap(blockIdx.x, nqb * ncb);
+  const int cb = L / nqb, qb = L - cb * nqb;
+  const int c0 = cb * CONV_CB;
+  const int rt = (g.ct - 1) / 2, ry = (g.cy - 1) / 2, rx = (g.cx - 1) / 2;
+  const int sgn = flip ? -1 : 1;
+  for (int i = tid; i < g.taps * CONV_CB; i += 256) {
+    const int tap = i / CONV_CB, cl = i - tap * CONV_CB;
+    lw[i] = c0 + cl < g.C ? w[(size_t)(c0 + cl) * g.taps + tap] : 0.f;
+  }
+  for (int tap = tid; tap < g.taps; tap += 256) {
+    const int a = tap / (g.cy * g.cx), r = tap - a * (g.cy * g.cx), e = r / g.cx, f = r - e * g.cx;
+    lsh[tap] = pack_shift(sgn * (a - rt), sgn * (e - ry), sgn * (f - rx));
+  }
+  __syncthreads();
+  const int cg = tid & 7, ql = tid >> 3;
+  const long long qd = (long long)qb * CONV_TOK + ql;
+  const int c = c0 + cg * 8;
+  if (qd >= nquads || c >= g.C) return;
+  const int qx = (int)(qd % nqx);
+  const int ty = (int)(qd / nqx);  // t * Hp + y
+  const int t = ty / g.Hp, yy = ty - t * g.Hp, x0 = qx * CONV_Q;
+  const size_t n0 = (size_t)ty * g.Wp + x0;
+  float acc[CONV_Q][8];
+#pragma unroll
+  for (int q = 0; q < CONV_Q; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[q][e] = (b && !flip) ? b[c + e] : 0.f;
+  for (int tap = 0; tap < g.taps; ++tap) {
+    int da, de, df;
+    unpack_shift(lsh[tap], da, de, df);
+    const int ts = t + da, ys = yy + de;
+    const bool row_ok = (unsigned)ts < (unsigned)g.F && (unsigned)ys < (unsigned)g.Hp;
+    const T* row = x + ((size_t)(ts * g.Hp + ys) * g.Wp) * g.C + c;
+    const T* zero = reinterpret_cast<const T*>(g_zero_row);
+    float v[CONV_Q][8];
+#pragma unroll
+    for (int q = 0; q < CONV_Q; ++q) {
+      const int xs = x0 + q + df;
+      const bool ok = row_ok && x0 + q < g.Wp && (unsigned)xs < (unsigned)g.Wp;
+      ld8(ok ? row + (size_t)xs * g.C : zero, v[q]);
+    }
+    const float4 w0 = *reinterpret_cast<const float4*>(lw + tap * CONV_CB + cg * 8);
+    const float4 w1 = *reinterpret_cast<const float4*>(lw + tap * CONV_CB + cg * 8 + 4);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int q = 0; q < CONV_Q; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(wv[e], v[q][e], acc[q][e]);
+  }
+#pragma unroll
+  for (int q = 0; q < CONV_Q; ++q) {
+    if (x0 + q >= g.Wp) break;
+    T* out = y + (n0 + q) * g.C + c;
+    if (accumulate) {
+      float v[8];
+      ld8(out, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q][e] += v[e];
+    }
+    st8(out, acc[q]);
+  }
+}
+
+// The same, specialised on the filter width CX: per (da, de) row pair a thread loads the
+// CONV_Q + CX - 1 row positions its CONV_Q tokens reach once and takes all CX taps from
+// them (CONV_Q + CX - 1 loads instead of CONV_Q * CX).  Filters in LDS as [taps][CONV_CB].
+template <typename T, int CX>
+__global__ __launch_bounds__(256) void k_dwconv_w(const T* __restrict__ x, const float* __restrict__ w,
+                                                  const float* __restrict__ b, T* __restrict__ y, CGeom g,
+                                                  int accumulate, int flip) {
+  extern __shared__ float lw[];  // [taps][CONV_CB]
+  constexpr int NV = CONV_Q + CX - 1;
+  const int tid = threadIdx.x;
+  const int nqx = (g.Wp + CONV_Q - 1) / CONV_Q;
+  const long long nquads = (long long)g.F * g.Hp * nqx;
+  const int nqb = (int)((nquads + CONV_TOK - 1) / CONV_TOK), ncb = (g.C + CONV_CB - 1) / CONV_CB;
+  const int L = xcd_remap(blockIdx.x, nqb * ncb);
+  const int cb = L / nqb, qb = L - cb * nqb;
+  const int c0 = cb * CONV_CB;
   for (int i = tid; i < g.taps * CONV_CB; i += 256) {
     const int tap = i / CONV_CB, cl = i - tap * CONV_CB;
     lw[i] = c0 + cl < g.C ? w[(size_t)(c0 + cl) * g.taps + tap] : 0.f;
   }
   __syncthreads();
-  const int cg = tid & 7, tl = tid >> 3;
-  const int n = blockIdx.x * CONV_TOK + tl;
+  const int cg = tid & 7, ql = tid >> 3;
+  const long long qd = (long long)qb * CONV_TOK + ql;
   const int c = c0 + cg * 8;
-  if (n >= g.N || c >= g.C) return;
-  const int plane = g.Hp * g.Wp;
-  const int t = n / plane, yy = (n - t * plane) / g.Wp, xx = n - t * plane - yy * g.Wp;
-  const int rt = (g.ct - 1) / 2, ry = (g.cy - 1) / 2, rx = (g.cx - 1) / 2;
+  if (qd >= nquads || c >= g.C) return;
+  const int qx = (int)(qd % nqx);
+  const int ty = (int)(qd / nqx);
+  const int t = ty / g.Hp, yy = ty - t * g.Hp, x0 = qx * CONV_Q;
+  const size_t n0 = (size_t)ty * g.Wp + x0;
+  const int rt = (g.ct - 1) / 2, ry = (g.cy - 1) / 2, rx = (CX - 1) / 2;
   const int sgn = flip ? -1 : 1;
-  float acc[8], v[8];
+  const T* zero = reinterpret_cast<const T*>(g_zero_row);
+  float acc[CONV_Q][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = (b && !flip) ? b[c + e] : 0.f;
-  int tap = 0;
-  for (int a = 0; a < g.ct; ++a) {
-    const int ts = t + sgn * (a - rt);
-    for (int e = 0; e < g.cy; ++e) {
-      const int ys = yy + sgn * (e - ry);
-      const bool row_in = (unsigned)ts < (unsigned)g.F && (unsigned)ys < (unsigned)g.Hp;
-      for (int f = 0; f < g.cx; ++f, ++tap) {
-        const int xs = xx + sgn * (f - rx);
-        if (!row_in || (unsigned)xs >= (unsigned)g.Wp) continue;
-        ld8(x + (size_t)((ts * g.Hp + ys) * g.Wp + xs) * g.C + c, v);
+  for (int q = 0; q < CONV_Q; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[q][e] = (b && !flip) ? b[c + e] : 0.f;
+  for (int a = 0; a < g.ct; ++a)
+    for (int e2 = 0; e2 < g.cy; ++e2) {
+      const int ts = t + sgn * (a - rt), ys = yy + sgn * (e2 - ry);
+      const bool row_ok = (unsigned)ts < (unsigned)g.F && (unsigned)ys < (unsigned)g.Hp;
+      const T* row = x + ((size_t)(ts * g.Hp + ys) * g.Wp) * g.C + c;
+      // positions x0 - rx .. x0 + CONV_Q - 1 + rx
+      float v[NV][8];
+#pragma unroll
+      for (int p = 0; p < NV; ++p) {
+        const int xs = x0 - rx + p;
+        const bool ok = row_ok && (unsigned)xs < (unsigned)g.Wp;
+        ld8(ok ? row + (size_t)xs * g.C : zero, v[p]);
+      }
+      const int tap_row = (a * g.cy + e2) * CX;
+#pragma unroll
+      for (int f = 0; f < CX; ++f) {
+        // flip mirrors the tap: output x reads x - (f - rx), i.e. position index 2 rx - f
+        const int tap = tap_row + f;
         const float4 w0 = *reinterpret_cast<const float4*>(lw + tap * CONV_CB + cg * 8);
         const float4 w1 = *reinterpret_cast<const float4*>(lw + tap * CONV_CB + cg * 8 + 4);
-        acc[0] = fmaf(w0.x, v[0], acc[0]); acc[1] = fmaf(w0.y, v[1], acc[1]);
-        acc[2] = fmaf(w0.z, v[2], acc[2]); acc[3] = fmaf(w0.w, v[3], acc[3]);
-        acc[4] = fmaf(w1.x, v[4], acc[4]); acc[5] = fmaf(w1.y, v[5], acc[5]);
-        acc[6] = fmaf(w1.z, v[6], acc[6]); acc[7] = fmaf(w1.w, v[7], acc[7]);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int q = 0; q < CONV_Q; ++q) {
+          const int pidx = q + (flip ? 2 * rx - f : f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(wv[e], v[pidx][e], acc[q][e]);
+        }
       }
     }
-  }
-  T* out = y + (size_t)n * g.C + c;
-  if (accumulate) {
-    ld8(out, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+  for (int q = 0; q < CONV_Q; ++q) {
+    if (x0 + q >= g.Wp) break;
+    T* out = y + (n0 + q) * g.C + c;
+    if (accumulate) {
+      float v[8];
+      ld8(out, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[q][e] += v[e];
+    }
+    st8(out, acc[q]);
   }
-  st8(out, acc);
 }
 
-// Filter / bias gradient partial sums of frame blockIdx.x for 32 channels.  Thread
-// (channel lane cl, tap group tg) owns taps tg, tg + 8, ...; tap group 0 also sums dy
-// for the bias.  part[(t * C + c) * (taps + 1) + tap], the bias at index taps.
-constexpr int DW_CH = 32, DW_TG = 8, DW_MAXT = (CONV_MAX_TAPS + DW_TG - 1) / DW_TG;
+// Filter / bias gradient partial sums.  A block takes one frame t, a span of its rows
+// (yc of nyc spans), 2048 channels (8 a thread) and up to DW_TAPS taps (chunk tc); each
+// thread walks the span's tokens in order, loading its 8 channels of dy and, per tap, of x
+// (a tap outside the grid reads a row of zeros), and keeps 8 x DW_TAPS sums.  Blocks are
+// ordered (channel block, tap chunk, row span, frame) with frames fastest and each XCD
+// given a contiguous run, so neighbouring frames' rows meet in one L2.
+// part[((t * nyc + yc) * C + c) * (taps + 1) + tap], the bias sum at index taps.
+constexpr int DW_CPB = 2048, DW_TAPS = 8;
 
-template <typename T, int MT>
+struct DwSplit {
+  int ncb, ntc, nyc, rows;  // channel blocks, tap chunks, row spans, rows per span
+};
+
+template <typename T>
 __global__ __launch_bounds__(256) void k_dwconv_dw(const T* __restrict__ x, const T* __restrict__ dy,
-                                                   float* __restrict__ part, CGeom g) {
-  const int t = blockIdx.x;
-  const int cl = threadIdx.x & (DW_CH - 1), tg = threadIdx.x / DW_CH;
-  const int c = blockIdx.y * DW_CH + cl;
+                                                   float* __restrict__ part, CGeom g, DwSplit sp) {
+  const int total = sp.ncb * sp.ntc * sp.nyc * g.F;
+  int L = xcd_remap(blockIdx.x, total);
+  const int t = L % g.F;
+  L /= g.F;
+  const int yc = L % sp.nyc;
+  L /= sp.nyc;
+  const int tc = L % sp.ntc, cb = L / sp.ntc;
+  const int c = cb * DW_CPB + 8 * threadIdx.x;
   if (c >= g.C) return;
+  const int tap0 = tc * DW_TAPS, ntap = min(DW_TAPS, g.taps - tap0);
   const int rt = (g.ct - 1) / 2, ry = (g.cy - 1) / 2, rx = (g.cx - 1) / 2;
-  float acc[MT], bsum = 0.f;
-  int ta[MT], te[MT], tf[MT];
+  const T* zero = reinterpret_cast<const T*>(g_zero_row);
+  float acc[DW_TAPS][8], bs[8];
+  int sh[DW_TAPS];  // packed (da, de, df) shifts of this chunk's taps
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    acc[i] = 0.f;
-    const int tap = tg + i * DW_TG;
-    const int a = tap / (g.cy * g.cx), r = tap - a * (g.cy * g.cx);
-    ta[i] = tap < g.taps ? a - rt : 1 << 20;  // taps past the filter never land in the grid
-    te[i] = r / g.cx - ry;
-    tf[i] = r - (r / g.cx) * g.cx - rx;
+  for (int i = 0; i < DW_TAPS; ++i) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+    const int tap = tap0 + min(i, ntap - 1);
+    const int a = tap / (g.cy * g.cx), r = tap - a * (g.cy * g.cx), e = r / g.cx, f = r - e * g.cx;
+    sh[i] = pack_shift(a - rt, e - ry, f - rx);
   }
-  for (int yy = 0; yy < g.Hp; ++yy)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bs[e] = 0.f;
+  const int y0 = yc * sp.rows, y1 = min(y0 + sp.rows, g.Hp);
+  for (int yy = y0; yy < y1; ++yy)
     for (int xx = 0; xx < g.Wp; ++xx) {
       const int n = (t * g.Hp + yy) * g.Wp + xx;
-      const float d = to_f32(dy[(size_t)n * g.C + c]);
-      bsum += d;
+      float d[8], v[DW_TAPS][8];
+      ld8(dy + (size_t)n * g.C + c, d);
+      // every tap's load first (taps past ntap repeat the last one and are never written)
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const int ts = t + ta[i], ys = yy + te[i], xs = xx + tf[i];
-        if ((unsigned)ts < (unsigned)g.F && (unsigned)ys < (unsigned)g.Hp && (unsigned)xs < (unsigned)g.Wp)
-          acc[i] = fmaf(d, to_f32(x[(size_t)((ts * g.Hp + ys) * g.Wp + xs) * g.C + c]), acc[i]);
+      for (int i = 0; i < DW_TAPS; ++i) {
+        int da, de, df;
+        unpack_shift(sh[i], da, de, df);
+        const int ts = t + da, ys = yy + de, xs = xx + df;
+        const bool ok = (unsigned)ts < (unsigned)g.F && (unsigned)ys < (unsigned)g.Hp && (unsigned)xs < (unsigned)g.Wp;
+        ld8(ok ? x + (size_t)((ts * g.Hp + ys) * g.Wp + xs) * g.C + c : zero, v[i]);
       }
-    }
-  float* pp = part + ((size_t)t * g.C + c) * (g.taps + 1);
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
-    if (tg + i * DW_TG < g.taps) pp[tg + i * DW_TG] = acc[i];
-  if (tg == 0) pp[g.taps] = bsum;
+      for (int e = 0; e < 8; ++e) bs[e] += d[e];
+#pragma unroll
+      for (int i = 0; i < DW_TAPS; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(d[e], v[i][e], acc[i][e]);
+    }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float* p = part + (((size_t)t * sp.nyc + yc) * g.C + c + e) * (g.taps + 1);
+#pragma unroll
+    for (int i = 0; i < DW_TAPS; ++i)
+      if (i < ntap) p[tap0 + i] = acc[i][e];
+    if (tc == 0) p[g.taps] = bs[e];
+  }
 }
 
-// dw[c][tap] (and db[c]) = sum over frames in order of the partial sums.
+// dw[c][tap] (and db[c]) = sum of the partial sums, frames and row spans in order.
 __global__ __launch_bounds__(256) void k_dwconv_dw_sum(const float* __restrict__ part, float* __restrict__ dw,
-                                                       float* __restrict__ db, CGeom g) {
+                                                       float* __restrict__ db, CGeom g, int nparts) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long per = (long long)g.C * (g.taps + 1);
   if (i >= per) return;
   float s = 0.f;
-  for (int t = 0; t < g.F; ++t) s += part[(size_t)t * per + i];
+  for (int t = 0; t < nparts; ++t) s += part[(size_t)t * per + i];
   const int c = (int)(i / (g.taps + 1)), tap = (int)(i - (long long)c * (g.taps + 1));
   if (tap < g.taps) {
     dw[(size_t)c * g.taps + tap] = s;
@@ -165,34 +320,60 @@ __global__ __launch_bounds__(256) void k_dwconv_dw_sum(const float* __restrict__
   }
 }
 
-template <typename T>
-static hipError_t conv_launch(const void* x, const float* w, const float* b, void* y, const CGeom& g, int acc,
-                              int flip, hipStream_t s) {
-  const size_t lds = (size_t)g.taps * CONV_CB * 4;  // the block's filters, up to 128 KiB
-  // dynamic LDS past 64 KiB needs the kernel's limit raised (a host-side attribute)
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dwconv<T>),
+template <typename T, int CX>
+static hipError_t conv_launch_w(const void* x, const float* w, const float* b, void* y, const CGeom& g, int acc,
+                                int flip, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dwconv_w<T, CX>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      CONV_MAX_TAPS * CONV_CB * 4);
   if (attr != hipSuccess) return attr;
-  dim3 grid((g.N + CONV_TOK - 1) / CONV_TOK, (g.C + CONV_CB - 1) / CONV_CB);
-  k_dwconv<T><<<grid, 256, lds, s>>>((const T*)x, w, b, (T*)y, g, acc, flip);
+  const long long nquads = (long long)g.F * g.Hp * ((g.Wp + CONV_Q - 1) / CONV_Q);
+  const long long total = ((nquads + CONV_TOK - 1) / CONV_TOK) * ((g.C + CONV_CB - 1) / CONV_CB);
+  k_dwconv_w<T, CX><<<(unsigned)total, 256, (size_t)g.taps * CONV_CB * 4, s>>>((const T*)x, w, b, (T*)y, g, acc,
+                                                                              flip);
   return hipGetLastError();
 }
 
-template <typename T, int MT>
-static void dw_launch(const void* x, const void* dy, float* part, const CGeom& g, hipStream_t s) {
-  dim3 grid(g.F, (g.C + DW_CH - 1) / DW_CH);
-  k_dwconv_dw<T, MT><<<grid, 256, 0, s>>>((const T*)x, (const T*)dy, part, g);
+template <typename T>
+static hipError_t conv_launch(const void* x, const float* w, const float* b, void* y, const CGeom& g, int acc,
+                              int flip, hipStream_t s) {
+  switch (g.cx) {
+    case 1: return conv_launch_w<T, 1>(x, w, b, y, g, acc, flip, s);
+    case 3: return conv_launch_w<T, 3>(x, w, b, y, g, acc, flip, s);
+    case 5: return conv_launch_w<T, 5>(x, w, b, y, g, acc, flip, s);
+    case 7: return conv_launch_w<T, 7>(x, w, b, y, g, acc, flip, s);
+    case 9: return conv_launch_w<T, 9>(x, w, b, y, g, acc, flip, s);
+    default: break;
+  }
+  const size_t lds = (size_t)g.taps * (CONV_CB + 1) * 4;  // filters and tap shifts, up to 130 KiB
+  // dynamic LDS past 64 KiB needs the kernel's limit raised (a host-side attribute)
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dwconv<T>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     CONV_MAX_TAPS * (CONV_CB + 1) * 4);
+  if (attr != hipSuccess) return attr;
+  const long long nquads = (long long)g.F * g.Hp * ((g.Wp + CONV_Q - 1) / CONV_Q);
+  const long long total = ((nquads + CONV_TOK - 1) / CONV_TOK) * ((g.C + CONV_CB - 1) / CONV_CB);
+  k_dwconv<T><<<(unsigned)total, 256, lds, s>>>((const T*)x, w, b, (T*)y, g, acc, flip);
+  return hipGetLastError();
+}
+
+// Row spans per frame: enough blocks to fill the chip (>= 1024) without splitting rows.
+static DwSplit dw_split(const CGeom& g) {
+  DwSplit sp;
+  sp.ncb = (g.C + DW_CPB - 1) / DW_CPB;
+  sp.ntc = (g.taps + DW_TAPS - 1) / DW_TAPS;
+  const long long base = (long long)sp.ncb * sp.ntc * g.F;
+  sp.nyc = (int)std::min<long long>(g.Hp, std::max<long long>(1, (1024 + base - 1) / base));
+  sp.rows = (g.Hp + sp.nyc - 1) / sp.nyc;
+  sp.nyc = (g.Hp + sp.rows - 1) / sp.rows;
+  return sp;
 }
 
 template <typename T>
-static hipError_t dw_dispatch(const void* x, const void* dy, float* part, const CGeom& g, hipStream_t s) {
-  const int mt = (g.taps + DW_TG - 1) / DW_TG;
-  if (mt <= 4) dw_launch<T, 4>(x, dy, part, g, s);
-  else if (mt <= 8) dw_launch<T, 8>(x, dy, part, g, s);
-  else if (mt <= 16) dw_launch<T, 16>(x, dy, part, g, s);
-  else if (mt <= 32) dw_launch<T, 32>(x, dy, part, g, s);
-  else dw_launch<T, DW_MAXT>(x, dy, part, g, s);
+static hipError_t dw_launch(const void* x, const void* dy, float* part, const CGeom& g, const DwSplit& sp,
+                            hipStream_t s) {
+  const long long total = (long long)sp.ncb * sp.ntc * sp.nyc * g.F;
+  k_dwconv_dw<T><<<(unsigned)total, 256, 0, s>>>((const T*)x, (const T*)dy, part, g, sp);
   return hipGetLastError();
 }
 
@@ -218,7 +399,10 @@ int check_conv(const void* x, const float* w, int F, int Hp, int Wp, int C, int 
   return DSA3D_OK;
 }
 
-size_t conv_ws(const CGeom& g) { return (((size_t)g.F * g.C * (g.taps + 1) * 4) + 255) & ~(size_t)255; }
+size_t conv_ws(const CGeom& g) {
+  const DwSplit sp = dw_split(g);
+  return (((size_t)g.F * sp.nyc * g.C * (g.taps + 1) * 4) + 255) & ~(size_t)255;
+}
 
 }  // namespace
 
@@ -261,10 +445,11 @@ int dsa3d_dwconv3d_backward(const void* x, const float* weight, const void* dy, 
   hipError_t e = bf ? conv_launch<u16>(dy, weight, nullptr, dx, g, 0, 1, stream)
                     : conv_launch<float>(dy, weight, nullptr, dx, g, 0, 1, stream);
   if (e != hipSuccess) return DSA3D_ERR_LAUNCH;
-  e = bf ? dw_dispatch<u16>(x, dy, part, g, stream) : dw_dispatch<float>(x, dy, part, g, stream);
+  const DwSplit sp = dw_split(g);
+  e = bf ? dw_launch<u16>(x, dy, part, g, sp, stream) : dw_launch<float>(x, dy, part, g, sp, stream);
   if (e != hipSuccess) return DSA3D_ERR_LAUNCH;
   const long long per = (long long)g.C * (g.taps + 1);
-  k_dwconv_dw_sum<<<(unsigned)((per + 255) / 256), 256, 0, stream>>>(part, dweight, dbias, g);
+  k_dwconv_dw_sum<<<(unsigned)((per + 255) / 256), 256, 0, stream>>>(part, dweight, dbias, g, g.F * sp.nyc);
   return hipGetLastError() == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
 

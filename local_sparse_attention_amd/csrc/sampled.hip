@@ -70,6 +70,28 @@ __device__ __forceinline__ void store8(float* p, const float* x) {
   store4(p + 4, x[4], x[5], x[6], x[7]);
 }
 
+// Raw 16- (bf16) or 32-byte (fp32) loads of 8 row elements, converted after all the loads
+// of a batch are issued, so a lane keeps a batch of corner rows in flight.
+template <typename T> struct Raw8;
+template <> struct Raw8<u16> { uint4 u; };
+template <> struct Raw8<float> { float4 a, b; };
+__device__ __forceinline__ Raw8<u16> ldraw(const u16* p) { return {*reinterpret_cast<const uint4*>(p)}; }
+__device__ __forceinline__ Raw8<float> ldraw(const float* p) {
+  return {reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
+}
+__device__ __forceinline__ void unraw(const Raw8<u16>& r, float* x) {
+  const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unraw(const Raw8<float>& r, float* x) {
+  x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+  x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+}
+
 __device__ __forceinline__ float dot8(const float* a, const float* b) {
   float s = 0.f;
 #pragma unroll
@@ -126,10 +148,10 @@ __device__ __forceinline__ QPos query_pos(const SGeom& g, const float* off, int 
   return q;
 }
 
-// Position of sample j: floor (i) and fraction (f) per axis.
-__device__ __forceinline__ void sample_pos(const SGeom& g, const QPos& q, int j, int* i, float* f) {
-  const int u = j / (g.ky * g.kx), r = j - u * (g.ky * g.kx), v = r / g.kx, w = r - v * g.kx;
-  const int lat[3] = {u, v, w};
+// Position of sample j = (u, v, w) (lat packs u << 20 | v << 10 | w): floor (i) and
+// fraction (f) per axis.
+__device__ __forceinline__ void sample_pos_lat(const SGeom& g, const QPos& q, int j, int packed, int* i, float* f) {
+  const int lat[3] = {packed >> 20, (packed >> 10) & 1023, packed & 1023};
   if (g.mode == DSA3D_SAMPLE_BOX) {
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
@@ -148,6 +170,22 @@ __device__ __forceinline__ void sample_pos(const SGeom& g, const QPos& q, int j,
       f[d] = od - fl;
     }
   }
+}
+
+__device__ __forceinline__ int lattice_of(const SGeom& g, int j) {
+  const int u = j / (g.ky * g.kx), r = j - u * (g.ky * g.kx), v = r / g.kx, w = r - v * g.kx;
+  return (u << 20) | (v << 10) | w;
+}
+
+__device__ __forceinline__ void sample_pos(const SGeom& g, const QPos& q, int j, int* i, float* f) {
+  sample_pos_lat(g, q, j, lattice_of(g, j), i, f);
+}
+
+// The lattice of every sample (window extents < 1024) in LDS, shared by a block's waves.
+constexpr int MAX_SAMPLES = 4096;
+__device__ __forceinline__ void fill_lattice(const SGeom& g, int* lat) {
+  for (int j = threadIdx.x; j < g.K; j += blockDim.x) lat[j] = lattice_of(g, j);
+  __syncthreads();
 }
 
 // Corner c (bits t, y, x) of a sample: token (-1 outside the grid) and weight.
@@ -171,6 +209,8 @@ __global__ __launch_bounds__(256) void k_sampled_fwd(const T* __restrict__ q, co
                                                      const T* __restrict__ v, const float* __restrict__ off,
                                                      T* __restrict__ out, float* __restrict__ lse, SGeom g) {
   constexpr int G = D / EL, NG = 64 / G;
+  __shared__ int lat[MAX_SAMPLES];
+  fill_lattice(g, lat);
   const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wv >= (long long)g.N * g.H) return;
   const int n = (int)(wv / g.H), h = (int)(wv - (long long)n * g.H);
@@ -187,22 +227,33 @@ __global__ __launch_bounds__(256) void k_sampled_fwd(const T* __restrict__ q, co
   for (int j = grp; j < g.K; j += NG) {
     int i[3];
     float f[3];
-    sample_pos(g, qp, j, i, f);
-    float ks[EL], vs[EL], x[EL];
+    sample_pos_lat(g, qp, j, lat[j], i, f);
+    float ks[EL], vs[EL], x[EL], wc[8];
+    size_t rr[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // a corner outside the grid or of zero weight reads the query's own row (w = 0)
+      const int tok = corner_tok(g, i, c);
+      const float w = corner_w(f, c);
+      const bool ok = tok >= 0 && w != 0.f;
+      wc[c] = ok ? w : 0.f;
+      rr[c] = ((size_t)(ok ? tok : n) * g.H + h) * D + gl * EL;
+    }
+    Raw8<T> kr[8], vr[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) kr[c] = ldraw(k + rr[c]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) vr[c] = ldraw(v + rr[c]);
 #pragma unroll
     for (int e = 0; e < EL; ++e) ks[e] = vs[e] = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int tok = corner_tok(g, i, c);
-      const float w = corner_w(f, c);
-      if (tok < 0 || w == 0.f) continue;
-      const size_t r = ((size_t)tok * g.H + h) * D + gl * EL;
-      load8(k + r, x);
+      unraw(kr[c], x);
 #pragma unroll
-      for (int e = 0; e < EL; ++e) ks[e] = fmaf(w, x[e], ks[e]);
-      load8(v + r, x);
+      for (int e = 0; e < EL; ++e) ks[e] = fmaf(wc[c], x[e], ks[e]);
+      unraw(vr[c], x);
 #pragma unroll
-      for (int e = 0; e < EL; ++e) vs[e] = fmaf(w, x[e], vs[e]);
+      for (int e = 0; e < EL; ++e) vs[e] = fmaf(wc[c], x[e], vs[e]);
     }
     const float s = gsum<G>(dot8(qf, ks)) * sl2;
     const float mn = fmaxf(m, s);
@@ -243,6 +294,8 @@ __global__ __launch_bounds__(256) void k_sampled_bwd_q(const T* __restrict__ q, 
                                                        float* __restrict__ coef_a, float* __restrict__ coef_g,
                                                        float* __restrict__ gpos, SGeom g) {
   constexpr int G = D / EL, NG = 64 / G;
+  __shared__ int lat[MAX_SAMPLES];
+  fill_lattice(g, lat);
   const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wv >= (long long)g.N * g.H) return;
   const int n = (int)(wv / g.H), h = (int)(wv - (long long)n * g.H);
@@ -264,38 +317,55 @@ __global__ __launch_bounds__(256) void k_sampled_bwd_q(const T* __restrict__ q, 
   for (int j = grp; j < g.K; j += NG) {
     int i[3];
     float f[3];
-    sample_pos(g, qp, j, i, f);
+    sample_pos_lat(g, qp, j, lat[j], i, f);
     float ks[EL], vs[EL], kd[3][EL], vd[3][EL];
 #pragma unroll
     for (int e = 0; e < EL; ++e) {
       ks[e] = vs[e] = 0.f;
       kd[0][e] = kd[1][e] = kd[2][e] = vd[0][e] = vd[1][e] = vd[2][e] = 0.f;
     }
+    // the 8 corners' weights and weight derivatives (0 for corners outside the grid,
+    // which read the query's own row); then all K rows, then all V rows, each batch of
+    // loads issued before its products
+    float wc[8], dwc[8][3];
+    size_t rr[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int tok = corner_tok(g, i, c);
-      if (tok < 0) continue;
+      const bool ok = tok >= 0;
       const float pt = (c & 4) ? f[0] : 1.f - f[0], py = (c & 2) ? f[1] : 1.f - f[1],
                   px = (c & 1) ? f[2] : 1.f - f[2];
-      const float w = pt * py * px;
-      const float dw[3] = {((c & 4) ? 1.f : -1.f) * py * px, ((c & 2) ? 1.f : -1.f) * pt * px,
-                           ((c & 1) ? 1.f : -1.f) * pt * py};
-      const size_t r = ((size_t)tok * g.H + h) * D + gl * EL;
-      load8(k + r, x);
+      wc[c] = ok ? pt * py * px : 0.f;
+      dwc[c][0] = ok ? ((c & 4) ? 1.f : -1.f) * py * px : 0.f;
+      dwc[c][1] = ok ? ((c & 2) ? 1.f : -1.f) * pt * px : 0.f;
+      dwc[c][2] = ok ? ((c & 1) ? 1.f : -1.f) * pt * py : 0.f;
+      rr[c] = ((size_t)(ok ? tok : n) * g.H + h) * D + gl * EL;
+    }
+    Raw8<T> raw[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) raw[c] = ldraw(k + rr[c]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      unraw(raw[c], x);
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        ks[e] = fmaf(w, x[e], ks[e]);
-        kd[0][e] = fmaf(dw[0], x[e], kd[0][e]);
-        kd[1][e] = fmaf(dw[1], x[e], kd[1][e]);
-        kd[2][e] = fmaf(dw[2], x[e], kd[2][e]);
+        ks[e] = fmaf(wc[c], x[e], ks[e]);
+        kd[0][e] = fmaf(dwc[c][0], x[e], kd[0][e]);
+        kd[1][e] = fmaf(dwc[c][1], x[e], kd[1][e]);
+        kd[2][e] = fmaf(dwc[c][2], x[e], kd[2][e]);
       }
-      load8(v + r, x);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) raw[c] = ldraw(v + rr[c]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      unraw(raw[c], x);
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        vs[e] = fmaf(w, x[e], vs[e]);
-        vd[0][e] = fmaf(dw[0], x[e], vd[0][e]);
-        vd[1][e] = fmaf(dw[1], x[e], vd[1][e]);
-        vd[2][e] = fmaf(dw[2], x[e], vd[2][e]);
+        vs[e] = fmaf(wc[c], x[e], vs[e]);
+        vd[0][e] = fmaf(dwc[c][0], x[e], vd[0][e]);
+        vd[1][e] = fmaf(dwc[c][1], x[e], vd[1][e]);
+        vd[2][e] = fmaf(dwc[c][2], x[e], vd[2][e]);
       }
     }
     const float z = gsum<G>(dot8(qf, ks));
@@ -365,12 +435,34 @@ __global__ __launch_bounds__(256) void k_sampled_keys(const float* __restrict__ 
   keys[e] = key;
 }
 
+// The sorted samples as contiguous records for the key side: sorted position i holds
+// (query token, fractions f_t, f_y, f_x of its position) and (alpha, scale * dz), so a
+// key's wave reads its samples in order with no index arithmetic.
+__global__ __launch_bounds__(256) void k_sampled_pack(const float* __restrict__ off, const int* __restrict__ ids,
+                                                      const float* __restrict__ coef_a,
+                                                      const float* __restrict__ coef_g, int n_sorted,
+                                                      int4* __restrict__ rec, float2* __restrict__ rcoef, SGeom g) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_sorted) return;
+  const int e = ids[i];
+  const int j = e % g.K;
+  const int hn = e / g.K;
+  const int n = hn % g.N, h = hn / g.N;
+  const QPos qp = query_pos(g, off, n, h);
+  int ip[3];
+  float f[3];
+  sample_pos(g, qp, j, ip, f);
+  rec[i] = make_int4(n, __float_as_int(f[0]), __float_as_int(f[1]), __float_as_int(f[2]));
+  rcoef[i] = make_float2(coef_a[e], coef_g[e]);
+}
+
+constexpr int DK_B = 4;  // samples per lane group in flight on the key side
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_sampled_dkdv(const T* __restrict__ q, const T* __restrict__ dout,
-                                                      const float* __restrict__ off, const int* __restrict__ ids,
-                                                      const int* __restrict__ cell_ptr,
-                                                      const float* __restrict__ coef_a,
-                                                      const float* __restrict__ coef_g, T* __restrict__ dk,
+                                                      const int4* __restrict__ rec,
+                                                      const float2* __restrict__ rcoef,
+                                                      const int* __restrict__ cell_ptr, T* __restrict__ dk,
                                                       T* __restrict__ dv, SGeom g) {
   constexpr int G = D / EL, NG = 64 / G;
   const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -389,23 +481,39 @@ __global__ __launch_bounds__(256) void k_sampled_dkdv(const T* __restrict__ q, c
     const int bt = (c >> 2) & 1, by = (c >> 1) & 1, bx = c & 1;
     const int cell = h * ncell + ((mt - bt + 1) * (g.Hp + 1) + (my - by + 1)) * (g.Wp + 1) + (mx - bx + 1);
     const int beg = cell_ptr[cell], end = cell_ptr[cell + 1];
-    for (int it = beg + grp; it < end; it += NG) {
-      const int e = ids[it];
-      const int j = e % g.K;
-      const int n = (e / g.K) % g.N;
-      const QPos qp = query_pos(g, off, n, h);
-      int i[3];
-      float f[3];
-      sample_pos(g, qp, j, i, f);
-      const float w = corner_w(f, c);
-      const float a = w * coef_a[e], gz = w * coef_g[e];
-      const size_t r = ((size_t)n * g.H + h) * D + gl * EL;
-      load8(dout + r, x);
+    // DK_B samples per lane group at a time: their records, then all their q / dO rows,
+    // then the products (samples past the cell add zero)
+    for (int base = beg; base < end; base += NG * DK_B) {
+      int nn[DK_B];
+      float a[DK_B], gz[DK_B];
 #pragma unroll
-      for (int t = 0; t < EL; ++t) dva[t] = fmaf(a, x[t], dva[t]);
-      load8(q + r, x);
+      for (int b = 0; b < DK_B; ++b) {
+        const int it = base + grp + b * NG;
+        const bool ok = it < end;
+        const int4 r = rec[ok ? it : beg];
+        const float2 cf = rcoef[ok ? it : beg];
+        const float f[3] = {__int_as_float(r.y), __int_as_float(r.z), __int_as_float(r.w)};
+        const float w = ok ? corner_w(f, c) : 0.f;
+        nn[b] = r.x;
+        a[b] = w * cf.x;
+        gz[b] = w * cf.y;
+      }
+      Raw8<T> dr[DK_B], qr[DK_B];
 #pragma unroll
-      for (int t = 0; t < EL; ++t) dka[t] = fmaf(gz, x[t], dka[t]);
+      for (int b = 0; b < DK_B; ++b) {
+        const size_t r = ((size_t)nn[b] * g.H + h) * D + gl * EL;
+        dr[b] = ldraw(dout + r);
+        qr[b] = ldraw(q + r);
+      }
+#pragma unroll
+      for (int b = 0; b < DK_B; ++b) {
+        unraw(dr[b], x);
+#pragma unroll
+        for (int t = 0; t < EL; ++t) dva[t] = fmaf(a[b], x[t], dva[t]);
+        unraw(qr[b], x);
+#pragma unroll
+        for (int t = 0; t < EL; ++t) dka[t] = fmaf(gz[b], x[t], dka[t]);
+      }
     }
   }
 #pragma unroll
@@ -462,6 +570,8 @@ struct SampledWs {
   float* coef_a;
   float* coef_g;
   float* gpos;
+  int4* rec;      // sorted samples: (token, fractions)
+  float2* rcoef;  //                 (alpha, scale * dz)
   int passes;
 };
 
@@ -490,6 +600,8 @@ size_t sampled_layout(const SGeom& g, char* base, SampledWs* w) {
   s.coef_a = (float*)take(E * 4);
   s.coef_g = (float*)take(E * 4);
   s.gpos = (float*)take((g.mode == DSA3D_SAMPLE_BOX ? (size_t)g.N * g.H : E) * 3 * 4);
+  s.rec = (int4*)take(E * sizeof(int4));
+  s.rcoef = (float2*)take(E * sizeof(float2));
   s.passes = (bits + 7) / 8;
   if (w) *w = s;
   return off;
@@ -531,8 +643,13 @@ static hipError_t sampled_bwd_impl(const void* q, const void* k, const void* v, 
   k_sampled_bwd_q<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)k, (const T*)v, (const T*)o,
                                                           (const T*)dout, lse, off, (T*)dq, w.coef_a, w.coef_g,
                                                           w.gpos, g);
-  k_sampled_dkdv<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)dout, off, vals[cur], w.cell_ptr,
-                                                         w.coef_a, w.coef_g, (T*)dk, (T*)dv, g);
+  // every sample is packed; those with all corners outside the grid sort after every
+  // cell and are never visited
+  const int n_sorted = (int)E;
+  k_sampled_pack<<<nblocks(n_sorted, 256), 256, 0, s>>>(off, vals[cur], w.coef_a, w.coef_g, n_sorted, w.rec,
+                                                        w.rcoef, g);
+  k_sampled_dkdv<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)dout, w.rec, w.rcoef, w.cell_ptr,
+                                                         (T*)dk, (T*)dv, g);
   const long long nout = (long long)g.N * (g.sh == 0 ? 1 : g.H) *
                          ((g.mode == DSA3D_SAMPLE_BOX || g.ss == 0) ? 1 : g.K);
   k_sampled_doff<<<nblocks(nout, 256), 256, 0, s>>>(w.gpos, doff, g);
