@@ -84,11 +84,54 @@ def kernel_work(wl):
     }
 
 
+# the sources the integer-offset path's kernels are built from (the counters in
+# profiles/traffic.json are valid while these are unchanged)
+MAIN_PATH_SOURCES = ("attn_fwd.hip", "attn_dq.hip", "attn_dkdv.hip", "attn.hip", "prep.hip", "qsched.hip",
+                     "common.hpp", "internal.hpp", "qs_common.hpp", "tube.hpp")
+
+
 def source_hash():
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "local_sparse_attention_amd", "csrc", "*"))):
-        h.update(open(f, "rb").read())
+    for f in MAIN_PATH_SOURCES:
+        h.update(open(os.path.join(ROOT, "local_sparse_attention_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def _short(name):
+    return name.split("(")[0].split("<")[0].replace("void ", "").replace("dsa3d::", "").strip()
+
+
+def _counter_means(csv_path, counter):
+    """Mean value per dispatch of `counter` for each kernel in a rocprofv3 counter CSV."""
+    import csv
+
+    acc = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        k = _short(r["Kernel_Name"])
+        acc.setdefault(k, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload):
+    """profiles/traffic.json from two rocprofv3 --pmc runs of the benchmark (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) and the same two counters over a device copy of known size
+    (bench.py --copy-calibration, 3 launches of 1 GiB read + 1 GiB written)."""
+    fetch, write = _counter_means(fetch_csv, "FETCH_SIZE"), _counter_means(write_csv, "WRITE_SIZE")
+    cf, cw = _counter_means(copy_fetch_csv, "FETCH_SIZE"), _counter_means(copy_write_csv, "WRITE_SIZE")
+    copy_name = max(cf, key=cf.get)
+    fs = (1 << 30) / (cf[copy_name] * 1024.0)
+    ws = (1 << 30) / (cw[copy_name] * 1024.0)
+    kernels = {}
+    for k in sorted(set(fetch) & set(write)):
+        rb, wb = fetch[k] * 1024.0 * fs, write[k] * 1024.0 * ws
+        kernels[k] = {"hbm_bytes_per_launch": rb + wb, "read_bytes": rb, "write_bytes": wb}
+    out = {"workload": workload, "source_hash": source_hash(), "fetch_scale": fs, "write_scale": ws,
+           "copy_kernel": copy_name, "kernels": kernels, "summary": "dsa3d_256frame_fwd_bwd.md",
+           "note": "bytes between L2 and the memory fabric (Infinity-Cache hits included), per dispatch"}
+    json.dump(out, open(os.path.join(ROOT, "profiles", "traffic.json"), "w"), indent=1)
+    return out
 
 
 def measured_traffic(kernel, workload):
@@ -292,6 +335,46 @@ def run_sampled(dsa3d, steps, warmup):
     return res
 
 
+def run_c2_warm_cold(dsa3d, steps):
+    """The bf16 forward workload (16 x 32 x 32, 8 heads x 64, 3 x 7 x 7; its tensors, 16.8 MB
+    each, fit the 256 MB Infinity Cache): forward time with the inputs warm from the previous
+    call, and after a 1 GiB write that scrubs the caches before each call."""
+    import torch
+
+    from local_sparse_attention_amd import configs, synth
+
+    wl = configs.C2
+    grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
+    inp = synth.make_inputs(wl, with_dout=False)
+    t = {k: torch.from_numpy(inp[k].view("int16")).cuda().view(torch.bfloat16) for k in ("q", "k", "v")}
+    off = torch.from_numpy(inp["offsets"]).cuda()
+    out = torch.empty_like(t["q"])
+    lse = torch.empty((wl.heads, wl.N), dtype=torch.float32, device="cuda")
+    ws = dsa3d.workspace(grid, wl.heads, window, False)
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        dsa3d.forward(t["q"], t["k"], t["v"], off, grid, window, wl.scale, out=out, lse=lse, ws=ws)
+
+    warm = _timed(fwd, steps, 3)
+    cold = []
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(steps):
+        scrub.fill_(1)
+        a.record()
+        fwd()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del t, off, out, lse, ws, scrub
+    torch.cuda.empty_cache()
+    cold_ms = sorted(cold)[len(cold) // 2]
+    return {"workload": f"{wl.name}: grid {wl.F}x{wl.Hp}x{wl.Wp}, {wl.heads} heads x {wl.head_dim}, window "
+                        f"{wl.kt}x{wl.ky}x{wl.kx}, bf16, forward (prep + attention)",
+            "warm_ms": warm, "cold_ms": cold_ms,
+            "note": "warm: mean of back-to-back calls; cold: median over calls each preceded by a 1 GiB fill"}
+
+
 def run_predictor(dsa3d, steps, warmup):
     """The DWConv3D term of Eq. (1) on the 256-frame grid (hidden 16 x 128 = 2048 channels,
     3 x 3 x 3 filter: the pages give no size), added into an attention output, forward and
@@ -375,7 +458,14 @@ def main():
                     help="main line only: no measured peaks, linear-in-N run or operator variants")
     ap.add_argument("--variants-only", action="store_true",
                     help="only the operator variants (for profiling their kernels)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 counter CSVs (no GPU needed)")
     args = ap.parse_args()
+    if args.write_traffic:
+        from local_sparse_attention_amd import configs
+
+        print(json.dumps(write_traffic(*args.write_traffic, configs.ALL[args.workload].name)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards by heads without "
               "communication, so an N-GPU figure would be N independent copies of this run.", file=sys.stderr)
@@ -570,6 +660,8 @@ def main():
         res.setdefault("variants", {}).update(run_sampled(dsa3d, 3, 1))
         log("DWConv3D term and offset predictor")
         res["variants"].update(run_predictor(dsa3d, 3, 1))
+        log("bf16 forward workload, warm and cold caches")
+        res["c2_forward_warm_cold"] = run_c2_warm_cold(dsa3d, 10)
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(wl)
