@@ -68,7 +68,8 @@ def test_workspace_bytes(lib):
     assert lib.dsa3d_workspace_bytes(4, 8, 8, 0, 3, 3, 3, 0) == 0
 
 
-P = 1 << 20  # a fake, aligned, non-null "device" address: validation fails before any use
+P = 1 << 20  # a fake, aligned, non-null "device" address: every call below fails validation
+# before any launch (calls meant to be valid stop at a deliberately null output)
 
 
 def fwd(lib, flags=None, **kw):
@@ -186,3 +187,120 @@ def test_binding_checks_shapes_and_dtypes(lib):
         dsa3d.backward(q, q, q, off, q, lse, q, grid, window, dv=q[:10])
     with pytest.raises(E, match="offsets has dtype"):
         dsa3d.window_starts(off.long(), grid, window)
+
+
+ERR_MODE, ERR_LAYOUT = -12, -13
+
+
+def test_status_strings_of_the_wider_forms(lib):
+    for code in (ERR_MODE, ERR_LAYOUT):
+        assert dsa3d.status_string(code) != "unknown status"
+
+
+def sampled_fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, off=P, sn=3, sh=0, ss=0, mode=0, F=4, Hp=8, Wp=8, H=2, D=64, kt=3, ky=3, kx=3,
+             scale=0.125, dtype=1, out=P, lse=P)
+    a.update(kw)
+    return lib.dsa3d_sampled_forward(a["q"], a["k"], a["v"], a["off"], a["sn"], a["sh"], a["ss"], a["mode"], a["F"],
+                                     a["Hp"], a["Wp"], a["H"], a["D"], a["kt"], a["ky"], a["kx"], a["scale"],
+                                     a["dtype"], a["out"], a["lse"], None)
+
+
+def test_sampled_validation(lib):
+    f = sampled_fwd
+    assert f(lib, q=None) == ERR_NULL
+    assert f(lib, off=None) == ERR_NULL
+    assert f(lib, mode=2) == ERR_MODE
+    assert f(lib, dtype=3) == ERR_DTYPE
+    assert f(lib, D=32) == ERR_HEAD_DIM
+    assert f(lib, kt=2) == ERR_WINDOW
+    assert f(lib, kt=5) == ERR_WINDOW                      # box windows must fit the grid
+    # free positions may leave the grid (a valid call: out=None stops it before any launch)
+    assert f(lib, kt=5, mode=1, ss=3, sh=135, sn=270, out=None) == ERR_NULL
+    assert f(lib, kt=17, ky=17, kx=17, mode=1, ss=3, sh=3 * 4913, sn=6 * 4913) == ERR_WINDOW  # > 4096 samples
+    assert f(lib, scale=float("nan")) == ERR_SCALE
+    assert f(lib, ss=3) == ERR_LAYOUT                      # box mode takes one offset per (query, head)
+    assert f(lib, sn=2) == ERR_LAYOUT                      # entries of 3 floats overlap
+    assert f(lib, sh=1) == ERR_LAYOUT                      # heads overlap the tokens' entries
+    assert f(lib, sh=-3) == ERR_LAYOUT
+    # valid layouts get as far as the output check (out=None): [N][H][3] and [H][N][3]
+    assert f(lib, sn=6, sh=3, out=None) == ERR_NULL
+    assert f(lib, sn=3, sh=3 * 256, out=None) == ERR_NULL
+    assert f(lib, q=P + 4) == ERR_ALIGN
+    assert f(lib, off=P + 2) == ERR_ALIGN
+    assert f(lib, out=None) == ERR_NULL
+    free = dict(mode=1, sn=3 * 2 * 27, sh=3 * 27, ss=3)
+    assert f(lib, **{**free, "sh": 3 * 26}) == ERR_LAYOUT  # samples of two heads overlap
+    assert f(lib, **free, out=None) == ERR_NULL
+    # workspace sizes: 0 for invalid geometry, the forward needs none
+    ws = lib.dsa3d_sampled_workspace_bytes
+    assert ws(4, 8, 8, 2, 3, 3, 3, 0, 0) == 256
+    assert ws(4, 8, 8, 2, 3, 3, 3, 1, 1) > 4 * 8 * 8 * 2 * 27 * 36
+    assert ws(4, 8, 8, 2, 2, 3, 3, 1, 1) == 0
+    assert ws(4, 8, 8, 2, 3, 3, 3, 5, 1) == 0
+
+
+def test_sampled_backward_validation(lib):
+    f = lib.dsa3d_sampled_backward
+    base = [P, P, P, P, 3, 0, 0, 0, P, P, P, 4, 8, 8, 2, 64, 3, 3, 3, 0.125, 1, P, P, P, P, P]
+    args = list(base)
+    args[25] = None  # workspace
+    assert f(*args, 1 << 40, None) == ERR_NULL
+    assert f(*base, 100, None) == ERR_WORKSPACE
+    args = list(base)
+    args[24] = P + 2  # doffsets misaligned
+    assert f(*args, 1 << 40, None) == ERR_ALIGN
+
+
+def test_heads_validation(lib):
+    f = lib.dsa3d_forward_heads
+    ok = [P, P, P, P, 4, 8, 8, 2, 64, 3, 3, 3, 0.125, 1, P, P, P, 1 << 40, None]
+    assert f(*ok, 4) == ERR_FLAGS
+    bad = list(ok)
+    bad[16] = None
+    assert f(*bad, 0) == ERR_NULL
+    bad = list(ok)
+    bad[17] = 100
+    assert f(*bad, 0) == ERR_WORKSPACE
+    b = lib.dsa3d_backward_heads
+    okb = [P] * 7 + [4, 8, 8, 2, 64, 3, 3, 3, 0.125, 0, P, P, P, P, 1 << 40, None]
+    assert b(*okb, 2) == ERR_FLAGS
+    bad = list(okb)
+    bad[11] = 96  # head_dim
+    assert b(*bad, 0) == ERR_HEAD_DIM
+
+
+def test_dwconv_and_linear_validation(lib):
+    fw = lib.dsa3d_dwconv3d_forward
+    ok = [P, P, P, 4, 8, 8, 64, 3, 3, 3, 1, P, 0, None]
+    assert fw(*[None] + ok[1:]) == ERR_NULL
+    bad = list(ok); bad[6] = 12  # C not a multiple of 8
+    assert fw(*bad) == ERR_GRID
+    bad = list(ok); bad[7] = 2
+    assert fw(*bad) == ERR_WINDOW
+    bad = list(ok); bad[7], bad[8], bad[9] = 9, 9, 9  # 729 taps > 512
+    assert fw(*bad) == ERR_WINDOW
+    bad = list(ok); bad[10] = 2
+    assert fw(*bad) == ERR_DTYPE
+    bad = list(ok); bad[11] = P + 8
+    assert fw(*bad) == ERR_ALIGN
+    assert lib.dsa3d_dwconv3d_workspace_bytes(4, 8, 8, 64, 3, 3, 3) > 0
+    assert lib.dsa3d_dwconv3d_workspace_bytes(4, 8, 8, 63, 3, 3, 3) == 0
+    bw = lib.dsa3d_dwconv3d_backward
+    okb = [P, P, P, 4, 8, 8, 64, 3, 3, 3, 1, P, P, P, P, 1 << 40, None]
+    bad = list(okb); bad[15] = 10
+    assert bw(*bad) == ERR_WORKSPACE
+    lf = lib.dsa3d_linear_forward
+    okl = [P, P, P, 100, 64, 81, 1, P, None]
+    bad = list(okl); bad[3] = 0
+    assert lf(*bad) == ERR_GRID
+    bad = list(okl); bad[6] = 5
+    assert lf(*bad) == ERR_DTYPE
+    bad = list(okl); bad[1] = P + 4
+    assert lf(*bad) == ERR_ALIGN
+    assert lib.dsa3d_linear_workspace_bytes(100, 64, 81, 1) > 0
+    assert lib.dsa3d_linear_workspace_bytes(1 << 20, 1 << 12, 81, 1) == 0  # M K >= 2^31
+    lb = lib.dsa3d_linear_backward
+    okb = [P, P, P, 100, 64, 81, 1, P, P, P, P, 1 << 40, None]
+    bad = list(okb); bad[11] = 1
+    assert lb(*bad) == ERR_WORKSPACE
