@@ -304,6 +304,91 @@ __global__ __launch_bounds__(256) void k_dwconv_dw(const T* __restrict__ x, cons
   }
 }
 
+// The filter gradient specialised on the filter width CX: a block takes one frame t, a
+// span of rows, 2048 channels (8 a thread) and ROWS consecutive filter rows (da, de) of
+// one frame offset (chunk tc of ct * cy / ROWS); each thread slides along its rows keeping,
+// per filter row, the CX input positions x - rx .. x + rx in registers, so each step loads
+// one dy row and one new input row per filter row (instead of one per tap).
+template <typename T, int ROWS, int CX>
+__global__ __launch_bounds__(256) void k_dwconv_dw_w(const T* __restrict__ x, const T* __restrict__ dy,
+                                                     float* __restrict__ part, CGeom g, DwSplit sp) {
+  const int total = sp.ncb * sp.ntc * sp.nyc * g.F;
+  int L = xcd_remap(blockIdx.x, total);
+  const int t = L % g.F;
+  L /= g.F;
+  const int yc = L % sp.nyc;
+  L /= sp.nyc;
+  const int tc = L % sp.ntc, cb = L / sp.ntc;
+  const int c = cb * DW_CPB + 8 * threadIdx.x;
+  if (c >= g.C) return;
+  constexpr int rx = (CX - 1) / 2;
+  const int rt = (g.ct - 1) / 2, ry = (g.cy - 1) / 2;
+  const int row0 = tc * ROWS;  // filter rows (a * cy + e) row0 .. row0 + ROWS - 1
+  const T* zero = reinterpret_cast<const T*>(g_zero_row);
+  float acc[ROWS][CX][8], win[ROWS][CX][8], bs[8];
+  int da[ROWS], de[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int fr = min(row0 + r, g.ct * g.cy - 1);  // rows past the filter repeat the last, never written
+    da[r] = fr / g.cy - rt;
+    de[r] = fr % g.cy - ry;
+#pragma unroll
+    for (int f = 0; f < CX; ++f)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][f][e] = 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bs[e] = 0.f;
+  const int y0 = yc * sp.rows, y1 = min(y0 + sp.rows, g.Hp);
+  for (int yy = y0; yy < y1; ++yy) {
+    const T* rows[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int ts = t + da[r], ys = yy + de[r];
+      const bool ok = (unsigned)ts < (unsigned)g.F && (unsigned)ys < (unsigned)g.Hp;
+      rows[r] = ok ? x + ((size_t)(ts * g.Hp + ys) * g.Wp) * g.C + c : nullptr;
+      // the window before the row's first token: positions -rx - 1 .. rx - 1
+#pragma unroll
+      for (int f = 1; f < CX; ++f) {
+        const int xs = f - 1 - rx;
+        ld8(rows[r] && (unsigned)xs < (unsigned)g.Wp ? rows[r] + (size_t)xs * g.C : zero, win[r][f]);
+      }
+    }
+    for (int xx = 0; xx < g.Wp; ++xx) {
+      float d[8];
+      ld8(dy + ((size_t)(t * g.Hp + yy) * g.Wp + xx) * g.C + c, d);
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        // slide: positions xx - rx .. xx + rx
+#pragma unroll
+        for (int f = 0; f < CX - 1; ++f)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) win[r][f][e] = win[r][f + 1][e];
+        const int xs = xx + rx;
+        ld8(rows[r] && xs < g.Wp ? rows[r] + (size_t)xs * g.C : zero, win[r][CX - 1]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bs[e] += d[e];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int f = 0; f < CX; ++f)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r][f][e] = fmaf(d[e], win[r][f][e], acc[r][f][e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float* p = part + (((size_t)t * sp.nyc + yc) * g.C + c + e) * (g.taps + 1);
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+      if (row0 + r < g.ct * g.cy)
+#pragma unroll
+        for (int f = 0; f < CX; ++f) p[(row0 + r) * CX + f] = acc[r][f][e];
+    if (tc == 0) p[g.taps] = bs[e];
+  }
+}
+
 // dw[c][tap] (and db[c]) = sum of the partial sums, frames and row spans in order.
 __global__ __launch_bounds__(256) void k_dwconv_dw_sum(const float* __restrict__ part, float* __restrict__ dw,
                                                        float* __restrict__ db, CGeom g, int nparts) {
@@ -357,11 +442,18 @@ static hipError_t conv_launch(const void* x, const float* w, const float* b, voi
   return hipGetLastError();
 }
 
-// Row spans per frame: enough blocks to fill the chip (>= 1024) without splitting rows.
+// Filter rows per block of the sliding-window filter-gradient kernel (at most 9 taps a
+// thread), 0 where the width has no specialisation.
+static int dw_rows(int cx) { return cx == 1 ? 9 : cx == 3 ? 3 : (cx == 5 || cx == 7 || cx == 9) ? 1 : 0; }
+
+// The filter-gradient blocks: channel blocks, tap chunks (filter-row groups for the
+// sliding-window kernel, DW_TAPS taps otherwise) and row spans per frame, enough blocks
+// to fill the chip (>= 1024) without splitting rows.
 static DwSplit dw_split(const CGeom& g) {
   DwSplit sp;
   sp.ncb = (g.C + DW_CPB - 1) / DW_CPB;
-  sp.ntc = (g.taps + DW_TAPS - 1) / DW_TAPS;
+  const int rows = dw_rows(g.cx);
+  sp.ntc = rows ? (g.ct * g.cy + rows - 1) / rows : (g.taps + DW_TAPS - 1) / DW_TAPS;
   const long long base = (long long)sp.ncb * sp.ntc * g.F;
   sp.nyc = (int)std::min<long long>(g.Hp, std::max<long long>(1, (1024 + base - 1) / base));
   sp.rows = (g.Hp + sp.nyc - 1) / sp.nyc;
@@ -375,6 +467,27 @@ static hipError_t dw_launch(const void* x, const void* dy, float* part, const CG
   const long long total = (long long)sp.ncb * sp.ntc * sp.nyc * g.F;
   k_dwconv_dw<T><<<(unsigned)total, 256, 0, s>>>((const T*)x, (const T*)dy, part, g, sp);
   return hipGetLastError();
+}
+
+// Filter rows per block for the sliding-window kernel: at most 9 taps a thread.
+template <typename T, int ROWS, int CX>
+static hipError_t dw_launch_w(const void* x, const void* dy, float* part, const CGeom& g, hipStream_t s) {
+  const DwSplit sp = dw_split(g);  // ntc = filter-row groups of ROWS (dw_rows(CX) == ROWS)
+  const long long total = (long long)sp.ncb * sp.ntc * sp.nyc * g.F;
+  k_dwconv_dw_w<T, ROWS, CX><<<(unsigned)total, 256, 0, s>>>((const T*)x, (const T*)dy, part, g, sp);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dw_dispatch(const void* x, const void* dy, float* part, const CGeom& g, hipStream_t s) {
+  switch (g.cx) {
+    case 1: return dw_launch_w<T, 9, 1>(x, dy, part, g, s);
+    case 3: return dw_launch_w<T, 3, 3>(x, dy, part, g, s);
+    case 5: return dw_launch_w<T, 1, 5>(x, dy, part, g, s);
+    case 7: return dw_launch_w<T, 1, 7>(x, dy, part, g, s);
+    case 9: return dw_launch_w<T, 1, 9>(x, dy, part, g, s);
+    default: return dw_launch<T>(x, dy, part, g, dw_split(g), s);
+  }
 }
 
 }  // namespace dsa3d
@@ -445,11 +558,11 @@ int dsa3d_dwconv3d_backward(const void* x, const float* weight, const void* dy, 
   hipError_t e = bf ? conv_launch<u16>(dy, weight, nullptr, dx, g, 0, 1, stream)
                     : conv_launch<float>(dy, weight, nullptr, dx, g, 0, 1, stream);
   if (e != hipSuccess) return DSA3D_ERR_LAUNCH;
-  const DwSplit sp = dw_split(g);
-  e = bf ? dw_launch<u16>(x, dy, part, g, sp, stream) : dw_launch<float>(x, dy, part, g, sp, stream);
+  e = bf ? dw_dispatch<u16>(x, dy, part, g, stream) : dw_dispatch<float>(x, dy, part, g, stream);
   if (e != hipSuccess) return DSA3D_ERR_LAUNCH;
   const long long per = (long long)g.C * (g.taps + 1);
-  k_dwconv_dw_sum<<<(unsigned)((per + 255) / 256), 256, 0, stream>>>(part, dweight, dbias, g, g.F * sp.nyc);
+  k_dwconv_dw_sum<<<(unsigned)((per + 255) / 256), 256, 0, stream>>>(part, dweight, dbias, g,
+                                                                      g.F * dw_split(g).nyc);
   return hipGetLastError() == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
 
