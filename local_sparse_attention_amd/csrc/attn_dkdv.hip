@@ -59,12 +59,29 @@ __global__ __launch_bounds__(256) void k_kvitem_count(Geom g, const int* __restr
   off[i] = (cnt + KV_Q - 1) / KV_Q;
 }
 
+// Bit 4 i + j set: key (4 kby + i, 4 kbx + j) of the block lies in the window of
+// the query whose window starts at (sy, sx).
+__device__ __forceinline__ int block_mask(const Geom& g, int kby, int kbx, int sy, int sx) {
+  int rows = 0, cols = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rows |= (unsigned)(4 * kby + i - sy) < (unsigned)g.ky ? 1 << i : 0;
+    cols |= (unsigned)(4 * kbx + i - sx) < (unsigned)g.kx ? 1 << i : 0;
+  }
+  int m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m |= (rows >> i & 1) ? cols << (4 * i) : 0;
+  return m;
+}
+
 // One wave per (key block column, slice): the queries of the blob box in sort
-// order, then padding (query 0 with a start no key matches) to whole items.
+// order, then padding (query 0, no key of the block in its window) to whole items.
+// Each query comes with the mask of the block's keys its window holds, so the
+// dK / dV kernel tests a key with one bit extract instead of two range tests.
 __global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restrict__ cell_ptr,
                                                      const int* __restrict__ perm, const int4* __restrict__ starts,
                                                      const int* __restrict__ off, int* __restrict__ ids,
-                                                     int2* __restrict__ kst) {
+                                                     int* __restrict__ kmask) {
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
   const long long i = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -84,13 +101,13 @@ __global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restri
       const int qid = perm[s0 + j];
       const int4 st = starts[qid];
       ids[base + pos + j] = qid;
-      kst[base + pos + j] = make_int2(st.y, st.z);
+      kmask[base + pos + j] = block_mask(g, kby, kbx, st.y, st.z);
     }
     pos += n;
   }
   for (int j = pos + lane; j < total; j += 64) {
     ids[base + j] = 0;
-    kst[base + j] = make_int2(-(1 << 29), -(1 << 29));
+    kmask[base + j] = 0;
   }
 }
 
@@ -100,8 +117,9 @@ template <int D, int KT>
 struct DkdvCfg {
   static constexpr int NPH = D / 64;                 // 128-byte column phases of a bf16 row
   static constexpr int TILE = KV_Q * 128;            // one phase of an item's KV_Q rows
-  static constexpr int META = 2 * NPH * TILE;        // item: starts (8 B), lse, delta (4 B each) per query
-  static constexpr int SINK = META + 16 * KV_Q;      // 16 bytes nobody reads: target of the padding loads
+  static constexpr int META = 2 * NPH * TILE;        // item: key mask, lse, delta (4 B each) per query
+  static constexpr int MASK = META, LSE = META + 4 * KV_Q, DELTA = META + 8 * KV_Q;
+  static constexpr int SINK = META + 12 * KV_Q;      // 16 bytes nobody reads: target of the padding loads
   static constexpr int ENTRY = SINK + 16;
   static constexpr int NL = 2 * NPH * (TILE / 1024) + 3;  // direct loads per entry
   static constexpr int NBUF = D == 128 ? 7 : 8;   // ring entries (LDS: ring and P / dS)
@@ -113,7 +131,7 @@ struct DkdvCfg {
 struct KvItems {
   const int* off;   // [nkb * Lt + 1]: items of (kb, tau) are off[kb Lt + tau] .. off[kb Lt + tau + 1]
   const int* ids;   // [items * KV_Q] query tokens
-  const int2* st;   // [items * KV_Q] (sy, sx) window starts
+  const int* mask;  // [items * KV_Q] mask of the block's keys in the query's window
 };
 
 // Position in the entry stream of a workgroup: slice tau, entry j of the slice
@@ -188,7 +206,7 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
     reinterpret_cast<uint4*>(&ring[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 
-  // this lane's key (key r16 of the block) for the window test
+  // this lane's key (key r16 of the block)
   const int key_y = 4 * kby + (r16 >> 2), key_x = 4 * kbx + (r16 & 3);
 
   auto slice_off = [&](int tau) { return __builtin_amdgcn_readfirstlane(s_off[tau - tau_lo]); };
@@ -264,10 +282,10 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
               constexpr int ti = j / PARTS, part = j % PARTS, tensor = ti / C::NPH, ph = ti % C::NPH;
               dma16((tensor ? dout : q) + rowoff[jj % NQ] + ph * 64, e + ti * C::TILE + part * 1024);
             } else if constexpr (j == NR) {
-              if (lane < KV_Q / 2) dma16(it.st + (size_t)item * KV_Q + 2 * lane, e + C::META);
+              if (lane < KV_Q / 4) dma16(it.mask + (size_t)item * KV_Q + 4 * lane, e + C::MASK);
             } else if constexpr (j < C::NL) {
               if (lane < KV_Q)
-                dma4((j == NR + 1 ? lse : delta) + meta_off, e + C::META + 8 * KV_Q + (j == NR + 1 ? 0 : 4 * KV_Q));
+                dma4((j == NR + 1 ? lse : delta) + meta_off, e + (j == NR + 1 ? C::LSE : C::DELTA));
             } else {
               if (lane == 0) dma4(lse, e + C::SINK);  // padding of the load count
             }
@@ -397,11 +415,10 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
     // fragments in xch[par] (8 of their 16 bytes per lane)
     auto produce = [&](char* e, int par) {
       const int q0 = 16 * hf + 4 * quad;
-      // the queries' starts, lse and Delta first: they do not depend on the products
-      const float4 de = *reinterpret_cast<const float4*>(e + C::META + 12 * KV_Q + q0 * 4);
-      const int4 sa = *reinterpret_cast<const int4*>(e + C::META + q0 * 8);
-      const int4 sb = *reinterpret_cast<const int4*>(e + C::META + q0 * 8 + 16);
-      const float4 ls = *reinterpret_cast<const float4*>(e + C::META + 8 * KV_Q + q0 * 4);
+      // the queries' key masks, lse and Delta first: they do not depend on the products
+      const float4 de = *reinterpret_cast<const float4*>(e + C::DELTA + q0 * 4);
+      const int4 km = *reinterpret_cast<const int4*>(e + C::MASK + q0 * 4);
+      const float4 ls = *reinterpret_cast<const float4*>(e + C::LSE + q0 * 4);
       // dP - Delta: the products accumulate onto -Delta of the lane's four queries
       const f32x4_t ndq = f32x4_t{-de.x, -de.y, -de.z, -de.w};
       f32x4_t sc[NSG], dp[NSG];
@@ -431,21 +448,24 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
 #pragma unroll
         for (int i = 0; i < NSG; ++i) dp[i] = mma(ao[c], vf[i][c], dp[i]);
       }
-      const int sy[4] = {sa.x, sa.z, sb.x, sb.z}, sx[4] = {sa.y, sa.w, sb.y, sb.w};
+      const int mk[4] = {km.x, km.y, km.z, km.w};
       const float lq[4] = {ls.x, ls.y, ls.z, ls.w};
-      // per query: -lse (log2 units) inside the window, -inf outside (exp2 gives 0)
-      float qb[4];
+      // per query: -lse in log2 units, and all ones if the lane's key is in its
+      // window, else zero: P outside the window is +0 whatever exp2 gave (finite
+      // scores, so no NaN can reach the mask)
+      float nl[4];
+      int keep[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        qb[j] = (unsigned)(key_y - sy[j]) < (unsigned)g.ky && (unsigned)(key_x - sx[j]) < (unsigned)g.kx
-                    ? -lq[j] * LOG2E
-                    : -__builtin_inff();
+      for (int j = 0; j < 4; ++j) {
+        nl[j] = -lq[j] * LOG2E;
+        keep[j] = __builtin_amdgcn_sbfe(mk[j], r16, 1);
+      }
 #pragma unroll
       for (int i = 0; i < NSG; ++i) {
         f32x4_t pe, ds;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          pe[j] = __builtin_amdgcn_exp2f(sc[i][j] * sl2 + qb[j]);
+          pe[j] = __uint_as_float(__float_as_uint(__builtin_amdgcn_exp2f(sc[i][j] * sl2 + nl[j])) & keep[j]);
           ds[j] = pe[j] * dp[i][j];
         }
         // bf16 (round to nearest even), two values per conversion instruction
@@ -529,7 +549,7 @@ hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s) {
   const long long n = (long long)kv_item_columns(g) * g.Lt;
   k_kvitem_count<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(g, p.cell_ptr, p.kv_off);
   if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.kv_off), (int)(n + 1), s) != hipSuccess) return hipGetLastError();
-  k_kvitem_fill<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(g, p.cell_ptr, p.perm, p.starts, p.kv_off, p.kv_ids, p.kv_st);
+  k_kvitem_fill<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(g, p.cell_ptr, p.perm, p.starts, p.kv_off, p.kv_ids, p.kv_mask);
   return hipGetLastError();
 }
 
@@ -558,7 +578,7 @@ static hipError_t dkdv_impl(const AttnArgs& a, const Geom& g, const Prep& p, hip
   while (ts > 8 && (long long)nkb * g.nh * ((g.F + ts - 1) / ts) < 512) ts = (ts + 1) / 2;
   const int nchunk = (g.F + ts - 1) / ts;
   const long long total = (long long)nkb * nchunk * g.nh;
-  KvItems it{p.kv_off, p.kv_ids, p.kv_st};
+  KvItems it{p.kv_off, p.kv_ids, p.kv_mask};
   k_dkdv_tube<D, KT, FPG><<<(unsigned)total, 128 * NG + 64 * DKDV_LW, 0, s>>>(
       (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, a.lse, p.delta, (u16*)a.dk, (u16*)a.dv, g,
       it, ts, a.scale * LOG2E, a.scale);

@@ -7,7 +7,14 @@
 namespace dsa3d {
 
 // Eight independent accumulator chains per wave keep the matrix core busy without
-// waiting on a result; the operands stay in registers.
+// waiting on a result; the operands stay in registers.  Each MFMA is written as
+// one inline instruction with its accumulator tied to the result registers: left
+// to the register allocator, this loop rotated the accumulators through shared
+// registers with about six moves per MFMA, which halved the rate it measured.
+// The compiler does not see the asm's latency, so the waits are explicit: before
+// the first MFMAs (which start from a zero accumulator and read only a and b) and
+// after the last, in a statement that takes the accumulators as operands so the
+// reads below cannot move above it.
 __global__ __launch_bounds__(256) void k_peak_mfma_bf16(float* __restrict__ out, int iters, float seed) {
   bf16x8_t a, b;
 #pragma unroll
@@ -16,12 +23,16 @@ __global__ __launch_bounds__(256) void k_peak_mfma_bf16(float* __restrict__ out,
     b[j] = static_cast<__bf16>(seed - 0.002f * j);
   }
   f32x4_t c[8];
+  __asm__ __volatile__("s_nop 7\n\ts_nop 7" ::"v"(a), "v"(b));
 #pragma unroll
-  for (int u = 0; u < 8; ++u) c[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < iters; ++i) {
+  for (int u = 0; u < 8; ++u) __asm__ __volatile__("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=v"(c[u]) : "v"(a), "v"(b));
+  for (int i = 1; i < iters; ++i) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) c[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[u], 0, 0, 0);
+    for (int u = 0; u < 8; ++u)
+      __asm__ __volatile__("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c[u]) : "v"(a), "v"(b));
   }
+  __asm__ __volatile__("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                       : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]), "+v"(c[6]), "+v"(c[7]));
   float s = 0.f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) s += c[u][0] + c[u][1] + c[u][2] + c[u][3];

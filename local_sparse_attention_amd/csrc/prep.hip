@@ -60,7 +60,7 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   const bool kv = backward && kv_items_geometry(g);
   q.kv_off = kv ? (int*)take(((size_t)kv_item_columns(g) * g.Lt + 1) * 4) : nullptr;
   q.kv_ids = kv ? (int*)take(max_kv_items(g) * KV_Q * 4) : nullptr;
-  q.kv_st = kv ? (int2*)take(max_kv_items(g) * KV_Q * sizeof(int2)) : nullptr;
+  q.kv_mask = kv ? (int*)take(max_kv_items(g) * KV_Q * sizeof(int)) : nullptr;
   const bool qsg = qs_geometry(g);
   q.qt_off = qsg ? (int*)take(((size_t)qs_items(g) + 1) * 4) : nullptr;
   q.qt = qsg ? (int*)take((size_t)max_groups * QT_INTS * 4) : nullptr;

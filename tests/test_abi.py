@@ -57,8 +57,8 @@ def test_workspace_bytes(lib):
     N = 256 * 68 * 120
     assert fwd > 16 * N and bwd >= fwd + 4 * 16 * N  # starts + fp32 Delta [H][N]
     # key-centric dK/dV item lists: every query listed for at most 3 x 3 key block
-    # columns, 12 bytes each (token, window start y / x)
-    assert bwd >= fwd + 4 * 16 * N + 9 * 12 * N
+    # columns, 8 bytes each (token, mask of the block's keys in its window)
+    assert bwd >= fwd + 4 * 16 * N + 9 * 8 * N
     assert bwd < 400 * N  # modest: a tenth of one [N][16][128] bf16 tensor
     assert lib.dsa3d_workspace_bytes(4, 8, 8, 2, 3, 3, 3, 1) > 0
     # invalid geometry -> 0
