@@ -148,10 +148,14 @@ int dsa3d_backward_ex(const void* q, const void* k, const void* v, const int32_t
    [heads][N][3] (head h's (dt, dy, dx) of token n at offsets_heads + 3 * (h * N + n)),
    and head h of out / lse (forward) or of dq / dk / dv (backward) is exactly what
    dsa3d_forward / dsa3d_backward compute for that head with those offsets.  Every
-   other argument, the workspace size (dsa3d_workspace_bytes with the same
-   arguments), the flags, tolerances, determinism and errors are those of the
-   *_ex calls.  The window starts, buckets and work lists are built per head, one
-   head after the other in stream order on the one workspace. */
+   other argument, the flags, tolerances, determinism and errors are those of the
+   *_ex calls.  Workspace: at least dsa3d_workspace_bytes (same arguments); with
+   at least dsa3d_workspace_bytes_heads, bf16 and no DSA3D_FLAG_GENERIC_KERNELS,
+   the window starts, buckets and work lists of all heads are built together
+   (head-major) and each attention kernel runs once over every head; otherwise
+   they are built per head, one head after the other in stream order on the one
+   workspace, and the kernels run per head.  The results are the same either way. */
+size_t dsa3d_workspace_bytes_heads(int F, int Hp, int Wp, int heads, int kt, int ky, int kx, int backward);
 int dsa3d_forward_heads(const void* q, const void* k, const void* v, const int32_t* offsets_heads, int F, int Hp,
                         int Wp, int heads, int head_dim, int kt, int ky, int kx, float scale, int dtype, void* out,
                         float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream, unsigned flags);

@@ -34,6 +34,14 @@ int check_common(int F, int Hp, int Wp, int heads, int head_dim, int kt, int ky,
   return DSA3D_OK;
 }
 
+// Per-head offsets in one set of launches: the bucketing of every head at once
+// (g.ph = heads: sort keys head-major, every list one block per head) when the
+// frame-sweeping kernels apply and the head-major counts stay inside int32.
+bool heads_batchable(const Geom& g) {
+  return g.H > 1 && qs_geometry(g) && kv_items_geometry(g) && (long long)g.N * g.H < (1LL << 31) &&
+         (long long)g.keyspace * g.H < (1LL << 31);
+}
+
 }  // namespace
 
 namespace dsa3d {
@@ -130,6 +138,13 @@ size_t dsa3d_workspace_bytes(int F, int Hp, int Wp, int heads, int kt, int ky, i
   return workspace_layout(g, backward != 0, nullptr, nullptr);
 }
 
+size_t dsa3d_workspace_bytes_heads(int F, int Hp, int Wp, int heads, int kt, int ky, int kx, int backward) {
+  if (check_geom(F, Hp, Wp, heads, kt, ky, kx) != DSA3D_OK) return 0;
+  Geom g = make_geom(F, Hp, Wp, heads, kt, ky, kx);
+  if (heads_batchable(g)) g.ph = heads;
+  return workspace_layout(g, backward != 0, nullptr, nullptr);
+}
+
 int dsa3d_window_starts(const int32_t* offsets, int F, int Hp, int Wp, int kt, int ky, int kx, int32_t* starts,
                         hipStream_t stream) {
   if (!offsets || !starts) return DSA3D_ERR_NULL;
@@ -198,8 +213,15 @@ int dsa3d_forward_heads(const void* q, const void* k, const void* v, const int32
   if (!aligned16(workspace)) return DSA3D_ERR_ALIGN;
   Geom g = make_geom(F, Hp, Wp, heads, kt, ky, kx);
   if (workspace_bytes < workspace_layout(g, false, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
-  // one head at a time: its own window starts, buckets and work lists (the workspace is
-  // reused in stream order), then the attention kernels on that head only
+  // every head at once when the workspace holds the bucketing of all heads
+  Geom gb = g;
+  gb.ph = heads;
+  if (!(flags & DSA3D_FLAG_GENERIC_KERNELS) && heads_batchable(g) && fwd_qs_eligible(g, dtype, head_dim) &&
+      workspace_bytes >= workspace_layout(gb, false, nullptr, nullptr))
+    return run_forward(q, k, v, offsets, gb, head_dim, scale, dtype, out, lse, static_cast<char*>(workspace), stream,
+                       flags, nullptr);
+  // else one head at a time: its own window starts, buckets and work lists (the
+  // workspace is reused in stream order), then the attention kernels on that head only
   for (int h = 0; h < heads; ++h) {
     g.h0 = h;
     g.nh = 1;
@@ -222,6 +244,12 @@ int dsa3d_backward_heads(const void* q, const void* k, const void* v, const int3
   if (!aligned16(workspace)) return DSA3D_ERR_ALIGN;
   Geom g = make_geom(F, Hp, Wp, heads, kt, ky, kx);
   if (workspace_bytes < workspace_layout(g, true, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
+  Geom gb = g;
+  gb.ph = heads;
+  if (!(flags & DSA3D_FLAG_GENERIC_KERNELS) && heads_batchable(g) && dq_qs_eligible(g, dtype, head_dim) &&
+      dkdv_tube_eligible(g, dtype, head_dim) && workspace_bytes >= workspace_layout(gb, true, nullptr, nullptr))
+    return run_backward(q, k, v, offsets, out, lse, dout, gb, head_dim, scale, dtype, dq, dk, dv,
+                        static_cast<char*>(workspace), stream, flags, nullptr, false);
   // Delta of every head once (it does not depend on the offsets)
   const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dq_qs_eligible(g, dtype, head_dim);
   if (qs) {

@@ -41,12 +41,16 @@ __device__ __forceinline__ void blob_span(int kb, int k, int L, int& b0, int& b1
 
 // ---- item lists -------------------------------------------------------------
 
-// Items (KV_Q queries) per (key block column, slice): into off[kb * Lt + tau].
+// Items (KV_Q queries) per (head block, key block column, slice): into
+// off[(hb * nkb + kb) * Lt + tau] (one head block unless the offsets are per head).
 __global__ __launch_bounds__(256) void k_kvitem_count(Geom g, const int* __restrict__ cell_ptr, int* __restrict__ off) {
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long long)nkb * g.Lt) return;
-  const int kb = (int)(i / g.Lt), tau = (int)(i - (long long)kb * g.Lt);
+  if (i >= (long long)nkb * g.Lt * g.ph) return;
+  const int hb = (int)(i / ((long long)nkb * g.Lt));
+  const long long il = i - (long long)hb * nkb * g.Lt;
+  const int kb = (int)(il / g.Lt), tau = (int)(il - (long long)kb * g.Lt);
+  cell_ptr += (size_t)hb * g.keyspace;  // the head block's cells (their positions are global)
   const int kby = kb / nkbx, kbx = kb - kby * nkbx;
   int by0, by1, bx0, bx1;
   blob_span(kby, g.ky, g.Ly, by0, by1);
@@ -85,8 +89,12 @@ __global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restri
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
   const long long i = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (i >= (long long)nkb * g.Lt) return;
-  const int kb = (int)(i / g.Lt), tau = (int)(i - (long long)kb * g.Lt);
+  if (i >= (long long)nkb * g.Lt * g.ph) return;
+  const int hb = (int)(i / ((long long)nkb * g.Lt));
+  const long long il = i - (long long)hb * nkb * g.Lt;
+  const int kb = (int)(il / g.Lt), tau = (int)(il - (long long)kb * g.Lt);
+  cell_ptr += (size_t)hb * g.keyspace;
+  const int tok0 = hb * g.N;  // sorted queries are numbered across head blocks
   const int kby = kb / nkbx, kbx = kb - kby * nkbx;
   int by0, by1, bx0, bx1;
   blob_span(kby, g.ky, g.Ly, by0, by1);
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restri
     for (int j = lane; j < n; j += 64) {
       const int qid = perm[s0 + j];
       const int4 st = starts[qid];
-      ids[base + pos + j] = qid;
+      ids[base + pos + j] = qid - tok0;
       kmask[base + pos + j] = block_mask(g, kby, kbx, st.y, st.z);
     }
     pos += n;
@@ -199,7 +207,9 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
   // entries ahead of use.
   __shared__ int s_off[DKDV_TS_MAX + 8 + 1];
   __shared__ int s_ids[C::NIDS][KV_Q];
-  for (int i = tid; i <= tau_hi - tau_lo + 1; i += 64 * NW) s_off[i] = it.off[(size_t)kb * g.Lt + tau_lo + i];
+  const int hb = g.ph > 1 ? hl : 0;  // the head's item lists (per-head offsets)
+  for (int i = tid; i <= tau_hi - tau_lo + 1; i += 64 * NW)
+    s_off[i] = it.off[((size_t)hb * nkb + kb) * g.Lt + tau_lo + i];
   // The in-loop apply runs its MFMAs with P = dS = 0 when it has nothing to add,
   // so every ring byte it may read must hold a finite value from the start.
   for (int i = tid; i < C::NBUF * C::ENTRY / 16; i += 64 * NW)
@@ -546,7 +556,7 @@ bool dkdv_tube_eligible(const Geom& g, int dtype, int D) {
 }
 
 hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s) {
-  const long long n = (long long)kv_item_columns(g) * g.Lt;
+  const long long n = (long long)kv_item_columns(g) * g.Lt * g.ph;
   k_kvitem_count<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(g, p.cell_ptr, p.kv_off);
   if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.kv_off), (int)(n + 1), s) != hipSuccess) return hipGetLastError();
   k_kvitem_fill<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(g, p.cell_ptr, p.perm, p.starts, p.kv_off, p.kv_ids, p.kv_mask);

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64 * DQ_NW) void k_dq_qs(const u16* __restrict__ q,
   KeyTileLoadsW<D, NBX, C::NB, C::NBPAD, DQ_NW> kl;
   kl.init(g, h, by, bx, lane, wave);
   const size_t frame_el = (size_t)g.Hp * g.Wp * g.H * D;
-  const int* sp = p.qs + p.qs_off[w];
+  const int* sp = p.qs + p.qs_off[(g.ph > 1 ? hl : 0) * nw + w];  // per-head offsets: the head's lists
   const int npass = sp[0];
   sp += 1;
   for (int pass = 0; pass < npass; ++pass) {

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
   const bool loader = wave >= FWD_NW;
   const int lw = wave - FWD_NW;
 
-  const int* sp = p.qs + p.qs_off[w];
+  const int* sp = p.qs + p.qs_off[(g.ph > 1 ? hl : 0) * nw + w];  // per-head offsets: the head's lists
   const int npass = sp[0];
   sp += 1;
   if (loader) {

@@ -27,6 +27,9 @@ struct Geom {
   int nby, nbx;      // start blobs per lattice row / column (Lt blobs along t)
   int H;             // heads (the row stride of [N][H][D] tensors)
   int h0, nh;        // heads an attention launch covers: h0 .. h0 + nh - 1
+  int ph;            // heads the bucketing covers: 1 (offsets shared by every head) or nh
+                     // (per-head offsets: the bucketing arrays hold one block per head,
+                     // head-major, block hl for head h0 + hl)
   int N;             // tokens
   int nblobs;        // Lt * nby * nbx
   int keyspace;      // nblobs * BLOB_CELLS

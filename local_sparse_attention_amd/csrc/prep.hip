@@ -23,6 +23,7 @@ Geom make_geom(int F, int Hp, int Wp, int H, int kt, int ky, int kx) {
   g.H = H;
   g.h0 = 0;
   g.nh = H;
+  g.ph = 1;
   g.N = F * Hp * Wp;
   g.nblobs = g.Lt * g.nby * g.nbx;
   g.keyspace = g.nblobs * BLOB_CELLS;
@@ -31,14 +32,16 @@ Geom make_geom(int F, int Hp, int Wp, int H, int kt, int ky, int kx) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Carves the workspace (base may be null to only size it).  Returns its size.
+// Carves the workspace (base may be null to only size it).  Returns its size.  With
+// g.ph heads of bucketing every array below holds g.ph blocks, one per head.
 size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
-  const size_t N = (size_t)g.N;
+  const size_t NH = (size_t)g.N;            // tokens (delta is [H][N])
+  const size_t N = NH * g.ph;               // bucketed queries
   const int rb = (int)((N + RADIX_TILE - 1) / RADIX_TILE);
   int bits = 1;
-  while ((1u << bits) < (uint32_t)g.keyspace) ++bits;
+  while ((1ull << bits) < (unsigned long long)g.keyspace * g.ph) ++bits;
   const int passes = (bits + 7) / 8;
-  const int max_groups = g.N / GROUP_Q + g.nblobs + 1;
+  const int max_groups = (g.N / GROUP_Q + g.nblobs + 1) * g.ph;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* ptr = base ? base + off : nullptr;
@@ -52,23 +55,23 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   q.vals[0] = (int*)take(N * 4);
   q.vals[1] = (int*)take(N * 4);
   q.ghist = (uint32_t*)take((size_t)256 * rb * 4);
-  q.cell_ptr = (int*)take(((size_t)g.keyspace + 1) * 4);
-  q.goff = (int*)take(((size_t)g.nblobs + 1) * 4);
+  q.cell_ptr = (int*)take(((size_t)g.keyspace * g.ph + 1) * 4);
+  q.goff = (int*)take(((size_t)g.nblobs * g.ph + 1) * 4);
   q.groups = (int2*)take((size_t)max_groups * sizeof(int2));
   q.ngroups = (int*)take(4);
-  q.delta = backward ? (float*)take(N * g.H * 4) : nullptr;
+  q.delta = backward ? (float*)take(NH * g.H * 4) : nullptr;
   const bool kv = backward && kv_items_geometry(g);
-  q.kv_off = kv ? (int*)take(((size_t)kv_item_columns(g) * g.Lt + 1) * 4) : nullptr;
-  q.kv_ids = kv ? (int*)take(max_kv_items(g) * KV_Q * 4) : nullptr;
-  q.kv_mask = kv ? (int*)take(max_kv_items(g) * KV_Q * sizeof(int)) : nullptr;
+  q.kv_off = kv ? (int*)take(((size_t)kv_item_columns(g) * g.Lt * g.ph + 1) * 4) : nullptr;
+  q.kv_ids = kv ? (int*)take(max_kv_items(g) * g.ph * KV_Q * 4) : nullptr;
+  q.kv_mask = kv ? (int*)take(max_kv_items(g) * g.ph * KV_Q * sizeof(int)) : nullptr;
   const bool qsg = qs_geometry(g);
-  q.qt_off = qsg ? (int*)take(((size_t)qs_items(g) + 1) * 4) : nullptr;
+  q.qt_off = qsg ? (int*)take(((size_t)qs_items(g) * g.ph + 1) * 4) : nullptr;
   q.qt = qsg ? (int*)take((size_t)max_groups * QT_INTS * 4) : nullptr;
   q.tq_ids = qsg ? (int*)take((size_t)max_groups * 16 * 4) : nullptr;
   q.tq_st = qsg ? (int2*)take((size_t)max_groups * 16 * sizeof(int2)) : nullptr;
   q.tq_dt = qsg ? (signed char*)take((size_t)max_groups * 16) : nullptr;
-  q.qs_off = qsg ? (int*)take(((size_t)qs_items(g) + 1) * 4) : nullptr;
-  q.qs = qsg ? (int*)take(qs_ints(g, max_groups) * 4) : nullptr;
+  q.qs_off = qsg ? (int*)take(((size_t)qs_items(g) * g.ph + 1) * 4) : nullptr;
+  q.qs = qsg ? (int*)take((qs_ints(g, max_groups / g.ph) * g.ph) * 4) : nullptr;
   q.perm = q.vals[passes & 1];
   q.radix_blocks = rb;
   q.radix_passes = passes;
@@ -107,12 +110,16 @@ __global__ __launch_bounds__(256) void k_window_starts(const int32_t* off, Geom 
   starts3[3 * (size_t)n + 2] = s.z;
 }
 
+// Query i of the bucketing is token n = i mod N of head block i / N (offsets of
+// that block at off + 3 N (i / N)); its key puts the block's cells after those of
+// the blocks before it.
 __global__ __launch_bounds__(256) void k_starts_keys(const int32_t* off, Geom g, int4* starts, uint32_t* keys) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= g.N) return;
-  const int4 s = query_start(off, g, n);
-  starts[n] = s;
-  keys[n] = (uint32_t)cell_key(g, s.x, s.y, s.z);
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= g.N * g.ph) return;
+  const int hb = i / g.N, n = i - hb * g.N;
+  const int4 s = query_start(off + (size_t)3 * g.N * hb, g, n);
+  starts[i] = s;
+  keys[i] = (uint32_t)hb * (uint32_t)g.keyspace + (uint32_t)cell_key(g, s.x, s.y, s.z);
 }
 
 // ---- stable LSD radix sort (8-bit digits) ---------------------------------------
@@ -316,7 +323,8 @@ hipError_t launch_cell_ptr(const uint32_t* sorted_keys, int n, int keyspace, int
 }
 
 hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, hipStream_t s) {
-  const int n = g.N, nb = p.radix_blocks;
+  const int n = g.N * g.ph, nb = p.radix_blocks;
+  const int keyspace = g.keyspace * g.ph, nblobs = g.nblobs * g.ph;
   k_starts_keys<<<blocks(n, 256), 256, 0, s>>>(off, g, p.starts, p.keys[0]);
   int cur = 0;
   for (int pass = 0; pass < p.radix_passes; ++pass) {
@@ -327,11 +335,10 @@ hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, hipStream_t s
     cur ^= 1;
   }
   // p.perm was set to vals[passes & 1] == vals[cur]
-  k_cell_ptr<<<blocks((long long)g.keyspace + 1, 256), 256, 0, s>>>(p.keys[cur], n, g.keyspace, p.cell_ptr);
-  k_blob_ngroups<<<blocks((long long)g.nblobs + 1, 256), 256, 0, s>>>(p.cell_ptr, g.nblobs, p.goff);
-  k_scan_excl<<<1, 1024, 0, s>>>(reinterpret_cast<uint32_t*>(p.goff), g.nblobs + 1);
-  k_groups<<<blocks(g.nblobs > 0 ? g.nblobs : 1, 256), 256, 0, s>>>(p.cell_ptr, p.goff, g.nblobs, p.groups,
-                                                                     p.ngroups);
+  k_cell_ptr<<<blocks((long long)keyspace + 1, 256), 256, 0, s>>>(p.keys[cur], n, keyspace, p.cell_ptr);
+  k_blob_ngroups<<<blocks((long long)nblobs + 1, 256), 256, 0, s>>>(p.cell_ptr, nblobs, p.goff);
+  k_scan_excl<<<1, 1024, 0, s>>>(reinterpret_cast<uint32_t*>(p.goff), nblobs + 1);
+  k_groups<<<blocks(nblobs > 0 ? nblobs : 1, 256), 256, 0, s>>>(p.cell_ptr, p.goff, nblobs, p.groups, p.ngroups);
   return hipGetLastError();
 }
 

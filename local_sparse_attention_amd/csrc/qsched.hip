@@ -1,5 +1,7 @@
 // Query-side work lists shared by the frame-sweeping forward and dQ kernels
-// (head-independent: built once per call, used by every head).
+// (built once per call: one set used by every head when the offsets are shared, or
+// one set per head, head-major, for per-head offsets).  Work item w of the lists is
+// item w mod qs_items of head block w / qs_items.
 //
 // Row tiles: a work item is one start blob column (by, bx) and QS_TS consecutive
 // slices (1 x 4 x 4 start cells of the lattice of the 3D Deformable Slide
@@ -29,7 +31,10 @@ namespace dsa3d {
 // null) and returns their count, which is at most the item's group count.
 __device__ int item_tiles(const Geom& g, const int* __restrict__ goff, const int2* __restrict__ groups, int w,
                           int* out) {
-  const int nbc = g.nby * g.nbx;
+  const int nbc = g.nby * g.nbx, nw = qs_items(g);
+  const int hb = w / nw;
+  w -= hb * nw;
+  goff += (size_t)hb * g.nblobs;  // the head block's blobs (their group indices are global)
   const int chunk = w / nbc, bc = w - chunk * nbc;
   const int by = bc / g.nbx, bx = bc - by * g.nbx;
   const int c0 = chunk * QS_TS, ns = min(QS_TS, g.Lt - c0);
@@ -87,9 +92,10 @@ __global__ __launch_bounds__(64) void k_qtile_fill(Geom g, const int* __restrict
   if (w < nw) item_tiles(g, goff, groups, w, qt + (size_t)qt_off[w] * QT_INTS);
 }
 
-// Rows of the tiles: 16 lanes per tile, row j from the part that holds it.
+// Rows of the tiles: 16 lanes per tile, row j from the part that holds it.  The
+// sorted queries are numbered across head blocks; a row keeps its token (mod N).
 __global__ __launch_bounds__(256) void k_tile_fill(const int* __restrict__ perm, const int4* __restrict__ starts,
-                                                   const int* __restrict__ qt, const int* __restrict__ ntiles,
+                                                   const int* __restrict__ qt, const int* __restrict__ ntiles, int N,
                                                    int* __restrict__ tq_ids, int2* __restrict__ tq_st,
                                                    signed char* __restrict__ tq_dt) {
   const int t = blockIdx.x * 16 + (threadIdx.x >> 4), j = threadIdx.x & 15;
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(256) void k_tile_fill(const int* __restrict__ perm,
     }
     r -= cnt;
   }
-  tq_ids[(size_t)t * 16 + j] = id;
+  tq_ids[(size_t)t * 16 + j] = id % N;
   tq_st[(size_t)t * 16 + j] = st;
   tq_dt[(size_t)t * 16 + j] = (signed char)dt;
 }
@@ -122,7 +128,7 @@ template <typename Tiles>
 __device__ int build_schedule(const Geom& g, int w, int t0, int ntiles, const Tiles& tiles, int* out, int* work,
                               int lane, int nlanes) {
   const int nbc = g.nby * g.nbx;
-  const int chunk = w / nbc;
+  const int chunk = (w % qs_items(g)) / nbc;
   const int c0 = chunk * QS_TS, ns = min(QS_TS, g.Lt - c0);
   // cur[i] .. lim[i]: the tiles (of the item) whose first slice is c0 + i that are
   // still to be scheduled.  Both arrays are cleared in a loop of their own with a
@@ -237,13 +243,13 @@ __global__ __launch_bounds__(64 * SCHED_WAVES) void k_sched_fill(Geom g, const i
 }
 
 hipError_t launch_qsched(const Geom& g, const Prep& p, hipStream_t s) {
-  const int nw = qs_items(g);
+  const int nw = qs_items(g) * g.ph;
   const unsigned wb = (unsigned)((nw + 1 + 63) / 64);
   k_qtile_count<<<wb, 64, 0, s>>>(g, p.goff, p.groups, nw, p.qt_off);
   if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.qt_off), nw + 1, s) != hipSuccess) return hipGetLastError();
   k_qtile_fill<<<wb, 64, 0, s>>>(g, p.goff, p.groups, nw, p.qt_off, p.qt);
-  k_tile_fill<<<(unsigned)((p.max_groups + 15) / 16), 256, 0, s>>>(p.perm, p.starts, p.qt, p.qt_off + nw, p.tq_ids,
-                                                                   p.tq_st, p.tq_dt);
+  k_tile_fill<<<(unsigned)((p.max_groups + 15) / 16), 256, 0, s>>>(p.perm, p.starts, p.qt, p.qt_off + nw, g.N,
+                                                                   p.tq_ids, p.tq_st, p.tq_dt);
   k_sched_count<<<wb, 64, 0, s>>>(g, p.qt_off, nw, p.qs_off);
   if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.qs_off), nw + 1, s) != hipSuccess) return hipGetLastError();
   k_sched_fill<<<(unsigned)((nw + SCHED_WAVES - 1) / SCHED_WAVES), 64 * SCHED_WAVES, 0, s>>>(g, p.qt, p.qt_off, nw,

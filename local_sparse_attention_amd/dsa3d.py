@@ -36,6 +36,8 @@ def load():
         i32, u32, vp, sz, f32 = ctypes.c_int, ctypes.c_uint, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
         lib.dsa3d_workspace_bytes.argtypes = [i32] * 8
         lib.dsa3d_workspace_bytes.restype = sz
+        lib.dsa3d_workspace_bytes_heads.argtypes = [i32] * 8
+        lib.dsa3d_workspace_bytes_heads.restype = sz
         lib.dsa3d_window_starts.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp]
         lib.dsa3d_window_starts.restype = i32
         fwd = [vp, vp, vp, vp] + [i32] * 8 + [f32, i32, vp, vp, vp, sz, vp]
@@ -113,12 +115,15 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def workspace_bytes(grid, heads, window, backward):
-    return int(load().dsa3d_workspace_bytes(*grid, heads, *window, int(bool(backward))))
+def workspace_bytes(grid, heads, window, backward, per_head=False):
+    """Workspace of dsa3d_forward / dsa3d_backward; per_head=True: the size with which
+    the per-head-offset calls bucket every head at once (dsa3d_workspace_bytes_heads)."""
+    fn = load().dsa3d_workspace_bytes_heads if per_head else load().dsa3d_workspace_bytes
+    return int(fn(*grid, heads, *window, int(bool(backward))))
 
 
-def workspace(grid, heads, window, backward, device="cuda"):
-    n = max(workspace_bytes(grid, heads, window, backward), 256)
+def workspace(grid, heads, window, backward, device="cuda", per_head=False):
+    n = max(workspace_bytes(grid, heads, window, backward, per_head), 256)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
@@ -142,9 +147,9 @@ def _shape(q, grid):
     return N, H, D
 
 
-def _workspace_arg(ws, grid, H, window, backward, device):
+def _workspace_arg(ws, grid, H, window, backward, device, per_head=False):
     if ws is None:
-        return workspace(grid, H, window, backward, device)
+        return workspace(grid, H, window, backward, device, per_head)
     if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1:
         raise DSA3DError("ws must be a 1-D uint8 tensor")
     return ws
@@ -174,7 +179,7 @@ def forward(q, k, v, offsets, grid, window, scale=None, out=None, lse=None, ws=N
     ptrs = [_dev(t, n, dev) for t, n in ((q, "q"), (k, "k"), (v, "v"), (offsets, "offsets"))]
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((H, N), dtype=torch.float32, device=dev) if lse is None else lse
-    ws = _workspace_arg(ws, grid, H, window, False, dev)
+    ws = _workspace_arg(ws, grid, H, window, False, dev, per_head)
     flags = FLAG_GENERIC_KERNELS if generic else 0
     args = (*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q), _dev(out, "out", dev), _dev(lse, "lse", dev),
             _dev(ws, "workspace", dev), ws.numel(), _stream(), flags)
@@ -229,7 +234,7 @@ def backward(q, k, v, offsets, out, lse, dout, grid, window, scale=None, dq=None
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    ws = _workspace_arg(ws, grid, H, window, True, dev)
+    ws = _workspace_arg(ws, grid, H, window, True, dev, per_head)
     flags = FLAG_GENERIC_KERNELS if generic else 0
     args = (*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q), _dev(dq, "dq", dev), _dev(dk, "dk", dev),
             _dev(dv, "dv", dev), _dev(ws, "workspace", dev), ws.numel(), _stream(), flags)

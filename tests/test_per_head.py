@@ -1,6 +1,8 @@
 """Per-head offsets (dsa3d_forward_heads / dsa3d_backward_heads): each head has its own
 integer offsets [H][N][3].  The HIP path, through the C ABI, against the oracle's per-head
-form element by element, for both kernel families, on small and multi-work-item grids."""
+form element by element, on small and multi-work-item grids, along its three routes: all
+heads bucketed together (workspace of dsa3d_workspace_bytes_heads), one head after the
+other (the minimum workspace), and the per-group kernels; the first two bit for bit."""
 from dataclasses import replace
 
 import numpy as np
@@ -35,21 +37,37 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("generic", [False, True], ids=["default", "generic"])
-@pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
-def test_per_head_offsets(dsa3d_gpu, wl, generic):
+def run_heads(dsa3d_gpu, wl, q, k, v, do, off, route):
+    """Forward + backward with per-head offsets along one route; returns (out, lse, dq, dk, dv)."""
     grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
-    print(f"case {wl.name} grid={grid} window={window} H={wl.heads} generic={generic}", flush=True)
+    generic = route == "generic"
+    wsf = wsb = None
+    if route == "per-head":  # the minimum workspace: one head after the other
+        wsf = dsa3d_gpu.workspace(grid, wl.heads, window, False)
+        wsb = dsa3d_gpu.workspace(grid, wl.heads, window, True)
+    out, lse = dsa3d_gpu.forward(q, k, v, off, grid, window, wl.scale, out=nan_like(q),
+                                 lse=torch.full((wl.heads, wl.N), float("nan"), device="cuda"), ws=wsf,
+                                 generic=generic)
+    dq, dk, dv = dsa3d_gpu.backward(q, k, v, off, out, lse, do, grid, window, wl.scale, dq=nan_like(q),
+                                    dk=nan_like(q), dv=nan_like(q), ws=wsb, generic=generic)
+    torch.cuda.synchronize()
+    return out, lse, dq, dk, dv
+
+
+ROUTES = ["together", "per-head", "generic"]
+
+
+@pytest.mark.parametrize("route", ROUTES)
+@pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
+def test_per_head_offsets(dsa3d_gpu, wl, route):
+    grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
+    print(f"case {wl.name} grid={grid} window={window} H={wl.heads} route={route}", flush=True)
     inp = synth.make_inputs(wl)
     offh = head_offsets(wl)
     assert not all(np.array_equal(offh[0], offh[h]) for h in range(1, wl.heads))
     q, k, v, do = (to_dev(inp[x]) for x in ("q", "k", "v", "dout"))
     off = to_dev(offh)
-    out, lse = dsa3d_gpu.forward(q, k, v, off, grid, window, wl.scale, out=nan_like(q),
-                                 lse=torch.full((wl.heads, wl.N), float("nan"), device="cuda"), generic=generic)
-    dq, dk, dv = dsa3d_gpu.backward(q, k, v, off, out, lse, do, grid, window, wl.scale, dq=nan_like(q),
-                                    dk=nan_like(q), dv=nan_like(q), generic=generic)
-    torch.cuda.synchronize()
+    out, lse, dq, dk, dv = run_heads(dsa3d_gpu, wl, q, k, v, do, off, route)
     o_ref, lse_ref = oracle.forward_heads(inp["q"], inp["k"], inp["v"], offh, grid, window, wl.scale)
     errs = {"out": assert_close(to_host_f64(out), o_ref, wl.dtype, "out"),
             "lse": assert_lse_close(lse.cpu().numpy(), lse_ref)}
@@ -73,3 +91,18 @@ def test_per_head_deterministic(dsa3d_gpu):
         runs.append([out.view(torch.int16), lse.view(torch.int32)] + [g.view(torch.int16) for g in grads])
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("wl", [c for c in CASES if c.dtype == "bf16"], ids=[c.name for c in CASES if c.dtype == "bf16"])
+def test_per_head_together_equals_one_by_one(dsa3d_gpu, wl):
+    """All heads bucketed together and one head after the other give the same bits: the
+    head-major sort keeps each head's queries in the order of its own sort."""
+    print(f"case {wl.name}", flush=True)
+    inp = synth.make_inputs(wl)
+    q, k, v, do = (to_dev(inp[x]) for x in ("q", "k", "v", "dout"))
+    off = to_dev(head_offsets(wl))
+    a = run_heads(dsa3d_gpu, wl, q, k, v, do, off, "together")
+    b = run_heads(dsa3d_gpu, wl, q, k, v, do, off, "per-head")
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
