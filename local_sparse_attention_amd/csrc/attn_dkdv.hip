@@ -558,7 +558,8 @@ bool dkdv_tube_eligible(const Geom& g, int dtype, int D) {
 hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s) {
   const long long n = (long long)kv_item_columns(g) * g.Lt * g.ph;
   k_kvitem_count<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(g, p.cell_ptr, p.kv_off);
-  if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.kv_off), (int)(n + 1), s) != hipSuccess) return hipGetLastError();
+  if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.kv_off), (int)(n + 1), s, p.scan_part) != hipSuccess)
+    return hipGetLastError();
   k_kvitem_fill<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(g, p.cell_ptr, p.perm, p.starts, p.kv_off, p.kv_ids, p.kv_mask);
   return hipGetLastError();
 }

@@ -33,26 +33,36 @@ struct Prep {
   int* qs_off;         // [qs_items + 1] schedule of work item w at qs + qs_off[w]
   int* qs;             // schedules (see qsched.hip)
   int* perm;           // = the vals buffer the sort ends in
-  int radix_blocks;
+  uint32_t* scan_part; // chunk totals of the multi-workgroup scans (scan_part_words(n) each)
+  int radix_blocks;    // per head block of the bucketing
   int radix_passes;
   int max_groups;
 };
 
 constexpr int RADIX_TILE = 4096;
+constexpr int SCAN_CHUNK_N = 16384;  // values one scan workgroup takes at a time
+inline size_t scan_part_words(size_t n) { return (n + SCAN_CHUNK_N - 1) / SCAN_CHUNK_N + 1; }
 
 Geom make_geom(int F, int Hp, int Wp, int H, int kt, int ky, int kx);
 size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p);
 
 hipError_t launch_window_starts(const int32_t* off, const Geom& g, int32_t* starts3, hipStream_t s);
 hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, hipStream_t s);
-// In-place exclusive scan of n uint32 values (one workgroup).
-hipError_t launch_scan_excl(uint32_t* data, int n, hipStream_t s);
-// Stable LSD radix sort of n (key, value) pairs, 8 bits a pass from bit 0, values
-// starting as the item index: ping-pong buffers, ghist holds 256 * ceil(n / RADIX_TILE)
-// words.  Returns the buffer index (0 or 1) that holds the result, -1 on a launch error.
-int radix_sort(uint32_t* keys[2], int* vals[2], uint32_t* ghist, int n, int passes, hipStream_t s);
-// cell_ptr[c] = number of sorted keys below c, c = 0 .. keyspace.
-hipError_t launch_cell_ptr(const uint32_t* sorted_keys, int n, int keyspace, int* cell_ptr, hipStream_t s);
+// In-place exclusive scan of n uint32 values: one workgroup, or, given part
+// (scan_part_words(n) words of scratch) and more than a few chunks, a scan per chunk
+// on its own workgroup, a scan of the chunk totals and an add.
+hipError_t launch_scan_excl(uint32_t* data, int n, hipStream_t s, uint32_t* part = nullptr);
+// Stable LSD radix sort of nseg segments of seglen (key, value) pairs each, every
+// segment on its own (segment i stays at i * seglen ..), 8 bits a pass from bit 0,
+// values starting as the item index: ping-pong buffers, ghist holds
+// 256 * nseg * ceil(seglen / RADIX_TILE) words.  Returns the buffer index (0 or 1)
+// that holds the result, -1 on a launch error.
+int radix_sort(uint32_t* keys[2], int* vals[2], uint32_t* ghist, int seglen, int nseg, int passes, hipStream_t s,
+               uint32_t* part = nullptr);
+// cell_ptr[i * keyspace + c] = number of sorted keys before the first key >= c of
+// segment i (segments of seglen sorted keys), for i * keyspace + c = 0 .. nseg * keyspace.
+hipError_t launch_cell_ptr(const uint32_t* sorted_keys, int seglen, int nseg, int keyspace, int* cell_ptr,
+                           hipStream_t s);
 
 // Key-centric dK/dV: windows whose key blocks reach at most 3 x 3 start blobs
 // (ky, kx <= 9) and kt <= 8 (one wave per frame in flight).

@@ -37,9 +37,9 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   const size_t NH = (size_t)g.N;            // tokens (delta is [H][N])
   const size_t N = NH * g.ph;               // bucketed queries
-  const int rb = (int)((N + RADIX_TILE - 1) / RADIX_TILE);
+  const int rb = (int)((NH + RADIX_TILE - 1) / RADIX_TILE);  // radix blocks per head block
   int bits = 1;
-  while ((1ull << bits) < (unsigned long long)g.keyspace * g.ph) ++bits;
+  while ((1u << bits) < (uint32_t)g.keyspace) ++bits;  // keys are cells; head blocks sort apart
   const int passes = (bits + 7) / 8;
   const int max_groups = (g.N / GROUP_Q + g.nblobs + 1) * g.ph;
   size_t off = 0;
@@ -54,7 +54,7 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   q.keys[1] = (uint32_t*)take(N * 4);
   q.vals[0] = (int*)take(N * 4);
   q.vals[1] = (int*)take(N * 4);
-  q.ghist = (uint32_t*)take((size_t)256 * rb * 4);
+  q.ghist = (uint32_t*)take((size_t)256 * rb * g.ph * 4);
   q.cell_ptr = (int*)take(((size_t)g.keyspace * g.ph + 1) * 4);
   q.goff = (int*)take(((size_t)g.nblobs * g.ph + 1) * 4);
   q.groups = (int2*)take((size_t)max_groups * sizeof(int2));
@@ -72,6 +72,12 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   q.tq_dt = qsg ? (signed char*)take((size_t)max_groups * 16) : nullptr;
   q.qs_off = qsg ? (int*)take(((size_t)qs_items(g) * g.ph + 1) * 4) : nullptr;
   q.qs = qsg ? (int*)take((qs_ints(g, max_groups / g.ph) * g.ph) * 4) : nullptr;
+  // the longest scan: radix counts, blob group counts, work-list and item offsets
+  size_t scan_n = (size_t)256 * rb * g.ph;
+  scan_n = max(scan_n, (size_t)g.nblobs * g.ph + 1);
+  if (qsg) scan_n = max(scan_n, (size_t)qs_items(g) * g.ph + 1);
+  if (kv) scan_n = max(scan_n, (size_t)kv_item_columns(g) * g.Lt * g.ph + 1);
+  q.scan_part = (uint32_t*)take(scan_part_words(scan_n) * 4);
   q.perm = q.vals[passes & 1];
   q.radix_blocks = rb;
   q.radix_passes = passes;
@@ -111,35 +117,37 @@ __global__ __launch_bounds__(256) void k_window_starts(const int32_t* off, Geom 
 }
 
 // Query i of the bucketing is token n = i mod N of head block i / N (offsets of
-// that block at off + 3 N (i / N)); its key puts the block's cells after those of
-// the blocks before it.
+// that block at off + 3 N (i / N)); the head blocks are sorted as separate segments.
 __global__ __launch_bounds__(256) void k_starts_keys(const int32_t* off, Geom g, int4* starts, uint32_t* keys) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= g.N * g.ph) return;
   const int hb = i / g.N, n = i - hb * g.N;
   const int4 s = query_start(off + (size_t)3 * g.N * hb, g, n);
   starts[i] = s;
-  keys[i] = (uint32_t)hb * (uint32_t)g.keyspace + (uint32_t)cell_key(g, s.x, s.y, s.z);
+  keys[i] = (uint32_t)cell_key(g, s.x, s.y, s.z);
 }
 
-// ---- stable LSD radix sort (8-bit digits) ---------------------------------------
-// Each block owns RADIX_TILE consecutive items.  hist: per-block digit counts,
-// stored digit-major so one exclusive scan gives every (digit, block) its output
-// base.  scatter: items are ranked in their original order (16 rounds of 256),
-// which keeps the sort stable.
+// ---- stable LSD radix sort (8-bit digits), by segments --------------------------
+// The items are nseg segments of seglen, each sorted on its own.  Block x owns
+// RADIX_TILE consecutive items of segment x / nbs (nbs blocks per segment).  hist:
+// per-block digit counts, stored segment-, then digit-major, so that one exclusive
+// scan over all of them gives every (segment, digit, block) its output base: the
+// counts of a segment add up to seglen, so segment i's bases start at i * seglen.
+// scatter: items are ranked in their original order (16 rounds of 256), which keeps
+// the sort stable.
 
-__global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* keys, int n, int shift, uint32_t* ghist, int nblk) {
+__global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* keys, int seglen, int nbs, int shift,
+                                                    uint32_t* ghist) {
   __shared__ uint32_t h[256];
   const int tid = threadIdx.x;
   h[tid] = 0;
   __syncthreads();
-  const int base = blockIdx.x * RADIX_TILE;
-  for (int i = tid; i < RADIX_TILE; i += 256) {
-    const int idx = base + i;
-    if (idx < n) atomicAdd(&h[(keys[idx] >> shift) & 255u], 1u);
-  }
+  const int sg = blockIdx.x / nbs, b = blockIdx.x - sg * nbs;
+  const size_t base = (size_t)sg * seglen + (size_t)b * RADIX_TILE;
+  const int lim = min(RADIX_TILE, seglen - b * RADIX_TILE);
+  for (int i = tid; i < lim; i += 256) atomicAdd(&h[(keys[base + i] >> shift) & 255u], 1u);
   __syncthreads();
-  ghist[(size_t)tid * nblk + blockIdx.x] = h[tid];
+  ghist[((size_t)sg * 256 + tid) * nbs + b] = h[tid];
 }
 
 // In-place exclusive scan (one workgroup of 1024 threads): chunks of 16384 values,
@@ -162,17 +170,23 @@ __device__ __forceinline__ void scan_load(const uint32_t* data, int n, int i0, u
     for (int j = 0; j < SCAN_PER; ++j) v[j] = i0 + j < n ? data[i0 + j] : 0u;
   }
 }
-__global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n) {
+// part == nullptr: one workgroup scans all n values, chunk after chunk with a
+// running carry.  Otherwise workgroup b scans chunk b alone and leaves its total in
+// part[b] (k_scan_add then adds the scanned totals).
+static_assert(SCAN_CHUNK == SCAN_CHUNK_N, "scan chunk");
+__global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n, uint32_t* part) {
   __shared__ uint32_t wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int start = part ? blockIdx.x * SCAN_CHUNK : 0;
+  const int end = part ? min(start + SCAN_CHUNK, n) : n;
   uint32_t carry = 0;
   uint32_t v[SCAN_PER], nx[SCAN_PER];
-  scan_load(data, n, SCAN_PER * tid, nx);
-  for (int base = 0; base < n; base += SCAN_CHUNK) {
+  scan_load(data, end, start + SCAN_PER * tid, nx);
+  for (int base = start; base < end; base += SCAN_CHUNK) {
     const int i0 = base + SCAN_PER * tid;
 #pragma unroll
     for (int j = 0; j < SCAN_PER; ++j) v[j] = nx[j];
-    if (base + SCAN_CHUNK < n) scan_load(data, n, i0 + SCAN_CHUNK, nx);
+    if (base + SCAN_CHUNK < end) scan_load(data, end, i0 + SCAN_CHUNK, nx);
     uint32_t t = 0;
 #pragma unroll
     for (int j = 0; j < SCAN_PER; ++j) t += v[j];
@@ -192,7 +206,7 @@ __global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n) {
       total += x;
     }
     uint32_t run = carry + before + inc - t;
-    if (i0 + SCAN_PER <= n) {
+    if (i0 + SCAN_PER <= end) {
 #pragma unroll
       for (int j = 0; j < SCAN_PER / 4; ++j) {
         uint4 u;
@@ -205,26 +219,35 @@ __global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n) {
     } else {
 #pragma unroll
       for (int j = 0; j < SCAN_PER; ++j) {
-        if (i0 + j < n) data[i0 + j] = run;
+        if (i0 + j < end) data[i0 + j] = run;
         run += v[j];
       }
     }
     carry += total;
     __syncthreads();  // wsum is rewritten by the next chunk
   }
+  if (part && tid == 0) part[blockIdx.x] = carry;
 }
 
-__global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* kin, const int* vin, int n, int shift,
-                                                       const uint32_t* gbase, int nblk, uint32_t* kout, int* vout) {
+__global__ __launch_bounds__(256) void k_scan_add(uint32_t* data, int n, const uint32_t* part) {
+  const int b = blockIdx.x / (SCAN_CHUNK / 256);
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) data[i] += part[b];
+}
+
+__global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* kin, const int* vin, int seglen, int nbs,
+                                                       int shift, const uint32_t* gbase, uint32_t* kout, int* vout) {
   __shared__ uint32_t base[256], run[256];
   __shared__ uint32_t wcnt[4][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  base[tid] = gbase[(size_t)tid * nblk + blockIdx.x];
+  const int sg = blockIdx.x / nbs, b = blockIdx.x - sg * nbs;
+  base[tid] = gbase[((size_t)sg * 256 + tid) * nbs + b];
   run[tid] = 0;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r = 0; r < RADIX_TILE / 256; ++r) {
-    const int idx = blockIdx.x * RADIX_TILE + r * 256 + tid;
-    const bool valid = idx < n;
+    const int local = b * RADIX_TILE + r * 256 + tid;
+    const bool valid = local < seglen;
+    const int idx = sg * seglen + local;
     const uint32_t key = valid ? kin[idx] : 0u;
     const uint32_t d = (key >> shift) & 255u;
     const int val = valid ? (vin ? vin[idx] : idx) : 0;
@@ -261,16 +284,20 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* kin, cons
   }
 }
 
-// cell_ptr[c] = number of sorted keys below c, for c = 0 .. keyspace.
-__global__ __launch_bounds__(256) void k_cell_ptr(const uint32_t* skeys, int n, int keyspace, int* cell_ptr) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c > keyspace) return;
-  int lo = 0, hi = n;
+// cell_ptr[i keyspace + c]: position of the first key >= c of segment i (the end of
+// the segment when there is none), for i keyspace + c = 0 .. nseg keyspace.
+__global__ __launch_bounds__(256) void k_cell_ptr(const uint32_t* skeys, int seglen, int nseg, int keyspace,
+                                                  int* cell_ptr) {
+  const long long cc = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (cc > (long long)nseg * keyspace) return;
+  const int sg = cc == (long long)nseg * keyspace ? nseg - 1 : (int)(cc / keyspace);
+  const int c = (int)(cc - (long long)sg * keyspace);  // keyspace for the very last entry
+  int lo = sg * seglen, hi = lo + seglen;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (skeys[mid] < (uint32_t)c) lo = mid + 1; else hi = mid;
   }
-  cell_ptr[c] = lo;
+  cell_ptr[cc] = lo;
 }
 
 __global__ __launch_bounds__(256) void k_blob_ngroups(const int* cell_ptr, int nblobs, int* goff) {
@@ -294,8 +321,15 @@ __global__ __launch_bounds__(256) void k_groups(const int* cell_ptr, const int* 
 
 static unsigned blocks(long long n, int per) { return (unsigned)((n + per - 1) / per); }
 
-hipError_t launch_scan_excl(uint32_t* data, int n, hipStream_t s) {
-  k_scan_excl<<<1, 1024, 0, s>>>(data, n);
+hipError_t launch_scan_excl(uint32_t* data, int n, hipStream_t s, uint32_t* part) {
+  if (!part || n <= 4 * SCAN_CHUNK) {
+    k_scan_excl<<<1, 1024, 0, s>>>(data, n, nullptr);
+    return hipGetLastError();
+  }
+  const int nb = (n + SCAN_CHUNK - 1) / SCAN_CHUNK;
+  k_scan_excl<<<nb, 1024, 0, s>>>(data, n, part);
+  k_scan_excl<<<1, 1024, 0, s>>>(part, nb, nullptr);
+  k_scan_add<<<blocks(n, 256), 256, 0, s>>>(data, n, part);
   return hipGetLastError();
 }
 
@@ -304,40 +338,38 @@ hipError_t launch_window_starts(const int32_t* off, const Geom& g, int32_t* star
   return hipGetLastError();
 }
 
-int radix_sort(uint32_t* keys[2], int* vals[2], uint32_t* ghist, int n, int passes, hipStream_t s) {
-  const int nb = (int)(((long long)n + RADIX_TILE - 1) / RADIX_TILE);
+int radix_sort(uint32_t* keys[2], int* vals[2], uint32_t* ghist, int seglen, int nseg, int passes, hipStream_t s,
+               uint32_t* part) {
+  const int nbs = (seglen + RADIX_TILE - 1) / RADIX_TILE, nb = nbs * nseg;
   int cur = 0;
   for (int pass = 0; pass < passes; ++pass) {
-    k_radix_hist<<<nb, 256, 0, s>>>(keys[cur], n, 8 * pass, ghist, nb);
-    k_scan_excl<<<1, 1024, 0, s>>>(ghist, 256 * nb);
-    k_radix_scatter<<<nb, 256, 0, s>>>(keys[cur], pass == 0 ? nullptr : vals[cur], n, 8 * pass, ghist, nb,
+    k_radix_hist<<<nb, 256, 0, s>>>(keys[cur], seglen, nbs, 8 * pass, ghist);
+    if (launch_scan_excl(ghist, 256 * nb, s, part) != hipSuccess) return -1;
+    k_radix_scatter<<<nb, 256, 0, s>>>(keys[cur], pass == 0 ? nullptr : vals[cur], seglen, nbs, 8 * pass, ghist,
                                        keys[cur ^ 1], vals[cur ^ 1]);
     cur ^= 1;
   }
   return hipGetLastError() == hipSuccess ? cur : -1;
 }
 
-hipError_t launch_cell_ptr(const uint32_t* sorted_keys, int n, int keyspace, int* cell_ptr, hipStream_t s) {
-  k_cell_ptr<<<blocks((long long)keyspace + 1, 256), 256, 0, s>>>(sorted_keys, n, keyspace, cell_ptr);
+hipError_t launch_cell_ptr(const uint32_t* sorted_keys, int seglen, int nseg, int keyspace, int* cell_ptr,
+                           hipStream_t s) {
+  k_cell_ptr<<<blocks((long long)keyspace * nseg + 1, 256), 256, 0, s>>>(sorted_keys, seglen, nseg, keyspace,
+                                                                          cell_ptr);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, hipStream_t s) {
-  const int n = g.N * g.ph, nb = p.radix_blocks;
-  const int keyspace = g.keyspace * g.ph, nblobs = g.nblobs * g.ph;
+  const int n = g.N * g.ph, nblobs = g.nblobs * g.ph;
   k_starts_keys<<<blocks(n, 256), 256, 0, s>>>(off, g, p.starts, p.keys[0]);
-  int cur = 0;
-  for (int pass = 0; pass < p.radix_passes; ++pass) {
-    k_radix_hist<<<nb, 256, 0, s>>>(p.keys[cur], n, 8 * pass, p.ghist, nb);
-    k_scan_excl<<<1, 1024, 0, s>>>(p.ghist, 256 * nb);
-    k_radix_scatter<<<nb, 256, 0, s>>>(p.keys[cur], pass == 0 ? nullptr : p.vals[cur], n, 8 * pass, p.ghist, nb,
-                                       p.keys[cur ^ 1], p.vals[cur ^ 1]);
-    cur ^= 1;
-  }
+  // each head block of the bucketing is a segment of its own
+  const int cur = radix_sort(p.keys, p.vals, p.ghist, g.N, g.ph, p.radix_passes, s, p.scan_part);
+  if (cur < 0) return hipErrorLaunchFailure;
   // p.perm was set to vals[passes & 1] == vals[cur]
-  k_cell_ptr<<<blocks((long long)keyspace + 1, 256), 256, 0, s>>>(p.keys[cur], n, keyspace, p.cell_ptr);
+  if (launch_cell_ptr(p.keys[cur], g.N, g.ph, g.keyspace, p.cell_ptr, s) != hipSuccess) return hipGetLastError();
   k_blob_ngroups<<<blocks((long long)nblobs + 1, 256), 256, 0, s>>>(p.cell_ptr, nblobs, p.goff);
-  k_scan_excl<<<1, 1024, 0, s>>>(reinterpret_cast<uint32_t*>(p.goff), nblobs + 1);
+  if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.goff), nblobs + 1, s, p.scan_part) != hipSuccess)
+    return hipGetLastError();
   k_groups<<<blocks(nblobs > 0 ? nblobs : 1, 256), 256, 0, s>>>(p.cell_ptr, p.goff, nblobs, p.groups, p.ngroups);
   return hipGetLastError();
 }

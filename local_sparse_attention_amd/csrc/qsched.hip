@@ -246,12 +246,14 @@ hipError_t launch_qsched(const Geom& g, const Prep& p, hipStream_t s) {
   const int nw = qs_items(g) * g.ph;
   const unsigned wb = (unsigned)((nw + 1 + 63) / 64);
   k_qtile_count<<<wb, 64, 0, s>>>(g, p.goff, p.groups, nw, p.qt_off);
-  if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.qt_off), nw + 1, s) != hipSuccess) return hipGetLastError();
+  if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.qt_off), nw + 1, s, p.scan_part) != hipSuccess)
+    return hipGetLastError();
   k_qtile_fill<<<wb, 64, 0, s>>>(g, p.goff, p.groups, nw, p.qt_off, p.qt);
   k_tile_fill<<<(unsigned)((p.max_groups + 15) / 16), 256, 0, s>>>(p.perm, p.starts, p.qt, p.qt_off + nw, g.N,
                                                                    p.tq_ids, p.tq_st, p.tq_dt);
   k_sched_count<<<wb, 64, 0, s>>>(g, p.qt_off, nw, p.qs_off);
-  if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.qs_off), nw + 1, s) != hipSuccess) return hipGetLastError();
+  if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.qs_off), nw + 1, s, p.scan_part) != hipSuccess)
+    return hipGetLastError();
   k_sched_fill<<<(unsigned)((nw + SCHED_WAVES - 1) / SCHED_WAVES), 64 * SCHED_WAVES, 0, s>>>(g, p.qt, p.qt_off, nw,
                                                                                           p.qs_off, p.qs);
   return hipGetLastError();

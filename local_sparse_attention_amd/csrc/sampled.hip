@@ -635,10 +635,10 @@ static hipError_t sampled_bwd_impl(const void* q, const void* k, const void* v, 
   k_sampled_keys<<<nblocks(E, 256), 256, 0, s>>>(off, g, w.keys[0]);
   uint32_t* keys[2] = {w.keys[0], w.keys[1]};
   int* vals[2] = {w.vals[0], w.vals[1]};
-  const int cur = radix_sort(keys, vals, w.ghist, (int)E, w.passes, s);
+  const int cur = radix_sort(keys, vals, w.ghist, (int)E, 1, w.passes, s);
   if (cur < 0) return hipErrorLaunchFailure;
   const int ncell = (g.F + 1) * (g.Hp + 1) * (g.Wp + 1);
-  hipError_t e = launch_cell_ptr(keys[cur], (int)E, g.H * ncell, w.cell_ptr, s);
+  hipError_t e = launch_cell_ptr(keys[cur], (int)E, 1, g.H * ncell, w.cell_ptr, s);
   if (e != hipSuccess) return e;
   k_sampled_bwd_q<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)k, (const T*)v, (const T*)o,
                                                           (const T*)dout, lse, off, (T*)dq, w.coef_a, w.coef_g,
