@@ -463,6 +463,8 @@ def main():
                     help="only the operator variants (for profiling their kernels)")
     ap.add_argument("--per-head-only", action="store_true",
                     help="only the per-head-offsets variant (for profiling its kernels)")
+    ap.add_argument("--predictor-only", action="store_true",
+                    help="only the DWConv3D term and offset predictor variants (for profiling their kernels)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json from rocprofv3 counter CSVs (no GPU needed)")
     args = ap.parse_args()
@@ -489,6 +491,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+        return
+    if args.predictor_only:
+        print(json.dumps({"variants": run_predictor(dsa3d, 3, 1)}), flush=True)
         return
     if args.variants_only or args.per_head_only:
         wl = configs.C5

@@ -405,6 +405,364 @@ __global__ __launch_bounds__(256) void k_dwconv_dw_sum(const float* __restrict__
   }
 }
 
+// ---- frame-sweeping forms: filters up to 3 x 3 x 3, C a multiple of 64 ------------
+// A block owns a TB_Y x TB_X tile of token positions and TB_C channels and sweeps a
+// run of frames.  The input slices of the frames its taps read -- the tile plus a halo
+// of (cy - 1) / 2 rows and (cx - 1) / 2 columns, [token][TB_C] in LDS -- sit in a ring
+// of TB_RING slices, one new slice per output frame, so every input row comes from
+// memory about once (halo aside) instead of once per tap row.  The next frame's slice is
+// loaded into registers while the current frame is computed.
+constexpr int TB_Y = 8, TB_X = 16, TB_C = 64, TB_RING = 3;
+
+template <typename T, int CY, int CX>
+struct Tube {
+  static constexpr int SY = TB_Y + CY - 1, SX = TB_X + CX - 1, SLICE = SY * SX;  // slice rows, columns, tokens
+  static constexpr int CH = SLICE * (TB_C / 8);   // 8-channel chunks per slice
+  static constexpr int LOADS = (CH + 255) / 256;  // chunks per thread
+};
+
+// 8 consecutive elements as one or two 16-byte words
+template <typename T> struct Chunk8;
+template <> struct Chunk8<u16> { uint4 a; };
+template <> struct Chunk8<float> { uint4 a, b; };
+__device__ __forceinline__ Chunk8<u16> ld_chunk(const u16* p) { return {*reinterpret_cast<const uint4*>(p)}; }
+__device__ __forceinline__ Chunk8<float> ld_chunk(const float* p) {
+  return {reinterpret_cast<const uint4*>(p)[0], reinterpret_cast<const uint4*>(p)[1]};
+}
+__device__ __forceinline__ void st_chunk(u16* p, const Chunk8<u16>& c) { *reinterpret_cast<uint4*>(p) = c.a; }
+__device__ __forceinline__ void st_chunk(float* p, const Chunk8<float>& c) {
+  reinterpret_cast<uint4*>(p)[0] = c.a;
+  reinterpret_cast<uint4*>(p)[1] = c.b;
+}
+template <typename T> __device__ __forceinline__ Chunk8<T> zero_chunk();
+template <> __device__ __forceinline__ Chunk8<u16> zero_chunk<u16>() { return {make_uint4(0u, 0u, 0u, 0u)}; }
+template <> __device__ __forceinline__ Chunk8<float> zero_chunk<float>() {
+  return {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+}
+// 4 consecutive elements as fp32
+__device__ __forceinline__ void ld4(const u16* p, float* x) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  x[0] = __uint_as_float(u.x << 16);
+  x[1] = __uint_as_float(u.x & 0xffff0000u);
+  x[2] = __uint_as_float(u.y << 16);
+  x[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+__device__ __forceinline__ void ld4(const float* p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+
+// Block order: tile column fastest, then tile row, frame run, channel block, each XCD
+// given a contiguous run (neighbouring tiles share their halo rows in one L2).
+struct TubeBlock {
+  int c0, y0, x0, t0, t1;
+};
+__device__ __forceinline__ TubeBlock tube_block(const CGeom& g, int fchunk) {
+  const int ntx = (g.Wp + TB_X - 1) / TB_X, nty = (g.Hp + TB_Y - 1) / TB_Y;
+  const int nfc = (g.F + fchunk - 1) / fchunk, ncb = g.C / TB_C;
+  int L = xcd_remap(blockIdx.x, ncb * nfc * nty * ntx);
+  TubeBlock b;
+  const int tx = L % ntx;
+  L /= ntx;
+  const int ty = L % nty;
+  L /= nty;
+  const int fc = L % nfc;
+  b.c0 = (L / nfc) * TB_C;
+  b.y0 = ty * TB_Y;
+  b.x0 = tx * TB_X;
+  b.t0 = fc * fchunk;
+  b.t1 = min(b.t0 + fchunk, g.F);
+  return b;
+}
+
+// This thread's chunks of the slice of frame f (zeros outside the grid).
+template <typename T, int CY, int CX>
+__device__ __forceinline__ void tube_load(const T* __restrict__ x, const CGeom& g, const TubeBlock& b, int f,
+                                          Chunk8<T>* buf) {
+  using U = Tube<T, CY, CX>;
+  constexpr int ry = (CY - 1) / 2, rx = (CX - 1) / 2;
+#pragma unroll
+  for (int k = 0; k < U::LOADS; ++k) {
+    const int j = threadIdx.x + 256 * k;
+    if (j < U::CH) {
+      const int tok = j >> 3, sy = tok / U::SX, sx = tok - sy * U::SX;
+      const int gy = b.y0 - ry + sy, gx = b.x0 - rx + sx;
+      const bool ok = (unsigned)f < (unsigned)g.F && (unsigned)gy < (unsigned)g.Hp && (unsigned)gx < (unsigned)g.Wp;
+      buf[k] = ok ? ld_chunk(x + ((size_t)(f * g.Hp + gy) * g.Wp + gx) * g.C + b.c0 + (j & 7) * 8) : zero_chunk<T>();
+    }
+  }
+}
+template <typename T, int CY, int CX>
+__device__ __forceinline__ void tube_store(T* slot, const Chunk8<T>* buf) {
+  using U = Tube<T, CY, CX>;
+#pragma unroll
+  for (int k = 0; k < U::LOADS; ++k) {
+    const int j = threadIdx.x + 256 * k;
+    if (j < U::CH) st_chunk(slot + (size_t)j * 8, buf[k]);
+  }
+}
+__device__ __forceinline__ int ring_slot(int f) { return ((f % TB_RING) + TB_RING) % TB_RING; }
+
+// Forward (or, with the filters mirrored, the input gradient): thread (cg, column, row
+// quad) computes 4 tokens down its column of the tile for 8 channels; a wave reads 8
+// neighbouring tokens' 128 contiguous bytes at a time from the slice.
+template <typename T, int CY, int CX>
+__global__ __launch_bounds__(256) void k_dwconv_tube(const T* __restrict__ x, const float* __restrict__ w,
+                                                     const float* __restrict__ b, T* __restrict__ y, CGeom g,
+                                                     int fchunk, int accumulate, int flip) {
+  using U = Tube<T, CY, CX>;
+  __shared__ __attribute__((aligned(16))) T ring[TB_RING][U::SLICE * TB_C];
+  __shared__ __attribute__((aligned(16))) float lw[27 * TB_C];
+  const int tid = threadIdx.x;
+  const TubeBlock bk = tube_block(g, fchunk);
+  const int rt = (g.ct - 1) / 2;
+  for (int i = tid; i < g.taps * TB_C; i += 256) {
+    const int tap = i / TB_C, cl = i - tap * TB_C;
+    lw[i] = w[(size_t)(bk.c0 + cl) * g.taps + (flip ? g.taps - 1 - tap : tap)];
+  }
+  Chunk8<T> pre[U::LOADS];
+  for (int f = bk.t0 - rt; f <= bk.t0 + rt; ++f) {
+    tube_load<T, CY, CX>(x, g, bk, f, pre);
+    tube_store<T, CY, CX>(ring[ring_slot(f)], pre);
+  }
+  __syncthreads();
+  const int cg = tid & 7, col = (tid >> 3) & 15, rq = tid >> 7;
+  const int c = bk.c0 + cg * 8;
+  float bias[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bias[e] = (b && !flip) ? b[c + e] : 0.f;
+  for (int t = bk.t0; t < bk.t1; ++t) {
+    const bool more = t + 1 < bk.t1;
+    if (more) tube_load<T, CY, CX>(x, g, bk, t + 1 + rt, pre);
+    float acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[i][e] = bias[e];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      if (a >= g.ct) break;
+      const T* sl = ring[ring_slot(t - rt + a)];
+#pragma unroll
+      for (int f = 0; f < CX; ++f) {
+        // rows 4 rq .. 4 rq + 3 + CY - 1 of the slice at column col + f
+        float v[4 + CY - 1][8];
+#pragma unroll
+        for (int p = 0; p < 4 + CY - 1; ++p) ld8(sl + ((4 * rq + p) * U::SX + col + f) * TB_C + cg * 8, v[p]);
+#pragma unroll
+        for (int e2 = 0; e2 < CY; ++e2) {
+          const float* wp = lw + ((a * CY + e2) * CX + f) * TB_C + cg * 8;
+          const float4 w0 = *reinterpret_cast<const float4*>(wp), w1 = *reinterpret_cast<const float4*>(wp + 4);
+          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(wv[e], v[i + e2][e], acc[i][e]);
+        }
+      }
+    }
+    const int gx = bk.x0 + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gy = bk.y0 + 4 * rq + i;
+      if (gy < g.Hp && gx < g.Wp) {
+        T* out = y + ((size_t)(t * g.Hp + gy) * g.Wp + gx) * g.C + c;
+        if (accumulate) {
+          float o[8];
+          ld8(out, o);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[i][e] += o[e];
+        }
+        st8(out, acc[i]);
+      }
+    }
+    __syncthreads();  // every read of the leaving frame's slice is done
+    if (more) tube_store<T, CY, CX>(ring[ring_slot(t + 1 + rt)], pre);
+    __syncthreads();
+  }
+}
+
+// Filter / bias gradient over the same tiles: thread (cg2, cp) keeps the partial sums of
+// all taps for 2 channels and the tile columns cp and cp + 8, walking each column's rows
+// in groups of 4 (its own dy values -- 2 columns x 8 rows x 2 channels -- in registers,
+// loaded a frame ahead like the slices; x from the slices; a wave reads two neighbouring
+// tokens' 128 bytes at a time); at the end the 8 column pairs' sums are added pairwise
+// in LDS in a fixed order and the block writes its part, [part][C][taps + 1] as
+// k_dwconv_dw_sum reads it (part = (frame run, tile row, tile column)).
+template <typename T> struct Dy2;  // 2 consecutive elements
+template <> struct Dy2<u16> { uint32_t v; };
+template <> struct Dy2<float> { float2 v; };
+__device__ __forceinline__ void dy2_unpack(const Dy2<u16>& d, float* x) {
+  x[0] = __uint_as_float(d.v << 16);
+  x[1] = __uint_as_float(d.v & 0xffff0000u);
+}
+__device__ __forceinline__ void dy2_unpack(const Dy2<float>& d, float* x) {
+  x[0] = d.v.x;
+  x[1] = d.v.y;
+}
+__device__ __forceinline__ void ld2(const u16* p, float* x) { dy2_unpack(Dy2<u16>{*reinterpret_cast<const uint32_t*>(p)}, x); }
+__device__ __forceinline__ void ld2(const float* p, float* x) { dy2_unpack(Dy2<float>{*reinterpret_cast<const float2*>(p)}, x); }
+
+template <typename T, int CY, int CX>
+__global__ __launch_bounds__(256, 2) void k_dwconv_dw_tube(const T* __restrict__ x, const T* __restrict__ dy,
+                                                           float* __restrict__ part, CGeom g, int fchunk) {
+  using U = Tube<T, CY, CX>;
+  constexpr int NT = 3 * CY * CX;  // tap slots (ct <= 3)
+  __shared__ __attribute__((aligned(16))) T ring[TB_RING][U::SLICE * TB_C];
+  const int tid = threadIdx.x;
+  const TubeBlock bk = tube_block(g, fchunk);
+  const int rt = (g.ct - 1) / 2;
+  const int cg2 = tid & 31, cp = tid >> 5;
+  const int c = bk.c0 + cg2 * 2;
+  // this thread's dy values of frame f: columns cp, cp + 8, rows 0 .. TB_Y - 1 (zeros outside)
+  auto dy_fetch = [&](int f, Dy2<T>* buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < TB_Y; ++i) {
+        const int gy = bk.y0 + i, gx = bk.x0 + cp + 8 * h;
+        if (gy < g.Hp && gx < g.Wp)
+          buf[h * TB_Y + i] = *reinterpret_cast<const Dy2<T>*>(dy + ((size_t)(f * g.Hp + gy) * g.Wp + gx) * g.C + c);
+        else
+          __builtin_memset(&buf[h * TB_Y + i], 0, sizeof(Dy2<T>));
+      }
+  };
+  Chunk8<T> pre[U::LOADS];
+  Dy2<T> dcur[2 * TB_Y], dnext[2 * TB_Y];
+  for (int f = bk.t0 - rt; f <= bk.t0 + rt; ++f) {
+    tube_load<T, CY, CX>(x, g, bk, f, pre);
+    tube_store<T, CY, CX>(ring[ring_slot(f)], pre);
+  }
+  dy_fetch(bk.t0, dcur);
+  __syncthreads();
+  float acc[NT + 1][2];  // taps, then the bias
+#pragma unroll
+  for (int i = 0; i <= NT; ++i) acc[i][0] = acc[i][1] = 0.f;
+  for (int t = bk.t0; t < bk.t1; ++t) {
+    const bool more = t + 1 < bk.t1;
+    if (more) {
+      tube_load<T, CY, CX>(x, g, bk, t + 1 + rt, pre);
+      dy_fetch(t + 1, dnext);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = cp + 8 * h;
+#pragma unroll
+      for (int rq = 0; rq < TB_Y / 4; ++rq) {
+        float d[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dy2_unpack(dcur[h * TB_Y + 4 * rq + i], d[i]);
+          acc[NT][0] += d[i][0];
+          acc[NT][1] += d[i][1];
+        }
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+          if (a >= g.ct) break;
+          const T* sl = ring[ring_slot(t - rt + a)];
+#pragma unroll
+          for (int f = 0; f < CX; ++f) {
+            float v[4 + CY - 1][2];
+#pragma unroll
+            for (int p = 0; p < 4 + CY - 1; ++p) ld2(sl + ((4 * rq + p) * U::SX + col + f) * TB_C + cg2 * 2, v[p]);
+#pragma unroll
+            for (int e2 = 0; e2 < CY; ++e2) {
+              const int tap = (a * CY + e2) * CX + f;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                acc[tap][0] = fmaf(d[i][0], v[i + e2][0], acc[tap][0]);
+                acc[tap][1] = fmaf(d[i][1], v[i + e2][1], acc[tap][1]);
+              }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (more) {
+      tube_store<T, CY, CX>(ring[ring_slot(t + 1 + rt)], pre);
+#pragma unroll
+      for (int i = 0; i < 2 * TB_Y; ++i) dcur[i] = dnext[i];
+    }
+    __syncthreads();
+  }
+  // column pairs 0 .. 7: add pair cp + h into pair cp for h = 4, 2, 1, through LDS
+  float* red = reinterpret_cast<float*>(&ring[0][0]);  // [pair][NT + 1][32 cg2][2]
+  constexpr int PER = (NT + 1) * 64;                   // floats per pair
+  static_assert(4 * PER * 4 <= (int)sizeof(ring), "the reduction fits in the ring");
+  for (int h = 4; h >= 1; h >>= 1) {
+    if (cp >= h && cp < 2 * h)
+#pragma unroll
+      for (int i = 0; i <= NT; ++i)
+        *reinterpret_cast<float2*>(red + (cp - h) * PER + (i * 32 + cg2) * 2) = make_float2(acc[i][0], acc[i][1]);
+    __syncthreads();
+    if (cp < h)
+#pragma unroll
+      for (int i = 0; i <= NT; ++i) {
+        const float2 o = *reinterpret_cast<const float2*>(red + cp * PER + (i * 32 + cg2) * 2);
+        acc[i][0] += o.x;
+        acc[i][1] += o.y;
+      }
+    __syncthreads();
+  }
+  if (cp == 0) {
+    const int ntx = (g.Wp + TB_X - 1) / TB_X, nty = (g.Hp + TB_Y - 1) / TB_Y;
+    const int pidx = ((bk.t0 / fchunk) * nty + bk.y0 / TB_Y) * ntx + bk.x0 / TB_X;
+    float* out = part + ((size_t)pidx * g.C + c) * (g.taps + 1);
+    // tap slot (a, e, f) of this kernel is filter tap (a * cy + e) * cx + f (cy = CY, cx = CX)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      static_for<0, NT>([&](auto TC) {
+        constexpr int tap = decltype(TC)::value;
+        if (tap < g.taps) out[(size_t)e * (g.taps + 1) + tap] = acc[tap][e];
+      });
+      out[(size_t)e * (g.taps + 1) + g.taps] = acc[NT][e];
+    }
+  }
+}
+
+// The frame-sweeping forms: filters up to 3 x 3 x 3 (odd sides), C a multiple of 64.
+static bool tube_ok(const CGeom& g) {
+  return g.C % TB_C == 0 && g.ct <= 3 && (g.cy == 1 || g.cy == 3) && (g.cx == 1 || g.cx == 3);
+}
+// Frames per block: the whole run unless that leaves fewer than 1024 blocks (4 per CU),
+// then shorter runs of at least 4 frames.
+static int tube_fchunk(const CGeom& g) {
+  const long long tiles =
+      (long long)(g.C / TB_C) * ((g.Hp + TB_Y - 1) / TB_Y) * ((g.Wp + TB_X - 1) / TB_X);
+  const long long nfc = std::min<long long>(g.F, std::max<long long>(1, (1024 + tiles - 1) / tiles));
+  const int fchunk = (int)((g.F + nfc - 1) / nfc);
+  return std::max(fchunk, std::min(4, g.F));
+}
+static long long tube_parts(const CGeom& g) {  // filter-gradient parts per channel
+  const int fchunk = tube_fchunk(g);
+  return (long long)((g.F + fchunk - 1) / fchunk) * ((g.Hp + TB_Y - 1) / TB_Y) * ((g.Wp + TB_X - 1) / TB_X);
+}
+static unsigned tube_blocks(const CGeom& g) { return (unsigned)(tube_parts(g) * (g.C / TB_C)); }
+
+template <typename T, int CY, int CX>
+static hipError_t tube_conv(const void* x, const float* w, const float* b, void* y, const CGeom& g, int acc,
+                            int flip, hipStream_t s) {
+  k_dwconv_tube<T, CY, CX><<<tube_blocks(g), 256, 0, s>>>((const T*)x, w, b, (T*)y, g, tube_fchunk(g), acc, flip);
+  return hipGetLastError();
+}
+template <typename T, int CY, int CX>
+static hipError_t tube_dw(const void* x, const void* dy, float* part, const CGeom& g, hipStream_t s) {
+  k_dwconv_dw_tube<T, CY, CX><<<tube_blocks(g), 256, 0, s>>>((const T*)x, (const T*)dy, part, g, tube_fchunk(g));
+  return hipGetLastError();
+}
+template <typename T>
+static hipError_t tube_conv_dispatch(const void* x, const float* w, const float* b, void* y, const CGeom& g, int acc,
+                                     int flip, hipStream_t s) {
+  if (g.cy == 1) return g.cx == 1 ? tube_conv<T, 1, 1>(x, w, b, y, g, acc, flip, s) : tube_conv<T, 1, 3>(x, w, b, y, g, acc, flip, s);
+  return g.cx == 1 ? tube_conv<T, 3, 1>(x, w, b, y, g, acc, flip, s) : tube_conv<T, 3, 3>(x, w, b, y, g, acc, flip, s);
+}
+template <typename T>
+static hipError_t tube_dw_dispatch(const void* x, const void* dy, float* part, const CGeom& g, hipStream_t s) {
+  if (g.cy == 1) return g.cx == 1 ? tube_dw<T, 1, 1>(x, dy, part, g, s) : tube_dw<T, 1, 3>(x, dy, part, g, s);
+  return g.cx == 1 ? tube_dw<T, 3, 1>(x, dy, part, g, s) : tube_dw<T, 3, 3>(x, dy, part, g, s);
+}
+
 template <typename T, int CX>
 static hipError_t conv_launch_w(const void* x, const float* w, const float* b, void* y, const CGeom& g, int acc,
                                 int flip, hipStream_t s) {
@@ -422,6 +780,7 @@ static hipError_t conv_launch_w(const void* x, const float* w, const float* b, v
 template <typename T>
 static hipError_t conv_launch(const void* x, const float* w, const float* b, void* y, const CGeom& g, int acc,
                               int flip, hipStream_t s) {
+  if (tube_ok(g)) return tube_conv_dispatch<T>(x, w, b, y, g, acc, flip, s);
   switch (g.cx) {
     case 1: return conv_launch_w<T, 1>(x, w, b, y, g, acc, flip, s);
     case 3: return conv_launch_w<T, 3>(x, w, b, y, g, acc, flip, s);
@@ -512,10 +871,9 @@ int check_conv(const void* x, const float* w, int F, int Hp, int Wp, int C, int 
   return DSA3D_OK;
 }
 
-size_t conv_ws(const CGeom& g) {
-  const DwSplit sp = dw_split(g);
-  return (((size_t)g.F * sp.nyc * g.C * (g.taps + 1) * 4) + 255) & ~(size_t)255;
-}
+// filter-gradient parts: [parts][C][taps + 1] fp32
+long long conv_parts(const CGeom& g) { return tube_ok(g) ? tube_parts(g) : (long long)g.F * dw_split(g).nyc; }
+size_t conv_ws(const CGeom& g) { return (((size_t)conv_parts(g) * g.C * (g.taps + 1) * 4) + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -558,11 +916,13 @@ int dsa3d_dwconv3d_backward(const void* x, const float* weight, const void* dy, 
   hipError_t e = bf ? conv_launch<u16>(dy, weight, nullptr, dx, g, 0, 1, stream)
                     : conv_launch<float>(dy, weight, nullptr, dx, g, 0, 1, stream);
   if (e != hipSuccess) return DSA3D_ERR_LAUNCH;
-  e = bf ? dw_dispatch<u16>(x, dy, part, g, stream) : dw_dispatch<float>(x, dy, part, g, stream);
+  if (tube_ok(g))
+    e = bf ? tube_dw_dispatch<u16>(x, dy, part, g, stream) : tube_dw_dispatch<float>(x, dy, part, g, stream);
+  else
+    e = bf ? dw_dispatch<u16>(x, dy, part, g, stream) : dw_dispatch<float>(x, dy, part, g, stream);
   if (e != hipSuccess) return DSA3D_ERR_LAUNCH;
   const long long per = (long long)g.C * (g.taps + 1);
-  k_dwconv_dw_sum<<<(unsigned)((per + 255) / 256), 256, 0, stream>>>(part, dweight, dbias, g,
-                                                                      g.F * dw_split(g).nyc);
+  k_dwconv_dw_sum<<<(unsigned)((per + 255) / 256), 256, 0, stream>>>(part, dweight, dbias, g, (int)conv_parts(g));
   return hipGetLastError() == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
 

@@ -6,8 +6,9 @@ Bounds (from the arithmetic; S = the same sum taken over absolute values, comput
 oracle on |inputs|):
   - convolution output: fp32 sums of at most `taps` products (+ bias, + the accumulated
     value): |err| <= 2^-22 taps S; bf16 outputs add their rounding, 2^-8 |ref|.
-  - dweight / dbias: fp32 partial sums over a frame, then over frames:
-    |err| <= 2^-24 (Hp Wp + F) S.
+  - dweight / dbias: fp32 sums of N = F Hp Wp products in some fixed order (per block and
+    thread, then over threads, then over blocks): |err| <= 2^-24 (N - 1) S whatever the
+    order.
   - linear: fp32 sums over K products: |err| <= 2^-22 K S; on the bf16 path dy is rounded
     to bf16 before the two backward products: + 2^-8 S; bf16 dx adds 2^-8 |ref|.
   - the end-to-end output: the sampled-window tolerance of the attention term (bf16
@@ -40,8 +41,14 @@ def host(a):
 
 
 CONV_CASES = [
-    # grid, C, filter, dtype
+    # grid, C, filter, dtype; filters up to 3 x 3 x 3 with C a multiple of 64 take the
+    # frame-sweeping kernels (8 x 16 token tiles, 64 channels), the rest the general ones
     ((5, 9, 11), 64, (3, 3, 3), "f32"),
+    ((7, 13, 35), 128, (3, 3, 3), "bf16"),   # ragged tiles in both directions, two channel blocks
+    ((9, 10, 20), 192, (1, 3, 3), "bf16"),   # one frame tap
+    ((4, 6, 7), 64, (3, 1, 3), "f32"),       # one row tap
+    ((40, 9, 17), 64, (3, 3, 1), "bf16"),    # runs of frames (fewer tiles than blocks wanted)
+    ((2, 3, 3), 64, (3, 3, 3), "bf16"),      # grid smaller than a tile and than the filter along t
     ((6, 12, 10), 128, (3, 7, 7), "bf16"),
     ((4, 5, 6), 24, (5, 5, 3), "bf16"),     # filter wider than the grid along t, C not a multiple of 64
     ((3, 8, 8), 16, (1, 1, 1), "f32"),
@@ -74,7 +81,7 @@ def test_dwconv3d(dsa3d_gpu, case):
     rdx, rdw, rdb = oracle.dwconv3d_backward(x, w, dy, grid)
     Sx, Sw, Sb = oracle.dwconv3d_backward(np.abs(host(x)), np.abs(w), np.abs(host(dy)), grid)
     assert_bound(to_host_f64(dx), rdx, 2.0**-22 * taps * Sx + out_r * np.abs(rdx), "dx")
-    acc = 2.0**-24 * (grid[1] * grid[2] + grid[0])
+    acc = 2.0**-24 * max(N - 1, 1)
     assert_bound(dw.cpu().numpy(), rdw, acc * Sw + 1e-30, "dweight")
     assert_bound(db.cpu().numpy(), rdb, acc * Sb + 1e-30, "dbias")
 
