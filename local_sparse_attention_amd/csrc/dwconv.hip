@@ -503,77 +503,92 @@ __device__ __forceinline__ void tube_store(T* slot, const Chunk8<T>* buf) {
 }
 __device__ __forceinline__ int ring_slot(int f) { return ((f % TB_RING) + TB_RING) % TB_RING; }
 
-// Forward (or, with the filters mirrored, the input gradient): thread (cg, column, row
-// quad) computes 4 tokens down its column of the tile for 8 channels; a wave reads 8
-// neighbouring tokens' 128 contiguous bytes at a time from the slice.
+// 4 consecutive elements (a thread's channels of one token), raw
+template <typename T> struct Dy4;
+template <> struct Dy4<u16> { uint2 v; };
+template <> struct Dy4<float> { float4 v; };
+__device__ __forceinline__ void dy4_unpack(const Dy4<u16>& d, float* x) {
+  x[0] = __uint_as_float(d.v.x << 16);
+  x[1] = __uint_as_float(d.v.x & 0xffff0000u);
+  x[2] = __uint_as_float(d.v.y << 16);
+  x[3] = __uint_as_float(d.v.y & 0xffff0000u);
+}
+__device__ __forceinline__ void dy4_unpack(const Dy4<float>& d, float* x) {
+  x[0] = d.v.x; x[1] = d.v.y; x[2] = d.v.z; x[3] = d.v.w;
+}
+
+// Forward (or, with the filters mirrored, the input gradient): thread (cg4, column)
+// computes the tile's TB_Y rows of its column for 4 channels, with those channels'
+// filters in registers for the whole sweep; per frame offset and filter column it reads
+// one window of TB_Y + cy - 1 rows from the slice (a wave: four neighbouring tokens'
+// 128 bytes at a time).  With accumulate, the output's old values are added as the
+// results are written.
 template <typename T, int CY, int CX>
-__global__ __launch_bounds__(256) void k_dwconv_tube(const T* __restrict__ x, const float* __restrict__ w,
-                                                     const float* __restrict__ b, T* __restrict__ y, CGeom g,
-                                                     int fchunk, int accumulate, int flip) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_tube(
+    const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ b, T* __restrict__ y, CGeom g,
+    int fchunk, int accumulate, int flip) {
   using U = Tube<T, CY, CX>;
+  constexpr int NT = 3 * CY * CX;  // tap slots (ct <= 3)
   __shared__ __attribute__((aligned(16))) T ring[TB_RING][U::SLICE * TB_C];
-  __shared__ __attribute__((aligned(16))) float lw[27 * TB_C];
   const int tid = threadIdx.x;
   const TubeBlock bk = tube_block(g, fchunk);
   const int rt = (g.ct - 1) / 2;
-  for (int i = tid; i < g.taps * TB_C; i += 256) {
-    const int tap = i / TB_C, cl = i - tap * TB_C;
-    lw[i] = w[(size_t)(bk.c0 + cl) * g.taps + (flip ? g.taps - 1 - tap : tap)];
-  }
+  const int cg4 = tid & 15, col = tid >> 4;
+  const int c = bk.c0 + cg4 * 4, gx = bk.x0 + col;
+  float wr[NT][4];
+  static_for<0, NT>([&](auto TC) {
+    constexpr int tap = decltype(TC)::value;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      wr[tap][e] = tap < g.taps ? w[(size_t)(c + e) * g.taps + (flip ? g.taps - 1 - tap : tap)] : 0.f;
+  });
+  float bias[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bias[e] = (b && !flip) ? b[c + e] : 0.f;
   Chunk8<T> pre[U::LOADS];
   for (int f = bk.t0 - rt; f <= bk.t0 + rt; ++f) {
     tube_load<T, CY, CX>(x, g, bk, f, pre);
     tube_store<T, CY, CX>(ring[ring_slot(f)], pre);
   }
   __syncthreads();
-  const int cg = tid & 7, col = (tid >> 3) & 15, rq = tid >> 7;
-  const int c = bk.c0 + cg * 8;
-  float bias[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) bias[e] = (b && !flip) ? b[c + e] : 0.f;
   for (int t = bk.t0; t < bk.t1; ++t) {
     const bool more = t + 1 < bk.t1;
     if (more) tube_load<T, CY, CX>(x, g, bk, t + 1 + rt, pre);
-    float acc[4][8];
+    float acc[TB_Y][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TB_Y; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[i][e] = bias[e];
+      for (int e = 0; e < 4; ++e) acc[i][e] = bias[e];
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
       if (a >= g.ct) break;
       const T* sl = ring[ring_slot(t - rt + a)];
 #pragma unroll
       for (int f = 0; f < CX; ++f) {
-        // rows 4 rq .. 4 rq + 3 + CY - 1 of the slice at column col + f
-        float v[4 + CY - 1][8];
+        float v[TB_Y + CY - 1][4];
 #pragma unroll
-        for (int p = 0; p < 4 + CY - 1; ++p) ld8(sl + ((4 * rq + p) * U::SX + col + f) * TB_C + cg * 8, v[p]);
+        for (int p = 0; p < TB_Y + CY - 1; ++p) ld4(sl + (p * U::SX + col + f) * TB_C + cg4 * 4, v[p]);
 #pragma unroll
         for (int e2 = 0; e2 < CY; ++e2) {
-          const float* wp = lw + ((a * CY + e2) * CX + f) * TB_C + cg * 8;
-          const float4 w0 = *reinterpret_cast<const float4*>(wp), w1 = *reinterpret_cast<const float4*>(wp + 4);
-          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+          const int tap = (a * CY + e2) * CX + f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < TB_Y; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(wv[e], v[i + e2][e], acc[i][e]);
+            for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wr[tap][e], v[i + e2][e], acc[i][e]);
         }
       }
     }
-    const int gx = bk.x0 + col;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gy = bk.y0 + 4 * rq + i;
+    for (int i = 0; i < TB_Y; ++i) {
+      const int gy = bk.y0 + i;
       if (gy < g.Hp && gx < g.Wp) {
-        T* out = y + ((size_t)(t * g.Hp + gy) * g.Wp + gx) * g.C + c;
         if (accumulate) {
-          float o[8];
-          ld8(out, o);
+          float o[4];
+          dy4_unpack(*reinterpret_cast<const Dy4<T>*>(y + ((size_t)(t * g.Hp + gy) * g.Wp + gx) * g.C + c), o);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i][e] += o[e];
+          for (int e = 0; e < 4; ++e) acc[i][e] += o[e];
         }
-        st8(out, acc[i]);
+        store4(y + ((size_t)(t * g.Hp + gy) * g.Wp + gx) * g.C + c, acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
       }
     }
     __syncthreads();  // every read of the leaving frame's slice is done
@@ -604,7 +619,7 @@ __device__ __forceinline__ void ld2(const u16* p, float* x) { dy2_unpack(Dy2<u16
 __device__ __forceinline__ void ld2(const float* p, float* x) { dy2_unpack(Dy2<float>{*reinterpret_cast<const float2*>(p)}, x); }
 
 template <typename T, int CY, int CX>
-__global__ __launch_bounds__(256, 2) void k_dwconv_dw_tube(const T* __restrict__ x, const T* __restrict__ dy,
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_dw_tube(const T* __restrict__ x, const T* __restrict__ dy,
                                                            float* __restrict__ part, CGeom g, int fchunk) {
   using U = Tube<T, CY, CX>;
   constexpr int NT = 3 * CY * CX;  // tap slots (ct <= 3)
