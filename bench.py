@@ -596,6 +596,11 @@ def main():
     roof["traffic_note"] = ("bytes between L2 and the memory fabric (FETCH_SIZE x fetch scale + WRITE_SIZE x write "
                             "scale, both scales from a device copy of known size; fabric reads that hit the "
                             "Infinity Cache count too), from profiles/traffic.json when it matches the sources")
+    if roof["traffic"] is not None:
+        # the same kernel time over the bytes it actually moved (counters), not the algorithmic ones
+        roof["traffic_gbs"] = roof["traffic"] / t_dom / 1e9
+        roof["traffic_frac"] = roof["traffic_gbs"] / PEAK_HBM_GBS
+        roof["traffic_over_algorithmic"] = roof["traffic"] / kb
     roof["kernel"] = KERNEL_OF[dom] if wl.dtype == "bf16" else dom
     roof["kernel_ms"] = phases[dom]
 
