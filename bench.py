@@ -241,6 +241,17 @@ def sampled_flops(wl, fwd=True, bwd=True):
     return float(per) * wl.head_dim * wl.K * wl.N * wl.heads
 
 
+def box_flops(wl):
+    """Algorithmic fp32 VALU flops of box windows (one offset per query) per fwd+bwd, in the
+    lattice form the box kernels use: every sample shares the fraction, so the samples' 8
+    corners are the L = (kt+1)(ky+1)(kx+1) rows of one lattice.  Per (query, head): the
+    forward takes L dots q . K[l] and L updates A_l V[l] (4DL), the query-side backward the
+    dots q . K[l], dO . V[l] and the dQ updates (6DL), the key side dK[l] += B_l q and
+    dV[l] += A_l dO (4DL)."""
+    L = (wl.kt + 1) * (wl.ky + 1) * (wl.kx + 1)
+    return float(14 * L) * wl.head_dim * wl.N * wl.heads
+
+
 def _timed(fn, steps, warmup):
     import torch
 
@@ -323,7 +334,7 @@ def run_sampled(dsa3d, steps, warmup):
         ms_f = _timed(fwd, steps, warmup)
         ms_b = _timed(bwd, steps, warmup)
         ms = ms_f + ms_b
-        fl = sampled_flops(wl)
+        fl = box_flops(wl) if mode == "box" else sampled_flops(wl)
         res[key] = {
             "workload": f"{wl.name}: grid {wl.F}x{wl.Hp}x{wl.Wp} (N={wl.N}), {wl.heads} heads x {wl.head_dim}, "
                         f"window {wl.kt}x{wl.ky}x{wl.kx}, {wl.dtype}, "
@@ -332,7 +343,9 @@ def run_sampled(dsa3d, steps, warmup):
             "unit": "query-token-heads/s",
             "roofline": {"bound": "alu", "achieved": fl / (ms / 1e3) / 1e12, "peak": PEAK_F32_TFLOPS,
                          "unit": "TFLOP/s", "frac": fl / (ms / 1e3) / 1e12 / PEAK_F32_TFLOPS,
-                         "note": "fp32 VALU flops of the trilinear form (36D fwd + 102D bwd per sample)"}}
+                         "note": ("fp32 VALU flops of the lattice form (14DL per query-head, L = (kt+1)(ky+1)"
+                                  "(kx+1))" if mode == "box" else
+                                  "fp32 VALU flops of the trilinear form (36D fwd + 102D bwd per sample)")}}
         del t, off, ws, box
         torch.cuda.empty_cache()
     return res
@@ -463,6 +476,8 @@ def main():
                     help="only the operator variants (for profiling their kernels)")
     ap.add_argument("--per-head-only", action="store_true",
                     help="only the per-head-offsets variant (for profiling its kernels)")
+    ap.add_argument("--sampled-only", action="store_true",
+                    help="only the sampled-window variants (for profiling their kernels)")
     ap.add_argument("--predictor-only", action="store_true",
                     help="only the DWConv3D term and offset predictor variants (for profiling their kernels)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -494,6 +509,9 @@ def main():
         return
     if args.predictor_only:
         print(json.dumps({"variants": run_predictor(dsa3d, 3, 1)}), flush=True)
+        return
+    if args.sampled_only:
+        print(json.dumps({"variants": run_sampled(dsa3d, 3, 1)}), flush=True)
         return
     if args.variants_only or args.per_head_only:
         wl = configs.C5

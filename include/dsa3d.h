@@ -196,7 +196,11 @@ int dsa3d_backward_heads(const void* q, const void* k, const void* v, const int3
 /* Workspace bytes of dsa3d_sampled_backward (backward = 1; the forward needs none and
    reports 256); 0 for an invalid geometry or one past the backward's limits
    (N * heads * kt*ky*kx < 2^31 samples, heads * (F+1)(Hp+1)(Wp+1) < 2^31 cells).
-   About 60 bytes per sample in free mode, 48 in box mode. */
+   About 60 bytes per sample in free mode.  Box mode works on the lattice of the
+   L = (kt+1)(ky+1)(kx+1) grid rows that one offset's samples blend, when that lattice
+   fits the kernels' LDS (4 (2L + 2 kt*ky*kx) floats <= 16384, so L <= 1024) and
+   N * heads * L < 2^31: about 40 bytes per lattice point; otherwise it works per sample
+   like free mode (about 48 bytes per sample). */
 size_t dsa3d_sampled_workspace_bytes(int F, int Hp, int Wp, int heads, int kt, int ky, int kx, int mode,
                                      int backward);
 
@@ -213,7 +217,8 @@ int dsa3d_sampled_forward(const void* q, const void* k, const void* v, const flo
    one-sided derivative of floor-based weights); in box mode also through the clamp
    (1 where p_d + o_d - (k_d-1)/2 lies strictly inside (0, G_d - k_d), else 0).
    dk and dv are gathered per key from its samples (sorted by base cell, fixed
-   order): no atomics. */
+   order), or in box mode on the lattice from the lattice points on that key (sorted
+   by token per head, in (query, point) order): no atomics. */
 int dsa3d_sampled_backward(const void* q, const void* k, const void* v, const float* offsets, long long stride_token,
                            long long stride_head, long long stride_sample, int mode, const void* out,
                            const float* lse, const void* dout, int F, int Hp, int Wp, int heads, int head_dim, int kt,

@@ -411,6 +411,279 @@ __global__ __launch_bounds__(256) void k_sampled_bwd_q(const T* __restrict__ q, 
 }
 
 // ---------------------------------------------------------------------------
+// box windows on the start's lattice
+// ---------------------------------------------------------------------------
+// With one offset per (query, head) every sample shares the fraction f of the start s,
+// so sample (u, v, w) blends the rows s_i + (u, v, w) + c, c in {0,1}^3, with the same
+// 8 weights: all samples read the (kt+1)(ky+1)(kx+1) rows of the lattice s_i + [0, k]^3.
+// Since the blend is linear, q . K~(sample) is the same blend of the lattice dots
+// T_l = q . K[l], and sum_j p_j V~(sample j) = sum_l A_l V[l] with A_l the blend's
+// transpose applied to p.  A wave per (query, head) reads each lattice row once
+// instead of each sample's 8 corners (147 samples: 256 rows against 1176).  The backward
+// hands the key side the lattice weights of dO and q per lattice point, so the key side
+// too visits L rows per (query, head) rather than 8 K corners.
+constexpr int BOX_LDS_BYTES = 65536;  // a block's 4 waves: lattice and sample arrays
+
+struct BoxLat {
+  int e1, e2;        // lattice extents: ky + 1, kx + 1 (lattice index (lt e1 + ly) e2 + lx)
+  int L;             // (kt + 1) e1 e2
+  int coff[8];       // lattice index offset of corner c
+  float w[8];        // corner weights
+  float dw[8][3];    // their derivatives by f_t, f_y, f_x
+};
+__device__ __forceinline__ BoxLat box_lattice(const SGeom& g, const QPos& qp) {
+  BoxLat b;
+  b.e1 = g.ky + 1;
+  b.e2 = g.kx + 1;
+  b.L = (g.kt + 1) * b.e1 * b.e2;
+  const float* f = qp.sf;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int ct = (c >> 2) & 1, cy = (c >> 1) & 1, cx = c & 1;
+    b.coff[c] = (ct * b.e1 + cy) * b.e2 + cx;
+    const float pt = ct ? f[0] : 1.f - f[0], py = cy ? f[1] : 1.f - f[1], px = cx ? f[2] : 1.f - f[2];
+    b.w[c] = pt * py * px;
+    b.dw[c][0] = (ct ? 1.f : -1.f) * py * px;
+    b.dw[c][1] = (cy ? 1.f : -1.f) * pt * px;
+    b.dw[c][2] = (cx ? 1.f : -1.f) * pt * py;
+  }
+  return b;
+}
+// grid token of lattice point l, -1 outside the grid
+__device__ __forceinline__ int box_tok(const SGeom& g, const QPos& qp, const BoxLat& b, int l) {
+  const int lt = l / (b.e1 * b.e2), r = l - lt * b.e1 * b.e2, ly = r / b.e2, lx = r - ly * b.e2;
+  const int t = qp.si[0] + lt, y = qp.si[1] + ly, x = qp.si[2] + lx;
+  if ((unsigned)t >= (unsigned)g.F || (unsigned)y >= (unsigned)g.Hp || (unsigned)x >= (unsigned)g.Wp) return -1;
+  return (t * g.Hp + y) * g.Wp + x;
+}
+// lattice index of sample j's base corner
+__device__ __forceinline__ int box_base(const SGeom& g, const BoxLat& b, int j) {
+  const int u = j / (g.ky * g.kx), r = j - u * (g.ky * g.kx), v = r / g.kx, w = r - v * g.kx;
+  return (u * b.e1 + v) * b.e2 + w;
+}
+// sum over the samples j with base corner l - coff[c] of wc[c] x[j] (the blend's transpose)
+__device__ __forceinline__ float box_gather(const SGeom& g, const BoxLat& b, const float* wc, const float* x, int l) {
+  const int lt = l / (b.e1 * b.e2), r = l - lt * b.e1 * b.e2, ly = r / b.e2, lx = r - ly * b.e2;
+  float a = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int u = lt - ((c >> 2) & 1), v = ly - ((c >> 1) & 1), w = lx - (c & 1);
+    if ((unsigned)u < (unsigned)g.kt && (unsigned)v < (unsigned)g.ky && (unsigned)w < (unsigned)g.kx)
+      a = fmaf(wc[c], x[(u * g.ky + v) * g.kx + w], a);
+  }
+  return a;
+}
+// wave-wide sum / max
+__device__ __forceinline__ float wsum(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ float wmax(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+// LDS written by some lanes of the wave, read by others: order the accesses
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+// The lattice rows of (n, h) for a wave's lane groups, BU rows per group in flight:
+// f(l, values of row l for this lane, tok >= 0) is called for every lattice point.
+template <int BU, typename T, int D, typename Fn>
+__device__ __forceinline__ void box_rows(const SGeom& g, const QPos& qp, const BoxLat& b, const T* __restrict__ src,
+                                         int h, int grp, int gl, Fn&& fn) {
+  constexpr int G = D / EL, NG = 64 / G;
+  for (int l0 = grp; l0 < b.L; l0 += NG * BU) {
+    Raw8<T> raw[BU];
+    int ok[BU];
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int l = l0 + u * NG;
+      const int tok = l < b.L ? box_tok(g, qp, b, l) : -1;
+      ok[u] = tok >= 0;
+      raw[u] = ldraw(src + ((size_t)(ok[u] ? tok : 0) * g.H + h) * D + gl * EL);
+    }
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int l = l0 + u * NG;
+      if (l < b.L) {
+        float x[EL];
+        unraw(raw[u], x);
+        fn(l, x, ok[u] != 0);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_box_fwd(const T* __restrict__ q, const T* __restrict__ k,
+                                                 const T* __restrict__ v, const float* __restrict__ off,
+                                                 T* __restrict__ out, float* __restrict__ lse, SGeom g) {
+  constexpr int G = D / EL;
+  extern __shared__ float box_lds[];  // per wave: L lattice values (T_l, then A_l), K samples (scores, then p_j)
+  const int wq = threadIdx.x >> 6;
+  const long long wv = (long long)blockIdx.x * 4 + wq;
+  if (wv >= (long long)g.N * g.H) return;
+  const int n = (int)(wv / g.H), h = (int)(wv - (long long)n * g.H);
+  const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
+  const QPos qp = query_pos(g, off, n, h);
+  const BoxLat b = box_lattice(g, qp);
+  float* sl = box_lds + (size_t)wq * (b.L + g.K);
+  float* ss = sl + b.L;
+  const size_t row = ((size_t)n * g.H + h) * D + gl * EL;
+  float qf[EL];
+  load8(q + row, qf);
+  // lattice dots q . K[l] (0 outside the grid)
+  box_rows<4, T, D>(g, qp, b, k, h, grp, gl, [&](int l, const float* x, bool ok) {
+    const float t = gsum<G>(dot8(qf, x));
+    if (gl == 0) sl[l] = ok ? t : 0.f;
+  });
+  wave_lds_sync();
+  // sample scores (log2 units), their max, p and its sum
+  const float sl2 = g.scale * LOG2E;
+  float mx = -INFINITY;
+  for (int j = lane; j < g.K; j += 64) {
+    const int lb = box_base(g, b, j);
+    float z = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) z = fmaf(b.w[c], sl[lb + b.coff[c]], z);
+    ss[j] = z * sl2;
+    mx = fmaxf(mx, z * sl2);
+  }
+  mx = wmax(mx);
+  float sum = 0.f;
+  for (int j = lane; j < g.K; j += 64) {
+    const float p = exp2f(ss[j] - mx);
+    ss[j] = p;
+    sum += p;
+  }
+  sum = wsum(sum);
+  wave_lds_sync();
+  // A_l, the lattice weights of V
+  for (int l = lane; l < b.L; l += 64) sl[l] = box_gather(g, b, b.w, ss, l);
+  wave_lds_sync();
+  float acc[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) acc[e] = 0.f;
+  box_rows<4, T, D>(g, qp, b, v, h, grp, gl, [&](int l, const float* x, bool ok) {
+    const float a = ok ? sl[l] : 0.f;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] = fmaf(a, x[e], acc[e]);
+  });
+#pragma unroll
+  for (int mask = G; mask < 64; mask <<= 1)
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] += __shfl_xor(acc[e], mask, 64);
+  if (grp == 0) {
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] *= inv;
+    store8(out + row, acc);
+    if (gl == 0) lse[(size_t)h * g.N + n] = (mx + log2f(sum)) * LN2;
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_box_bwd_q(const T* __restrict__ q, const T* __restrict__ k,
+                                                   const T* __restrict__ v, const T* __restrict__ o,
+                                                   const T* __restrict__ dout, const float* __restrict__ lse,
+                                                   const float* __restrict__ off, T* __restrict__ dq,
+                                                   float* __restrict__ coef_a, float* __restrict__ coef_g,
+                                                   float* __restrict__ gpos, SGeom g) {
+  constexpr int G = D / EL;
+  // per wave: L values T_l = q . K[l] (then B_l), L values U_l = dO . V[l] (then A_l),
+  // K values scale * dS and K values alpha
+  extern __shared__ float box_lds[];
+  const int wq = threadIdx.x >> 6;
+  const long long wv = (long long)blockIdx.x * 4 + wq;
+  if (wv >= (long long)g.N * g.H) return;
+  const int n = (int)(wv / g.H), h = (int)(wv - (long long)n * g.H);
+  const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
+  const QPos qp = query_pos(g, off, n, h);
+  const BoxLat b = box_lattice(g, qp);
+  float* st = box_lds + (size_t)wq * 2 * (b.L + g.K);
+  float* su = st + b.L;
+  float* sg = su + b.L;
+  float* sa = sg + g.K;
+  const size_t row = ((size_t)n * g.H + h) * D + gl * EL;
+  float qf[EL], df[EL], x0[EL];
+  load8(q + row, qf);
+  load8(dout + row, df);
+  load8(o + row, x0);
+  const float delta = gsum<G>(dot8(df, x0));
+  const float sl2 = g.scale * LOG2E;
+  const float l2 = lse[(size_t)h * g.N + n] * LOG2E;
+  box_rows<4, T, D>(g, qp, b, k, h, grp, gl, [&](int l, const float* x, bool ok) {
+    const float t = gsum<G>(dot8(qf, x));
+    if (gl == 0) st[l] = ok ? t : 0.f;
+  });
+  box_rows<4, T, D>(g, qp, b, v, h, grp, gl, [&](int l, const float* x, bool ok) {
+    const float u = gsum<G>(dot8(df, x));
+    if (gl == 0) su[l] = ok ? u : 0.f;
+  });
+  wave_lds_sync();
+  // per sample: alpha, scale * dS, and the position gradient through the weights
+  float gp[3] = {0.f, 0.f, 0.f};
+  for (int j = lane; j < g.K; j += 64) {
+    const int lb = box_base(g, b, j);
+    float z = 0.f, da = 0.f, qk[3] = {0.f, 0.f, 0.f}, dv_[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float t = st[lb + b.coff[c]], u = su[lb + b.coff[c]];
+      z = fmaf(b.w[c], t, z);
+      da = fmaf(b.w[c], u, da);
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        qk[d] = fmaf(b.dw[c][d], t, qk[d]);
+        dv_[d] = fmaf(b.dw[c][d], u, dv_[d]);
+      }
+    }
+    const float alpha = exp2f(z * sl2 - l2);
+    const float gz = g.scale * alpha * (da - delta);
+    sg[j] = gz;
+    sa[j] = alpha;
+#pragma unroll
+    for (int d = 0; d < 3; ++d) gp[d] += gz * qk[d] + alpha * dv_[d];
+  }
+  wave_lds_sync();
+  // B_l, the lattice weights of K for dQ and of q for dK, and A_l, those of dO for dV
+  // (into st and su: every T_l and U_l has been read); the key side takes both
+  const size_t e0 = ((size_t)h * g.N + n) * b.L;
+  for (int l = lane; l < b.L; l += 64) {
+    const float bl = box_gather(g, b, b.w, sg, l), al = box_gather(g, b, b.w, sa, l);
+    st[l] = bl;
+    coef_a[e0 + l] = al;
+    coef_g[e0 + l] = bl;
+  }
+  wave_lds_sync();
+  float dqa[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) dqa[e] = 0.f;
+  box_rows<4, T, D>(g, qp, b, k, h, grp, gl, [&](int l, const float* x, bool ok) {
+    const float bl = ok ? st[l] : 0.f;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) dqa[e] = fmaf(bl, x[e], dqa[e]);
+  });
+#pragma unroll
+  for (int mask = G; mask < 64; mask <<= 1)
+#pragma unroll
+    for (int e = 0; e < EL; ++e) dqa[e] += __shfl_xor(dqa[e], mask, 64);
+#pragma unroll
+  for (int d = 0; d < 3; ++d) gp[d] = wsum(gp[d]);
+  if (grp == 0) {
+    store8(dq + row, dqa);
+    if (gl == 0) {
+      float* gq = gpos + ((size_t)h * g.N + n) * 3;
+#pragma unroll
+      for (int d = 0; d < 3; ++d) gq[d] = qp.act[d] ? gp[d] : 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // backward, key side
 // ---------------------------------------------------------------------------
 // Sort key of sample e = (h * N + n) * K + j: (head, base cell floor(P) + 1), base cells
@@ -531,6 +804,99 @@ __global__ __launch_bounds__(256) void k_sampled_dkdv(const T* __restrict__ q, c
   }
 }
 
+// Box windows on the lattice: entry e = (h * N + n) * L + l is lattice point l of
+// (query n, head h), keyed by its grid token inside head h's segment; points outside the
+// grid, and those of zero weight (the far slice of an axis whose fraction is 0), get the
+// sentinel N and are never visited.
+__global__ __launch_bounds__(256) void k_box_keys(const float* __restrict__ off, SGeom g,
+                                                  uint32_t* __restrict__ keys) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int L = (g.kt + 1) * (g.ky + 1) * (g.kx + 1);
+  if (e >= (long long)g.N * g.H * L) return;
+  const int l = (int)(e % L);
+  const long long hn = e / L;
+  const int n = (int)(hn % g.N), h = (int)(hn / g.N);
+  const QPos qp = query_pos(g, off, n, h);
+  const int e1 = g.ky + 1, e2 = g.kx + 1;
+  const int lt = l / (e1 * e2), r = l - lt * e1 * e2, ly = r / e2, lx = r - ly * e2;
+  const bool dead = (lt == g.kt && qp.sf[0] == 0.f) || (ly == g.ky && qp.sf[1] == 0.f) || (lx == g.kx && qp.sf[2] == 0.f);
+  const int t = qp.si[0] + lt, y = qp.si[1] + ly, x = qp.si[2] + lx;
+  const bool in = (unsigned)t < (unsigned)g.F && (unsigned)y < (unsigned)g.Hp && (unsigned)x < (unsigned)g.Wp;
+  keys[e] = (in && !dead) ? (uint32_t)((t * g.Hp + y) * g.Wp + x) : (uint32_t)g.N;
+}
+
+// sorted lattice entries as records (query token, A_l, B_l)
+__global__ __launch_bounds__(256) void k_box_pack(const int* __restrict__ ids, const float* __restrict__ coef_a,
+                                                  const float* __restrict__ coef_g, int n_sorted,
+                                                  int4* __restrict__ rec, SGeom g) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_sorted) return;
+  const int e = ids[i];
+  const int L = (g.kt + 1) * (g.ky + 1) * (g.kx + 1);
+  const int n = (e / L) % g.N;
+  rec[i] = make_int4(n, __float_as_int(coef_a[e]), __float_as_int(coef_g[e]), 0);
+}
+
+// dK[m] = sum B_l q_n, dV[m] = sum A_l dO_n over the lattice entries on key m, in sorted
+// (query, lattice point) order; a wave per (key, head)
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_box_dkdv(const T* __restrict__ q, const T* __restrict__ dout,
+                                                  const int4* __restrict__ rec, const int* __restrict__ cell_ptr,
+                                                  T* __restrict__ dk, T* __restrict__ dv, SGeom g) {
+  constexpr int G = D / EL, NG = 64 / G;
+  const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wv >= (long long)g.N * g.H) return;
+  const int m = (int)(wv / g.H), h = (int)(wv - (long long)m * g.H);
+  const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
+  const int cell = h * (g.N + 1) + m;
+  const int beg = cell_ptr[cell], end = cell_ptr[cell + 1];
+  float dka[EL], dva[EL], x[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) dka[e] = dva[e] = 0.f;
+  for (int base = beg; base < end; base += NG * DK_B) {
+    int nn[DK_B];
+    float a[DK_B], bq[DK_B];
+#pragma unroll
+    for (int u = 0; u < DK_B; ++u) {
+      const int it = base + grp + u * NG;
+      const bool ok = it < end;
+      const int4 r = rec[ok ? it : beg];
+      nn[u] = r.x;
+      a[u] = ok ? __int_as_float(r.y) : 0.f;
+      bq[u] = ok ? __int_as_float(r.z) : 0.f;
+    }
+    Raw8<T> dr[DK_B], qr[DK_B];
+#pragma unroll
+    for (int u = 0; u < DK_B; ++u) {
+      const size_t r = ((size_t)nn[u] * g.H + h) * D + gl * EL;
+      dr[u] = ldraw(dout + r);
+      qr[u] = ldraw(q + r);
+    }
+#pragma unroll
+    for (int u = 0; u < DK_B; ++u) {
+      unraw(dr[u], x);
+#pragma unroll
+      for (int t = 0; t < EL; ++t) dva[t] = fmaf(a[u], x[t], dva[t]);
+      unraw(qr[u], x);
+#pragma unroll
+      for (int t = 0; t < EL; ++t) dka[t] = fmaf(bq[u], x[t], dka[t]);
+    }
+  }
+#pragma unroll
+  for (int mask = G; mask < 64; mask <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      dka[e] += __shfl_xor(dka[e], mask, 64);
+      dva[e] += __shfl_xor(dva[e], mask, 64);
+    }
+  }
+  if (grp == 0) {
+    const size_t r = ((size_t)m * g.H + h) * D + gl * EL;
+    store8(dk + r, dka);
+    store8(dv + r, dva);
+  }
+}
+
 // Offset gradients in the caller's layout: entry (n, ho, jo) sums the per-sample (free)
 // or per-(query, head) (box) gradients over the heads (sh == 0) and samples (ss == 0)
 // that share it, heads then samples in ascending order.
@@ -562,28 +928,50 @@ __global__ __launch_bounds__(256) void k_sampled_doff(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Box windows whose lattice arrays fit a block's LDS run on the lattice kernels: a block
+// of 4 waves holds nl lattice arrays and ns sample arrays per wave (the backward 2 and 2).
+static long long box_lattice_points(const SGeom& g) { return (long long)(g.kt + 1) * (g.ky + 1) * (g.kx + 1); }
+static size_t box_lds_bytes(const SGeom& g, int nl, int ns) {
+  return (size_t)4 * (nl * box_lattice_points(g) + ns * g.K) * sizeof(float);
+}
+static bool box_on_lattice(const SGeom& g) {
+  return g.mode == DSA3D_SAMPLE_BOX && box_lds_bytes(g, 2, 2) <= (size_t)BOX_LDS_BYTES;
+}
+// ... and their backward on the lattice when the N H L lattice entries fit 32-bit indices
+static bool box_lattice_bwd(const SGeom& g) {
+  return box_on_lattice(g) && (long long)g.N * g.H * box_lattice_points(g) < (1LL << 31);
+}
+
 struct SampledWs {
   uint32_t* keys[2];
   int* vals[2];
   uint32_t* ghist;
+  uint32_t* scan_part;  // chunk totals of the histogram scans
   int* cell_ptr;
-  float* coef_a;
-  float* coef_g;
+  float* coef_a;  // per sample alpha, or per lattice point A_l (box windows on the lattice)
+  float* coef_g;  // per sample scale * dz, or per lattice point B_l
   float* gpos;
-  int4* rec;      // sorted samples: (token, fractions)
-  float2* rcoef;  //                 (alpha, scale * dz)
+  int4* rec;      // sorted samples: (token, fractions), or lattice points: (token, A_l, B_l)
+  float2* rcoef;  // sorted samples: (alpha, scale * dz)
   int passes;
+  int nseg;       // sort segments: 1, or one per head (lattice points)
+  int keyspace;   // keys per segment, the sentinel included
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t sampled_layout(const SGeom& g, char* base, SampledWs* w) {
-  const size_t E = (size_t)g.N * g.H * g.K;
-  const size_t nb = (E + RADIX_TILE - 1) / RADIX_TILE;
+  // sorted entries: samples keyed by (head, base cell) in one segment with the sentinel
+  // H * ncell, or lattice points keyed by token in one segment per head, sentinel N
+  const bool lat = box_lattice_bwd(g);
+  const size_t E = (size_t)g.N * g.H * (lat ? box_lattice_points(g) : g.K);
+  const int nseg = lat ? g.H : 1;
+  const size_t seglen = E / nseg;
+  const size_t nb = (seglen + RADIX_TILE - 1) / RADIX_TILE * nseg;
   const size_t ncell = (size_t)(g.F + 1) * (g.Hp + 1) * (g.Wp + 1);
-  const size_t keyspace = ncell * g.H;
+  const size_t sentinel = lat ? (size_t)g.N : ncell * g.H;
   int bits = 1;
-  while (((size_t)1 << bits) <= keyspace) ++bits;  // the sentinel H * ncell sorts last
+  while (((size_t)1 << bits) <= sentinel) ++bits;  // the sentinel sorts last
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;
@@ -596,24 +984,32 @@ size_t sampled_layout(const SGeom& g, char* base, SampledWs* w) {
   s.vals[0] = (int*)take(E * 4);
   s.vals[1] = (int*)take(E * 4);
   s.ghist = (uint32_t*)take(256 * nb * 4);
-  s.cell_ptr = (int*)take((keyspace + 1) * 4);
+  s.scan_part = (uint32_t*)take(scan_part_words(256 * nb) * 4);
+  s.cell_ptr = (int*)take(((sentinel + 1) * nseg + 1) * 4);
   s.coef_a = (float*)take(E * 4);
   s.coef_g = (float*)take(E * 4);
-  s.gpos = (float*)take((g.mode == DSA3D_SAMPLE_BOX ? (size_t)g.N * g.H : E) * 3 * 4);
+  s.gpos = (float*)take((g.mode == DSA3D_SAMPLE_BOX ? (size_t)g.N * g.H : (size_t)g.N * g.H * g.K) * 3 * 4);
   s.rec = (int4*)take(E * sizeof(int4));
-  s.rcoef = (float2*)take(E * sizeof(float2));
+  s.rcoef = lat ? nullptr : (float2*)take(E * sizeof(float2));
   s.passes = (bits + 7) / 8;
+  s.nseg = nseg;
+  s.keyspace = lat ? (int)sentinel + 1 : (int)sentinel;
   if (w) *w = s;
   return off;
 }
 
 static unsigned nblocks(long long n, int per) { return (unsigned)((n + per - 1) / per); }
 
+
 template <typename T, int D>
 static hipError_t sampled_fwd_impl(const void* q, const void* k, const void* v, const float* off, void* out,
                                    float* lse, const SGeom& g, hipStream_t s) {
-  k_sampled_fwd<T, D><<<nblocks((long long)g.N * g.H, 4), 256, 0, s>>>(
-      (const T*)q, (const T*)k, (const T*)v, off, (T*)out, lse, g);
+  if (box_on_lattice(g))
+    k_box_fwd<T, D><<<nblocks((long long)g.N * g.H, 4), 256, box_lds_bytes(g, 1, 1), s>>>(
+        (const T*)q, (const T*)k, (const T*)v, off, (T*)out, lse, g);
+  else
+    k_sampled_fwd<T, D><<<nblocks((long long)g.N * g.H, 4), 256, 0, s>>>(
+        (const T*)q, (const T*)k, (const T*)v, off, (T*)out, lse, g);
   return hipGetLastError();
 }
 
@@ -630,26 +1026,39 @@ template <typename T, int D>
 static hipError_t sampled_bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                    const float* lse, const float* off, void* dq, void* dk, void* dv, float* doff,
                                    const SGeom& g, const SampledWs& w, hipStream_t s) {
-  const long long E = (long long)g.N * g.H * g.K;
   const long long waves = (long long)g.N * g.H;
-  k_sampled_keys<<<nblocks(E, 256), 256, 0, s>>>(off, g, w.keys[0]);
+  const bool lat = box_lattice_bwd(g);
+  const long long E = waves * (lat ? box_lattice_points(g) : g.K);
+  if (lat)
+    k_box_keys<<<nblocks(E, 256), 256, 0, s>>>(off, g, w.keys[0]);
+  else
+    k_sampled_keys<<<nblocks(E, 256), 256, 0, s>>>(off, g, w.keys[0]);
   uint32_t* keys[2] = {w.keys[0], w.keys[1]};
   int* vals[2] = {w.vals[0], w.vals[1]};
-  const int cur = radix_sort(keys, vals, w.ghist, (int)E, 1, w.passes, s);
+  const int seglen = (int)(E / w.nseg);
+  const int cur = radix_sort(keys, vals, w.ghist, seglen, w.nseg, w.passes, s, w.scan_part);
   if (cur < 0) return hipErrorLaunchFailure;
-  const int ncell = (g.F + 1) * (g.Hp + 1) * (g.Wp + 1);
-  hipError_t e = launch_cell_ptr(keys[cur], (int)E, 1, g.H * ncell, w.cell_ptr, s);
+  hipError_t e = launch_cell_ptr(keys[cur], seglen, w.nseg, w.keyspace, w.cell_ptr, s);
   if (e != hipSuccess) return e;
-  k_sampled_bwd_q<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)k, (const T*)v, (const T*)o,
-                                                          (const T*)dout, lse, off, (T*)dq, w.coef_a, w.coef_g,
-                                                          w.gpos, g);
-  // every sample is packed; those with all corners outside the grid sort after every
-  // cell and are never visited
+  // every entry is packed; those keyed by the sentinel sort after every key (of their
+  // segment) and are never visited
   const int n_sorted = (int)E;
-  k_sampled_pack<<<nblocks(n_sorted, 256), 256, 0, s>>>(off, vals[cur], w.coef_a, w.coef_g, n_sorted, w.rec,
-                                                        w.rcoef, g);
-  k_sampled_dkdv<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)dout, w.rec, w.rcoef, w.cell_ptr,
-                                                         (T*)dk, (T*)dv, g);
+  if (lat) {
+    k_box_bwd_q<T, D><<<nblocks(waves, 4), 256, box_lds_bytes(g, 2, 2), s>>>(
+        (const T*)q, (const T*)k, (const T*)v, (const T*)o, (const T*)dout, lse, off, (T*)dq, w.coef_a, w.coef_g,
+        w.gpos, g);
+    k_box_pack<<<nblocks(n_sorted, 256), 256, 0, s>>>(vals[cur], w.coef_a, w.coef_g, n_sorted, w.rec, g);
+    k_box_dkdv<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)dout, w.rec, w.cell_ptr, (T*)dk,
+                                                       (T*)dv, g);
+  } else {
+    k_sampled_bwd_q<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)k, (const T*)v, (const T*)o,
+                                                            (const T*)dout, lse, off, (T*)dq, w.coef_a, w.coef_g,
+                                                            w.gpos, g);
+    k_sampled_pack<<<nblocks(n_sorted, 256), 256, 0, s>>>(off, vals[cur], w.coef_a, w.coef_g, n_sorted, w.rec,
+                                                          w.rcoef, g);
+    k_sampled_dkdv<T, D><<<nblocks(waves, 4), 256, 0, s>>>((const T*)q, (const T*)dout, w.rec, w.rcoef,
+                                                           w.cell_ptr, (T*)dk, (T*)dv, g);
+  }
   const long long nout = (long long)g.N * (g.sh == 0 ? 1 : g.H) *
                          ((g.mode == DSA3D_SAMPLE_BOX || g.ss == 0) ? 1 : g.K);
   k_sampled_doff<<<nblocks(nout, 256), 256, 0, s>>>(w.gpos, doff, g);
@@ -737,8 +1146,10 @@ int check_sampled(const void* q, const void* k, const void* v, const float* off,
   return DSA3D_OK;
 }
 
-// the backward sorts N * H * K samples with 32-bit indices and (H * cells) 32-bit keys
+// the backward sorts N * H * L lattice points (box windows on the lattice) or N * H * K
+// samples with 32-bit indices and (H * cells) 32-bit keys
 bool backward_fits(const SGeom& g) {
+  if (box_lattice_bwd(g)) return true;
   const long long E = (long long)g.N * g.H * g.K;
   const long long cells = (long long)(g.F + 1) * (g.Hp + 1) * (g.Wp + 1) * g.H;
   return E < (1LL << 31) && cells < (1LL << 31) - 1;

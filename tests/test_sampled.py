@@ -3,7 +3,8 @@ through the C ABI against the oracle's sampled form, element by element.
 
 Box windows with one real offset per query (shared by heads) or per (query, head), and
 free per-sample offsets, some of them leaving the grid (zero padding), for fp32 and bf16,
-head_dim 64 and 128.  Also: box windows with integer-valued offsets equal the integer
+head_dim 64 and 128; box windows up to and past the largest lattice of corner rows that the
+box kernels hold per wave.  Also: box windows with integer-valued offsets equal the integer
 path, and the backward is bitwise reproducible.
 
 Tolerances: O, LSE, dQ, dK, dV as everywhere (fp32 1e-5 absolute; bf16 2e-2 + 1e-2|ref|;
@@ -41,6 +42,11 @@ CASES = [
     (W("box-query-bf16", 6, 12, 14, 3, 128, 3, 7, 7, "bf16"), "box", "query", 2.5),
     (W("box-head-bf16", 5, 10, 12, 4, 64, 3, 5, 5, "bf16"), "box", "head", 3.0),
     (W("box-head-major-f32", 4, 8, 9, 3, 128, 3, 3, 3, "f32"), "box", "head-major", 1.5),
+    (W("box-one-frame-f32", 5, 9, 11, 2, 64, 1, 3, 5, "f32"), "box", "query", 2.0),
+    # the largest lattice the box kernels take ((kt+1)(ky+1)(kx+1) = 1024), and one past it,
+    # which runs the per-sample corner kernels
+    (W("box-lattice-1024-bf16", 5, 16, 17, 1, 64, 3, 15, 15, "bf16"), "box", "head", 3.0),
+    (W("box-lattice-1536-bf16", 6, 16, 17, 1, 64, 5, 15, 15, "bf16"), "box", "query", 3.0),
     (W("free-sample-f32", 4, 7, 8, 2, 64, 3, 3, 3, "f32"), "free", "sample", 1.5),
     (W("free-sample-bf16", 5, 10, 12, 3, 128, 3, 5, 5, "bf16"), "free", "sample", 1.2),
     (W("free-query-bf16-64", 4, 9, 11, 2, 64, 3, 3, 5, "bf16"), "free", "query", 2.0),
