@@ -475,32 +475,52 @@ __device__ __forceinline__ TubeBlock tube_block(const CGeom& g, int fchunk) {
   return b;
 }
 
-// This thread's chunks of the slice of frame f (zeros outside the grid).
+// A thread's share of a block's frame slices: U::LOADS chunks at offsets within a frame
+// that are fixed per block.  Every load is issued (chunks outside the grid read the
+// tensor's first chunk) and every chunk written to LDS (those past the slice to a dummy
+// chunk), the ones outside the grid zeroed by a mask on the way: no branch around a load
+// or its use, so the compiler's wait for a slice's loads sits at one unconditional place
+// rather than being repeated, conservatively, at the top of the next frame.
+__device__ __forceinline__ Chunk8<u16> mask_chunk(const Chunk8<u16>& c, uint32_t m) {
+  return {make_uint4(c.a.x & m, c.a.y & m, c.a.z & m, c.a.w & m)};
+}
+__device__ __forceinline__ Chunk8<float> mask_chunk(const Chunk8<float>& c, uint32_t m) {
+  return {make_uint4(c.a.x & m, c.a.y & m, c.a.z & m, c.a.w & m), make_uint4(c.b.x & m, c.b.y & m, c.b.z & m, c.b.w & m)};
+}
 template <typename T, int CY, int CX>
-__device__ __forceinline__ void tube_load(const T* __restrict__ x, const CGeom& g, const TubeBlock& b, int f,
-                                          Chunk8<T>* buf) {
+struct TubeSlices {
   using U = Tube<T, CY, CX>;
-  constexpr int ry = (CY - 1) / 2, rx = (CX - 1) / 2;
+  long long off[U::LOADS];  // element offset within a frame, -1 outside the grid or past the slice
+  long long fstride;
+  int F;
+  __device__ __forceinline__ TubeSlices(const CGeom& g, const TubeBlock& b) {
+    constexpr int ry = (CY - 1) / 2, rx = (CX - 1) / 2;
+    fstride = (long long)g.Hp * g.Wp * g.C;
+    F = g.F;
 #pragma unroll
-  for (int k = 0; k < U::LOADS; ++k) {
-    const int j = threadIdx.x + 256 * k;
-    if (j < U::CH) {
+    for (int k = 0; k < U::LOADS; ++k) {
+      const int j = threadIdx.x + 256 * k;
       const int tok = j >> 3, sy = tok / U::SX, sx = tok - sy * U::SX;
       const int gy = b.y0 - ry + sy, gx = b.x0 - rx + sx;
-      const bool ok = (unsigned)f < (unsigned)g.F && (unsigned)gy < (unsigned)g.Hp && (unsigned)gx < (unsigned)g.Wp;
-      buf[k] = ok ? ld_chunk(x + ((size_t)(f * g.Hp + gy) * g.Wp + gx) * g.C + b.c0 + (j & 7) * 8) : zero_chunk<T>();
+      const bool ok = j < U::CH && (unsigned)gy < (unsigned)g.Hp && (unsigned)gx < (unsigned)g.Wp;
+      off[k] = ok ? ((long long)gy * g.Wp + gx) * g.C + b.c0 + (j & 7) * 8 : -1;
     }
   }
-}
-template <typename T, int CY, int CX>
-__device__ __forceinline__ void tube_store(T* slot, const Chunk8<T>* buf) {
-  using U = Tube<T, CY, CX>;
+  __device__ __forceinline__ void load(const T* __restrict__ x, int f, Chunk8<T>* buf) const {
+    const bool fin = (unsigned)f < (unsigned)F;
 #pragma unroll
-  for (int k = 0; k < U::LOADS; ++k) {
-    const int j = threadIdx.x + 256 * k;
-    if (j < U::CH) st_chunk(slot + (size_t)j * 8, buf[k]);
+    for (int k = 0; k < U::LOADS; ++k)
+      buf[k] = ld_chunk(x + ((fin && off[k] >= 0) ? (size_t)f * fstride + off[k] : (size_t)0));
   }
-}
+  __device__ __forceinline__ void store(T* slot, T* dummy, int f, const Chunk8<T>* buf) const {
+    const bool fin = (unsigned)f < (unsigned)F;
+#pragma unroll
+    for (int k = 0; k < U::LOADS; ++k) {
+      const int j = threadIdx.x + 256 * k;
+      st_chunk(j < U::CH ? slot + (size_t)j * 8 : dummy, mask_chunk(buf[k], (fin && off[k] >= 0) ? ~0u : 0u));
+    }
+  }
+};
 __device__ __forceinline__ int ring_slot(int f) { return ((f % TB_RING) + TB_RING) % TB_RING; }
 
 // 4 consecutive elements (a thread's channels of one token), raw
@@ -518,42 +538,62 @@ __device__ __forceinline__ void dy4_unpack(const Dy4<float>& d, float* x) {
 }
 
 // Forward (or, with the filters mirrored, the input gradient): thread (cg4, column)
-// computes the tile's TB_Y rows of its column for 4 channels, with those channels'
-// filters in registers for the whole sweep; per frame offset and filter column it reads
-// one window of TB_Y + cy - 1 rows from the slice (a wave: four neighbouring tokens'
-// 128 bytes at a time).  With accumulate, the output's old values are added as the
-// results are written.
-template <typename T, int CY, int CX>
+// computes the tile's TB_Y rows of its column for 4 channels; the block's filters sit in
+// LDS as [tap][channel] fp32; per frame offset and filter column a thread reads one
+// window of TB_Y + cy - 1 rows from the slice (a wave: four neighbouring tokens' 128
+// bytes at a time) and each tap's 4 weights.  Every global load of a frame -- the next
+// slice and, with accumulate, the output's old values -- is issued at the frame's start
+// and its data used only after the products (the slice's out-of-grid chunks are zeroed
+// as they are written to LDS), so the loads are in flight while the frame is computed.
+// The last frame of a run loads (in bounds) and writes to its free ring slot a slice that
+// is never read, so that no load or LDS write sits behind a branch.
+template <typename T, int CY, int CX, bool ACC>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_tube(
     const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ b, T* __restrict__ y, CGeom g,
-    int fchunk, int accumulate, int flip) {
+    int fchunk, int flip) {
   using U = Tube<T, CY, CX>;
   constexpr int NT = 3 * CY * CX;  // tap slots (ct <= 3)
   __shared__ __attribute__((aligned(16))) T ring[TB_RING][U::SLICE * TB_C];
+  __shared__ __attribute__((aligned(16))) float wl[NT + 1][TB_C];  // taps, then the bias
+  __shared__ __attribute__((aligned(16))) T dummy[8];
   const int tid = threadIdx.x;
   const TubeBlock bk = tube_block(g, fchunk);
   const int rt = (g.ct - 1) / 2;
   const int cg4 = tid & 15, col = tid >> 4;
   const int c = bk.c0 + cg4 * 4, gx = bk.x0 + col;
-  float wr[NT][4];
-  static_for<0, NT>([&](auto TC) {
-    constexpr int tap = decltype(TC)::value;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      wr[tap][e] = tap < g.taps ? w[(size_t)(c + e) * g.taps + (flip ? g.taps - 1 - tap : tap)] : 0.f;
-  });
-  float bias[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) bias[e] = (b && !flip) ? b[c + e] : 0.f;
+  // filters (the tap index runs fastest in global memory; mirrored for the input
+  // gradient) and bias, through LDS so that no global load of the prologue is pending
+  // when the frame loop starts
+  for (int i = tid; i < TB_C * g.taps; i += 256) {
+    const int ch = i / g.taps, tap = i - ch * g.taps;
+    wl[flip ? g.taps - 1 - tap : tap][ch] = w[(size_t)bk.c0 * g.taps + i];
+  }
+  for (int i = g.taps * TB_C + tid; i < NT * TB_C; i += 256) wl[i / TB_C][i % TB_C] = 0.f;
+  if (tid < TB_C) wl[NT][tid] = (b && !flip) ? b[bk.c0 + tid] : 0.f;
+  const TubeSlices<T, CY, CX> sl_io(g, bk);
+  const long long fstride = sl_io.fstride;
+  auto load_slice = [&](int f, Chunk8<T>* buf) { sl_io.load(x, f, buf); };
+  auto store_slice = [&](int f, const Chunk8<T>* buf) { sl_io.store(ring[ring_slot(f)], dummy, f, buf); };
   Chunk8<T> pre[U::LOADS];
   for (int f = bk.t0 - rt; f <= bk.t0 + rt; ++f) {
-    tube_load<T, CY, CX>(x, g, bk, f, pre);
-    tube_store<T, CY, CX>(ring[ring_slot(f)], pre);
+    load_slice(f, pre);
+    store_slice(f, pre);
   }
   __syncthreads();
+  const size_t ybase = ((size_t)bk.y0 * g.Wp + gx) * g.C + c;  // row 0 of this thread's column, frame 0
+  const bool colin = gx < g.Wp;
+  const float4 bv = *reinterpret_cast<const float4*>(&wl[NT][cg4 * 4]);
+  const float bias[4] = {bv.x, bv.y, bv.z, bv.w};
   for (int t = bk.t0; t < bk.t1; ++t) {
-    const bool more = t + 1 < bk.t1;
-    if (more) tube_load<T, CY, CX>(x, g, bk, t + 1 + rt, pre);
+    load_slice(t + 1 + rt, pre);
+    Dy4<T> old[TB_Y];
+    if constexpr (ACC) {
+#pragma unroll
+      for (int i = 0; i < TB_Y; ++i) {
+        const bool in = colin && bk.y0 + i < g.Hp;
+        old[i] = *reinterpret_cast<const Dy4<T>*>(y + (in ? (size_t)t * fstride + ybase + (size_t)i * g.Wp * g.C : c));
+      }
+    }
     float acc[TB_Y][4];
 #pragma unroll
     for (int i = 0; i < TB_Y; ++i)
@@ -571,28 +611,34 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_tube(
 #pragma unroll
         for (int e2 = 0; e2 < CY; ++e2) {
           const int tap = (a * CY + e2) * CX + f;
+          const float4 wv = *reinterpret_cast<const float4*>(&wl[tap][cg4 * 4]);
+          const float wt[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
           for (int i = 0; i < TB_Y; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wr[tap][e], v[i + e2][e], acc[i][e]);
+            for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wt[e], v[i + e2][e], acc[i][e]);
         }
+      }
+    }
+    __syncthreads();  // every read of the leaving frame's slice is done
+    // the next slice into LDS before the output stores, so that waiting for its loads
+    // never means waiting for stores
+    store_slice(t + 1 + rt, pre);
+    if constexpr (ACC) {
+#pragma unroll
+      for (int i = 0; i < TB_Y; ++i) {
+        float o[4];
+        dy4_unpack(old[i], o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] += o[e];
       }
     }
 #pragma unroll
     for (int i = 0; i < TB_Y; ++i) {
-      const int gy = bk.y0 + i;
-      if (gy < g.Hp && gx < g.Wp) {
-        if (accumulate) {
-          float o[4];
-          dy4_unpack(*reinterpret_cast<const Dy4<T>*>(y + ((size_t)(t * g.Hp + gy) * g.Wp + gx) * g.C + c), o);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][e] += o[e];
-        }
-        store4(y + ((size_t)(t * g.Hp + gy) * g.Wp + gx) * g.C + c, acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+      if (colin && bk.y0 + i < g.Hp) {
+        store4(y + (size_t)t * fstride + ybase + (size_t)i * g.Wp * g.C, acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
       }
     }
-    __syncthreads();  // every read of the leaving frame's slice is done
-    if (more) tube_store<T, CY, CX>(ring[ring_slot(t + 1 + rt)], pre);
     __syncthreads();
   }
 }
@@ -624,41 +670,50 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_dw_tube(
   using U = Tube<T, CY, CX>;
   constexpr int NT = 3 * CY * CX;  // tap slots (ct <= 3)
   __shared__ __attribute__((aligned(16))) T ring[TB_RING][U::SLICE * TB_C];
+  __shared__ __attribute__((aligned(16))) T dummy[8];
   const int tid = threadIdx.x;
   const TubeBlock bk = tube_block(g, fchunk);
   const int rt = (g.ct - 1) / 2;
   const int cg2 = tid & 31, cp = tid >> 5;
   const int c = bk.c0 + cg2 * 2;
-  // this thread's dy values of frame f: columns cp, cp + 8, rows 0 .. TB_Y - 1 (zeros outside)
+  const TubeSlices<T, CY, CX> sl_io(g, bk);
+  // this thread's dy values of frame f: columns cp, cp + 8, rows 0 .. TB_Y - 1, loaded
+  // unconditionally (from the tensor's start outside the grid) and zeroed by dmask on use
+  uint32_t dmask = 0;  // bit h * TB_Y + i: the row is inside the grid
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < TB_Y; ++i)
+      if (bk.y0 + i < g.Hp && bk.x0 + cp + 8 * h < g.Wp) dmask |= 1u << (h * TB_Y + i);
   auto dy_fetch = [&](int f, Dy2<T>* buf) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < TB_Y; ++i) {
-        const int gy = bk.y0 + i, gx = bk.x0 + cp + 8 * h;
-        if (gy < g.Hp && gx < g.Wp)
-          buf[h * TB_Y + i] = *reinterpret_cast<const Dy2<T>*>(dy + ((size_t)(f * g.Hp + gy) * g.Wp + gx) * g.C + c);
-        else
-          __builtin_memset(&buf[h * TB_Y + i], 0, sizeof(Dy2<T>));
+        const bool in = ((dmask >> (h * TB_Y + i)) & 1u) && f < g.F;
+        const size_t o = ((size_t)(f * g.Hp + bk.y0 + i) * g.Wp + bk.x0 + cp + 8 * h) * g.C + c;
+        buf[h * TB_Y + i] = *reinterpret_cast<const Dy2<T>*>(dy + (in ? o : (size_t)0));
       }
   };
   Chunk8<T> pre[U::LOADS];
   Dy2<T> dcur[2 * TB_Y], dnext[2 * TB_Y];
   for (int f = bk.t0 - rt; f <= bk.t0 + rt; ++f) {
-    tube_load<T, CY, CX>(x, g, bk, f, pre);
-    tube_store<T, CY, CX>(ring[ring_slot(f)], pre);
+    sl_io.load(x, f, pre);
+    sl_io.store(ring[ring_slot(f)], dummy, f, pre);
   }
   dy_fetch(bk.t0, dcur);
+  // the first frame's dy arrives before the frame loop, as every later frame's does (its
+  // copy into dcur waits for it), so the loop's products need no wait for the loads in flight
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   float acc[NT + 1][2];  // taps, then the bias
 #pragma unroll
   for (int i = 0; i <= NT; ++i) acc[i][0] = acc[i][1] = 0.f;
+  // as in the forward, the last frame of the run loads and stores a slice (and loads dy
+  // rows) that are never used, so that no load, LDS write or copy sits behind a branch
   for (int t = bk.t0; t < bk.t1; ++t) {
-    const bool more = t + 1 < bk.t1;
-    if (more) {
-      tube_load<T, CY, CX>(x, g, bk, t + 1 + rt, pre);
-      dy_fetch(t + 1, dnext);
-    }
+    sl_io.load(x, t + 1 + rt, pre);
+    dy_fetch(t + 1, dnext);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int col = cp + 8 * h;
@@ -668,6 +723,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_dw_tube(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           dy2_unpack(dcur[h * TB_Y + 4 * rq + i], d[i]);
+          if (!((dmask >> (h * TB_Y + 4 * rq + i)) & 1u)) d[i][0] = d[i][1] = 0.f;
           acc[NT][0] += d[i][0];
           acc[NT][1] += d[i][1];
         }
@@ -694,11 +750,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_dw_tube(
       }
     }
     __syncthreads();
-    if (more) {
-      tube_store<T, CY, CX>(ring[ring_slot(t + 1 + rt)], pre);
+    sl_io.store(ring[ring_slot(t + 1 + rt)], dummy, t + 1 + rt, pre);
 #pragma unroll
-      for (int i = 0; i < 2 * TB_Y; ++i) dcur[i] = dnext[i];
-    }
+    for (int i = 0; i < 2 * TB_Y; ++i) dcur[i] = dnext[i];
     __syncthreads();
   }
   // column pairs 0 .. 7: add pair cp + h into pair cp for h = 4, 2, 1, through LDS
@@ -740,14 +794,28 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_dw_tube(
 static bool tube_ok(const CGeom& g) {
   return g.C % TB_C == 0 && g.ct <= 3 && (g.cy == 1 || g.cy == 3) && (g.cx == 1 || g.cx == 3);
 }
-// Frames per block: the whole run unless that leaves fewer than 1024 blocks (4 per CU),
-// then shorter runs of at least 4 frames.
+// Frames per block: the run length, among the clip split into 1 .. 64 runs, whose blocks
+// fill the chip's block slots (256 CUs x 2 resident blocks) in whole rounds best, weighed
+// against the ct - 1 extra frames each run loads (a last, partly filled round of blocks
+// leaves CUs idle).  A function of the geometry only: the filter gradient's workspace is
+// sized with it.
 static int tube_fchunk(const CGeom& g) {
+  constexpr long long SLOTS = 512;
   const long long tiles =
       (long long)(g.C / TB_C) * ((g.Hp + TB_Y - 1) / TB_Y) * ((g.Wp + TB_X - 1) / TB_X);
-  const long long nfc = std::min<long long>(g.F, std::max<long long>(1, (1024 + tiles - 1) / tiles));
-  const int fchunk = (int)((g.F + nfc - 1) / nfc);
-  return std::max(fchunk, std::min(4, g.F));
+  int best = g.F;
+  double best_eff = -1.0;
+  for (int nfc = 1; nfc <= std::min(g.F, 64); ++nfc) {
+    const int fchunk = (g.F + nfc - 1) / nfc;
+    const long long blocks = tiles * ((g.F + fchunk - 1) / fchunk);
+    const long long rounds = (blocks + SLOTS - 1) / SLOTS;
+    const double eff = (double)blocks / (double)(rounds * SLOTS) * fchunk / (double)(fchunk + g.ct - 1);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = fchunk;
+    }
+  }
+  return best;
 }
 static long long tube_parts(const CGeom& g) {  // filter-gradient parts per channel
   const int fchunk = tube_fchunk(g);
@@ -758,7 +826,10 @@ static unsigned tube_blocks(const CGeom& g) { return (unsigned)(tube_parts(g) * 
 template <typename T, int CY, int CX>
 static hipError_t tube_conv(const void* x, const float* w, const float* b, void* y, const CGeom& g, int acc,
                             int flip, hipStream_t s) {
-  k_dwconv_tube<T, CY, CX><<<tube_blocks(g), 256, 0, s>>>((const T*)x, w, b, (T*)y, g, tube_fchunk(g), acc, flip);
+  if (acc)
+    k_dwconv_tube<T, CY, CX, true><<<tube_blocks(g), 256, 0, s>>>((const T*)x, w, b, (T*)y, g, tube_fchunk(g), flip);
+  else
+    k_dwconv_tube<T, CY, CX, false><<<tube_blocks(g), 256, 0, s>>>((const T*)x, w, b, (T*)y, g, tube_fchunk(g), flip);
   return hipGetLastError();
 }
 template <typename T, int CY, int CX>
