@@ -234,10 +234,11 @@ def measure_peaks(lib, hip, stream_ptr):
 def sampled_flops(wl, fwd=True, bwd=True):
     """Algorithmic fp32 VALU flops of sampled windows per launch: per (query, head, sample)
     the forward blends 8 corner rows of K and of V (2 x 16D) and takes q . K~ and
-    alpha V~ (2 x 2D) = 36D; the backward recomputes K~, V~ and their dots (36D), takes
-    dQ += scale dz K~ (2D), the 8 corner dots q . k_c and dO . v_c of the position
-    gradient (32D) and scatters w alpha dO and w scale dz q to the 8 corners (32D) = 102D."""
-    per = (36 if fwd else 0) + (102 if bwd else 0)
+    alpha V~ (2 x 2D) = 36D; the backward takes the 8 corner dots q . k_c and dO . v_c
+    (32D: every quantity of the sample, the position gradient included, is a weighted sum
+    of them), dQ += scale dz w_c k_c over the corners (16D), and scatters w alpha dO and
+    w scale dz q to the 8 corners (32D) = 80D."""
+    per = (36 if fwd else 0) + (80 if bwd else 0)
     return float(per) * wl.head_dim * wl.K * wl.N * wl.heads
 
 
@@ -345,7 +346,7 @@ def run_sampled(dsa3d, steps, warmup):
                          "unit": "TFLOP/s", "frac": fl / (ms / 1e3) / 1e12 / PEAK_F32_TFLOPS,
                          "note": ("fp32 VALU flops of the lattice form (14DL per query-head, L = (kt+1)(ky+1)"
                                   "(kx+1))" if mode == "box" else
-                                  "fp32 VALU flops of the trilinear form (36D fwd + 102D bwd per sample)")}}
+                                  "fp32 VALU flops of the trilinear form (36D fwd + 80D bwd per sample)")}}
         del t, off, ws, box
         torch.cuda.empty_cache()
     return res

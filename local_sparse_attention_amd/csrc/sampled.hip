@@ -99,11 +99,21 @@ __device__ __forceinline__ float dot8(const float* a, const float* b) {
   return s;
 }
 
-// Sum over the G lanes of a sample group (G a power of two; the masks stay inside it).
+// Sum over the G lanes of a sample group (8 or 16 lanes: a half row or a row of the
+// wave's DPP rows) by DPP moves, every lane getting the sum: the lanes of a quad swap in
+// pairs and then halves (quad_perm 1,0,3,2 and 2,3,0,1), then quads and half rows swap by
+// mirroring the half row and the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 template <int G>
 __device__ __forceinline__ float gsum(float v) {
-#pragma unroll
-  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
+  static_assert(G == 8 || G == 16, "lane groups are half rows or rows");
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  if constexpr (G == 16) v += dpp_mov<0x140>(v);  // row_mirror
   return v;
 }
 
@@ -318,15 +328,8 @@ __global__ __launch_bounds__(256) void k_sampled_bwd_q(const T* __restrict__ q, 
     int i[3];
     float f[3];
     sample_pos_lat(g, qp, j, lat[j], i, f);
-    float ks[EL], vs[EL], kd[3][EL], vd[3][EL];
-#pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      ks[e] = vs[e] = 0.f;
-      kd[0][e] = kd[1][e] = kd[2][e] = vd[0][e] = vd[1][e] = vd[2][e] = 0.f;
-    }
     // the 8 corners' weights and weight derivatives (0 for corners outside the grid,
-    // which read the query's own row); then all K rows, then all V rows, each batch of
-    // loads issued before its products
+    // which read the query's own row); all 16 corner rows are loaded before any product
     float wc[8], dwc[8][3];
     size_t rr[8];
 #pragma unroll
@@ -341,45 +344,48 @@ __global__ __launch_bounds__(256) void k_sampled_bwd_q(const T* __restrict__ q, 
       dwc[c][2] = ok ? ((c & 1) ? 1.f : -1.f) * pt * py : 0.f;
       rr[c] = ((size_t)(ok ? tok : n) * g.H + h) * D + gl * EL;
     }
-    Raw8<T> raw[8];
+    Raw8<T> kr[8], vr[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) raw[c] = ldraw(k + rr[c]);
+    for (int c = 0; c < 8; ++c) kr[c] = ldraw(k + rr[c]);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      unraw(raw[c], x);
-#pragma unroll
-      for (int e = 0; e < EL; ++e) {
-        ks[e] = fmaf(wc[c], x[e], ks[e]);
-        kd[0][e] = fmaf(dwc[c][0], x[e], kd[0][e]);
-        kd[1][e] = fmaf(dwc[c][1], x[e], kd[1][e]);
-        kd[2][e] = fmaf(dwc[c][2], x[e], kd[2][e]);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) raw[c] = ldraw(v + rr[c]);
+    for (int c = 0; c < 8; ++c) vr[c] = ldraw(v + rr[c]);
+    // Every quantity of the sample is a weighted sum over the corners of the corner dots
+    // q . k_c and dO . v_c: K~ . q = sum w_c (q . k_c), and the position derivatives take
+    // the weight derivatives instead -- 16 dots rather than 8 blended rows.
+    float tk[8], tv[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      unraw(raw[c], x);
-#pragma unroll
-      for (int e = 0; e < EL; ++e) {
-        vs[e] = fmaf(wc[c], x[e], vs[e]);
-        vd[0][e] = fmaf(dwc[c][0], x[e], vd[0][e]);
-        vd[1][e] = fmaf(dwc[c][1], x[e], vd[1][e]);
-        vd[2][e] = fmaf(dwc[c][2], x[e], vd[2][e]);
-      }
+      unraw(kr[c], x);
+      tk[c] = dot8(qf, x);
+      unraw(vr[c], x);
+      tv[c] = dot8(df, x);
     }
-    const float z = gsum<G>(dot8(qf, ks));
-    const float da = gsum<G>(dot8(df, vs));
-    float qk[3], dv_[3];
 #pragma unroll
-    for (int d = 0; d < 3; ++d) {
-      qk[d] = gsum<G>(dot8(qf, kd[d]));
-      dv_[d] = gsum<G>(dot8(df, vd[d]));
+    for (int c = 0; c < 8; ++c) {
+      tk[c] = gsum<G>(tk[c]);
+      tv[c] = gsum<G>(tv[c]);
+    }
+    float z = 0.f, da = 0.f, qk[3] = {0.f, 0.f, 0.f}, dv_[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      z = fmaf(wc[c], tk[c], z);
+      da = fmaf(wc[c], tv[c], da);
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        qk[d] = fmaf(dwc[c][d], tk[c], qk[d]);
+        dv_[d] = fmaf(dwc[c][d], tv[c], dv_[d]);
+      }
     }
     const float alpha = exp2f(z * sl2 - l2);
     const float gz = g.scale * alpha * (da - delta);  // scale * dz
+    // dQ += scale dz K~, corner by corner
 #pragma unroll
-    for (int e = 0; e < EL; ++e) dqa[e] = fmaf(gz, ks[e], dqa[e]);
+    for (int c = 0; c < 8; ++c) {
+      unraw(kr[c], x);
+      const float sc = gz * wc[c];
+#pragma unroll
+      for (int e = 0; e < EL; ++e) dqa[e] = fmaf(sc, x[e], dqa[e]);
+    }
     float gp[3];
 #pragma unroll
     for (int d = 0; d < 3; ++d) gp[d] = gz * qk[d] + alpha * dv_[d];
