@@ -644,12 +644,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_tube(
 }
 
 // Filter / bias gradient over the same tiles: thread (cg2, cp) keeps the partial sums of
-// all taps for 2 channels and the tile columns cp and cp + 8, walking each column's rows
-// in groups of 4 (its own dy values -- 2 columns x 8 rows x 2 channels -- in registers,
-// loaded a frame ahead like the slices; x from the slices; a wave reads two neighbouring
-// tokens' 128 bytes at a time); at the end the 8 column pairs' sums are added pairwise
-// in LDS in a fixed order and the block writes its part, [part][C][taps + 1] as
-// k_dwconv_dw_sum reads it (part = (frame run, tile row, tile column)).
+// all taps for 2 channels over a 4 x 4 patch of the tile (rows 4 (cp >> 2) .. + 3,
+// columns 4 (cp & 3) .. + 3), its dy values in registers, loaded a frame ahead like the
+// slices.  Per frame offset and window row it unpacks the 4 + cx - 1 input columns once
+// and uses each for every (filter row, filter column, patch column) that reads it (a
+// wave reads two neighbouring tokens' 128 bytes at a time).  At the end the 8 patches'
+// sums are added pairwise in LDS in a fixed order and the block writes its part,
+// [part][C][taps + 1] as k_dwconv_dw_sum reads it (part = (frame run, tile row, tile
+// column)).
 template <typename T> struct Dy2;  // 2 consecutive elements
 template <> struct Dy2<u16> { uint32_t v; };
 template <> struct Dy2<float> { float2 v; };
@@ -669,34 +671,38 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_dw_tube(
                                                            float* __restrict__ part, CGeom g, int fchunk) {
   using U = Tube<T, CY, CX>;
   constexpr int NT = 3 * CY * CX;  // tap slots (ct <= 3)
+  constexpr int PR = 4, PC = 4;    // patch rows, columns
+  constexpr int WR = PR + CY - 1, WC = PC + CX - 1;  // input window rows, columns
+  static_assert(PR * 2 == TB_Y && PC * 4 == TB_X, "8 patches of 4 x 4 tokens per tile");
   __shared__ __attribute__((aligned(16))) T ring[TB_RING][U::SLICE * TB_C];
   __shared__ __attribute__((aligned(16))) T dummy[8];
   const int tid = threadIdx.x;
   const TubeBlock bk = tube_block(g, fchunk);
   const int rt = (g.ct - 1) / 2;
   const int cg2 = tid & 31, cp = tid >> 5;
+  const int pr0 = PR * (cp >> 2), pc0 = PC * (cp & 3);  // the patch's first tile row, column
   const int c = bk.c0 + cg2 * 2;
   const TubeSlices<T, CY, CX> sl_io(g, bk);
-  // this thread's dy values of frame f: columns cp, cp + 8, rows 0 .. TB_Y - 1, loaded
-  // unconditionally (from the tensor's start outside the grid) and zeroed by dmask on use
-  uint32_t dmask = 0;  // bit h * TB_Y + i: the row is inside the grid
+  // this thread's dy values of frame f: the patch's PR x PC tokens, loaded unconditionally
+  // (from the tensor's start outside the grid) and zeroed by dmask on use
+  uint32_t dmask = 0;  // bit i * PC + j: patch token (i, j) is inside the grid
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int i = 0; i < PR; ++i)
 #pragma unroll
-    for (int i = 0; i < TB_Y; ++i)
-      if (bk.y0 + i < g.Hp && bk.x0 + cp + 8 * h < g.Wp) dmask |= 1u << (h * TB_Y + i);
+    for (int j = 0; j < PC; ++j)
+      if (bk.y0 + pr0 + i < g.Hp && bk.x0 + pc0 + j < g.Wp) dmask |= 1u << (i * PC + j);
   auto dy_fetch = [&](int f, Dy2<T>* buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int i = 0; i < PR; ++i)
 #pragma unroll
-      for (int i = 0; i < TB_Y; ++i) {
-        const bool in = ((dmask >> (h * TB_Y + i)) & 1u) && f < g.F;
-        const size_t o = ((size_t)(f * g.Hp + bk.y0 + i) * g.Wp + bk.x0 + cp + 8 * h) * g.C + c;
-        buf[h * TB_Y + i] = *reinterpret_cast<const Dy2<T>*>(dy + (in ? o : (size_t)0));
+      for (int j = 0; j < PC; ++j) {
+        const bool in = ((dmask >> (i * PC + j)) & 1u) && f < g.F;
+        const size_t o = ((size_t)(f * g.Hp + bk.y0 + pr0 + i) * g.Wp + bk.x0 + pc0 + j) * g.C + c;
+        buf[i * PC + j] = *reinterpret_cast<const Dy2<T>*>(dy + (in ? o : (size_t)0));
       }
   };
   Chunk8<T> pre[U::LOADS];
-  Dy2<T> dcur[2 * TB_Y], dnext[2 * TB_Y];
+  Dy2<T> dcur[PR * PC], dnext[PR * PC];
   for (int f = bk.t0 - rt; f <= bk.t0 + rt; ++f) {
     sl_io.load(x, f, pre);
     sl_io.store(ring[ring_slot(f)], dummy, f, pre);
@@ -714,36 +720,37 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_dw_tube(
   for (int t = bk.t0; t < bk.t1; ++t) {
     sl_io.load(x, t + 1 + rt, pre);
     dy_fetch(t + 1, dnext);
+    float d[PR][PC][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int col = cp + 8 * h;
+    for (int i = 0; i < PR; ++i)
 #pragma unroll
-      for (int rq = 0; rq < TB_Y / 4; ++rq) {
-        float d[4][2];
+      for (int j = 0; j < PC; ++j) {
+        dy2_unpack(dcur[i * PC + j], d[i][j]);
+        if (!((dmask >> (i * PC + j)) & 1u)) d[i][j][0] = d[i][j][1] = 0.f;
+        acc[NT][0] += d[i][j][0];
+        acc[NT][1] += d[i][j][1];
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dy2_unpack(dcur[h * TB_Y + 4 * rq + i], d[i]);
-          if (!((dmask >> (h * TB_Y + 4 * rq + i)) & 1u)) d[i][0] = d[i][1] = 0.f;
-          acc[NT][0] += d[i][0];
-          acc[NT][1] += d[i][1];
-        }
+    for (int a = 0; a < 3; ++a) {
+      if (a >= g.ct) break;
+      const T* sl = ring[ring_slot(t - rt + a)];
 #pragma unroll
-        for (int a = 0; a < 3; ++a) {
-          if (a >= g.ct) break;
-          const T* sl = ring[ring_slot(t - rt + a)];
+      for (int p = 0; p < WR; ++p) {
+        // input window row p (patch row p - e2 for filter row e2), columns 0 .. WC - 1
+        float xw[WC][2];
+#pragma unroll
+        for (int q = 0; q < WC; ++q) ld2(sl + ((pr0 + p) * U::SX + pc0 + q) * TB_C + cg2 * 2, xw[q]);
+#pragma unroll
+        for (int e2 = 0; e2 < CY; ++e2) {
+          const int i = p - e2;
+          if (i < 0 || i >= PR) continue;
 #pragma unroll
           for (int f = 0; f < CX; ++f) {
-            float v[4 + CY - 1][2];
+            const int tap = (a * CY + e2) * CX + f;
 #pragma unroll
-            for (int p = 0; p < 4 + CY - 1; ++p) ld2(sl + ((4 * rq + p) * U::SX + col + f) * TB_C + cg2 * 2, v[p]);
-#pragma unroll
-            for (int e2 = 0; e2 < CY; ++e2) {
-              const int tap = (a * CY + e2) * CX + f;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                acc[tap][0] = fmaf(d[i][0], v[i + e2][0], acc[tap][0]);
-                acc[tap][1] = fmaf(d[i][1], v[i + e2][1], acc[tap][1]);
-              }
+            for (int j = 0; j < PC; ++j) {
+              acc[tap][0] = fmaf(d[i][j][0], xw[j + f][0], acc[tap][0]);
+              acc[tap][1] = fmaf(d[i][j][1], xw[j + f][1], acc[tap][1]);
             }
           }
         }
@@ -752,10 +759,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_dw_tube(
     __syncthreads();
     sl_io.store(ring[ring_slot(t + 1 + rt)], dummy, t + 1 + rt, pre);
 #pragma unroll
-    for (int i = 0; i < 2 * TB_Y; ++i) dcur[i] = dnext[i];
+    for (int i = 0; i < PR * PC; ++i) dcur[i] = dnext[i];
     __syncthreads();
   }
-  // column pairs 0 .. 7: add pair cp + h into pair cp for h = 4, 2, 1, through LDS
+  // patches 0 .. 7: add patch cp + h into patch cp for h = 4, 2, 1, through LDS
   float* red = reinterpret_cast<float*>(&ring[0][0]);  // [pair][NT + 1][32 cg2][2]
   constexpr int PER = (NT + 1) * 64;                   // floats per pair
   static_assert(4 * PER * 4 <= (int)sizeof(ring), "the reduction fits in the ring");
