@@ -13,6 +13,15 @@ launch configuration the benchmark times.
   corners and edge centres, and random rows, against the oracle computed row by row;
   plus properties that hold at any size, checked over every output.
 
+- 256-frame workload with per-head offsets (16 drifting motion fields, all heads bucketed
+  together, as the benchmark runs it): per head, the rows of its own work-item boundary
+  slices (heads 0 and 15), corners, edge centres and random rows, against the oracle with
+  that head's offsets.
+- the DWConv3D term on the 256-frame grid (2048 channels, 3 x 3 x 3 filter, added into an
+  existing output): every position of 32 channels spread over the 32 channel blocks and
+  their lanes, forward, input gradient, filter and bias gradients, against the oracle on
+  those channels (depthwise: channels are independent).
+
 Properties (P = softmax weights of a query, rows sum to one; dS rows sum to zero):
   sum_j dV[j,h] = sum_n dO[n,h]        sum_j dK[j,h] = 0        all outputs finite.
 """
@@ -152,3 +161,95 @@ def test_full_width_workload(dsa3d_gpu):
 @pytest.mark.timeout(900)
 def test_256_frame_workload(dsa3d_gpu):
     run_sampled(dsa3d_gpu, "C5")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_256_frame_workload_per_head_offsets(dsa3d_gpu):
+    wl = configs.C5
+    grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
+    H = wl.heads
+    print(f"case {wl.name} per-head offsets: generating inputs", flush=True)
+    inp = synth.make_inputs(wl)
+    offh = synth.make_head_offsets(wl)
+    q, k, v, do = (to_dev(inp[x]) for x in ("q", "k", "v", "dout"))
+    ws = dsa3d_gpu.workspace(grid, H, window, True, per_head=True)  # every head bucketed together
+    out, lse = dsa3d_gpu.forward(q, k, v, to_dev(offh), grid, window, wl.scale, out=nan_like(q),
+                                 lse=torch.full((H, wl.N), float("nan"), device="cuda"), ws=ws)
+    dq, dk, dv = dsa3d_gpu.backward(q, k, v, to_dev(offh), out, lse, do, grid, window, wl.scale, dq=nan_like(q),
+                                    dk=nan_like(q), dv=nan_like(q), ws=ws)
+    torch.cuda.synchronize()
+    del ws
+    check_properties(wl, do, out, lse, dq, dk, dv)
+    args = (inp["q"], inp["k"], inp["v"])
+    qall = border_and_random_rows(grid, H, 1024, seed=3)
+    kall = border_and_random_rows(grid, H, 256, seed=4)
+    lse_flat = lse.T.reshape(-1)
+    for h in range(H):
+        qrows = qall[qall % H == h]
+        if h in (0, H - 1):
+            _, brows = boundary_rows(wl, offh[h], boundaries=1)
+            qrows = np.unique(np.concatenate([qrows, brows[brows % H == h]]))
+        krows = kall[kall % H == h]
+        print(f"head {h}: {len(qrows)} query rows, {len(krows)} key rows", flush=True)
+        o_ref, lse_ref = oracle.forward_rows(*args, offh[h], grid, window, wl.scale, qrows)
+        assert_close(gather_rows(out, qrows), o_ref, wl.dtype, f"out h{h}")
+        assert_lse_close(lse_flat[torch.as_tensor(qrows, device=lse.device)].cpu().numpy(), lse_ref)
+        dq_ref = oracle.backward_q_rows(*args, inp["dout"], offh[h], grid, window, wl.scale, qrows)
+        assert_close(gather_rows(dq, qrows), dq_ref, wl.dtype, f"dq h{h}")
+        dk_ref, dv_ref = oracle.backward_kv_rows(*args, inp["dout"], offh[h], grid, window, wl.scale, krows)
+        assert_close(gather_rows(dk, krows), dk_ref, wl.dtype, f"dk h{h}")
+        assert_close(gather_rows(dv, krows), dv_ref, wl.dtype, f"dv h{h}")
+
+
+def _assert_bound(gpu, ref, bound, what):
+    gpu, ref, bound = (np.asarray(a, dtype=np.float64) for a in (gpu, ref, bound))
+    assert gpu.shape == ref.shape and np.isfinite(gpu).all(), what
+    excess = np.abs(gpu - ref) - bound
+    i = np.unravel_index(np.argmax(excess), excess.shape)
+    assert excess.max() <= 0, f"{what}: err {abs(gpu[i] - ref[i]):.3e} > bound {bound[i]:.3e} at {i}"
+    return float(np.abs(gpu - ref).max())
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_dwconv3d_term_256_frame_grid(dsa3d_gpu):
+    """Bounds as for the small DWConv3D cases: outputs 2^-22 taps S + 2^-8 |ref| (bf16
+    rounding), filter and bias gradients 2^-24 (N - 1) S (fp32 sums of N products in a fixed
+    order), S the oracle's sum over absolute values."""
+    wl = configs.C5
+    grid, N, C = (wl.F, wl.Hp, wl.Wp), wl.N, wl.heads * wl.head_dim
+    taps = 27
+    print(f"case DWConv3D term: grid {grid}, {C} channels, 3x3x3, bf16: generating inputs", flush=True)
+    x = synth.normal(43, 0, (N, C), "bf16")
+    y0 = synth.normal(43, 1, (N, C), "bf16")
+    dy = synth.normal(43, 3, (N, C), "bf16")
+    w = synth.normal(43, 4, (C, 3, 3, 3), "f32", 0.1)
+    b = synth.normal(43, 5, (C,), "f32")
+    xd, wd, bd = to_dev(x), to_dev(w), to_dev(b)
+    ya = to_dev(y0)
+    dsa3d_gpu.dwconv3d_forward(xd, wd, bd, grid, out=ya, accumulate=True)
+    dyd = to_dev(dy)
+    dx, dw, db = dsa3d_gpu.dwconv3d_backward(xd, wd, dyd, grid)
+    torch.cuda.synchronize()
+    del xd, dyd
+    # one channel of every 64-channel block, at lanes spread over the block
+    cs = np.arange(32) * 64 + (np.arange(32) * 7) % 64
+    cst = torch.as_tensor(cs, device="cuda")
+    xs, y0s, dys = (np.ascontiguousarray(a[:, cs]) for a in (x, y0, dy))
+    del x, y0, dy
+    ws_, bs_ = np.ascontiguousarray(w[cs]), np.ascontiguousarray(b[cs])
+    print("oracle on 32 channels", flush=True)
+    ref = oracle.dwconv3d_forward(xs, ws_, bs_, grid) + oracle.bf16_to_f64(y0s)
+    S = oracle.dwconv3d_forward(np.abs(oracle.bf16_to_f64(xs)), np.abs(ws_), np.abs(bs_), grid)
+    S += np.abs(oracle.bf16_to_f64(y0s))
+    errs = {"y+=": _assert_bound(to_host_f64(ya[:, cst]), ref, 2.0**-22 * taps * S + 2.0**-8 * np.abs(ref), "y+=")}
+    del ref, S
+    rdx, rdw, rdb = oracle.dwconv3d_backward(xs, ws_, dys, grid)
+    Sx, Sw, Sb = oracle.dwconv3d_backward(np.abs(oracle.bf16_to_f64(xs)), np.abs(ws_),
+                                          np.abs(oracle.bf16_to_f64(dys)), grid)
+    errs["dx"] = _assert_bound(to_host_f64(dx[:, cst]), rdx, 2.0**-22 * taps * Sx + 2.0**-8 * np.abs(rdx), "dx")
+    acc = 2.0**-24 * (N - 1)
+    errs["dw"] = _assert_bound(dw[cst].cpu().numpy(), rdw, acc * Sw + 1e-30, "dweight")
+    errs["db"] = _assert_bound(db[cst].cpu().numpy(), rdb, acc * Sb + 1e-30, "dbias")
+    print("max abs err", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
