@@ -21,6 +21,10 @@ launch configuration the benchmark times.
   existing output): every position of 32 channels spread over the 32 channel blocks and
   their lanes, forward, input gradient, filter and bias gradients, against the oracle on
   those channels (depthwise: channels are independent).
+- sampled windows on the benchmark's workloads (16 x 32 x 32, 8 heads x 128, the 3 x 7 x 7
+  window, bf16; box windows with one real offset per query on the lattice kernels, and free
+  per-sample offsets): every element of O, LSE, dQ, dK, dV and the offset gradient against
+  the full oracle.
 
 Properties (P = softmax weights of a query, rows sum to one; dS rows sum to zero):
   sum_j dV[j,h] = sum_n dO[n,h]        sum_j dK[j,h] = 0        all outputs finite.
@@ -253,3 +257,41 @@ def test_dwconv3d_term_256_frame_grid(dsa3d_gpu):
     errs["dw"] = _assert_bound(dw[cst].cpu().numpy(), rdw, acc * Sw + 1e-30, "dweight")
     errs["db"] = _assert_bound(db[cst].cpu().numpy(), rdb, acc * Sb + 1e-30, "dbias")
     print("max abs err", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,mode", [("S_BOX", "box"), ("S_FREE", "free")])
+def test_sampled_windows_benchmark_workloads(dsa3d_gpu, name, mode):
+    """Tolerances as for the small sampled cases (bf16: 2e-2 + 1e-2 |ref|, LSE 1e-4; the
+    offset gradient, an fp32 sum over heads, samples and corners of products of bf16-derived
+    values, at the bf16 form)."""
+    wl = getattr(configs, name)
+    grid, window = (wl.F, wl.Hp, wl.Wp), (wl.kt, wl.ky, wl.kx)
+    print(f"case {wl.name} ({mode}): generating inputs", flush=True)
+    inp = synth.make_inputs(wl)
+    off = synth.make_real_offsets(wl, mode)
+    q, k, v, do = (to_dev(inp[x]) for x in ("q", "k", "v", "dout"))
+    offd = to_dev(off)
+    out, lse = dsa3d_gpu.sampled_forward(q, k, v, offd, grid, window, mode, wl.scale, out=nan_like(q),
+                                         lse=torch.full((wl.heads, wl.N), float("nan"), device="cuda"))
+    dq, dk, dv, doff = dsa3d_gpu.sampled_backward(q, k, v, offd, out, lse, do, grid, window, mode, wl.scale)
+    torch.cuda.synchronize()
+    args = (inp["q"], inp["k"], inp["v"])
+    off64 = off.astype(np.float64)
+    print("full oracle forward", flush=True)
+    o_ref, lse_ref = oracle.sampled_forward(*args, off64, grid, window, wl.scale, mode)
+    errs = {"out": assert_close(to_host_f64(out), o_ref, wl.dtype, "out"),
+            "lse": assert_lse_close(lse.cpu().numpy(), lse_ref)}
+    del o_ref, lse_ref
+    print("full oracle backward", flush=True)
+    refs = oracle.sampled_backward(*args, inp["dout"], off64, grid, window, wl.scale, mode)
+    for nm, gpu, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs[:3]):
+        errs[nm] = assert_close(to_host_f64(gpu), ref, wl.dtype, nm)
+    g64, r64 = doff.cpu().numpy().astype(np.float64), np.asarray(refs[3], dtype=np.float64)
+    assert g64.shape == r64.shape and np.isfinite(g64).all()
+    excess = np.abs(g64 - r64) - (2e-2 + 1e-2 * np.abs(r64))
+    i = np.unravel_index(np.argmax(excess), excess.shape)
+    assert excess.max() <= 0, f"doffsets: err {abs(g64[i] - r64[i]):.3e} at {i}"
+    errs["doffsets"] = float(np.abs(g64 - r64).max())
+    print("max abs err", {k_: f"{v_:.2e}" for k_, v_ in errs.items()}, flush=True)
