@@ -21,6 +21,11 @@ launch configuration the benchmark times.
   existing output): every position of 32 channels spread over the 32 channel blocks and
   their lanes, forward, input gradient, filter and bias gradients, against the oracle on
   those channels (depthwise: channels are independent).
+- the offset predictor at the benchmark's size (16 x 32 x 32, 1024 channels, pointwise layer to
+  8 heads x 147 samples x 3 = 3528 offsets, bf16): the depthwise stages every element, the
+  pointwise layer on 256 rows (outputs, input gradient) and 64 output columns (weight and
+  bias gradients; both are independent per row / per column), each stage fed the GPU's
+  own input so that the stages are checked one at a time.
 - sampled windows on the benchmark's workloads (16 x 32 x 32, 8 heads x 128, the 3 x 7 x 7
   window, bf16; box windows with one real offset per query on the lattice kernels, and free
   per-sample offsets): every element of O, LSE, dQ, dK, dV and the offset gradient against
@@ -294,4 +299,60 @@ def test_sampled_windows_benchmark_workloads(dsa3d_gpu, name, mode):
     i = np.unravel_index(np.argmax(excess), excess.shape)
     assert excess.max() <= 0, f"doffsets: err {abs(g64[i] - r64[i]):.3e} at {i}"
     errs["doffsets"] = float(np.abs(g64 - r64).max())
+    print("max abs err", {k_: f"{v_:.2e}" for k_, v_ in errs.items()}, flush=True)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_offset_predictor_benchmark_workload(dsa3d_gpu):
+    """Bounds of the small predictor cases: convolution outputs 2^-22 taps S + 2^-8 |ref|,
+    filter / bias gradients 2^-24 (N - 1) S; the pointwise layer's outputs 2^-22 K S (fp32),
+    its input gradient (2^-22 O + 2^-8) S + 2^-8 |ref| (dy rounded to bf16 first, bf16
+    output), weight gradient (2^-22 M + 2^-8) S, bias gradient 2^-22 M S."""
+    wl = configs.S_FREE
+    grid, N = (wl.F, wl.Hp, wl.Wp), wl.N
+    C, O, taps = wl.heads * wl.head_dim, wl.heads * wl.K * 3, 27
+    x = synth.normal(47, 0, (N, C), "bf16")
+    w1 = synth.normal(47, 1, (C, 3, 3, 3), "f32", 0.1)
+    b1 = synth.normal(47, 2, (C,), "f32")
+    w2 = synth.normal(47, 3, (O, C), "bf16", 0.05)
+    b2 = synth.normal(47, 4, (O,), "f32")
+    dy = synth.normal(47, 5, (N, O), "f32")
+    print(f"case predictor N={N} C={C} O={O}", flush=True)
+    xd, w1d, w2d = to_dev(x), to_dev(w1), to_dev(w2)
+    h = dsa3d_gpu.dwconv3d_forward(xd, w1d, to_dev(b1), grid)
+    y = dsa3d_gpu.linear_forward(h, w2d, to_dev(b2))
+    dh, dw2, db2 = dsa3d_gpu.linear_backward(h, w2d, to_dev(dy))
+    dx, dw1, db1 = dsa3d_gpu.dwconv3d_backward(xd, w1d, dh, grid)
+    torch.cuda.synchronize()
+    xh, w2h = oracle.bf16_to_f64(x), oracle.bf16_to_f64(w2)
+    errs = {}
+    # depthwise convolution, every element
+    ref = oracle.dwconv3d_forward(x, w1, b1, grid)
+    S = oracle.dwconv3d_forward(np.abs(xh), np.abs(w1), np.abs(b1), grid)
+    errs["h"] = _assert_bound(to_host_f64(h), ref, 2.0**-22 * taps * S + 2.0**-8 * np.abs(ref), "h")
+    # pointwise layer on rows and columns, from the GPU's h and dh
+    hh = to_host_f64(h)
+    rows = border_and_random_rows((N, 1, 1), 1, 256, seed=5)
+    cols = np.unique(np.concatenate([[0, O - 1], np.random.default_rng(6).integers(0, O, 62)]))
+    ref = oracle.linear_forward(hh[rows], w2h, b2)
+    S = np.abs(hh[rows]) @ np.abs(w2h).T + np.abs(b2)
+    errs["y"] = _assert_bound(y[torch.as_tensor(rows, device="cuda")].cpu().numpy(), ref, 2.0**-22 * C * S, "y")
+    rdh, _, _ = oracle.linear_backward(hh[rows], w2h, dy[rows])
+    Sdh, _, _ = oracle.linear_backward(np.abs(hh[rows]), np.abs(w2h), np.abs(dy[rows]))
+    errs["dh"] = _assert_bound(to_host_f64(dh)[rows], rdh, (2.0**-22 * O + 2.0**-8) * Sdh + 2.0**-8 * np.abs(rdh),
+                               "dh")
+    _, rdw2, rdb2 = oracle.linear_backward(hh, w2h[cols], np.ascontiguousarray(dy[:, cols]))
+    _, Sdw2, Sdb2 = oracle.linear_backward(np.abs(hh), np.abs(w2h[cols]), np.abs(np.ascontiguousarray(dy[:, cols])))
+    cold = torch.as_tensor(cols, device="cuda")
+    errs["dw2"] = _assert_bound(to_host_f64(dw2[cold]), rdw2, (2.0**-22 * N + 2.0**-8) * Sdw2, "dweight2")
+    errs["db2"] = _assert_bound(db2[cold].cpu().numpy(), rdb2, 2.0**-22 * N * Sdb2, "dbias2")
+    # depthwise backward from the GPU's dh, every element
+    dhh = dh.view(torch.int16).cpu().numpy().view(np.uint16)
+    rdx, rdw1, rdb1 = oracle.dwconv3d_backward(x, w1, dhh, grid)
+    Sx, Sw, Sb = oracle.dwconv3d_backward(np.abs(xh), np.abs(w1), np.abs(oracle.bf16_to_f64(dhh)), grid)
+    errs["dx"] = _assert_bound(to_host_f64(dx), rdx, 2.0**-22 * taps * Sx + 2.0**-8 * np.abs(rdx), "dx")
+    acc = 2.0**-24 * (N - 1)
+    errs["dw1"] = _assert_bound(dw1.cpu().numpy(), rdw1, acc * Sw + 1e-30, "dweight1")
+    errs["db1"] = _assert_bound(db1.cpu().numpy(), rdb1, acc * Sb + 1e-30, "dbias1")
     print("max abs err", {k_: f"{v_:.2e}" for k_, v_ in errs.items()}, flush=True)
