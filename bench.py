@@ -3,9 +3,13 @@ bucketing, attention forward, dQ, dK/dV) on the 256-frame workload (grid 256 x 6
 N = 2,088,960 tokens, a 16-head slice of head_dim 128, window 5 x 9 x 9, bf16, smooth
 drifting motion field), inputs resident in HBM.
 
-One step = dsa3d_forward + dsa3d_backward over the whole grid.  Prints one JSON line.
+One step = dsa3d_forward + dsa3d_backward over the whole grid, on one workspace: the forward
+builds the window starts, buckets and query-side schedules, and the backward uses them
+(DSA3D_FLAG_REUSE_PREP), as a training step does; it builds its own key-side work lists and
+Delta.  Prints one JSON line.
   phases_ms  per step, from HIP events the library records on its stream: bucketing
-             and work lists (+ Delta in the backward), then each attention kernel
+             and work lists (the backward's: key-side lists + Delta), then each attention
+             kernel
   value      query-token-heads per second (N * heads / step time)
   roofline   the dominant kernel's algorithmic bytes per launch / its mean duration,
              timed with HIP events on the library's stream, against 8 TB/s HBM (and
@@ -296,7 +300,7 @@ def run_per_head(dsa3d, wl, t, out, lse, g, ws, steps, warmup):
     def step_heads():
         dsa3d.forward(t["q"], t["k"], t["v"], offh, grid, window, wl.scale, out=out, lse=lse, ws=wsh)
         dsa3d.backward(t["q"], t["k"], t["v"], offh, out, lse, t["dout"], grid, window, wl.scale, dq=g[0], dk=g[1],
-                       dv=g[2], ws=wsh)
+                       dv=g[2], ws=wsh, reuse_prep=True)
 
     ms = _timed(step_heads, steps, warmup)
     del wsh
@@ -567,7 +571,8 @@ def main():
         assert rc == 0, dsa3d.status_string(rc)
         rc = lib.dsa3d_backward_ex(ptr(dev["q"]), ptr(dev["k"]), ptr(dev["v"]), ptr(dev["offsets"]), ptr(out),
                                    ptr(lse), ptr(dev["dout"]), *grid, wl.heads, wl.head_dim, *window, wl.scale,
-                                   dtc, ptr(dq), ptr(dk), ptr(dv), ptr(ws), ws.numel(), sp, 0, bev)
+                                   dtc, ptr(dq), ptr(dk), ptr(dv), ptr(ws), ws.numel(), sp, dsa3d.FLAG_REUSE_PREP,
+                                   bev)
         assert rc == 0, dsa3d.status_string(rc)
 
     evp = ctypes.POINTER(ctypes.c_void_p)
@@ -664,8 +669,8 @@ def main():
                 assert rc == 0, dsa3d.status_string(rc)
                 rc = lib.dsa3d_backward_ex(ptr(dev["q"]), ptr(dev["k"]), ptr(dev["v"]), ptr(dev["offsets"]),
                                            ptr(out), ptr(lse), ptr(dev["dout"]), *gF, wl.heads, wl.head_dim, *window,
-                                           wl.scale, dtc, ptr(dq), ptr(dk), ptr(dv), ptr(ws), ws.numel(), sp, 0,
-                                           None)
+                                           wl.scale, dtc, ptr(dq), ptr(dk), ptr(dv), ptr(ws), ws.numel(), sp,
+                                           dsa3d.FLAG_REUSE_PREP, None)
                 assert rc == 0, dsa3d.status_string(rc)
 
             stepF()

@@ -92,7 +92,18 @@ enum {
   /* Run the per-group kernels, which serve every valid geometry, even where the
      frame-sweeping kernels would be chosen.  Results agree within the stated
      tolerances; used by the tests to cover both kernel families on one input. */
-  DSA3D_FLAG_GENERIC_KERNELS = 1
+  DSA3D_FLAG_GENERIC_KERNELS = 1,
+  /* Backward only (dsa3d_backward_ex, dsa3d_backward_heads): use the window starts,
+     buckets and query-side schedules that the forward call just before it built in the
+     same workspace, instead of building them again.  The caller guarantees that the
+     forward ran on this stream with the same workspace pointer and size (sized for the
+     backward), offsets (same values), geometry, dtype, head_dim and
+     DSA3D_FLAG_GENERIC_KERNELS bit, and that nothing wrote the workspace in between;
+     results are then identical to the plain call.  The forward and backward layouts put
+     those arrays first, at the same offsets.  dsa3d_backward_heads honours it on its
+     all-heads-together route only (the one-head-at-a-time route keeps one head's
+     buckets, so it rebuilds them). */
+  DSA3D_FLAG_REUSE_PREP = 2
 };
 
 /* Bytes of workspace needed by dsa3d_forward (backward = 0) or dsa3d_backward

@@ -107,12 +107,17 @@ int run_backward(const void* q, const void* k, const void* v, const int32_t* off
                  bool delta_ready) {
   Prep p;
   workspace_layout(g, true, workspace, &p);
+  // with DSA3D_FLAG_REUSE_PREP the workspace holds what run_forward built for the same
+  // offsets and geometry: the window starts and buckets always, the query-side schedules
+  // when the frame-sweeping forward ran
+  const bool reuse = (flags & DSA3D_FLAG_REUSE_PREP) != 0;
   if (events) hipEventRecord(events[0], stream);
-  if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (!reuse && launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   const bool kv_tube = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dkdv_tube_eligible(g, dtype, head_dim);
   const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dq_qs_eligible(g, dtype, head_dim);
+  const bool sched_built = reuse && fwd_qs_eligible(g, dtype, head_dim);
   if (kv_tube && launch_kv_items(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  if (qs && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (qs && !sched_built && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   const AttnArgs a = backward_args(q, k, v, out, lse, dout, scale, dq, dk, dv);
   // Delta = rowsum(dO * O) of every head for both kernels (the per-group dQ kernel makes
   // its own head's)
@@ -187,7 +192,7 @@ int dsa3d_backward_ex(const void* q, const void* k, const void* v, const int32_t
   const int st = check_backward_args(q, k, v, offsets, out, lse, dout, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale,
                                      dtype, dq, dk, dv);
   if (st != DSA3D_OK) return st;
-  if (flags & ~(unsigned)DSA3D_FLAG_GENERIC_KERNELS) return DSA3D_ERR_FLAGS;
+  if (flags & ~(unsigned)(DSA3D_FLAG_GENERIC_KERNELS | DSA3D_FLAG_REUSE_PREP)) return DSA3D_ERR_FLAGS;
   if (!aligned16(workspace)) return DSA3D_ERR_ALIGN;
   const Geom g = make_geom(F, Hp, Wp, heads, kt, ky, kx);
   if (workspace_bytes < workspace_layout(g, true, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
@@ -240,16 +245,21 @@ int dsa3d_backward_heads(const void* q, const void* k, const void* v, const int3
   const int st = check_backward_args(q, k, v, offsets, out, lse, dout, F, Hp, Wp, heads, head_dim, kt, ky, kx, scale,
                                      dtype, dq, dk, dv);
   if (st != DSA3D_OK) return st;
-  if (flags & ~(unsigned)DSA3D_FLAG_GENERIC_KERNELS) return DSA3D_ERR_FLAGS;
+  if (flags & ~(unsigned)(DSA3D_FLAG_GENERIC_KERNELS | DSA3D_FLAG_REUSE_PREP)) return DSA3D_ERR_FLAGS;
   if (!aligned16(workspace)) return DSA3D_ERR_ALIGN;
   Geom g = make_geom(F, Hp, Wp, heads, kt, ky, kx);
   if (workspace_bytes < workspace_layout(g, true, nullptr, nullptr)) return DSA3D_ERR_WORKSPACE;
   Geom gb = g;
   gb.ph = heads;
   if (!(flags & DSA3D_FLAG_GENERIC_KERNELS) && heads_batchable(g) && dq_qs_eligible(g, dtype, head_dim) &&
-      dkdv_tube_eligible(g, dtype, head_dim) && workspace_bytes >= workspace_layout(gb, true, nullptr, nullptr))
+      dkdv_tube_eligible(g, dtype, head_dim) && workspace_bytes >= workspace_layout(gb, true, nullptr, nullptr)) {
+    // the forward took its batched route with this workspace too when its kernels are
+    // the frame-sweeping ones; otherwise it left one head's buckets only
+    const unsigned fl = fwd_qs_eligible(g, dtype, head_dim) ? flags : flags & ~(unsigned)DSA3D_FLAG_REUSE_PREP;
     return run_backward(q, k, v, offsets, out, lse, dout, gb, head_dim, scale, dtype, dq, dk, dv,
-                        static_cast<char*>(workspace), stream, flags, nullptr, false);
+                        static_cast<char*>(workspace), stream, fl, nullptr, false);
+  }
+  flags &= ~(unsigned)DSA3D_FLAG_REUSE_PREP;  // one head after the other: each head's buckets are rebuilt
   // Delta of every head once (it does not depend on the offsets)
   const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dq_qs_eligible(g, dtype, head_dim);
   if (qs) {

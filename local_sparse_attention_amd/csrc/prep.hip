@@ -48,6 +48,9 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
     off += align256(bytes);
     return ptr;
   };
+  // The bucketing and the query-side schedules, which the forward and the backward build
+  // alike, come first and at the same offsets in both layouts, so that a backward may use
+  // what a forward built in the same workspace; the backward's own arrays follow.
   Prep q;
   q.starts = (int4*)take(N * sizeof(int4));
   q.keys[0] = (uint32_t*)take(N * 4);
@@ -59,11 +62,6 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   q.goff = (int*)take(((size_t)g.nblobs * g.ph + 1) * 4);
   q.groups = (int2*)take((size_t)max_groups * sizeof(int2));
   q.ngroups = (int*)take(4);
-  q.delta = backward ? (float*)take(NH * g.H * 4) : nullptr;
-  const bool kv = backward && kv_items_geometry(g);
-  q.kv_off = kv ? (int*)take(((size_t)kv_item_columns(g) * g.Lt * g.ph + 1) * 4) : nullptr;
-  q.kv_ids = kv ? (int*)take(max_kv_items(g) * g.ph * KV_Q * 4) : nullptr;
-  q.kv_mask = kv ? (int*)take(max_kv_items(g) * g.ph * KV_Q * sizeof(int)) : nullptr;
   const bool qsg = qs_geometry(g);
   q.qt_off = qsg ? (int*)take(((size_t)qs_items(g) * g.ph + 1) * 4) : nullptr;
   q.qt = qsg ? (int*)take((size_t)max_groups * QT_INTS * 4) : nullptr;
@@ -72,12 +70,19 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   q.tq_dt = qsg ? (signed char*)take((size_t)max_groups * 16) : nullptr;
   q.qs_off = qsg ? (int*)take(((size_t)qs_items(g) * g.ph + 1) * 4) : nullptr;
   q.qs = qsg ? (int*)take((qs_ints(g, max_groups / g.ph) * g.ph) * 4) : nullptr;
-  // the longest scan: radix counts, blob group counts, work-list and item offsets
+  // the longest scan of either pass: radix counts, blob group counts, work-list and item
+  // offsets
+  const bool kvg = kv_items_geometry(g);
   size_t scan_n = (size_t)256 * rb * g.ph;
   scan_n = max(scan_n, (size_t)g.nblobs * g.ph + 1);
   if (qsg) scan_n = max(scan_n, (size_t)qs_items(g) * g.ph + 1);
-  if (kv) scan_n = max(scan_n, (size_t)kv_item_columns(g) * g.Lt * g.ph + 1);
+  if (kvg) scan_n = max(scan_n, (size_t)kv_item_columns(g) * g.Lt * g.ph + 1);
   q.scan_part = (uint32_t*)take(scan_part_words(scan_n) * 4);
+  q.delta = backward ? (float*)take(NH * g.H * 4) : nullptr;
+  const bool kv = backward && kvg;
+  q.kv_off = kv ? (int*)take(((size_t)kv_item_columns(g) * g.Lt * g.ph + 1) * 4) : nullptr;
+  q.kv_ids = kv ? (int*)take(max_kv_items(g) * g.ph * KV_Q * 4) : nullptr;
+  q.kv_mask = kv ? (int*)take(max_kv_items(g) * g.ph * KV_Q * sizeof(int)) : nullptr;
   q.perm = q.vals[passes & 1];
   q.radix_blocks = rb;
   q.radix_passes = passes;

@@ -25,6 +25,7 @@ class DSA3DError(RuntimeError):
 
 
 FLAG_GENERIC_KERNELS = 1  # DSA3D_FLAG_GENERIC_KERNELS
+FLAG_REUSE_PREP = 2  # DSA3D_FLAG_REUSE_PREP
 
 
 def load():
@@ -215,8 +216,13 @@ def forward_static(q, k, v, offsets, grid, window, scale=None, out=None, lse=Non
 
 
 def backward(q, k, v, offsets, out, lse, dout, grid, window, scale=None, dq=None, dk=None, dv=None, ws=None,
-             generic=False):
-    """Returns (dq, dk, dv), each [N, H, D] in q's dtype.  offsets as in forward()."""
+             generic=False, reuse_prep=False):
+    """Returns (dq, dk, dv), each [N, H, D] in q's dtype.  offsets as in forward().
+    reuse_prep=True (DSA3D_FLAG_REUSE_PREP) uses the buckets and schedules that forward()
+    just built in the same `ws` (a workspace sized for the backward) with the same offsets,
+    geometry and `generic`."""
+    if reuse_prep and ws is None:
+        raise DSA3DError("reuse_prep needs the workspace the forward used")
     N, H, D = _shape(q, grid)
     for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
         _want(t, name, q.shape, q.dtype)
@@ -235,7 +241,7 @@ def backward(q, k, v, offsets, out, lse, dout, grid, window, scale=None, dq=None
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     ws = _workspace_arg(ws, grid, H, window, True, dev, per_head)
-    flags = FLAG_GENERIC_KERNELS if generic else 0
+    flags = (FLAG_GENERIC_KERNELS if generic else 0) | (FLAG_REUSE_PREP if reuse_prep else 0)
     args = (*ptrs, *grid, H, D, *window, float(scale), _dtype_code(q), _dev(dq, "dq", dev), _dev(dk, "dk", dev),
             _dev(dv, "dv", dev), _dev(ws, "workspace", dev), ws.numel(), _stream(), flags)
     if per_head:

@@ -113,7 +113,8 @@ def test_argument_validation(lib, call):
     assert call(lib, q=P + 8) == ERR_ALIGN
     assert call(lib, ws=P + 4) == ERR_ALIGN
     assert call(lib, wsb=1000) == ERR_WORKSPACE
-    assert call(lib, flags=2) == ERR_FLAGS
+    # DSA3D_FLAG_REUSE_PREP (2) is a backward flag
+    assert call(lib, flags=2 if call is fwd else 4) == ERR_FLAGS
     assert call(lib, flags=0x80000000) == ERR_FLAGS
     # thin grids: N < 2^30 but 2^28 blobs of start cells (32-bit sort keys of 16 cells each)
     assert call(lib, F=1 << 28, Hp=1, Wp=1, kt=1, ky=1, kx=1) == ERR_GRID
@@ -264,7 +265,8 @@ def test_heads_validation(lib):
     assert f(*bad, 0) == ERR_WORKSPACE
     b = lib.dsa3d_backward_heads
     okb = [P] * 7 + [4, 8, 8, 2, 64, 3, 3, 3, 0.125, 0, P, P, P, P, 1 << 40, None]
-    assert b(*okb, 2) == ERR_FLAGS
+    assert b(*okb, 4) == ERR_FLAGS
+    assert f(*ok, 2) == ERR_FLAGS  # DSA3D_FLAG_REUSE_PREP is a backward flag
     bad = list(okb)
     bad[11] = 96  # head_dim
     assert b(*bad, 0) == ERR_HEAD_DIM
