@@ -537,121 +537,6 @@ __device__ __forceinline__ void dy4_unpack(const Dy4<float>& d, float* x) {
   x[0] = d.v.x; x[1] = d.v.y; x[2] = d.v.z; x[3] = d.v.w;
 }
 
-// Forward (or, with the filters mirrored, the input gradient): thread (cg4, column)
-// computes the tile's TB_Y rows of its column for 4 channels; the block's filters sit in
-// LDS as [tap][channel] fp32; per frame offset and filter column a thread reads one
-// window of TB_Y + cy - 1 rows from the slice (a wave: four neighbouring tokens' 128
-// bytes at a time) and each tap's 4 weights.  Every global load of a frame -- the next
-// slice and, with accumulate, the output's old values -- is issued at the frame's start
-// and its data used only after the products (the slice's out-of-grid chunks are zeroed
-// as they are written to LDS), so the loads are in flight while the frame is computed.
-// The last frame of a run loads (in bounds) and writes to its free ring slot a slice that
-// is never read, so that no load or LDS write sits behind a branch.
-template <typename T, int CY, int CX, bool ACC>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_tube(
-    const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ b, T* __restrict__ y, CGeom g,
-    int fchunk, int flip) {
-  using U = Tube<T, CY, CX>;
-  constexpr int NT = 3 * CY * CX;  // tap slots (ct <= 3)
-  __shared__ __attribute__((aligned(16))) T ring[TB_RING][U::SLICE * TB_C];
-  __shared__ __attribute__((aligned(16))) float wl[NT + 1][TB_C];  // taps, then the bias
-  __shared__ __attribute__((aligned(16))) T dummy[8];
-  const int tid = threadIdx.x;
-  const TubeBlock bk = tube_block(g, fchunk);
-  const int rt = (g.ct - 1) / 2;
-  const int cg4 = tid & 15, col = tid >> 4;
-  const int c = bk.c0 + cg4 * 4, gx = bk.x0 + col;
-  // filters (the tap index runs fastest in global memory; mirrored for the input
-  // gradient) and bias, through LDS so that no global load of the prologue is pending
-  // when the frame loop starts
-  for (int i = tid; i < TB_C * g.taps; i += 256) {
-    const int ch = i / g.taps, tap = i - ch * g.taps;
-    wl[flip ? g.taps - 1 - tap : tap][ch] = w[(size_t)bk.c0 * g.taps + i];
-  }
-  for (int i = g.taps * TB_C + tid; i < NT * TB_C; i += 256) wl[i / TB_C][i % TB_C] = 0.f;
-  if (tid < TB_C) wl[NT][tid] = (b && !flip) ? b[bk.c0 + tid] : 0.f;
-  const TubeSlices<T, CY, CX> sl_io(g, bk);
-  const long long fstride = sl_io.fstride;
-  auto load_slice = [&](int f, Chunk8<T>* buf) { sl_io.load(x, f, buf); };
-  auto store_slice = [&](int f, const Chunk8<T>* buf) { sl_io.store(ring[ring_slot(f)], dummy, f, buf); };
-  Chunk8<T> pre[U::LOADS];
-  for (int f = bk.t0 - rt; f <= bk.t0 + rt; ++f) {
-    load_slice(f, pre);
-    store_slice(f, pre);
-  }
-  __syncthreads();
-  const size_t ybase = ((size_t)bk.y0 * g.Wp + gx) * g.C + c;  // row 0 of this thread's column, frame 0
-  const bool colin = gx < g.Wp;
-  const float4 bv = *reinterpret_cast<const float4*>(&wl[NT][cg4 * 4]);
-  const float bias[4] = {bv.x, bv.y, bv.z, bv.w};
-  for (int t = bk.t0; t < bk.t1; ++t) {
-    load_slice(t + 1 + rt, pre);
-    Dy4<T> old[TB_Y];
-    if constexpr (ACC) {
-#pragma unroll
-      for (int i = 0; i < TB_Y; ++i) {
-        const bool in = colin && bk.y0 + i < g.Hp;
-        old[i] = *reinterpret_cast<const Dy4<T>*>(y + (in ? (size_t)t * fstride + ybase + (size_t)i * g.Wp * g.C : c));
-      }
-    }
-    float acc[TB_Y][4];
-#pragma unroll
-    for (int i = 0; i < TB_Y; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][e] = bias[e];
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      if (a >= g.ct) break;
-      const T* sl = ring[ring_slot(t - rt + a)];
-#pragma unroll
-      for (int f = 0; f < CX; ++f) {
-        float v[TB_Y + CY - 1][4];
-#pragma unroll
-        for (int p = 0; p < TB_Y + CY - 1; ++p) ld4(sl + (p * U::SX + col + f) * TB_C + cg4 * 4, v[p]);
-#pragma unroll
-        for (int e2 = 0; e2 < CY; ++e2) {
-          const int tap = (a * CY + e2) * CX + f;
-          const float4 wv = *reinterpret_cast<const float4*>(&wl[tap][cg4 * 4]);
-          const float wt[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-          for (int i = 0; i < TB_Y; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wt[e], v[i + e2][e], acc[i][e]);
-        }
-      }
-    }
-    __syncthreads();  // every read of the leaving frame's slice is done
-    // the next slice into LDS before the output stores, so that waiting for its loads
-    // never means waiting for stores
-    store_slice(t + 1 + rt, pre);
-    if constexpr (ACC) {
-#pragma unroll
-      for (int i = 0; i < TB_Y; ++i) {
-        float o[4];
-        dy4_unpack(old[i], o);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][e] += o[e];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TB_Y; ++i) {
-      if (colin && bk.y0 + i < g.Hp) {
-        store4(y + (size_t)t * fstride + ybase + (size_t)i * g.Wp * g.C, acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// Filter / bias gradient over the same tiles: thread (cg2, cp) keeps the partial sums of
-// all taps for 2 channels over a 4 x 4 patch of the tile (rows 4 (cp >> 2) .. + 3,
-// columns 4 (cp & 3) .. + 3), its dy values in registers, loaded a frame ahead like the
-// slices.  Per frame offset and window row it unpacks the 4 + cx - 1 input columns once
-// and uses each for every (filter row, filter column, patch column) that reads it (a
-// wave reads two neighbouring tokens' 128 bytes at a time).  At the end the 8 patches'
-// sums are added pairwise in LDS in a fixed order and the block writes its part,
-// [part][C][taps + 1] as k_dwconv_dw_sum reads it (part = (frame run, tile row, tile
-// column)).
 template <typename T> struct Dy2;  // 2 consecutive elements
 template <> struct Dy2<u16> { uint32_t v; };
 template <> struct Dy2<float> { float2 v; };
@@ -666,6 +551,164 @@ __device__ __forceinline__ void dy2_unpack(const Dy2<float>& d, float* x) {
 __device__ __forceinline__ void ld2(const u16* p, float* x) { dy2_unpack(Dy2<u16>{*reinterpret_cast<const uint32_t*>(p)}, x); }
 __device__ __forceinline__ void ld2(const float* p, float* x) { dy2_unpack(Dy2<float>{*reinterpret_cast<const float2*>(p)}, x); }
 
+__device__ __forceinline__ void store2(u16* p, float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<bf16x2_t*>(p) = __builtin_convertvector((f32x2_t{a, b}), bf16x2_t);
+}
+__device__ __forceinline__ void store2(float* p, float a, float b) { *reinterpret_cast<float2*>(p) = make_float2(a, b); }
+
+// Forward (or, with the filters mirrored, the input gradient): thread (cg2, patch)
+// computes a 4 x 4 patch of the tile (rows 4 (cp >> 2) .. + 3, columns 4 (cp & 3) .. + 3)
+// for 2 channels, with those channels' filters in registers (read once from the block's
+// copy in LDS, [tap][channel] fp32).  Per frame offset and window row it widens the
+// 4 + cx - 1 input columns once and uses each for every (filter row, filter column,
+// patch column) that reads it: 4 products per widened value, where a thread that owns a
+// column of 8 rows gets 2.4 (a wave reads two neighbouring tokens' 128 bytes at a time).
+// Every global load of a frame -- the next slice and, with accumulate, the output's old
+// values -- is issued at the frame's start and its data used only after the products;
+// no load, LDS write or register copy of the frame loop sits behind a branch (chunks
+// outside the grid are loaded from a valid address and zeroed by a mask on the way to
+// LDS; the last frame of a run loads and writes to its free ring slot a slice nobody
+// reads), so the compiler's waits for the loads sit where the data is used.
+template <typename T, int CY, int CX, bool ACC>
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_tube(
+    const T* __restrict__ x, const float* __restrict__ w, const float* __restrict__ b, T* __restrict__ y, CGeom g,
+    int fchunk, int flip) {
+  using U = Tube<T, CY, CX>;
+  constexpr int NT = 3 * CY * CX;  // tap slots (ct <= 3)
+  constexpr int PR = 4, PC = 4;    // patch rows, columns
+  constexpr int WR = PR + CY - 1, WC = PC + CX - 1;  // input window rows, columns
+  static_assert(PR * 2 == TB_Y && PC * 4 == TB_X, "8 patches of 4 x 4 tokens per tile");
+  __shared__ __attribute__((aligned(16))) T ring[TB_RING][U::SLICE * TB_C];
+  __shared__ __attribute__((aligned(16))) float wl[NT + 1][TB_C];  // taps, then the bias
+  __shared__ __attribute__((aligned(16))) T dummy[8];
+  const int tid = threadIdx.x;
+  const TubeBlock bk = tube_block(g, fchunk);
+  const int rt = (g.ct - 1) / 2;
+  const int cg2 = tid & 31, cp = tid >> 5;
+  const int pr0 = PR * (cp >> 2), pc0 = PC * (cp & 3);  // the patch's first tile row, column
+  const int c = bk.c0 + cg2 * 2;
+  // filters (the tap index runs fastest in global memory; mirrored for the input
+  // gradient) and bias through LDS, so that every load of the prologue is complete before
+  // the frame loop
+  for (int i = tid; i < TB_C * g.taps; i += 256) {
+    const int ch = i / g.taps, tap = i - ch * g.taps;
+    wl[flip ? g.taps - 1 - tap : tap][ch] = w[(size_t)bk.c0 * g.taps + i];
+  }
+  for (int i = g.taps * TB_C + tid; i < NT * TB_C; i += 256) wl[i / TB_C][i % TB_C] = 0.f;
+  if (tid < TB_C) wl[NT][tid] = (b && !flip) ? b[bk.c0 + tid] : 0.f;
+  const TubeSlices<T, CY, CX> sl_io(g, bk);
+  const long long fstride = sl_io.fstride;
+  Chunk8<T> pre[U::LOADS];
+  for (int f = bk.t0 - rt; f <= bk.t0 + rt; ++f) {
+    sl_io.load(x, f, pre);
+    sl_io.store(ring[ring_slot(f)], dummy, f, pre);
+  }
+  __syncthreads();
+  float wr[NT][2];
+#pragma unroll
+  for (int tap = 0; tap < NT; ++tap) {
+    const float2 t2 = *reinterpret_cast<const float2*>(&wl[tap][cg2 * 2]);
+    wr[tap][0] = t2.x;
+    wr[tap][1] = t2.y;
+  }
+  const float2 bv = *reinterpret_cast<const float2*>(&wl[NT][cg2 * 2]);
+  // this thread's output tokens: offsets within a frame (first element of its 2 channels)
+  // and whether they lie inside the grid
+  uint32_t omask = 0;  // bit i * PC + j
+#pragma unroll
+  for (int i = 0; i < PR; ++i)
+#pragma unroll
+    for (int j = 0; j < PC; ++j)
+      if (bk.y0 + pr0 + i < g.Hp && bk.x0 + pc0 + j < g.Wp) omask |= 1u << (i * PC + j);
+  const size_t obase = ((size_t)(bk.y0 + pr0) * g.Wp + bk.x0 + pc0) * g.C + c;
+  auto oofs = [&](int i, int j) { return obase + ((size_t)i * g.Wp + j) * g.C; };
+  for (int t = bk.t0; t < bk.t1; ++t) {
+    sl_io.load(x, t + 1 + rt, pre);
+    Dy2<T> old[PR * PC];
+    if constexpr (ACC) {
+#pragma unroll
+      for (int i = 0; i < PR; ++i)
+#pragma unroll
+        for (int j = 0; j < PC; ++j) {
+          const bool in = (omask >> (i * PC + j)) & 1u;
+          old[i * PC + j] =
+              *reinterpret_cast<const Dy2<T>*>(y + (in ? (size_t)t * fstride + oofs(i, j) : (size_t)0));
+        }
+    }
+    float acc[PR][PC][2];
+#pragma unroll
+    for (int i = 0; i < PR; ++i)
+#pragma unroll
+      for (int j = 0; j < PC; ++j) {
+        acc[i][j][0] = bv.x;
+        acc[i][j][1] = bv.y;
+      }
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      if (a >= g.ct) break;
+      const T* sl = ring[ring_slot(t - rt + a)];
+#pragma unroll
+      for (int p = 0; p < WR; ++p) {
+        // input window row p (patch row p - e2 for filter row e2), columns 0 .. WC - 1
+        float xw[WC][2];
+#pragma unroll
+        for (int q = 0; q < WC; ++q) ld2(sl + ((pr0 + p) * U::SX + pc0 + q) * TB_C + cg2 * 2, xw[q]);
+#pragma unroll
+        for (int e2 = 0; e2 < CY; ++e2) {
+          const int i = p - e2;
+          if (i < 0 || i >= PR) continue;
+#pragma unroll
+          for (int f = 0; f < CX; ++f) {
+            const int tap = (a * CY + e2) * CX + f;
+#pragma unroll
+            for (int j = 0; j < PC; ++j) {
+              acc[i][j][0] = fmaf(wr[tap][0], xw[j + f][0], acc[i][j][0]);
+              acc[i][j][1] = fmaf(wr[tap][1], xw[j + f][1], acc[i][j][1]);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();  // every read of the leaving frame's slice is done
+    // the next slice into LDS before the output stores, so that waiting for its loads
+    // never means waiting for stores
+    sl_io.store(ring[ring_slot(t + 1 + rt)], dummy, t + 1 + rt, pre);
+    if constexpr (ACC) {
+#pragma unroll
+      for (int i = 0; i < PR; ++i)
+#pragma unroll
+        for (int j = 0; j < PC; ++j) {
+          float o[2];
+          dy2_unpack(old[i * PC + j], o);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            acc[i][j][e] += o[e];
+            // keeps the add (and so the wait for the old value) out of the conditional
+            // store below, where the compiler would otherwise sink it
+            __asm__ __volatile__("" ::"v"(acc[i][j][e]));
+          }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PR; ++i)
+#pragma unroll
+      for (int j = 0; j < PC; ++j)
+        if ((omask >> (i * PC + j)) & 1u) store2(y + (size_t)t * fstride + oofs(i, j), acc[i][j][0], acc[i][j][1]);
+    __syncthreads();
+  }
+}
+
+// Filter / bias gradient over the same tiles: thread (cg2, cp) keeps the partial sums of
+// all taps for 2 channels over a 4 x 4 patch of the tile (rows 4 (cp >> 2) .. + 3,
+// columns 4 (cp & 3) .. + 3), its dy values in registers, loaded a frame ahead like the
+// slices.  Per frame offset and window row it unpacks the 4 + cx - 1 input columns once
+// and uses each for every (filter row, filter column, patch column) that reads it (a
+// wave reads two neighbouring tokens' 128 bytes at a time).  At the end the 8 patches'
+// sums are added pairwise in LDS in a fixed order and the block writes its part,
+// [part][C][taps + 1] as k_dwconv_dw_sum reads it (part = (frame run, tile row, tile
+// column)).
 template <typename T, int CY, int CX>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dwconv_dw_tube(const T* __restrict__ x, const T* __restrict__ dy,
                                                            float* __restrict__ part, CGeom g, int fchunk) {
