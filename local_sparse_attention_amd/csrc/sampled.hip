@@ -135,6 +135,11 @@ __device__ __forceinline__ void box_axis(int p, float o, int k, int G, int& si, 
   }
 }
 
+// Wave order on the query side: a wave per (token, head), head-major, so that the waves
+// of a block and their neighbours in launch order take neighbouring tokens of one head,
+// whose windows (and the key rows they read) overlap, and share those rows in the caches
+// (3-7% faster than token-major; the key-side kernels keep token-major order, which
+// measured faster for them).
 struct QPos {
   int p[3];       // query position
   int si[3];      // box: start (integer part)
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(256) void k_sampled_fwd(const T* __restrict__ q, co
   fill_lattice(g, lat);
   const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wv >= (long long)g.N * g.H) return;
-  const int n = (int)(wv / g.H), h = (int)(wv - (long long)n * g.H);
+  const int h = (int)(wv / g.N), n = (int)(wv - (long long)h * g.N);  // head-major: see wave order
   const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
   const size_t row = ((size_t)n * g.H + h) * D + gl * EL;
   float qf[EL];
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(256) void k_sampled_bwd_q(const T* __restrict__ q, 
   fill_lattice(g, lat);
   const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wv >= (long long)g.N * g.H) return;
-  const int n = (int)(wv / g.H), h = (int)(wv - (long long)n * g.H);
+  const int h = (int)(wv / g.N), n = (int)(wv - (long long)h * g.N);  // head-major: see wave order
   const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
   const size_t row = ((size_t)n * g.H + h) * D + gl * EL;
   float qf[EL], df[EL], x[EL];
@@ -533,7 +538,7 @@ __global__ __launch_bounds__(256) void k_box_fwd(const T* __restrict__ q, const 
   const int wq = threadIdx.x >> 6;
   const long long wv = (long long)blockIdx.x * 4 + wq;
   if (wv >= (long long)g.N * g.H) return;
-  const int n = (int)(wv / g.H), h = (int)(wv - (long long)n * g.H);
+  const int h = (int)(wv / g.N), n = (int)(wv - (long long)h * g.N);  // head-major: see wave order
   const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
   const QPos qp = query_pos(g, off, n, h);
   const BoxLat b = box_lattice(g, qp);
@@ -606,7 +611,7 @@ __global__ __launch_bounds__(256) void k_box_bwd_q(const T* __restrict__ q, cons
   const int wq = threadIdx.x >> 6;
   const long long wv = (long long)blockIdx.x * 4 + wq;
   if (wv >= (long long)g.N * g.H) return;
-  const int n = (int)(wv / g.H), h = (int)(wv - (long long)n * g.H);
+  const int h = (int)(wv / g.N), n = (int)(wv - (long long)h * g.N);  // head-major: see wave order
   const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
   const QPos qp = query_pos(g, off, n, h);
   const BoxLat b = box_lattice(g, qp);
@@ -746,7 +751,7 @@ __global__ __launch_bounds__(256) void k_sampled_dkdv(const T* __restrict__ q, c
   constexpr int G = D / EL, NG = 64 / G;
   const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wv >= (long long)g.N * g.H) return;
-  const int m = (int)(wv / g.H), h = (int)(wv - (long long)m * g.H);
+  const int m = (int)(wv / g.H), h = (int)(wv - (long long)m * g.H);  // key side: token-major (measured faster)
   const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
   const int plane = g.Hp * g.Wp;
   const int mt = m / plane, my = (m - mt * plane) / g.Wp, mx = m - mt * plane - my * g.Wp;
@@ -852,7 +857,7 @@ __global__ __launch_bounds__(256) void k_box_dkdv(const T* __restrict__ q, const
   constexpr int G = D / EL, NG = 64 / G;
   const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wv >= (long long)g.N * g.H) return;
-  const int m = (int)(wv / g.H), h = (int)(wv - (long long)m * g.H);
+  const int m = (int)(wv / g.H), h = (int)(wv - (long long)m * g.H);  // key side: token-major (measured faster)
   const int lane = threadIdx.x & 63, grp = lane / G, gl = lane % G;
   const int cell = h * (g.N + 1) + m;
   const int beg = cell_ptr[cell], end = cell_ptr[cell + 1];
