@@ -434,23 +434,6 @@ __device__ __forceinline__ void st_chunk(float* p, const Chunk8<float>& c) {
   reinterpret_cast<uint4*>(p)[0] = c.a;
   reinterpret_cast<uint4*>(p)[1] = c.b;
 }
-template <typename T> __device__ __forceinline__ Chunk8<T> zero_chunk();
-template <> __device__ __forceinline__ Chunk8<u16> zero_chunk<u16>() { return {make_uint4(0u, 0u, 0u, 0u)}; }
-template <> __device__ __forceinline__ Chunk8<float> zero_chunk<float>() {
-  return {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
-}
-// 4 consecutive elements as fp32
-__device__ __forceinline__ void ld4(const u16* p, float* x) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
-  x[0] = __uint_as_float(u.x << 16);
-  x[1] = __uint_as_float(u.x & 0xffff0000u);
-  x[2] = __uint_as_float(u.y << 16);
-  x[3] = __uint_as_float(u.y & 0xffff0000u);
-}
-__device__ __forceinline__ void ld4(const float* p, float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-}
 
 // Block order: tile column fastest, then tile row, frame run, channel block, each XCD
 // given a contiguous run (neighbouring tiles share their halo rows in one L2).
@@ -522,20 +505,6 @@ struct TubeSlices {
   }
 };
 __device__ __forceinline__ int ring_slot(int f) { return ((f % TB_RING) + TB_RING) % TB_RING; }
-
-// 4 consecutive elements (a thread's channels of one token), raw
-template <typename T> struct Dy4;
-template <> struct Dy4<u16> { uint2 v; };
-template <> struct Dy4<float> { float4 v; };
-__device__ __forceinline__ void dy4_unpack(const Dy4<u16>& d, float* x) {
-  x[0] = __uint_as_float(d.v.x << 16);
-  x[1] = __uint_as_float(d.v.x & 0xffff0000u);
-  x[2] = __uint_as_float(d.v.y << 16);
-  x[3] = __uint_as_float(d.v.y & 0xffff0000u);
-}
-__device__ __forceinline__ void dy4_unpack(const Dy4<float>& d, float* x) {
-  x[0] = d.v.x; x[1] = d.v.y; x[2] = d.v.z; x[3] = d.v.w;
-}
 
 template <typename T> struct Dy2;  // 2 consecutive elements
 template <> struct Dy2<u16> { uint32_t v; };
