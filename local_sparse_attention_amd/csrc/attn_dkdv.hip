@@ -179,10 +179,7 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
   constexpr int NWC = 2 * NG, NW = NWC + DKDV_LW;
   constexpr int NTH = C::NT / 2;  // d tiles per half
   __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::ENTRY];
-  // [step parity][frame slot][P, dS][row tile half][lane] 8 bytes: a lane's 16-byte B
-  // fragment is its 8 bytes of each half, so each producing wave writes 512 contiguous
-  // bytes (no bank conflicts) and a consumer reads the two halves with one ds_read2
-  __shared__ __attribute__((aligned(16))) char xch[2][KT][2][64 * 16];
+  __shared__ __attribute__((aligned(16))) char xch[2][KT][2][64 * 16];  // [step parity][frame slot][P, dS]
 
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
   const int nchunk = (g.F + ts - 1) / ts;
@@ -390,13 +387,8 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
       Frag<u16> pb[NSG], db[NSG];
 #pragma unroll
       for (int i = 0; i < NSG; ++i) {
-        const uint2 p0 = *reinterpret_cast<const uint2*>(xch[par][s0 + i][0] + lane * 8);
-        const uint2 p1 = *reinterpret_cast<const uint2*>(xch[par][s0 + i][0] + 512 + lane * 8);
-        const uint2 d0 = *reinterpret_cast<const uint2*>(xch[par][s0 + i][1] + lane * 8);
-        const uint2 d1 = *reinterpret_cast<const uint2*>(xch[par][s0 + i][1] + 512 + lane * 8);
-        const uint4 pu = {p0.x, p0.y, p1.x, p1.y}, du = {d0.x, d0.y, d1.x, d1.y};
-        __builtin_memcpy(&pb[i].v, &pu, 16);
-        __builtin_memcpy(&db[i].v, &du, 16);
+        load_frag(pb[i], (const u16*)(xch[par][s0 + i][0] + lane * 16));
+        load_frag(db[i], (const u16*)(xch[par][s0 + i][1] + lane * 16));
       }
       // A slots j < 4: rows 4 quad + j of row tile 0; j >= 4: the same rows of row tile 1
       const int trow = 4 * quad + (r16 >> 2);
@@ -430,7 +422,7 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
 
     // S = Q K^T, dP = dO V^T of row tile hf against each slot's frame, then P and dS
     // of its queries 16 hf + 4 quad + i, which are slots 4 hf + i of the pair's B
-    // fragments in xch[par] (half hf: 8 of their 16 bytes per lane)
+    // fragments in xch[par] (8 of their 16 bytes per lane)
     auto produce = [&](char* e, int par) {
       const int q0 = 16 * hf + 4 * quad;
       // the queries' key masks, lse and Delta first: they do not depend on the products
@@ -487,8 +479,8 @@ __global__ __launch_bounds__(128 * ((KT + FPG - 1) / FPG) + 64 * DKDV_LW) void k
           ds[j] = pe[j] * dp[i][j];
         }
         // bf16 (round to nearest even), two values per conversion instruction
-        *reinterpret_cast<bf16x4_t*>(xch[par][s0 + i][0] + hf * 512 + lane * 8) = __builtin_convertvector(pe, bf16x4_t);
-        *reinterpret_cast<bf16x4_t*>(xch[par][s0 + i][1] + hf * 512 + lane * 8) = __builtin_convertvector(ds, bf16x4_t);
+        *reinterpret_cast<bf16x4_t*>(xch[par][s0 + i][0] + lane * 16 + hf * 8) = __builtin_convertvector(pe, bf16x4_t);
+        *reinterpret_cast<bf16x4_t*>(xch[par][s0 + i][1] + lane * 16 + hf * 8) = __builtin_convertvector(ds, bf16x4_t);
       }
     };
 
