@@ -78,12 +78,23 @@ __device__ __forceinline__ int block_mask(const Geom& g, int kby, int kbx, int s
   return m;
 }
 
+// The (sy, sx) window starts of the bucketed queries in bucket order, so that the item
+// fill below reads them contiguously rather than gathering each query's start once per
+// item that lists it (about nine times).
+__global__ __launch_bounds__(256) void k_sorted_starts(const int* __restrict__ perm, const int4* __restrict__ starts,
+                                                       long long n, int2* __restrict__ sst) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int4 st = starts[perm[i]];
+  sst[i] = make_int2(st.y, st.z);
+}
+
 // One wave per (key block column, slice): the queries of the blob box in sort
 // order, then padding (query 0, no key of the block in its window) to whole items.
 // Each query comes with the mask of the block's keys its window holds, so the
 // dK / dV kernel tests a key with one bit extract instead of two range tests.
 __global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restrict__ cell_ptr,
-                                                     const int* __restrict__ perm, const int4* __restrict__ starts,
+                                                     const int* __restrict__ perm, const int2* __restrict__ sst,
                                                      const int* __restrict__ off, int* __restrict__ ids,
                                                      int* __restrict__ kmask) {
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
@@ -107,9 +118,9 @@ __global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restri
     const int s0 = cell_ptr[b0 * BLOB_CELLS], n = cell_ptr[(b1 + 1) * BLOB_CELLS] - s0;
     for (int j = lane; j < n; j += 64) {
       const int qid = perm[s0 + j];
-      const int4 st = starts[qid];
+      const int2 st = sst[s0 + j];
       ids[base + pos + j] = qid - tok0;
-      kmask[base + pos + j] = block_mask(g, kby, kbx, st.y, st.z);
+      kmask[base + pos + j] = block_mask(g, kby, kbx, st.x, st.y);
     }
     pos += n;
   }
@@ -560,7 +571,10 @@ hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s) {
   k_kvitem_count<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(g, p.cell_ptr, p.kv_off);
   if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.kv_off), (int)(n + 1), s, p.scan_part) != hipSuccess)
     return hipGetLastError();
-  k_kvitem_fill<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(g, p.cell_ptr, p.perm, p.starts, p.kv_off, p.kv_ids, p.kv_mask);
+  const long long nq = (long long)g.N * g.ph;
+  k_sorted_starts<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>(p.perm, p.starts, nq, p.sorted_st);
+  k_kvitem_fill<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(g, p.cell_ptr, p.perm, p.sorted_st, p.kv_off, p.kv_ids,
+                                                        p.kv_mask);
   return hipGetLastError();
 }
 

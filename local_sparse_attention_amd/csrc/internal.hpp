@@ -24,6 +24,7 @@ struct Prep {
   int* kv_off;         // [nkb * Lt + 1]: items of key block column kb, slice tau
   int* kv_ids;         // [max_kv_items * KV_Q] query tokens, KV_Q per item
   int* kv_mask;        // [max_kv_items * KV_Q] mask of the key block in each query's window
+  int2* sorted_st;     // [N * ph] (sy, sx) of the window starts in bucket order
   // query-side frame-sweeping kernels (qs_geometry() only)
   int* qt_off;         // [qs_items + 1]: row tiles of work item w are qt[qt_off[w] .. qt_off[w+1])
   int* qt;             // [max_groups * QT_INTS] row tile descriptors (see qsched.hip)

@@ -83,6 +83,7 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p) {
   q.kv_off = kv ? (int*)take(((size_t)kv_item_columns(g) * g.Lt * g.ph + 1) * 4) : nullptr;
   q.kv_ids = kv ? (int*)take(max_kv_items(g) * g.ph * KV_Q * 4) : nullptr;
   q.kv_mask = kv ? (int*)take(max_kv_items(g) * g.ph * KV_Q * sizeof(int)) : nullptr;
+  q.sorted_st = kv ? (int2*)take(N * sizeof(int2)) : nullptr;
   q.perm = q.vals[passes & 1];
   q.radix_blocks = rb;
   q.radix_passes = passes;
