@@ -207,11 +207,11 @@ int dsa3d_backward_heads(const void* q, const void* k, const void* v, const int3
 /* Workspace bytes of dsa3d_sampled_backward (backward = 1; the forward needs none and
    reports 256); 0 for an invalid geometry or one past the backward's limits
    (N * heads * kt*ky*kx < 2^31 samples, heads * (F+1)(Hp+1)(Wp+1) < 2^31 cells).
-   About 60 bytes per sample in free mode.  Box mode works on the lattice of the
+   About 61 bytes per sample in free mode.  Box mode works on the lattice of the
    L = (kt+1)(ky+1)(kx+1) grid rows that one offset's samples blend, when that lattice
    fits the kernels' LDS (4 (2L + 2 kt*ky*kx) floats <= 16384, so L <= 1024) and
-   N * heads * L < 2^31: about 40 bytes per lattice point; otherwise it works per sample
-   like free mode (about 48 bytes per sample). */
+   N * heads * L < 2^31: about 41 bytes per lattice point; otherwise it works per sample
+   like free mode (about 49 bytes per sample). */
 size_t dsa3d_sampled_workspace_bytes(int F, int Hp, int Wp, int heads, int kt, int ky, int kx, int mode,
                                      int backward);
 
@@ -289,7 +289,7 @@ int dsa3d_linear_backward(const void* x, const void* weight, const float* dy, in
    process ends.  Arguments, outputs, results and errors are those of dsa3d_forward;
    in addition it returns DSA3D_ERR_SCRATCH (nothing launched) when
    dsa3d_workspace_bytes(F, Hp, Wp, heads, kt, ky, kx, 0) exceeds
-   DSA3D_STATIC_SCRATCH_BYTES (about 84 bytes per token: N up to ~790,000).  The
+   DSA3D_STATIC_SCRATCH_BYTES (about 85 bytes per token: N up to ~790,000).  The
    work runs on the current device (`stream` must belong to it); the first call on
    a device looks up that device's copy of the array.  Every call on one GPU shares
    its array, so calls that overlap on one GPU (other streams, other host threads)

@@ -64,9 +64,8 @@ int run_forward(const void* q, const void* k, const void* v, const int32_t* offs
   Prep p;
   workspace_layout(g, false, workspace, &p);
   if (events) hipEventRecord(events[0], stream);
-  if (launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && fwd_qs_eligible(g, dtype, head_dim);
-  if (qs && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (launch_prep(offsets, g, p, qs, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   if (events) hipEventRecord(events[1], stream);
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v;
@@ -112,12 +111,12 @@ int run_backward(const void* q, const void* k, const void* v, const int32_t* off
   // when the frame-sweeping forward ran
   const bool reuse = (flags & DSA3D_FLAG_REUSE_PREP) != 0;
   if (events) hipEventRecord(events[0], stream);
-  if (!reuse && launch_prep(offsets, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   const bool kv_tube = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dkdv_tube_eligible(g, dtype, head_dim);
   const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dq_qs_eligible(g, dtype, head_dim);
   const bool sched_built = reuse && fwd_qs_eligible(g, dtype, head_dim);
+  if (!reuse && launch_prep(offsets, g, p, qs, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   if (kv_tube && launch_kv_items(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  if (qs && !sched_built && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (qs && reuse && !sched_built && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   const AttnArgs a = backward_args(q, k, v, out, lse, dout, scale, dq, dk, dv);
   // Delta = rowsum(dO * O) of every head for both kernels (the per-group dQ kernel makes
   // its own head's)

@@ -43,9 +43,9 @@ __device__ __forceinline__ void blob_span(int kb, int k, int L, int& b0, int& b1
 
 // Items (KV_Q queries) per (head block, key block column, slice): into
 // off[(hb * nkb + kb) * Lt + tau] (one head block unless the offsets are per head).
-__global__ __launch_bounds__(256) void k_kvitem_count(Geom g, const int* __restrict__ cell_ptr, int* __restrict__ off) {
+__device__ __forceinline__ void kvitem_count(const Geom& g, const int* __restrict__ cell_ptr, int* __restrict__ off,
+                                             long long i) {
   const int nkbx = (g.Wp + 3) / 4, nkb = ((g.Hp + 3) / 4) * nkbx;
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long long)nkb * g.Lt * g.ph) return;
   const int hb = (int)(i / ((long long)nkb * g.Lt));
   const long long il = i - (long long)hb * nkb * g.Lt;
@@ -78,13 +78,22 @@ __device__ __forceinline__ int block_mask(const Geom& g, int kby, int kbx, int s
   return m;
 }
 
-// The (sy, sx) window starts of the bucketed queries in bucket order, so that the item
-// fill below reads them contiguously rather than gathering each query's start once per
-// item that lists it (about nine times).
-__global__ __launch_bounds__(256) void k_sorted_starts(const int* __restrict__ perm, const int4* __restrict__ starts,
-                                                       long long n, int2* __restrict__ sst) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+// One launch for two independent passes: blocks below cblocks count the items
+// (kvitem_count), the others copy the (sy, sx) window starts of the bucketed
+// queries in bucket order (nq of them), so that the item fill below reads them
+// contiguously rather than gathering each query's start once per item that lists
+// it (about nine times).
+__global__ __launch_bounds__(256) void k_kvitem_count_starts(Geom g, const int* __restrict__ cell_ptr,
+                                                             int* __restrict__ off, unsigned cblocks,
+                                                             const int* __restrict__ perm,
+                                                             const int4* __restrict__ starts, long long nq,
+                                                             int2* __restrict__ sst) {
+  if (blockIdx.x < cblocks) {
+    kvitem_count(g, cell_ptr, off, (long long)blockIdx.x * 256 + threadIdx.x);
+    return;
+  }
+  const long long i = (long long)(blockIdx.x - cblocks) * 256 + threadIdx.x;
+  if (i >= nq) return;
   const int4 st = starts[perm[i]];
   sst[i] = make_int2(st.y, st.z);
 }
@@ -567,12 +576,12 @@ bool dkdv_tube_eligible(const Geom& g, int dtype, int D) {
 }
 
 hipError_t launch_kv_items(const Geom& g, const Prep& p, hipStream_t s) {
-  const long long n = (long long)kv_item_columns(g) * g.Lt * g.ph;
-  k_kvitem_count<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(g, p.cell_ptr, p.kv_off);
+  const long long n = (long long)kv_item_columns(g) * g.Lt * g.ph, nq = (long long)g.N * g.ph;
+  const unsigned cblocks = (unsigned)((n + 255) / 256);
+  k_kvitem_count_starts<<<cblocks + (unsigned)((nq + 255) / 256), 256, 0, s>>>(g, p.cell_ptr, p.kv_off, cblocks,
+                                                                                p.perm, p.starts, nq, p.sorted_st);
   if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.kv_off), (int)(n + 1), s, p.scan_part) != hipSuccess)
     return hipGetLastError();
-  const long long nq = (long long)g.N * g.ph;
-  k_sorted_starts<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>(p.perm, p.starts, nq, p.sorted_st);
   k_kvitem_fill<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(g, p.cell_ptr, p.perm, p.sorted_st, p.kv_off, p.kv_ids,
                                                         p.kv_mask);
   return hipGetLastError();

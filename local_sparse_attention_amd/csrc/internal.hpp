@@ -40,7 +40,8 @@ struct Prep {
   int max_groups;
 };
 
-constexpr int RADIX_TILE = 4096;
+constexpr int RADIX_TILE = 1024;
+constexpr int RADIX_RAW_NBS = 64;  // segments of at most this many radix blocks scatter from raw counts
 constexpr int SCAN_CHUNK_N = 16384;  // values one scan workgroup takes at a time
 inline size_t scan_part_words(size_t n) { return (n + SCAN_CHUNK_N - 1) / SCAN_CHUNK_N + 1; }
 
@@ -48,20 +49,28 @@ Geom make_geom(int F, int Hp, int Wp, int H, int kt, int ky, int kx);
 size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p);
 
 hipError_t launch_window_starts(const int32_t* off, const Geom& g, int32_t* starts3, hipStream_t s);
-hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, hipStream_t s);
+// The bucketing (window starts, sort, cell_ptr, groups) and, with qs, the query-side
+// work lists of the frame-sweeping kernels (launch_qsched() in one pass with it).
+hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, bool qs, hipStream_t s);
 // In-place exclusive scan of n uint32 values: one workgroup, or, given part
 // (scan_part_words(n) words of scratch) and more than a few chunks, a scan per chunk
 // on its own workgroup, a scan of the chunk totals and an add.
 hipError_t launch_scan_excl(uint32_t* data, int n, hipStream_t s, uint32_t* part = nullptr);
+// Two such scans; one launch of two workgroups when both fit one workgroup each.
+hipError_t launch_scan_excl2(uint32_t* a, int na, uint32_t* b, int nb, hipStream_t s, uint32_t* part = nullptr);
 // Stable LSD radix sort of nseg segments of seglen (key, value) pairs each, every
 // segment on its own (segment i stays at i * seglen ..), 8 bits a pass from bit 0,
 // values starting as the item index: ping-pong buffers, ghist holds
 // 256 * nseg * ceil(seglen / RADIX_TILE) words.  Returns the buffer index (0 or 1)
-// that holds the result, -1 on a launch error.
+// that holds the result, -1 on a launch error.  first_hist_done: ghist already holds
+// the first pass's raw counts (k_radix_hist's layout), which the caller may only
+// leave for segments of at most RADIX_RAW_NBS blocks.
 int radix_sort(uint32_t* keys[2], int* vals[2], uint32_t* ghist, int seglen, int nseg, int passes, hipStream_t s,
-               uint32_t* part = nullptr);
+               uint32_t* part = nullptr, bool first_hist_done = false);
 // cell_ptr[i * keyspace + c] = number of sorted keys before the first key >= c of
 // segment i (segments of seglen sorted keys), for i * keyspace + c = 0 .. nseg * keyspace.
+// Keys must be below keyspace, except in the last segment, where keys equal to keyspace
+// (a sentinel) sort after every cell and are counted by no cell.
 hipError_t launch_cell_ptr(const uint32_t* sorted_keys, int seglen, int nseg, int keyspace, int* cell_ptr,
                            hipStream_t s);
 
@@ -89,6 +98,13 @@ __host__ __device__ inline int qs_items(const Geom& g) { return g.nby * g.nbx * 
 inline size_t qs_ints(const Geom& g, int max_groups) {
   return (size_t)qs_items(g) + (size_t)max_groups * (QS_TS + g.kt + 5);
 }
+// The work lists after a bucketing: row tile counts (qt_off), then (after their scan)
+// the groups and / or row tiles, then the tile rows and the schedules.
+// (with blob_groups also the blob group counts into goff, see k_blob_ngroups)
+hipError_t launch_qtile_count(const Geom& g, const Prep& p, hipStream_t s, bool blob_groups = false);
+hipError_t launch_groups_qtiles(const Geom& g, const Prep& p, bool groups, bool qtiles, hipStream_t s);
+hipError_t launch_qsched_rows(const Geom& g, const Prep& p, hipStream_t s);
+// All of it for a bucketing built earlier.
 hipError_t launch_qsched(const Geom& g, const Prep& p, hipStream_t s);
 
 struct AttnArgs {

@@ -133,14 +133,58 @@ __global__ __launch_bounds__(256) void k_starts_keys(const int32_t* off, Geom g,
   keys[i] = (uint32_t)cell_key(g, s.x, s.y, s.z);
 }
 
+// k_starts_keys and the first radix pass's histogram in one launch, for sorts of few
+// blocks (see k_radix_hist): block x takes RADIX_TILE queries of head block
+// x / nbs, RADIX_TILE / 256 a thread, their offsets loaded before any start is formed.
+__global__ __launch_bounds__(256) void k_starts_hist(const int32_t* off, Geom g, int nbs, int4* starts,
+                                                     uint32_t* keys, uint32_t* ghist) {
+  constexpr int PER = RADIX_TILE / 256;
+  __shared__ uint32_t h[256];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  const int hb = blockIdx.x / nbs, b = blockIdx.x - hb * nbs;
+  const int lim = min(RADIX_TILE, g.N - b * RADIX_TILE);
+  const int32_t* o = off + (size_t)3 * g.N * hb;
+  int os[PER][3];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int l = tid + 256 * j;
+    const int n = b * RADIX_TILE + (l < lim ? l : 0);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) os[j][c] = o[3 * (size_t)n + c];
+  }
+  __syncthreads();
+  const int plane = g.Hp * g.Wp;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int l = tid + 256 * j;
+    if (l < lim) {
+      const int n = b * RADIX_TILE + l;
+      const int t = n / plane, rem = n - t * plane, y = rem / g.Wp, x = rem - y * g.Wp;
+      int4 st;
+      st.x = clamp_start(t, os[j][0], g.kt, g.F);
+      st.y = clamp_start(y, os[j][1], g.ky, g.Hp);
+      st.z = clamp_start(x, os[j][2], g.kx, g.Wp);
+      st.w = 0;
+      const size_t i = (size_t)hb * g.N + n;
+      const uint32_t key = (uint32_t)cell_key(g, st.x, st.y, st.z);
+      starts[i] = st;
+      keys[i] = key;
+      atomicAdd(&h[key & 255u], 1u);
+    }
+  }
+  __syncthreads();
+  ghist[((size_t)hb * 256 + tid) * nbs + b] = h[tid];
+}
+
 // ---- stable LSD radix sort (8-bit digits), by segments --------------------------
 // The items are nseg segments of seglen, each sorted on its own.  Block x owns
 // RADIX_TILE consecutive items of segment x / nbs (nbs blocks per segment).  hist:
 // per-block digit counts, stored segment-, then digit-major, so that one exclusive
 // scan over all of them gives every (segment, digit, block) its output base: the
 // counts of a segment add up to seglen, so segment i's bases start at i * seglen.
-// scatter: items are ranked in their original order (16 rounds of 256), which keeps
-// the sort stable.
+// scatter: items are ranked in their original order (RADIX_TILE / 256 rounds of 256),
+// which keeps the sort stable.
 
 __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* keys, int seglen, int nbs, int shift,
                                                     uint32_t* ghist) {
@@ -180,11 +224,9 @@ __device__ __forceinline__ void scan_load(const uint32_t* data, int n, int i0, u
 // running carry.  Otherwise workgroup b scans chunk b alone and leaves its total in
 // part[b] (k_scan_add then adds the scanned totals).
 static_assert(SCAN_CHUNK == SCAN_CHUNK_N, "scan chunk");
-__global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n, uint32_t* part) {
+__device__ __forceinline__ void scan_range(uint32_t* data, int start, int end, uint32_t* part_slot) {
   __shared__ uint32_t wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int start = part ? blockIdx.x * SCAN_CHUNK : 0;
-  const int end = part ? min(start + SCAN_CHUNK, n) : n;
   uint32_t carry = 0;
   uint32_t v[SCAN_PER], nx[SCAN_PER];
   scan_load(data, end, start + SCAN_PER * tid, nx);
@@ -232,7 +274,18 @@ __global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n, uint3
     carry += total;
     __syncthreads();  // wsum is rewritten by the next chunk
   }
-  if (part && tid == 0) part[blockIdx.x] = carry;
+  if (part_slot && tid == 0) *part_slot = carry;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_excl(uint32_t* data, int n, uint32_t* part) {
+  const int start = part ? blockIdx.x * SCAN_CHUNK : 0;
+  scan_range(data, start, part ? min(start + SCAN_CHUNK, n) : n, part ? part + blockIdx.x : nullptr);
+}
+
+// Two independent single-workgroup scans in one launch: block 0 scans a, block 1 b.
+__global__ __launch_bounds__(1024) void k_scan_excl2(uint32_t* a, int na, uint32_t* b, int nb) {
+  if (blockIdx.x == 0) scan_range(a, 0, na, nullptr);
+  else scan_range(b, 0, nb, nullptr);
 }
 
 __global__ __launch_bounds__(256) void k_scan_add(uint32_t* data, int n, const uint32_t* part) {
@@ -241,13 +294,41 @@ __global__ __launch_bounds__(256) void k_scan_add(uint32_t* data, int n, const u
   if (i < n) data[i] += part[b];
 }
 
+// gbase holds the scanned counts, or (raw) the counts k_radix_hist left: then each
+// block forms its own bases from its segment's nbs counts per digit, the counts of the
+// smaller digits in every block of the segment plus those of its digit in the blocks
+// before it (the same values the scan gives, without its launches).
 __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* kin, const int* vin, int seglen, int nbs,
-                                                       int shift, const uint32_t* gbase, uint32_t* kout, int* vout) {
+                                                       int shift, const uint32_t* gbase, int raw, uint32_t* kout,
+                                                       int* vout) {
   __shared__ uint32_t base[256], run[256];
   __shared__ uint32_t wcnt[4][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sg = blockIdx.x / nbs, b = blockIdx.x - sg * nbs;
-  base[tid] = gbase[((size_t)sg * 256 + tid) * nbs + b];
+  if (raw) {
+    const uint32_t* hc = gbase + ((size_t)sg * 256 + tid) * nbs;
+    uint32_t tot = 0, pre = 0;
+    for (int j = 0; j < nbs; ++j) {
+      const uint32_t c = hc[j];
+      pre += j < b ? c : 0u;
+      tot += c;
+    }
+    uint32_t inc = tot;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += y;
+    }
+    if (lane == 63) run[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) before += w < wave ? run[w] : 0u;
+    __syncthreads();  // run is cleared below
+    base[tid] = (uint32_t)sg * (uint32_t)seglen + before + inc - tot + pre;
+  } else {
+    base[tid] = gbase[((size_t)sg * 256 + tid) * nbs + b];
+  }
   run[tid] = 0;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r = 0; r < RADIX_TILE / 256; ++r) {
@@ -291,38 +372,34 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* kin, cons
 }
 
 // cell_ptr[i keyspace + c]: position of the first key >= c of segment i (the end of
-// the segment when there is none), for i keyspace + c = 0 .. nseg keyspace.
+// the segment when there is none), for i keyspace + c = 0 .. nseg keyspace.  Thread
+// j = 0 .. seglen of segment i writes the cells c with key[j - 1] < c <= key[j]
+// (from cell 0 for j = 0, to the segment's last entry for j = seglen): exactly j keys
+// of the segment lie below each of them, and every entry is written once.  The last
+// entry of a segment is its own c = keyspace only in the last segment (elsewhere it
+// is the next segment's c = 0); keys equal to keyspace (a sentinel sorted after every
+// cell) are allowed there.
 __global__ __launch_bounds__(256) void k_cell_ptr(const uint32_t* skeys, int seglen, int nseg, int keyspace,
                                                   int* cell_ptr) {
-  const long long cc = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (cc > (long long)nseg * keyspace) return;
-  const int sg = cc == (long long)nseg * keyspace ? nseg - 1 : (int)(cc / keyspace);
-  const int c = (int)(cc - (long long)sg * keyspace);  // keyspace for the very last entry
-  int lo = sg * seglen, hi = lo + seglen;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (skeys[mid] < (uint32_t)c) lo = mid + 1; else hi = mid;
-  }
-  cell_ptr[cc] = lo;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long long)nseg * (seglen + 1)) return;
+  const int sg = (int)(t / (seglen + 1)), j = (int)(t - (long long)sg * (seglen + 1));
+  const uint32_t* k = skeys + (size_t)sg * seglen;
+  const int lo = j > 0 ? (int)k[j - 1] + 1 : 0;
+  const int fin = sg == nseg - 1 ? keyspace : keyspace - 1;  // the segment's last entry
+  const int hi = j < seglen ? min((int)k[j], fin) : fin;
+  int* cp = cell_ptr + (size_t)sg * keyspace;
+  const int v = sg * seglen + j;
+  for (int c = lo; c <= hi; ++c) cp[c] = v;
 }
 
+// Group counts of the blobs (up to GROUP_Q queries each) from cell_ptr, into goff
+// (goff[nblobs] = 0), for an exclusive scan.
 __global__ __launch_bounds__(256) void k_blob_ngroups(const int* cell_ptr, int nblobs, int* goff) {
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b > nblobs) return;
-  if (b == nblobs) { goff[b] = 0; return; }
-  const int cnt = cell_ptr[(b + 1) * BLOB_CELLS] - cell_ptr[b * BLOB_CELLS];
+  const int cnt = b == nblobs ? 0 : cell_ptr[(b + 1) * BLOB_CELLS] - cell_ptr[b * BLOB_CELLS];
   goff[b] = (cnt + GROUP_Q - 1) / GROUP_Q;
-}
-
-__global__ __launch_bounds__(256) void k_groups(const int* cell_ptr, const int* goff, int nblobs, int2* groups,
-                                                int* ngroups) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b == 0) *ngroups = goff[nblobs];
-  if (b >= nblobs) return;
-  const int beg = cell_ptr[b * BLOB_CELLS];
-  const int cnt = cell_ptr[(b + 1) * BLOB_CELLS] - beg;
-  const int g0 = goff[b], ng = goff[b + 1] - g0;
-  for (int i = 0; i < ng; ++i) groups[g0 + i] = make_int2(beg + i * GROUP_Q, min(GROUP_Q, cnt - i * GROUP_Q));
 }
 
 static unsigned blocks(long long n, int per) { return (unsigned)((n + per - 1) / per); }
@@ -339,19 +416,29 @@ hipError_t launch_scan_excl(uint32_t* data, int n, hipStream_t s, uint32_t* part
   return hipGetLastError();
 }
 
+hipError_t launch_scan_excl2(uint32_t* a, int na, uint32_t* b, int nb, hipStream_t s, uint32_t* part) {
+  if (na <= 4 * SCAN_CHUNK && nb <= 4 * SCAN_CHUNK) {
+    k_scan_excl2<<<2, 1024, 0, s>>>(a, na, b, nb);
+    return hipGetLastError();
+  }
+  const hipError_t e = launch_scan_excl(a, na, s, part);
+  return e != hipSuccess ? e : launch_scan_excl(b, nb, s, part);
+}
+
 hipError_t launch_window_starts(const int32_t* off, const Geom& g, int32_t* starts3, hipStream_t s) {
   k_window_starts<<<blocks(g.N, 256), 256, 0, s>>>(off, g, starts3);
   return hipGetLastError();
 }
 
 int radix_sort(uint32_t* keys[2], int* vals[2], uint32_t* ghist, int seglen, int nseg, int passes, hipStream_t s,
-               uint32_t* part) {
+               uint32_t* part, bool first_hist_done) {
   const int nbs = (seglen + RADIX_TILE - 1) / RADIX_TILE, nb = nbs * nseg;
+  const int raw = nbs <= RADIX_RAW_NBS;
   int cur = 0;
   for (int pass = 0; pass < passes; ++pass) {
-    k_radix_hist<<<nb, 256, 0, s>>>(keys[cur], seglen, nbs, 8 * pass, ghist);
-    if (launch_scan_excl(ghist, 256 * nb, s, part) != hipSuccess) return -1;
-    k_radix_scatter<<<nb, 256, 0, s>>>(keys[cur], pass == 0 ? nullptr : vals[cur], seglen, nbs, 8 * pass, ghist,
+    if (pass > 0 || !first_hist_done) k_radix_hist<<<nb, 256, 0, s>>>(keys[cur], seglen, nbs, 8 * pass, ghist);
+    if (!raw && launch_scan_excl(ghist, 256 * nb, s, part) != hipSuccess) return -1;
+    k_radix_scatter<<<nb, 256, 0, s>>>(keys[cur], pass == 0 ? nullptr : vals[cur], seglen, nbs, 8 * pass, ghist, raw,
                                        keys[cur ^ 1], vals[cur ^ 1]);
     cur ^= 1;
   }
@@ -360,24 +447,42 @@ int radix_sort(uint32_t* keys[2], int* vals[2], uint32_t* ghist, int seglen, int
 
 hipError_t launch_cell_ptr(const uint32_t* sorted_keys, int seglen, int nseg, int keyspace, int* cell_ptr,
                            hipStream_t s) {
-  k_cell_ptr<<<blocks((long long)keyspace * nseg + 1, 256), 256, 0, s>>>(sorted_keys, seglen, nseg, keyspace,
+  k_cell_ptr<<<blocks((long long)nseg * (seglen + 1), 256), 256, 0, s>>>(sorted_keys, seglen, nseg, keyspace,
                                                                           cell_ptr);
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, hipStream_t s) {
+// Bucketing, and with qs the query-side work lists too:
+//   window starts and keys (with the first radix pass's histogram for small sorts),
+//   the radix passes, cell_ptr, the blob group counts [with the row tile counts],
+//   the scans of the group [and tile] counts, the groups [and row tiles],
+//   [the tile rows and the schedules].
+hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, bool qs, hipStream_t s) {
   const int n = g.N * g.ph, nblobs = g.nblobs * g.ph;
-  k_starts_keys<<<blocks(n, 256), 256, 0, s>>>(off, g, p.starts, p.keys[0]);
+  const int nbs = (g.N + RADIX_TILE - 1) / RADIX_TILE;
+  const bool fused = nbs <= RADIX_RAW_NBS;  // the scatter then needs the raw counts the fused kernel leaves
+  if (fused)
+    k_starts_hist<<<(unsigned)(nbs * g.ph), 256, 0, s>>>(off, g, nbs, p.starts, p.keys[0], p.ghist);
+  else
+    k_starts_keys<<<blocks(n, 256), 256, 0, s>>>(off, g, p.starts, p.keys[0]);
   // each head block of the bucketing is a segment of its own
-  const int cur = radix_sort(p.keys, p.vals, p.ghist, g.N, g.ph, p.radix_passes, s, p.scan_part);
+  const int cur = radix_sort(p.keys, p.vals, p.ghist, g.N, g.ph, p.radix_passes, s, p.scan_part, fused);
   if (cur < 0) return hipErrorLaunchFailure;
   // p.perm was set to vals[passes & 1] == vals[cur]
   if (launch_cell_ptr(p.keys[cur], g.N, g.ph, g.keyspace, p.cell_ptr, s) != hipSuccess) return hipGetLastError();
-  k_blob_ngroups<<<blocks((long long)nblobs + 1, 256), 256, 0, s>>>(p.cell_ptr, nblobs, p.goff);
-  if (launch_scan_excl(reinterpret_cast<uint32_t*>(p.goff), nblobs + 1, s, p.scan_part) != hipSuccess)
-    return hipGetLastError();
-  k_groups<<<blocks(nblobs > 0 ? nblobs : 1, 256), 256, 0, s>>>(p.cell_ptr, p.goff, nblobs, p.groups, p.ngroups);
-  return hipGetLastError();
+  hipError_t e;
+  if (qs) {
+    // the blob group counts ride along with the row tile counts
+    if ((e = launch_qtile_count(g, p, s, true)) != hipSuccess) return e;
+    e = launch_scan_excl2(reinterpret_cast<uint32_t*>(p.goff), nblobs + 1, reinterpret_cast<uint32_t*>(p.qt_off),
+                          qs_items(g) * g.ph + 1, s, p.scan_part);
+  } else {
+    k_blob_ngroups<<<blocks((long long)nblobs + 1, 256), 256, 0, s>>>(p.cell_ptr, nblobs, p.goff);
+    e = launch_scan_excl(reinterpret_cast<uint32_t*>(p.goff), nblobs + 1, s, p.scan_part);
+  }
+  if (e != hipSuccess) return e;
+  if ((e = launch_groups_qtiles(g, p, true, qs, s)) != hipSuccess) return e;
+  return qs ? launch_qsched_rows(g, p, s) : hipSuccess;
 }
 
 }  // namespace dsa3d

@@ -240,12 +240,12 @@ def test_sampled_validation(lib):
     assert ws(4, 8, 8, 2, 2, 3, 3, 1, 1) == 0
     assert ws(4, 8, 8, 2, 3, 3, 3, 5, 1) == 0
     # box windows whose lattice of corner rows, (kt+1)(ky+1)(kx+1), fits the kernels' LDS
-    # work per lattice point (~40 bytes each); past it (5 x 15 x 15: 1536 points) per
-    # sample like free windows (~48 bytes a sample in box mode)
+    # work per lattice point (~41 bytes each); past it (5 x 15 x 15: 1536 points) per
+    # sample like free windows (~49 bytes a sample in box mode)
     NHL = 16 * 32 * 32 * 8 * 4 * 8 * 8
-    assert 40 * NHL <= ws(16, 32, 32, 8, 3, 7, 7, 0, 1) <= 41 * NHL
+    assert 40 * NHL <= ws(16, 32, 32, 8, 3, 7, 7, 0, 1) <= 42 * NHL
     NHK = 6 * 16 * 17 * 225 * 5
-    assert 48 * NHK <= ws(6, 16, 17, 1, 5, 15, 15, 0, 1) <= 49 * NHK
+    assert 48 * NHK <= ws(6, 16, 17, 1, 5, 15, 15, 0, 1) <= 50 * NHK
 
 
 def test_sampled_backward_validation(lib):
