@@ -92,6 +92,9 @@ LIN_CASES = [
     (1000, 256, 3 * 27 * 2, "bf16"),
     (257, 40, 130, "f32"),
     (129, 12, 7, "bf16"),        # K not a multiple of 8: element-wise loads
+    (5000, 72, 260, "bf16"),     # 256-column blocks with a ragged edge; dW with K split in 4 parts
+    (300, 520, 600, "bf16"),     # 256-column blocks for y and dx, K = 600 and 520 (ragged K steps)
+    (4500, 300, 40, "f32"),      # fp32 dW with K split in 4 parts (the last one shorter)
 ]
 
 
