@@ -16,6 +16,7 @@
 // sums of db; k_transpose the copies of W and x); db's column sums add in a fixed order.
 #include "dsa3d.h"
 #include "internal.hpp"
+#include "tube.hpp"
 
 namespace dsa3d {
 
@@ -86,6 +87,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  float bcol[WN];
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const int col = n0 + wn * 32 * WN + j * 32 + (lane & 31);
+    bcol[j] = bias && col < N ? bias[col] : 0.f;
+  }
 
   uint4 ra[NCA], rb[NCB];
   auto fetch = [&](int k0) {
@@ -162,6 +170,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][s], bv[j][s], acc[i][j], 0, 0, 0);
     }
   }
+  // every load done (a wait the compiler sees, so that it adds none before each of the
+  // conditional stores below, which would make each store wait for the one before it)
+  __builtin_amdgcn_s_waitcnt(0);
   // result: lane l holds column l % 32 and rows 8 (r / 4) + 4 (l / 32) + r % 4 of each tile
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -169,11 +180,135 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int j = 0; j < WN; ++j) {
       const int col = n0 + wn * 32 * WN + j * 32 + (lane & 31);
       if (col >= N) continue;
-      const float b = bias ? bias[col] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (row < M) C[(size_t)row * N + col] = cvt_out<OutT>(acc[i][j][r] + b);
+        if (row < M) C[(size_t)row * N + col] = cvt_out<OutT>(acc[i][j][r] + bcol[j]);
+      }
+    }
+}
+
+// Pipelined form for bf16 with K a multiple of 8 (rows of 16-byte chunks): 128 x 256
+// blocks, 64-deep K steps in a ring of RING_ST LDS stages filled by direct global->LDS
+// loads two steps ahead (each wave issues 12 per stage: 8 rows of 128 bytes a load, rows
+// swizzled as sw() so that the 16-byte fragment reads do not collide on LDS banks),
+// four waves of 64 x 128 as 2 x 4 tiles of v_mfma_f32_32x32x16_bf16.  Chunks outside
+// the matrix (rows past M or N, columns past K) load 16 zero bytes from zero16, so every
+// stage holds zeros there and every wave issues the same number of loads.
+constexpr int RING_ST = 3, RK = 64, RBN = 256, RING_GY = 8;
+constexpr int RING_STAGE = (GB + RBN) * RK * 2;  // bytes: A rows, then B rows
+static __device__ __attribute__((aligned(16))) uint4 zero16[1];
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void k_gemm_ring(const u16* __restrict__ A, const u16* __restrict__ B,
+                                                   const float* __restrict__ bias, OutT* __restrict__ C, int M,
+                                                   int N, int Kfull, int kc) {
+  __shared__ __attribute__((aligned(1024))) char ring[RING_ST][RING_STAGE];
+  const size_t ld = (size_t)Kfull;
+  const int kbeg = blockIdx.z * kc, K = min(kc, Kfull - kbeg);
+  A += kbeg;
+  B += kbeg;
+  C += (size_t)blockIdx.z * M * N;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  // block order: each XCD takes a contiguous range of blocks (xcd_remap), walked in
+  // groups of RING_GY block rows with the column index outer, so the A rows and B
+  // columns of the blocks in flight on one XCD stay in its L2
+  const int nbx = (N + RBN - 1) / RBN, nby = (M + GB - 1) / GB;
+  const int L = xcd_remap(blockIdx.x, nbx * nby);
+  const int g0 = (L / (RING_GY * nbx)) * RING_GY, gy = min(RING_GY, nby - g0);
+  const int rr = L - g0 * nbx;
+  const int m0 = (g0 + rr % gy) * GB, n0 = (rr / gy) * RBN;
+  const int nk = (K + RK - 1) / RK;
+  // this wave's 12 loads of a stage: load i covers stage rows 8 (4 i + wave) .. + 7
+  // (rows 0-127 are A's, 128-383 B's); lane l takes row + l / 8, physical chunk l % 8,
+  // which holds logical chunk (l % 8) ^ (row & 7)
+  // kmax[i]: the load's chunks are inside the matrix for K steps kt with kt RK < kmax[i]
+  // (0 for rows past the edge); src[i] points at row 0 then, never read.
+  const u16* src[12];
+  int kmax[12];
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    const int r = 8 * (4 * i + wave) + (lane >> 3);  // i < 4: A's rows (wave-uniform)
+    const int c = ((lane & 7) ^ r) & 7;
+    const int grow = i < 4 ? m0 + r : n0 + (r - GB);
+    const bool rin = grow < (i < 4 ? M : N);
+    src[i] = (i < 4 ? A : B) + (rin ? (size_t)grow * ld : 0) + c * 8;
+    kmax[i] = rin ? K - c * 8 : 0;
+  }
+  // loads i0 .. i1 - 1 of stage kt
+  auto issue = [&](int kt, int i0, int i1) {
+    char* st = ring[kt % RING_ST];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      if (i < i0 || i >= i1) continue;
+      const bool ok = kt * RK < kmax[i];
+      const uintptr_t g = ok ? reinterpret_cast<uintptr_t>(src[i] + (size_t)kt * RK)
+                             : reinterpret_cast<uintptr_t>(&zero16[0]);
+      dma16(reinterpret_cast<const void*>(g), st + 1024 * (4 * i + wave));
+    }
+  };
+  float bcol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+    bcol[j] = bias && col < N ? bias[col] : 0.f;
+  }
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < RING_ST - 1; ++s) issue(s, 0, 12);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt_c<(RING_ST - 2) * 12>();  // this wave's loads of stage kt have landed
+    lds_barrier();                       // everyone's have, and stage kt - 1 is read
+    typedef __attribute__((address_space(3))) char lds_char;
+    const lds_char* st = (const lds_char*)ring[kt % RING_ST];
+#pragma unroll
+    for (int ks = 0; ks < RK / 16; ++ks) {
+      // a quarter of stage kt + 2's loads (into the slot of stage kt - 1) before each
+      // 16-deep step, so that the CU's load issue spreads over the stage
+      issue(kt + RING_ST - 1, 3 * ks, 3 * ks + 3);
+      const int cb = (2 * ks + (lane >> 5)) * 16;  // logical byte of this lane's 16 bytes
+      bf16x8_t af[2], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + (lane & 31);
+        af[i] = *(const __attribute__((address_space(3))) bf16x8_t*)(st + sw(r, cb));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = GB + wn * 128 + j * 32 + (lane & 31);
+        bfr[j] = *(const __attribute__((address_space(3))) bf16x8_t*)(st + sw(r, cb));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // the zero loads of the last stages and the bias values: a wait the compiler sees, so
+  // that it adds none before each of the conditional stores below
+  __builtin_amdgcn_s_waitcnt(0);
+  // result: lane l holds column l % 32 and rows 8 (r / 4) + 4 (l / 32) + r % 4 of each tile
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (row < M) C[(size_t)row * N + col] = cvt_out<OutT>(acc[i][j][r] + bcol[j]);
       }
     }
 }
@@ -281,10 +416,22 @@ static int splitk_parts(int M, int N, int K) {
 }
 static int splitk_chunk(int K, int parts) { return ((K + parts - 1) / parts + GK - 1) / GK * GK; }
 
+// The pipelined bf16 form loads whole 16-byte chunks: rows of K elements must start on
+// 16 bytes.
+template <typename T>
+static bool Kfull_ok(int K, const T* A, const T* B) {
+  return K % 8 == 0 && ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15u) == 0;
+}
+
 template <typename T, typename OutT>
 static void launch_gemm(const T* A, const T* B, const float* bias, OutT* C, int M, int N, int K, int kc, int layers,
                         hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
+    if (N >= RBN && Kfull_ok(K, A, B)) {
+      k_gemm_ring<OutT><<<dim3(((N + RBN - 1) / RBN) * ((M + GB - 1) / GB), 1, layers), 256, 0, s>>>(A, B, bias, C, M,
+                                                                                                       N, K, kc);
+      return;
+    }
     if (gemm_wn<T>(N) == 4) {
       k_gemm_nt<T, OutT, 4><<<dim3((N + 255) / 256, (M + GB - 1) / GB, layers), 256, 0, s>>>(A, B, bias, C, M, N, K,
                                                                                              kc);
