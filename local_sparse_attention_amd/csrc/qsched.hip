@@ -226,20 +226,22 @@ __device__ int build_schedule(const Geom& g, int w, int t0, int ntiles, const Ti
 
 // The same schedule for an item of at most 128 tiles, held in registers: tile t's
 // first / last slice in lane t mod 64 of ta / tb [t / 64] (read back with readlane),
-// the tiles already scheduled in two 64-bit masks, a pass's frames (fewer than 64:
+// the slots' first free frames in lanes 0-7 of one register (the choice of slot by a
+// DPP minimum), the tiles already scheduled in two 64-bit masks, a pass's frames (fewer than 64:
 // QS_TS + kt - 1) and tile entries (at most QS_MAXT = 64) collected one per lane
 // (lane i keeps the i-th) and stored at the pass's end by one vector store each.  Tiles are
 // visited in order; once a tile finds no free slot, the rest of its slice waits for
 // the next pass, as above.
 static_assert(QS_MAXT <= 64 && QS_TS + 16 - 1 < 64, "one lane per frame and per tile entry");
+static_assert(QS_SLOTS == 8, "the slots' free frames sit in lanes 0-7 (one half row for DPP)");
 __device__ int build_schedule_regs(const Geom& g, int t0, int ntiles, int ta0, int tb0, int ta1, int tb1, int* out,
                                    int lane) {
+  constexpr int NOSLOT = 0x7fffffff;  // above every frame number
   uint64_t done0 = 0, done1 = 0;
   int size = 1, npass = 0;
   for (;;) {
-    int free_at[QS_SLOTS];
-#pragma unroll
-    for (int s = 0; s < QS_SLOTS; ++s) free_at[s] = -(1 << 29);
+    // slot s's first free frame in lane s (lanes past the slots: NOSLOT)
+    int fa = lane < QS_SLOTS ? -(1 << 29) : NOSLOT;
     int nf = 0, nt = 0, fmax = -1, blocked = -(1 << 30);
     int fr = 0, e0 = 0, e1 = 0, e2 = 0, e3 = 0;
     for (int t = 0; t < ntiles && nt < QS_MAXT; ++t) {
@@ -248,17 +250,20 @@ __device__ int build_schedule_regs(const Geom& g, int t0, int ntiles, int ta0, i
       if (((hi ? done1 : done0) >> bit) & 1) continue;
       const int tau = __builtin_amdgcn_readlane(hi ? ta1 : ta0, bit);
       if (tau == blocked) continue;
-      int best = -1, bestv = 0;
-#pragma unroll
-      for (int s = 0; s < QS_SLOTS; ++s)
-        if (free_at[s] <= tau && (best < 0 || free_at[s] < bestv)) {
-          best = s;
-          bestv = free_at[s];
-        }
-      if (best < 0) {
+      // the free slot that has been free the longest (the lowest such slot on a tie):
+      // the minimum over lanes 0-7 by DPP (within quads, then across the two quads of
+      // the half row), then the first lane that holds it
+      const int cand = fa <= tau ? fa : NOSLOT;
+      int m = cand;
+      m = min(m, __builtin_amdgcn_update_dpp(NOSLOT, m, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+      m = min(m, __builtin_amdgcn_update_dpp(NOSLOT, m, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+      m = min(m, __builtin_amdgcn_update_dpp(NOSLOT, m, 0x141, 0xF, 0xF, false));  // row_half_mirror
+      const int mn = __builtin_amdgcn_readlane(m, 0);
+      if (mn == NOSLOT) {
         blocked = tau;
         continue;
       }
+      const int best = __builtin_ctzll(__ballot(lane < QS_SLOTS && cand == mn));
       const int tlast = __builtin_amdgcn_readlane(hi ? tb1 : tb0, bit);
       const int fi = tau > fmax ? nf : nf - 1 - (fmax - tau);
       for (int f = max(tau, fmax + 1); f < tlast + g.kt; ++f, ++nf) fr = lane == nf ? f : fr;
@@ -269,9 +274,7 @@ __device__ int build_schedule_regs(const Geom& g, int t0, int ntiles, int ta0, i
       e2 = mine ? best : e2;
       e3 = mine ? fi : e3;
       ++nt;
-#pragma unroll
-      for (int s = 0; s < QS_SLOTS; ++s)
-        if (s == best) free_at[s] = tlast + g.kt;
+      fa = lane == best ? tlast + g.kt : fa;
       if (hi) done1 |= 1ull << bit;
       else done0 |= 1ull << bit;
     }
