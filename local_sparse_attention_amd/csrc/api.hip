@@ -63,17 +63,17 @@ int run_forward(const void* q, const void* k, const void* v, const int32_t* offs
                 const hipEvent_t* events) {
   Prep p;
   workspace_layout(g, false, workspace, &p);
-  if (events) hipEventRecord(events[0], stream);
+  if (events) (void)hipEventRecord(events[0], stream);
   const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && fwd_qs_eligible(g, dtype, head_dim);
   if (launch_prep(offsets, g, p, qs, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  if (events) hipEventRecord(events[1], stream);
+  if (events) (void)hipEventRecord(events[1], stream);
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v;
   a.out = out; a.lse_out = lse;
   a.scale = scale;
   const hipError_t e = qs ? launch_forward_qs(head_dim, a, g, p, stream)
                           : launch_forward_v1(dtype, head_dim, a, g, p, stream);
-  if (events) hipEventRecord(events[2], stream);
+  if (events) (void)hipEventRecord(events[2], stream);
   return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
 
@@ -110,7 +110,7 @@ int run_backward(const void* q, const void* k, const void* v, const int32_t* off
   // offsets and geometry: the window starts and buckets always, the query-side schedules
   // when the frame-sweeping forward ran
   const bool reuse = (flags & DSA3D_FLAG_REUSE_PREP) != 0;
-  if (events) hipEventRecord(events[0], stream);
+  if (events) (void)hipEventRecord(events[0], stream);
   const bool kv_tube = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dkdv_tube_eligible(g, dtype, head_dim);
   const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dq_qs_eligible(g, dtype, head_dim);
   const bool sched_built = reuse && fwd_qs_eligible(g, dtype, head_dim);
@@ -121,14 +121,14 @@ int run_backward(const void* q, const void* k, const void* v, const int32_t* off
   // Delta = rowsum(dO * O) of every head for both kernels (the per-group dQ kernel makes
   // its own head's)
   if (qs && !delta_ready && launch_delta(head_dim, a, g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  if (events) hipEventRecord(events[1], stream);
+  if (events) (void)hipEventRecord(events[1], stream);
   if (qs ? launch_dq_qs(head_dim, a, g, p, stream) != hipSuccess
          : launch_backward_dq_v1(dtype, head_dim, a, g, p, stream) != hipSuccess)
     return DSA3D_ERR_LAUNCH;
-  if (events) hipEventRecord(events[2], stream);
+  if (events) (void)hipEventRecord(events[2], stream);
   const hipError_t e = kv_tube ? launch_dkdv_tube(head_dim, a, g, p, stream)
                                : launch_backward_dkdv_v1(dtype, head_dim, a, g, p, stream);
-  if (events) hipEventRecord(events[3], stream);
+  if (events) (void)hipEventRecord(events[3], stream);
   return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_LAUNCH;
 }
 

@@ -121,14 +121,35 @@ __global__ __launch_bounds__(256) void k_kvitem_fill(Geom g, const int* __restri
   blob_span(kbx, g.kx, g.Lx, bx0, bx1);
   const size_t base = (size_t)off[i] * KV_Q;
   const int total = (off[i + 1] - off[i]) * KV_Q;
-  int pos = 0;
-  for (int by = by0; by <= by1; ++by) {
+  // The ranges of the blob rows first, their loads all in flight together, then one
+  // pass of the lanes over the rows' queries in order: two dependent gathers per
+  // wave instead of two per row.  A window up to 9 wide reaches at most three blob
+  // rows (cells 4 kb - k + 1 .. 4 kb + 3); rows beyond that take the loop after.
+  constexpr int MR = 3;
+  int s0[MR], cnt[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    s0[r] = cnt[r] = 0;
+    if (by0 + r <= by1) {
+      const int row = tau * g.nby + by0 + r;
+      s0[r] = cell_ptr[(row * g.nbx + bx0) * BLOB_CELLS];
+      cnt[r] = cell_ptr[(row * g.nbx + bx1 + 1) * BLOB_CELLS] - s0[r];
+    }
+  }
+  const int c01 = cnt[0] + cnt[1];
+  int pos = c01 + cnt[2];
+  for (int j = lane; j < pos; j += 64) {
+    const int src = j < cnt[0] ? s0[0] + j : j < c01 ? s0[1] + (j - cnt[0]) : s0[2] + (j - c01);
+    const int2 st = sst[src];
+    ids[base + j] = perm[src] - tok0;
+    kmask[base + j] = block_mask(g, kby, kbx, st.x, st.y);
+  }
+  for (int by = by0 + MR; by <= by1; ++by) {
     const int b0 = (tau * g.nby + by) * g.nbx + bx0, b1 = (tau * g.nby + by) * g.nbx + bx1;
-    const int s0 = cell_ptr[b0 * BLOB_CELLS], n = cell_ptr[(b1 + 1) * BLOB_CELLS] - s0;
+    const int sr = cell_ptr[b0 * BLOB_CELLS], n = cell_ptr[(b1 + 1) * BLOB_CELLS] - sr;
     for (int j = lane; j < n; j += 64) {
-      const int qid = perm[s0 + j];
-      const int2 st = sst[s0 + j];
-      ids[base + pos + j] = qid - tok0;
+      const int2 st = sst[sr + j];
+      ids[base + pos + j] = perm[sr + j] - tok0;
       kmask[base + pos + j] = block_mask(g, kby, kbx, st.x, st.y);
     }
     pos += n;
