@@ -344,10 +344,8 @@ def _ptr_or_none(t, name, dev):
     return None if t is None else _dev(t, name, dev)
 
 
-def dwconv3d_forward(x, weight, bias, grid, out=None, accumulate=False):
-    """Depthwise 3-D convolution of x [N, C] (float32 or bfloat16) with weight float32
-    [C, ct, cy, cx] and bias float32 [C] or None.  accumulate=True adds into `out` (e.g.
-    the attention output seen as [N, C]); otherwise `out` (or a new tensor) is overwritten."""
+def _conv_shape(x, weight, grid):
+    """(N, C) of x [N, C] on the grid, with weight float32 [C, ct, cy, cx]."""
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise DSA3DError("x must be a [N, C] tensor")
     N, C = x.shape
@@ -356,6 +354,14 @@ def dwconv3d_forward(x, weight, bias, grid, out=None, accumulate=False):
     if not isinstance(weight, torch.Tensor) or weight.dim() != 4 or weight.shape[0] != C:
         raise DSA3DError("weight must be float32 [C, ct, cy, cx]")
     _want(weight, "weight", weight.shape, torch.float32)
+    return N, C
+
+
+def dwconv3d_forward(x, weight, bias, grid, out=None, accumulate=False):
+    """Depthwise 3-D convolution of x [N, C] (float32 or bfloat16) with weight float32
+    [C, ct, cy, cx] and bias float32 [C] or None.  accumulate=True adds into `out` (e.g.
+    the attention output seen as [N, C]); otherwise `out` (or a new tensor) is overwritten."""
+    N, C = _conv_shape(x, weight, grid)
     if bias is not None:
         _want(bias, "bias", (C,), torch.float32)
     if accumulate and out is None:
@@ -373,9 +379,8 @@ def dwconv3d_forward(x, weight, bias, grid, out=None, accumulate=False):
 
 def dwconv3d_backward(x, weight, dy, grid, need_bias=True):
     """Returns (dx [N, C] in x's dtype, dweight float32 like weight, dbias float32 [C] or None)."""
-    N, C = x.shape
+    N, C = _conv_shape(x, weight, grid)
     _want(dy, "dy", x.shape, x.dtype)
-    _want(weight, "weight", weight.shape, torch.float32)
     dev = x.device
     ct, cy, cx = weight.shape[1:]
     dx = torch.empty_like(x)
@@ -410,6 +415,8 @@ def linear_forward(x, weight, bias=None):
 
 def linear_backward(x, weight, dy, need_bias=True):
     """Returns (dx [M, K] in x's dtype, dweight float32 [O, K], dbias float32 [O] or None)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise DSA3DError("x must be [M, K] and weight [O, K]")
     M, K = x.shape
     O = weight.shape[0]
     _want(weight, "weight", (O, K), x.dtype)

@@ -313,3 +313,36 @@ def test_dwconv_and_linear_validation(lib):
     okb = [P, P, P, 100, 64, 81, 1, P, P, P, P, 1 << 40, None]
     bad = list(okb); bad[11] = 1
     assert lb(*bad) == ERR_WORKSPACE
+
+
+def test_dwconv_and_linear_binding_checks_shapes(lib):
+    """The binding checks the token count, channel count and dtypes of the convolution and
+    linear calls before any pointer reaches the library: the C calls take sizes, not
+    tensors, so a mismatch would otherwise be read or written as raw memory."""
+    import torch
+
+    E = dsa3d.DSA3DError
+    grid = (4, 8, 8)
+    x = torch.zeros(256, 64)
+    w = torch.zeros(64, 3, 3, 3)
+    with pytest.raises(E, match="tokens"):
+        dsa3d.dwconv3d_backward(x, w, x, (4, 8, 9))
+    with pytest.raises(E, match="weight must be"):
+        dsa3d.dwconv3d_backward(x, w[:32], x, grid)
+    with pytest.raises(E, match="weight must be"):
+        dsa3d.dwconv3d_backward(x, w[:, 0], x, grid)
+    with pytest.raises(E, match="weight has dtype"):
+        dsa3d.dwconv3d_backward(x, w.double(), x, grid)
+    with pytest.raises(E, match="x must be"):
+        dsa3d.dwconv3d_backward(x[None], w, x, grid)
+    with pytest.raises(E, match="dy has shape"):
+        dsa3d.dwconv3d_backward(x, w, x[:100], grid)
+    with pytest.raises(E, match="tokens"):
+        dsa3d.dwconv3d_forward(x[:100], w, None, grid)
+    with pytest.raises(E, match="x must be"):
+        dsa3d.linear_backward(x[None], torch.zeros(81, 64), torch.zeros(256, 81))
+    with pytest.raises(E, match="weight has shape"):
+        dsa3d.linear_backward(x, torch.zeros(81, 32), torch.zeros(256, 81))
+    with pytest.raises(E, match="dy has shape"):
+        dsa3d.linear_backward(x, torch.zeros(81, 64), torch.zeros(256, 80))
+
