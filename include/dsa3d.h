@@ -94,8 +94,10 @@ enum {
      tolerances; used by the tests to cover both kernel families on one input. */
   DSA3D_FLAG_GENERIC_KERNELS = 1,
   /* Backward only (dsa3d_backward_ex, dsa3d_backward_heads): use the window starts,
-     buckets and query-side schedules that the forward call just before it built in the
-     same workspace, instead of building them again.  The caller guarantees that the
+     buckets and query-side row tiles that the forward call just before it built in the
+     same workspace, instead of building them again (the pass schedules of the dQ
+     kernel, which holds fewer row tiles in flight than the forward, are still built;
+     they overwrite the forward's in the workspace).  The caller guarantees that the
      forward ran on this stream with the same workspace pointer and size (sized for the
      backward), offsets (same values), geometry, dtype, head_dim and
      DSA3D_FLAG_GENERIC_KERNELS bit, and that nothing wrote the workspace in between;

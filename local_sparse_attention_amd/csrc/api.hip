@@ -65,7 +65,7 @@ int run_forward(const void* q, const void* k, const void* v, const int32_t* offs
   workspace_layout(g, false, workspace, &p);
   if (events) (void)hipEventRecord(events[0], stream);
   const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && fwd_qs_eligible(g, dtype, head_dim);
-  if (launch_prep(offsets, g, p, qs, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (launch_prep(offsets, g, p, qs, QS_SLOTS_FWD, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   if (events) (void)hipEventRecord(events[1], stream);
   AttnArgs a = {};
   a.q = q; a.k = k; a.v = v;
@@ -114,9 +114,12 @@ int run_backward(const void* q, const void* k, const void* v, const int32_t* off
   const bool kv_tube = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dkdv_tube_eligible(g, dtype, head_dim);
   const bool qs = !(flags & DSA3D_FLAG_GENERIC_KERNELS) && dq_qs_eligible(g, dtype, head_dim);
   const bool sched_built = reuse && fwd_qs_eligible(g, dtype, head_dim);
-  if (!reuse && launch_prep(offsets, g, p, qs, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (!reuse && launch_prep(offsets, g, p, qs, QS_SLOTS, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   if (kv_tube && launch_kv_items(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
-  if (qs && reuse && !sched_built && launch_qsched(g, p, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  // dQ holds fewer row tiles in flight than the forward: with the forward's tiles in the
+  // workspace only the pass schedules are built again, for dQ's slots
+  if (qs && reuse && !sched_built && launch_qsched(g, p, QS_SLOTS, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
+  if (qs && sched_built && launch_sched_fill(g, p, QS_SLOTS, stream) != hipSuccess) return DSA3D_ERR_LAUNCH;
   const AttnArgs a = backward_args(q, k, v, out, lse, dout, scale, dq, dk, dv);
   // Delta = rowsum(dO * O) of every head for both kernels (the per-group dQ kernel makes
   // its own head's)

@@ -6,7 +6,7 @@
 // qsched.hip).  Every frame's key tile -- the (4 + ky - 1) x (4 + kx - 1) keys
 // anchored at (4 by, 4 bx), in NBY x NBX blocks of 4 x 4 -- is staged once into an
 // LDS ring with direct global->LDS loads (issued by two loader waves) and read by
-// all QS_SLOTS row tiles in flight (one per compute wave), which belong to the kt
+// all QS_SLOTS_FWD row tiles in flight (one per compute wave), which belong to the kt
 // slices that read that frame.
 //
 // Per frame and busy slot (a wave whose slot holds no tile this frame skips it):
@@ -35,16 +35,18 @@ struct FwdCfg {
   static constexpr int QTILE = 16 * 128;            // one phase of a staged row tile
 };
 
-// Row-tile slots per compute wave: with one (the default), the QS_SLOTS slots take
-// 8 waves (2 per SIMD, plus the loaders), so one wave's LDS and scalar work issues
-// beside the other's VALU and MFMA work; with two, a K / V fragment read from LDS
-// feeds the MFMAs of both slots, but four waves hide latency poorly (measured
-// slower).
+// Row-tile slots per compute wave: with one (the default), the QS_SLOTS_FWD = 10
+// slots take 10 waves (with the two loaders, 3 per SIMD: the 168-register cap that 8
+// compute waves and the loaders already had), so one wave's LDS and scalar work
+// issues beside another's VALU and MFMA work; ten slots rather than eight leave fewer
+// tiles waiting for a further pass over the frames (11% fewer frames swept at the
+// 256-frame workload).  With two slots a wave, a K / V fragment read from LDS feeds
+// the MFMAs of both, but five waves hide latency poorly (measured slower).
 #ifndef DSA3D_FWD_NS
 #define DSA3D_FWD_NS 1
 #endif
 constexpr int FWD_NS = DSA3D_FWD_NS;
-constexpr int FWD_NW = QS_SLOTS / FWD_NS;  // compute waves
+constexpr int FWD_NW = QS_SLOTS_FWD / FWD_NS;  // compute waves
 constexpr int FWD_LW = 2;                  // loader waves
 
 template <int D, int NBY, int NBX>
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
   using C = FwdCfg<D, NBY, NBX>;
   constexpr int NS = FWD_NS;
   __shared__ __attribute__((aligned(1024))) char ring[C::NBUF][C::TILE];
-  __shared__ __attribute__((aligned(1024))) char stage[QS_SLOTS][C::NPH * C::QTILE];
+  __shared__ __attribute__((aligned(1024))) char stage[QS_SLOTS_FWD][C::NPH * C::QTILE];
   __shared__ QsPass T;
 
   const int nbc = g.nby * g.nbx, nw = qs_items(g);
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(64 * (FWD_NW + FWD_LW)) void k_forward_qs(const u16
           const int f = __builtin_amdgcn_readfirstlane(T.frames[fi]);
           if (ph == 0) {
 #pragma unroll
-            for (int sl = LWI; sl < QS_SLOTS; sl += FWD_LW) {
+            for (int sl = LWI; sl < QS_SLOTS_FWD; sl += FWD_LW) {
               const int t = __builtin_amdgcn_readfirstlane((int)T.act[fi][sl]);
               if (t >= 0) issue_rows<D>(stage[sl], q, T.ids[t], g, h, lane);
             }

@@ -51,7 +51,7 @@ size_t workspace_layout(const Geom& g, bool backward, char* base, Prep* p);
 hipError_t launch_window_starts(const int32_t* off, const Geom& g, int32_t* starts3, hipStream_t s);
 // The bucketing (window starts, sort, cell_ptr, groups) and, with qs, the query-side
 // work lists of the frame-sweeping kernels (launch_qsched() in one pass with it).
-hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, bool qs, hipStream_t s);
+hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, bool qs, int nslots, hipStream_t s);
 // In-place exclusive scan of n uint32 values: one workgroup, or, given part
 // (scan_part_words(n) words of scratch) and more than a few chunks, a scan per chunk
 // on its own workgroup, a scan of the chunk totals and an add.
@@ -90,6 +90,9 @@ inline size_t max_kv_items(const Geom& g) {
 // queries of one slice, or the leftover queries (fewer than 16 each) of up to
 // QS_SPAN consecutive slices; its descriptor is QT_INTS ints.
 constexpr int QS_TS = 32, QS_SLOTS = 8, QS_MAXT = 64, QS_SPAN = 3;
+// The forward holds QS_SLOTS_FWD row tiles in flight (its schedules are built for that many
+// slots), dQ QS_SLOTS; pass tables are sized for the larger.
+constexpr int QS_SLOTS_FWD = 10, QS_SLOTS_MAX = 10;
 constexpr int QT_INTS = 2 + 3 * QS_SPAN;
 __host__ __device__ inline bool qs_geometry(const Geom& g) { return g.kt >= 3 && g.kt <= 16 && g.ky <= 9 && g.kx <= 9; }
 __host__ __device__ inline int qs_items(const Geom& g) { return g.nby * g.nbx * ((g.Lt + QS_TS - 1) / QS_TS); }
@@ -103,9 +106,10 @@ inline size_t qs_ints(const Geom& g, int max_groups) {
 // (with blob_groups also the blob group counts into goff, see k_blob_ngroups)
 hipError_t launch_qtile_count(const Geom& g, const Prep& p, hipStream_t s, bool blob_groups = false);
 hipError_t launch_groups_qtiles(const Geom& g, const Prep& p, bool groups, bool qtiles, hipStream_t s);
-hipError_t launch_qsched_rows(const Geom& g, const Prep& p, hipStream_t s);
+hipError_t launch_qsched_rows(const Geom& g, const Prep& p, int nslots, hipStream_t s);
+hipError_t launch_sched_fill(const Geom& g, const Prep& p, int nslots, hipStream_t s);
 // All of it for a bucketing built earlier.
-hipError_t launch_qsched(const Geom& g, const Prep& p, hipStream_t s);
+hipError_t launch_qsched(const Geom& g, const Prep& p, int nslots, hipStream_t s);
 
 struct AttnArgs {
   const void* q;

@@ -457,7 +457,7 @@ hipError_t launch_cell_ptr(const uint32_t* sorted_keys, int seglen, int nseg, in
 //   the radix passes, cell_ptr, the blob group counts [with the row tile counts],
 //   the scans of the group [and tile] counts, the groups [and row tiles],
 //   [the tile rows and the schedules].
-hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, bool qs, hipStream_t s) {
+hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, bool qs, int nslots, hipStream_t s) {
   const int n = g.N * g.ph, nblobs = g.nblobs * g.ph;
   const int nbs = (g.N + RADIX_TILE - 1) / RADIX_TILE;
   const bool fused = nbs <= RADIX_RAW_NBS;  // the scatter then needs the raw counts the fused kernel leaves
@@ -482,7 +482,7 @@ hipError_t launch_prep(const int32_t* off, const Geom& g, Prep& p, bool qs, hipS
   }
   if (e != hipSuccess) return e;
   if ((e = launch_groups_qtiles(g, p, true, qs, s)) != hipSuccess) return e;
-  return qs ? launch_qsched_rows(g, p, s) : hipSuccess;
+  return qs ? launch_qsched_rows(g, p, nslots, s) : hipSuccess;
 }
 
 }  // namespace dsa3d

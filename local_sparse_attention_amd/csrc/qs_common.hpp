@@ -14,7 +14,7 @@ struct QsPass {
   signed char dt[QS_MAXT][16];      // their slices minus the tile's first slice
   int tau[QS_MAXT];                 // first slice of each tile
   int tlast[QS_MAXT];               // last slice of each tile
-  short act[QS_TS + 16][QS_SLOTS];  // tile activated at (frame index, slot), or -1
+  short act[QS_TS + 16][QS_SLOTS_MAX];  // tile activated at (frame index, slot), or -1
   int frames[QS_TS + 16];           // frames swept by the pass
   int hdr[2];                       // frame count, tile count
 };
@@ -26,7 +26,7 @@ __device__ __forceinline__ void load_pass(QsPass& T, const int*& sp, const Prep&
     T.hdr[0] = sp[0];
     T.hdr[1] = sp[1];
   }
-  for (int i = tid; i < (QS_TS + 16) * QS_SLOTS; i += nthreads) (&T.act[0][0])[i] = -1;
+  for (int i = tid; i < (QS_TS + 16) * QS_SLOTS_MAX; i += nthreads) (&T.act[0][0])[i] = -1;
   __syncthreads();
   const int nf = T.hdr[0], nt = T.hdr[1];
   for (int i = tid; i < nf; i += nthreads) T.frames[i] = sp[2 + i];

@@ -17,7 +17,7 @@
 // hold each tile's query tokens and window starts (sy, sx), padded to 16 with
 // token 0 and a start no key matches.
 //
-// Schedules: a work item's row tiles get one of QS_SLOTS slots for the frames they
+// Schedules: a work item's row tiles get one of nslots slots for the frames they
 // read; greedy, in tile order, a tile takes the slot that has been free the longest
 // (a slot is free again once its tile has read its last frame).  Tiles that find
 // no free slot at their first frame wait for a further pass over the frames.
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void k_tile_fill(const int* __restrict__ perm,
 // whole wave runs the pass on the scalar unit.
 template <typename Tiles>
 __device__ int build_schedule(const Geom& g, int w, int t0, int ntiles, const Tiles& tiles, int* out, int* work,
-                              int lane, int nlanes) {
+                              int lane, int nlanes, int nslots) {
   const int nbc = g.nby * g.nbx;
   const int chunk = (w % qs_items(g)) / nbc;
   const int c0 = chunk * QS_TS, ns = min(QS_TS, g.Lt - c0);
@@ -178,8 +178,8 @@ __device__ int build_schedule(const Geom& g, int w, int t0, int ntiles, const Ti
   }
   int size = 1, npass = 0;
   for (;;) {
-    int free_at[QS_SLOTS];
-    for (int s = 0; s < QS_SLOTS; ++s) free_at[s] = -(1 << 29);
+    int free_at[QS_SLOTS_MAX];
+    for (int s = 0; s < QS_SLOTS_MAX; ++s) free_at[s] = s < nslots ? -(1 << 29) : (1 << 30);
     int nf = 0, nt = 0, fmax = -1;
     int* hdr = out ? out + size : nullptr;
     int* frames = hdr ? hdr + 2 : nullptr;
@@ -190,7 +190,7 @@ __device__ int build_schedule(const Geom& g, int w, int t0, int ntiles, const Ti
       const int tau = c0 + i;
       while (cur[i] < lim[i] && nt < QS_MAXT) {
         int best = -1;
-        for (int s = 0; s < QS_SLOTS; ++s)
+        for (int s = 0; s < QS_SLOTS_MAX; ++s)
           if (free_at[s] <= tau && (best < 0 || free_at[s] < free_at[best])) best = s;
         if (best < 0) break;
         const int ti = cur[i];
@@ -226,22 +226,22 @@ __device__ int build_schedule(const Geom& g, int w, int t0, int ntiles, const Ti
 
 // The same schedule for an item of at most 128 tiles, held in registers: tile t's
 // first / last slice in lane t mod 64 of ta / tb [t / 64] (read back with readlane),
-// the slots' first free frames in lanes 0-7 of one register (the choice of slot by a
+// the slots' first free frames in lanes 0 .. nslots - 1 of one register (the choice of slot by a
 // DPP minimum), the tiles already scheduled in two 64-bit masks, a pass's frames (fewer than 64:
 // QS_TS + kt - 1) and tile entries (at most QS_MAXT = 64) collected one per lane
 // (lane i keeps the i-th) and stored at the pass's end by one vector store each.  Tiles are
 // visited in order; once a tile finds no free slot, the rest of its slice waits for
 // the next pass, as above.
 static_assert(QS_MAXT <= 64 && QS_TS + 16 - 1 < 64, "one lane per frame and per tile entry");
-static_assert(QS_SLOTS == 8, "the slots' free frames sit in lanes 0-7 (one half row for DPP)");
+static_assert(QS_SLOTS_MAX <= 16, "the slots' free frames sit in lanes 0-15 (one row for DPP)");
 __device__ int build_schedule_regs(const Geom& g, int t0, int ntiles, int ta0, int tb0, int ta1, int tb1, int* out,
-                                   int lane) {
+                                   int lane, int nslots) {
   constexpr int NOSLOT = 0x7fffffff;  // above every frame number
   uint64_t done0 = 0, done1 = 0;
   int size = 1, npass = 0;
   for (;;) {
     // slot s's first free frame in lane s (lanes past the slots: NOSLOT)
-    int fa = lane < QS_SLOTS ? -(1 << 29) : NOSLOT;
+    int fa = lane < nslots ? -(1 << 29) : NOSLOT;
     int nf = 0, nt = 0, fmax = -1, blocked = -(1 << 30);
     int fr = 0, e0 = 0, e1 = 0, e2 = 0, e3 = 0;
     for (int t = 0; t < ntiles && nt < QS_MAXT; ++t) {
@@ -251,19 +251,20 @@ __device__ int build_schedule_regs(const Geom& g, int t0, int ntiles, int ta0, i
       const int tau = __builtin_amdgcn_readlane(hi ? ta1 : ta0, bit);
       if (tau == blocked) continue;
       // the free slot that has been free the longest (the lowest such slot on a tie):
-      // the minimum over lanes 0-7 by DPP (within quads, then across the two quads of
-      // the half row), then the first lane that holds it
+      // the minimum over lanes 0-15 by DPP (within quads, across the two quads of each
+      // half row, then across the two half rows), then the first lane that holds it
       const int cand = fa <= tau ? fa : NOSLOT;
       int m = cand;
       m = min(m, __builtin_amdgcn_update_dpp(NOSLOT, m, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
       m = min(m, __builtin_amdgcn_update_dpp(NOSLOT, m, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
       m = min(m, __builtin_amdgcn_update_dpp(NOSLOT, m, 0x141, 0xF, 0xF, false));  // row_half_mirror
+      m = min(m, __builtin_amdgcn_update_dpp(NOSLOT, m, 0x140, 0xF, 0xF, false));  // row_mirror
       const int mn = __builtin_amdgcn_readlane(m, 0);
       if (mn == NOSLOT) {
         blocked = tau;
         continue;
       }
-      const int best = __builtin_ctzll(__ballot(lane < QS_SLOTS && cand == mn));
+      const int best = __builtin_ctzll(__ballot(lane < nslots && cand == mn));
       const int tlast = __builtin_amdgcn_readlane(hi ? tb1 : tb0, bit);
       const int fi = tau > fmax ? nf : nf - 1 - (fmax - tau);
       for (int f = max(tau, fmax + 1); f < tlast + g.kt; ++f, ++nf) fr = lane == nf ? f : fr;
@@ -332,7 +333,8 @@ __device__ __forceinline__ int sched_offset(const Geom& g, const int* qt_off, in
 constexpr int SCHED_WAVES = 4, SCHED_CACHE = 1024;
 __global__ __launch_bounds__(64 * SCHED_WAVES) void k_sched_fill(Geom g, const int* __restrict__ qt,
                                                                  const int* __restrict__ qt_off, int nw,
-                                                                 int* __restrict__ off, int* __restrict__ sched) {
+                                                                 int* __restrict__ off, int* __restrict__ sched,
+                                                                 int nslots) {
   __shared__ int2 cache[SCHED_WAVES][SCHED_CACHE];
   __shared__ int work[SCHED_WAVES][4 * QS_MAXT];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -359,11 +361,11 @@ __global__ __launch_bounds__(64 * SCHED_WAVES) void k_sched_fill(Geom g, const i
   if (live) {
     int* out = sched + sched_offset(g, qt_off, w);
     if (regs)
-      build_schedule_regs(g, t0, ntiles, ta0, tb0, ta1, tb1, out, lane);
+      build_schedule_regs(g, t0, ntiles, ta0, tb0, ta1, tb1, out, lane, nslots);
     else if (cached)
-      build_schedule(g, w, t0, ntiles, TilesLds{cache[wv]}, out, work[wv], lane, 64);
+      build_schedule(g, w, t0, ntiles, TilesLds{cache[wv]}, out, work[wv], lane, 64, nslots);
     else
-      build_schedule(g, w, t0, ntiles, TilesGlobal{qt + (size_t)t0 * QT_INTS}, out, work[wv], lane, 64);
+      build_schedule(g, w, t0, ntiles, TilesGlobal{qt + (size_t)t0 * QT_INTS}, out, work[wv], lane, 64, nslots);
   }
 }
 
@@ -384,22 +386,27 @@ hipError_t launch_groups_qtiles(const Geom& g, const Prep& p, bool groups, bool 
   return hipGetLastError();
 }
 
-hipError_t launch_qsched_rows(const Geom& g, const Prep& p, hipStream_t s) {
+hipError_t launch_sched_fill(const Geom& g, const Prep& p, int nslots, hipStream_t s) {
   const int nw = qs_items(g) * g.ph;
-  k_tile_fill<<<(unsigned)((p.max_groups + 15) / 16), 256, 0, s>>>(p.perm, p.starts, p.qt, p.qt_off + nw, g.N,
-                                                                   p.tq_ids, p.tq_st, p.tq_dt);
   k_sched_fill<<<(unsigned)((nw + 1 + SCHED_WAVES - 1) / SCHED_WAVES), 64 * SCHED_WAVES, 0, s>>>(g, p.qt, p.qt_off, nw,
-                                                                                              p.qs_off, p.qs);
+                                                                                              p.qs_off, p.qs, nslots);
   return hipGetLastError();
 }
 
-hipError_t launch_qsched(const Geom& g, const Prep& p, hipStream_t s) {
+hipError_t launch_qsched_rows(const Geom& g, const Prep& p, int nslots, hipStream_t s) {
+  const int nw = qs_items(g) * g.ph;
+  k_tile_fill<<<(unsigned)((p.max_groups + 15) / 16), 256, 0, s>>>(p.perm, p.starts, p.qt, p.qt_off + nw, g.N,
+                                                                   p.tq_ids, p.tq_st, p.tq_dt);
+  return launch_sched_fill(g, p, nslots, s);
+}
+
+hipError_t launch_qsched(const Geom& g, const Prep& p, int nslots, hipStream_t s) {
   hipError_t e = launch_qtile_count(g, p, s);
   if (e != hipSuccess) return e;
   e = launch_scan_excl(reinterpret_cast<uint32_t*>(p.qt_off), qs_items(g) * g.ph + 1, s, p.scan_part);
   if (e != hipSuccess) return e;
   if ((e = launch_groups_qtiles(g, p, false, true, s)) != hipSuccess) return e;
-  return launch_qsched_rows(g, p, s);
+  return launch_qsched_rows(g, p, nslots, s);
 }
 
 }  // namespace dsa3d
